@@ -1,0 +1,309 @@
+"""Routing plan, permutation, the two expert projections, activation, requantization, combine.
+
+Test infrastructure (see the package docstring).  Everything is float64 except the rounding
+points the pages name (BF16 intermediate and expert outputs, FP32 combine), which are applied
+exactly.  The projections are computed exactly: every dequantized operand is an integer times
+2**-10 (quant.dequantize_int), so a dot product is an exact int64 sum times 2**-20, rounded once
+to float64.
+"""
+
+import numpy as np
+
+from .formats import bf16_bits_to_f32, round_to_bf16
+from .quant import SCALE_FIXED, SCALE_PER_GROUP, dequantize_int, quantize_nvfp4
+
+ACT_SWIGLU = 0
+ACT_RELU2 = 1
+
+_TWO_M20 = 2.0 ** -20
+
+
+def _round_up(v, a):
+    return (v + a - 1) // a * a
+
+
+def plan_capacity(M, top_k, num_local_experts, block_m):
+    """Largest plan extent any routing can produce (capacity of the plan arrays).
+
+    Each non-empty local segment adds at most block_m - 1 padding rows, and at most
+    min(num_local_experts, M * top_k) segments are non-empty.
+    """
+    A = M * top_k
+    return _round_up(A + min(num_local_experts, A) * (block_m - 1), block_m)
+
+
+def moe_plan(topk_ids, num_experts, local_expert_offset, num_local_experts, block_m):
+    """The aligned expert-sorted routing plan (alphamoe_nvfp4_aligned_moe page, plan paragraph).
+
+    A slot (t, j) is routed to this device when its expert id lies in
+    [local_expert_offset, local_expert_offset + num_local_experts) (CudnnGroupedGemmNvfp4Config:
+    non-local assignments are masked out; FrostLowLatencyConfig: ids outside the routed range mark
+    unrouted slots; Megatron-Core: -1 entries contribute zero).  Readings taken where the pages
+    leave the plan open:
+    * segments in ascending local expert id; each padded to a multiple of block_m; empty experts
+      get no blocks;
+    * a plan entry is the flat slot index f = t * top_k + j, ascending inside a segment;
+      padding entries and entries in [extent, capacity) hold the sentinel M * top_k;
+    * expert_ids[b] is the local expert id of block b, -1 past the extent;
+    * token_to_row[t, j] is the plan position of slot (t, j), -1 for unrouted slots.
+    Returns (sorted_token_ids int32 [cap], expert_ids int32 [cap/block_m],
+             num_tokens_post_padded int, token_to_row int32 [M, top_k]).
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    M, k = ids.shape
+    cap = plan_capacity(M, k, num_local_experts, block_m)
+    sentinel = M * k
+    flat = ids.reshape(-1)
+    local = flat - local_expert_offset
+    valid = (flat >= 0) & (flat < num_experts) & (local >= 0) & (local < num_local_experts)
+    sorted_ids = np.full(cap, sentinel, dtype=np.int64)
+    expert_ids = np.full(cap // block_m if block_m else 0, -1, dtype=np.int64)
+    token_to_row = np.full(M * k, -1, dtype=np.int64)
+    pos = 0
+    for e in range(num_local_experts):
+        fs = np.nonzero(valid & (local == e))[0]          # ascending flat indices
+        if len(fs) == 0:
+            continue
+        seg = _round_up(len(fs), block_m)
+        sorted_ids[pos:pos + len(fs)] = fs
+        token_to_row[fs] = pos + np.arange(len(fs))
+        expert_ids[pos // block_m:(pos + seg) // block_m] = e
+        pos += seg
+    return (sorted_ids.astype(np.int32), expert_ids.astype(np.int32), int(pos),
+            token_to_row.reshape(M, k).astype(np.int32))
+
+
+def moe_permute(q, sf, dec_scale, sorted_token_ids, num_tokens_post_padded, top_k):
+    """Gather quantized token rows into plan order (CudnnGroupedGemmNvfp4Config: rows and scale
+    rows are permuted into expert order).  Row r < extent takes token f // top_k of its entry f;
+    sentinel rows and rows past the extent are all-zero bytes with scale 0.
+    Returns (q_perm [cap, H/2], sf_perm [cap, H/16], s_perm float32 [cap]).
+    """
+    q = np.asarray(q)
+    sf = np.asarray(sf)
+    M = q.shape[0]
+    ent = np.asarray(sorted_token_ids, dtype=np.int64)
+    cap = ent.shape[0]
+    qp = np.zeros((cap, q.shape[1]), dtype=np.uint8)
+    sp = np.zeros((cap, sf.shape[1]), dtype=np.uint8)
+    s = np.zeros(cap, dtype=np.float32)
+    for r in range(min(num_tokens_post_padded, cap)):
+        f = ent[r]
+        if f < M * top_k:
+            t = f // top_k
+            qp[r] = q[t]
+            sp[r] = sf[t]
+            s[r] = dec_scale[t]
+    return qp, sp, s
+
+
+def quantize_expert_weights(w_bf16_bits):
+    """Per-expert NVFP4 of a BF16 stack [E, rows, cols]: one encode scale per expert matrix
+    (Megatron-Core: "one FP32 global scale per expert"; _global_encode_scale / _quantize_expert).
+    Returns (q [E, rows, cols/2], sf [E, rows, cols/16], alpha float32 [E]) where alpha is the
+    decode scale of each expert matrix.
+    """
+    w = bf16_bits_to_f32(w_bf16_bits)
+    E, R, C = w.shape
+    q, sf, dec = quantize_nvfp4(w.reshape(E * R, C), SCALE_PER_GROUP, group_rows=R)
+    return q.reshape(E, R, C // 2), sf.reshape(E, R, C // 16), dec.astype(np.float32)
+
+
+def _activation(pre, I, act):
+    """Typed activation on float64 pre-activations [rows, N1].
+
+    SwiGLU with default scalars (CudnnGroupedGemmNvfp4Config activation bullet): W1 rows are
+    [gate; up] (alphamoe page: "conventional [gate; up] row order"), h = silu(gate) * up with
+    silu(g) = g / (1 + exp(-g)).  Squared ReLU (Megatron-Core module): h = max(pre, 0)**2.
+    """
+    if act == ACT_SWIGLU:
+        g = pre[:, :I]
+        u = pre[:, I:2 * I]
+        with np.errstate(over="ignore"):
+            return g / (1.0 + np.exp(-g)) * u
+    if act == ACT_RELU2:
+        return np.maximum(pre, 0.0) ** 2
+    raise ValueError("unknown activation")
+
+
+def expert_rows_forward(a_q, a_sf, a_dec, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate, alpha1_up,
+                        alpha2, c2, act):
+    """One expert applied to rows of NVFP4 activations (the rows all route to this expert).
+
+    a_q [R, H/2], a_sf [R, H/16], a_dec float32 [R]; w1 [N1, H/2] / [N1, H/16];
+    w2 [H, I/2] / [H, I/16]; alpha1_gate, alpha1_up, alpha2: this expert's FP32 scales.
+    Steps (pages' order: GEMM1, typed activation, requantize, GEMM2):
+      pre  = (sum_h deq(a) deq(w1)) * a_dec * alpha1   (gate rows * alpha1_gate, up rows *
+             alpha1_up: alphamoe page, output1_scale_gate_scalar / output1_scale_scalar)
+      h    = activation(pre), rounded to BF16 (FrostLowLatencyConfig: intermediate rounding)
+      hq   = NVFP4 of h with fixed encode scale c2 (CudnnGroupedGemmNvfp4Config: "global scale
+             of one"; c2 = 1 unless a caller folds another constant in)
+      y    = bf16((sum_i deq(hq) deq(w2)) * dec(c2) * alpha2)  (alphamoe page,
+             output2_scale_scalar; expert outputs BF16 per FrostLowLatencyConfig)
+    Returns dict(pre float64 [R, N1], h float64 (BF16 values) [R, I], hq, hsf, y float64
+    (BF16 values) [R, H]).
+    """
+    R = a_q.shape[0]
+    N1 = w1_q.shape[0]
+    I = w2_q.shape[1] * 2
+    gated = (act == ACT_SWIGLU)
+    if N1 != (2 * I if gated else I):
+        raise ValueError("W1 rows do not match the activation")
+    s1 = dequantize_int(a_q, a_sf) @ dequantize_int(w1_q, w1_sf).T          # exact int64
+    # Non-gated FC1 has a single projection; it takes the up/FC1 scale (output1_scale_scalar).
+    alpha_rows = np.full(N1, float(alpha1_up), dtype=np.float64)
+    if gated:
+        alpha_rows[:I] = float(alpha1_gate)
+    pre = (s1.astype(np.float64) * _TWO_M20) * np.asarray(a_dec, np.float64).reshape(R, 1)
+    pre = pre * alpha_rows.reshape(1, N1)
+    h = round_to_bf16(_activation(pre, I, act))
+    hq, hsf, hdec = quantize_nvfp4(h.astype(np.float32), SCALE_FIXED, fixed_encode_scale=c2)
+    s2 = dequantize_int(hq, hsf) @ dequantize_int(w2_q, w2_sf).T            # exact int64
+    y = round_to_bf16((s2.astype(np.float64) * _TWO_M20) * float(hdec[0]) * float(alpha2))
+    return dict(pre=pre, h=h, hq=hq, hsf=hsf, y=y)
+
+
+def combine(out0_bits, y_rows, topk_weights, token_to_row, routed_scaling_factor=1.0):
+    """Finalize: out[t] = bf16(f32(out0[t]) (+) sum_j fl32(w[t,j] * y[row(t,j)])).
+
+    FrostLowLatencyConfig: "ordered, separate FP32 multiplication and addition"; alphamoe page:
+    contributions are added to the existing out values in FP32, converted to BF16 once.
+    Reading taken: j ascending; unrouted slots (token_to_row == -1) are skipped and their weights
+    never read (FrostLowLatencyConfig: scores of unrouted slots may be NaN/Inf);
+    routed_scaling_factor multiplies each product when it is not 1 (alphamoe page: applied to each
+    routed contribution); no flush of subnormals.
+    y_rows: float64 BF16 values indexed by plan row (dict or array).  Returns uint16 BF16 bits.
+    """
+    acc = bf16_bits_to_f32(out0_bits).astype(np.float32).copy()
+    w = np.asarray(topk_weights, dtype=np.float32)
+    ttr = np.asarray(token_to_row)
+    M, k = ttr.shape
+    rsf = np.float32(routed_scaling_factor)
+    for t in range(M):
+        for j in range(k):
+            r = int(ttr[t, j])
+            if r < 0:
+                continue
+            p = np.float32(w[t, j]) * np.asarray(y_rows[r], dtype=np.float32)     # fp32 product
+            if rsf != np.float32(1.0):
+                p = (p * rsf).astype(np.float32)
+            acc[t] = (acc[t] + p).astype(np.float32)                             # fp32 sum
+    r = round_to_bf16(acc.astype(np.float64)).astype(np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _experts_from(weights):
+    """Accept either a tuple of stacked arrays or a callable e -> per-expert tuple."""
+    if callable(weights):
+        return weights
+
+    w1_q, w1_sf, w2_q, w2_sf = weights
+    return lambda e: (w1_q[e], w1_sf[e], w2_q[e], w2_sf[e])
+
+
+def fused_moe_nvfp4(a_q, a_sf, a_dec, weights, alpha1_gate, alpha1_up, alpha2, c2,
+                    sorted_token_ids, expert_ids, num_tokens_post_padded, token_to_row,
+                    topk_weights, top_k, block_m, act, routed_scaling_factor=1.0, out0_bits=None,
+                    do_finalize=True, rows=None):
+    """Plan-driven forward: permute, per-block expert compute, finalize (or the unfinalized triple).
+
+    weights: (w1_q [E,N1,H/2], w1_sf [E,N1,H/16], w2_q [E,H,I/2], w2_sf [E,H,I/16]) indexed by
+    local expert id, or a callable local id -> that tuple.  ``rows``: optional iterable of plan
+    rows to compute (the others are skipped; for sampling large workloads).
+    Returns dict(out (uint16 [M,H] or None), y {row: BF16 float64 [H]}, pre {row: [N1]},
+    h {row: [I]}, hq {row}, hsf {row}, unfinalized=(y, topk_weights, token_to_row)).
+    """
+    get = _experts_from(weights)
+    M = a_q.shape[0]
+    H = a_q.shape[1] * 2
+    qp, sp, spd = moe_permute(a_q, a_sf, a_dec, sorted_token_ids, num_tokens_post_padded, top_k)
+    ent = np.asarray(sorted_token_ids, dtype=np.int64)
+    eids = np.asarray(expert_ids, dtype=np.int64)
+    wanted = None if rows is None else set(int(r) for r in rows)
+    by_expert = {}
+    for b in range(num_tokens_post_padded // block_m):
+        e = int(eids[b])
+        for r in range(b * block_m, (b + 1) * block_m):
+            if ent[r] >= M * top_k:
+                continue                                   # padding rows contribute nothing
+            if wanted is not None and r not in wanted:
+                continue
+            by_expert.setdefault(e, []).append(r)
+    res = dict(y={}, pre={}, h={}, hq={}, hsf={})
+    for e, rs in sorted(by_expert.items()):
+        w1q, w1s, w2q, w2s = get(e)
+        rs = np.array(rs)
+        o = expert_rows_forward(qp[rs], sp[rs], spd[rs], w1q, w1s, w2q, w2s,
+                                alpha1_gate[e], alpha1_up[e], alpha2[e], c2, act)
+        for i, r in enumerate(rs):
+            res["y"][int(r)] = o["y"][i]
+            res["pre"][int(r)] = o["pre"][i]
+            res["h"][int(r)] = o["h"][i]
+            res["hq"][int(r)] = o["hq"][i]
+            res["hsf"][int(r)] = o["hsf"][i]
+    res["unfinalized"] = (res["y"], np.asarray(topk_weights, np.float32), np.asarray(token_to_row))
+    res["out"] = None
+    if do_finalize and rows is None:
+        if out0_bits is None:
+            out0_bits = np.zeros((M, H), dtype=np.uint16)
+        res["out"] = combine(out0_bits, res["y"], topk_weights, token_to_row,
+                             routed_scaling_factor)
+    return res
+
+
+def dense_loop_moe(a_q, a_sf, a_dec, weights, alpha1_gate, alpha1_up, alpha2, c2, topk_ids,
+                   topk_weights, num_experts, local_expert_offset, num_local_experts, act,
+                   routed_scaling_factor=1.0, out0_bits=None):
+    """Per-token reference with no plan: for each token and each of its slots in order, run the
+    routed expert on that token's row and combine (ordered FP32 multiply then add).
+    Must equal fused_moe_nvfp4 bit for bit."""
+    get = _experts_from(weights)
+    M, k = np.asarray(topk_ids).shape
+    H = a_q.shape[1] * 2
+    acc = bf16_bits_to_f32(np.zeros((M, H), np.uint16) if out0_bits is None else out0_bits)
+    acc = acc.astype(np.float32).copy()
+    w = np.asarray(topk_weights, dtype=np.float32)
+    rsf = np.float32(routed_scaling_factor)
+    for t in range(M):
+        for j in range(k):
+            gid = int(topk_ids[t, j])
+            e = gid - local_expert_offset
+            if not (0 <= gid < num_experts and 0 <= e < num_local_experts):
+                continue
+            w1q, w1s, w2q, w2s = get(e)
+            o = expert_rows_forward(a_q[t:t + 1], a_sf[t:t + 1], np.asarray(a_dec)[t:t + 1],
+                                    w1q, w1s, w2q, w2s, alpha1_gate[e], alpha1_up[e], alpha2[e],
+                                    c2, act)
+            p = np.float32(w[t, j]) * o["y"][0].astype(np.float32)
+            if rsf != np.float32(1.0):
+                p = (p * rsf).astype(np.float32)
+            acc[t] = (acc[t] + p).astype(np.float32)
+    r = round_to_bf16(acc.astype(np.float64)).astype(np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def unquantized_moe_f64(x_bits, w1_bits_of, w2_bits_of, topk_ids, topk_weights, num_experts,
+                        local_expert_offset, num_local_experts, act, routed_scaling_factor=1.0,
+                        tokens=None):
+    """The same routed MoE with BF16 inputs and weights taken as float64 and no quantization or
+    intermediate rounding (reported alongside the NVFP4 result, not gated).
+    w1_bits_of(e) / w2_bits_of(e): BF16 bit arrays of local expert e."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    M, k = np.asarray(topk_ids).shape
+    toks = range(M) if tokens is None else tokens
+    out = {}
+    for t in toks:
+        acc = np.zeros(x.shape[1])
+        for j in range(k):
+            gid = int(topk_ids[t, j])
+            e = gid - local_expert_offset
+            if not (0 <= gid < num_experts and 0 <= e < num_local_experts):
+                continue
+            w1 = bf16_bits_to_f32(w1_bits_of(e)).astype(np.float64)
+            w2 = bf16_bits_to_f32(w2_bits_of(e)).astype(np.float64)
+            pre = (w1 @ x[t]).reshape(1, -1)
+            I = w2.shape[1]
+            h = _activation(pre, I, act)[0]
+            acc += float(topk_weights[t, j]) * routed_scaling_factor * (w2 @ h)
+        out[t] = acc
+    return out

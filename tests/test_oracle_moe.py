@@ -1,0 +1,356 @@
+"""Pins of the oracle's plan, permutation, expert projections, activation and combine.
+
+Sources by page title: "flashinfer.fused_moe.alphamoe_nvfp4_aligned_moe" (aligned plan arrays,
+[gate; up] row order, per-expert output scales, accumulation into out),
+"flashinfer.fused_moe.CudnnGroupedGemmNvfp4Config" (expert-sorted permutation, segments padded,
+masking of non-local experts, unfinalized triple, distinct experts per token),
+"flashinfer.fused_moe.FrostLowLatencyConfig" (BF16 intermediate and expert outputs, ordered
+separate FP32 multiply/add combine, unrouted slots ignored with their scores),
+Megatron-Core "core.inference.moe.flashinfer_nvfp4" (-1 routing entries contribute zero).
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.formats import bf16_bits_to_f32
+from synth import WORKLOADS, make_activations, make_routing, make_weights, to_bits
+from synth.workloads import Workload
+
+GOLDEN_COMBINE = os.path.join(os.path.dirname(__file__), "golden", "combine_order.txt")
+
+
+# ----------------------------------------------------------------------------- plan
+
+def _plan_bruteforce(ids, E, off, nloc, bm):
+    """Stable argsort of the local expert id over the flat slot index (a different algorithm)."""
+    flat = ids.reshape(-1).astype(np.int64)
+    loc = flat - off
+    ok = (flat >= 0) & (flat < E) & (loc >= 0) & (loc < nloc)
+    key = np.where(ok, loc, nloc)                        # unrouted slots sort last
+    order = np.argsort(key, kind="stable")
+    order = order[ok[order]]
+    rows, eids = [], []
+    for e in range(nloc):
+        seg = [int(f) for f in order if loc[f] == e]
+        if not seg:
+            continue
+        pad = -len(seg) % bm
+        rows += seg + [flat.size] * pad
+        eids += [e] * ((len(seg) + pad) // bm)
+    return rows, eids
+
+
+@pytest.mark.parametrize("bm", [8, 16, 128])
+@pytest.mark.parametrize("off,nloc", [(0, 8), (2, 4), (6, 2)])
+def test_plan_matches_bruteforce(bm, off, nloc):
+    rng = np.random.default_rng(bm + off)
+    M, k, E = 37, 3, 8
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
+    ids[3, 1] = -1
+    ids[5, 0] = 99
+    srt, eids, P, ttr = oracle.moe_plan(ids, E, off, nloc, bm)
+    rows, beids = _plan_bruteforce(ids, E, off, nloc, bm)
+    cap = oracle.plan_capacity(M, k, nloc, bm)
+    assert srt.shape == (cap,) and eids.shape == (cap // bm,)
+    assert P == len(rows) <= cap and P % bm == 0
+    assert list(srt[:P]) == rows
+    assert np.all(srt[P:] == M * k)
+    assert list(eids[:P // bm]) == beids and np.all(eids[P // bm:] == -1)
+    # token_to_row inverts the plan; unrouted slots are -1
+    for t in range(M):
+        for j in range(k):
+            r = ttr[t, j]
+            loc = ids[t, j] - off
+            if 0 <= ids[t, j] < E and 0 <= loc < nloc:
+                assert srt[r] == t * k + j and eids[r // bm] == loc
+            else:
+                assert r == -1
+
+
+def test_plan_capacity_is_tight_upper_bound():
+    # every non-empty expert needs bm-1 padding rows: the bound is reached
+    M, k, bm = 8, 1, 8
+    ids = np.arange(8, dtype=np.int32).reshape(8, 1)
+    _, _, P, _ = oracle.moe_plan(ids, 8, 0, 8, bm)
+    assert P == oracle.plan_capacity(M, k, 8, bm) == 64
+
+
+def test_plan_empty_and_all_masked():
+    ids = np.full((4, 2), -1, dtype=np.int32)
+    srt, eids, P, ttr = oracle.moe_plan(ids, 8, 0, 8, 8)
+    assert P == 0 and np.all(ttr == -1) and np.all(eids == -1)
+    srt, eids, P, ttr = oracle.moe_plan(np.zeros((0, 2), np.int32), 8, 0, 8, 8)
+    assert P == 0 and srt.shape == (0,)
+
+
+def test_generator_topk_distinct():
+    for name in ("tiny", "decode_ll", "decode", "prefill"):
+        ids, w = make_routing(WORKLOADS[name])
+        s = np.sort(ids, axis=1)
+        assert np.all(s[:, 1:] != s[:, :-1]), name
+        assert np.allclose(w.sum(axis=1), 1, atol=1e-6)
+    ids, w = make_routing(WORKLOADS["skewed_relu2"], M=2048)
+    s = np.sort(ids, axis=1)
+    assert np.all(s[:, 1:] != s[:, :-1])
+    assert ids.min() >= 0 and ids.max() < 288
+
+
+def test_permute_rows():
+    rng = np.random.default_rng(2)
+    M, k = 6, 2
+    q = rng.integers(0, 256, (M, 8), dtype=np.uint8)
+    sf = rng.integers(1, 127, (M, 1), dtype=np.uint8)
+    s = rng.uniform(0.1, 1, M).astype(np.float32)
+    ids = np.array([[0, 1], [1, 2], [2, 0], [0, 3], [3, 1], [2, 3]], np.int32)
+    srt, eids, P, ttr = oracle.moe_plan(ids, 4, 0, 4, 4)
+    qp, sp, spd = oracle.moe_permute(q, sf, s, srt, P, k)
+    for r in range(srt.shape[0]):
+        f = srt[r]
+        if r < P and f < M * k:
+            assert np.array_equal(qp[r], q[f // k]) and sp[r, 0] == sf[f // k, 0] and spd[r] == s[f // k]
+        else:
+            assert not qp[r].any() and not sp[r].any() and spd[r] == 0
+
+
+# ----------------------------------------------------------------------------- experts
+
+def _rand_nvfp4(rng, R, C):
+    q = rng.integers(0, 256, (R, C // 2), dtype=np.uint8)
+    sf = rng.integers(0x10, 0x60, (R, C // 16), dtype=np.uint8)
+    return q, sf
+
+
+def _exact_matrix(q, sf):
+    """Fractions from an explicit E2M1 dict and torch's float8_e4m3fn decode of the scales."""
+    e2m1 = {0: Fraction(0), 1: Fraction(1, 2), 2: Fraction(1), 3: Fraction(3, 2), 4: Fraction(2),
+            5: Fraction(3), 6: Fraction(4), 7: Fraction(6)}
+    sfv = torch.from_numpy(sf.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    R, Ch = q.shape
+    out = []
+    for r in range(R):
+        row = []
+        for c in range(2 * Ch):
+            byte = int(q[r, c // 2])
+            code = byte & 0xF if c % 2 == 0 else byte >> 4
+            v = e2m1[code & 7] * (-1 if code & 8 else 1)
+            row.append(v * Fraction(float(sfv[r, c // 16])))
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_SWIGLU, oracle.ACT_RELU2])
+def test_expert_projection_brute_force(act):
+    """pre, h and y against exact rational arithmetic on a tiny expert (H=32, I=16)."""
+    rng = np.random.default_rng(11 + act)
+    R, H, I = 3, 32, 16
+    N1 = 2 * I if act == oracle.ACT_SWIGLU else I
+    aq, asf = _rand_nvfp4(rng, R, H)
+    w1q, w1sf = _rand_nvfp4(rng, N1, H)
+    w2q, w2sf = _rand_nvfp4(rng, H, I)
+    adec = rng.uniform(0.01, 0.1, R).astype(np.float32)
+    ag, au, a2 = np.float32(0.003), np.float32(0.005), np.float32(0.007)
+    o = oracle.expert_rows_forward(aq, asf, adec, w1q, w1sf, w2q, w2sf, ag, au, a2, 1.0, act)
+    A = _exact_matrix(aq, asf)
+    W1 = _exact_matrix(w1q, w1sf)
+    for r in range(R):
+        pre = []
+        for n in range(N1):
+            s = sum(A[r][h] * W1[n][h] for h in range(H))
+            alpha = (ag if n < I else au) if act == oracle.ACT_SWIGLU else au
+            pre.append(s * Fraction(float(adec[r])) * Fraction(float(alpha)))
+        got = o["pre"][r]
+        for n in range(N1):
+            assert abs(got[n] - float(pre[n])) <= 4e-16 * abs(float(pre[n])) + 1e-300
+        # activation from the exact pre-activation with math.exp: gate rows first, then up
+        for i in range(I):
+            if act == oracle.ACT_SWIGLU:
+                g, u = float(pre[i]), float(pre[I + i])
+                h = g / (1 + math.exp(-g)) * u
+            else:
+                h = max(float(pre[i]), 0.0) ** 2
+            hb = o["h"][r, i]
+            assert abs(hb - h) <= abs(h) * 2.0 ** -8 * 1.0001 + 1e-300
+    # the intermediate is requantized with the fixed encode scale 1 (CudnnGroupedGemmNvfp4Config:
+    # "global scale of one"): block scale = E4M3(fl32(bmax / 6)), elements = E2M1(h / scale)
+    hb32 = o["h"].astype(np.float32)
+    bmax = np.abs(hb32.reshape(R, -1, 16)).max(axis=2)
+    assert np.array_equal(o["hsf"], oracle.e4m3_encode((bmax / np.float32(6)).astype(np.float32)))
+    deq = oracle.dequantize_nvfp4(o["hq"], o["hsf"])
+    sfv = np.repeat(oracle.e4m3_decode(o["hsf"]), 16, axis=1)
+    # within one E2M1 step of the block scale; a zero block scale only when bmax/6 rounds to 0
+    bound = np.where(sfv == 0, 6 * 2.0 ** -10, sfv)
+    assert np.all(np.abs(deq - o["h"]) <= bound)
+    # y from the oracle's own requantized intermediate, exactly
+    HQ = _exact_matrix(o["hq"], o["hsf"])
+    W2 = _exact_matrix(w2q, w2sf)
+    for r in range(R):
+        for hh in range(H):
+            s = sum(HQ[r][i] * W2[hh][i] for i in range(I)) * Fraction(float(a2))
+            ref = float(s)
+            assert abs(o["y"][r, hh] - ref) <= abs(ref) * 2.0 ** -8 * 1.0001 + 1e-300
+
+
+def test_gemm1_exact_grid_case():
+    """Grid-valued operands with unit scales: the pre-activation is an exactly representable sum."""
+    rng = np.random.default_rng(12)
+    H, I = 64, 16
+    aq = rng.integers(0, 256, (2, H // 2), dtype=np.uint8)
+    asf = np.full((2, H // 16), 0x38, np.uint8)                 # E4M3 1.0
+    w1q = rng.integers(0, 256, (2 * I, H // 2), dtype=np.uint8)
+    w1sf = np.full((2 * I, H // 16), 0x38, np.uint8)
+    w2q = rng.integers(0, 256, (H, I // 2), dtype=np.uint8)
+    w2sf = np.full((H, I // 16), 0x38, np.uint8)
+    o = oracle.expert_rows_forward(aq, asf, np.ones(2, np.float32), w1q, w1sf, w2q, w2sf,
+                                   1.0, 1.0, 1.0, 1.0, oracle.ACT_SWIGLU)
+    a = oracle.e2m1_decode(oracle.quant.unpack_codes(aq))
+    w = oracle.e2m1_decode(oracle.quant.unpack_codes(w1q))
+    exact = np.array([[math.fsum(a[r] * w[n]) for n in range(2 * I)] for r in range(2)])
+    assert np.array_equal(o["pre"], exact)
+
+
+def _small_problem(wl, seed=0, M=None):
+    M = wl.M if M is None else M
+    x = make_activations(wl, seed, M)
+    ids, w = make_routing(wl, seed, M)
+    w1, w2 = make_weights(wl, seed, "cpu")
+    w1q, w1sf, a1 = oracle.quantize_expert_weights(to_bits(w1))
+    w2q, w2sf, a2 = oracle.quantize_expert_weights(to_bits(w2))
+    aq, asf, adec = oracle.quantize_nvfp4(bf16_bits_to_f32(x), oracle.SCALE_PER_ROW)
+    return dict(x=x, ids=ids, w=w, w1=w1, w2=w2, W=(w1q, w1sf, w2q, w2sf), a1=a1, a2=a2,
+                aq=aq, asf=asf, adec=adec, M=M)
+
+
+def _run(wl, p, bm, out0=None, ids=None, w=None, rsf=1.0):
+    ids = p["ids"] if ids is None else ids
+    w = p["w"] if w is None else w
+    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    srt, eids, P, ttr = oracle.moe_plan(ids, wl.E, wl.local_offset, wl.n_local, bm)
+    return oracle.fused_moe_nvfp4(p["aq"], p["asf"], p["adec"], p["W"], p["a1"], p["a1"], p["a2"],
+                                  1.0, srt, eids, P, ttr, w, wl.top_k, bm, act, rsf, out0)
+
+
+SHRUNK_SKEWED = Workload("skewed_small", M=48, H=128, I=64, E=24, top_k=4, block_m=16,
+                         act="relu2", routing="zipf", local_offset=4, num_local=12)
+
+
+@pytest.mark.parametrize("wl", [WORKLOADS["tiny"], SHRUNK_SKEWED], ids=["tiny", "skewed_small"])
+def test_dense_loop_equals_plan_path(wl):
+    p = _small_problem(wl)
+    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    res = _run(wl, p, wl.block_m)
+    dense = oracle.dense_loop_moe(p["aq"], p["asf"], p["adec"], p["W"], p["a1"], p["a1"], p["a2"],
+                                  1.0, p["ids"], p["w"], wl.E, wl.local_offset, wl.n_local, act)
+    assert np.array_equal(res["out"], dense)
+    assert np.any(res["out"] != 0)
+
+
+def test_padding_rows_contribute_nothing():
+    wl = WORKLOADS["tiny"]
+    p = _small_problem(wl)
+    outs = [_run(wl, p, bm)["out"] for bm in (8, 16, 32, 128)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_masked_slots_ignored_with_nan_weights():
+    wl = SHRUNK_SKEWED
+    p = _small_problem(wl)
+    base = _run(wl, p, wl.block_m)["out"]
+    w = p["w"].copy()
+    loc = p["ids"] - wl.local_offset
+    masked = (loc < 0) | (loc >= wl.n_local)
+    assert masked.any()
+    w[masked] = np.nan
+    w[np.nonzero(masked)[0][:1], np.nonzero(masked)[1][:1]] = np.inf
+    assert np.array_equal(_run(wl, p, wl.block_m, w=w)["out"], base)
+    # a token whose slots are all unrouted keeps out0
+    ids = p["ids"].copy()
+    ids[0, :] = -1
+    out0 = np.full((wl.M, wl.H), 0x3F80, np.uint16)
+    res = _run(wl, p, wl.block_m, out0=out0, ids=ids)
+    assert np.all(res["out"][0] == 0x3F80)
+
+
+def test_out_accumulation_and_combine_closed_form():
+    wl = WORKLOADS["tiny"]
+    p = _small_problem(wl)
+    res0 = _run(wl, p, 8)
+    rng = np.random.default_rng(9)
+    out0 = to_bits(torch.from_numpy(rng.standard_normal((wl.M, wl.H)).astype(np.float32)).to(torch.bfloat16))
+    res1 = _run(wl, p, 8, out0=out0)
+    # closed form of the ordered FP32 combine, token by token
+    y, w, ttr = res1["unfinalized"]
+    for t in range(wl.M):
+        acc = bf16_bits_to_f32(out0[t]).copy()
+        for j in range(wl.top_k):
+            acc = acc + np.float32(w[t, j]) * y[ttr[t, j]].astype(np.float32)
+        want = oracle.f64_to_bf16_bits(acc.astype(np.float64))
+        assert np.array_equal(res1["out"][t], want)
+    assert not np.array_equal(res0["out"], res1["out"])
+    # finalize(unfinalized) reproduces the finalized output
+    again = oracle.combine(out0, y, w, ttr)
+    assert np.array_equal(again, res1["out"])
+
+
+def test_routed_scaling_factor_placement():
+    wl = WORKLOADS["tiny"]
+    p = _small_problem(wl)
+    r2 = _run(wl, p, 8, rsf=2.0)["out"]
+    r1 = _run(wl, p, 8)["out"]
+    # multiplying every product by 2 in FP32 is exact, so the result doubles exactly
+    assert np.array_equal(bf16_bits_to_f32(r2), 2 * bf16_bits_to_f32(r1))
+
+
+def test_token_permutation_equivariance():
+    wl = WORKLOADS["tiny"]
+    p = _small_problem(wl)
+    base = _run(wl, p, 8)["out"]
+    perm = np.random.default_rng(5).permutation(wl.M)
+    q = dict(p, aq=p["aq"][perm], asf=p["asf"][perm], adec=p["adec"][perm])
+    res = _run(wl, q, 8, ids=p["ids"][perm], w=p["w"][perm])
+    assert np.array_equal(res["out"], base[perm])
+
+
+def test_golden_combine_order():
+    slots, outs = [], {}
+    for line in open(GOLDEN_COMBINE):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = line.split()
+        if parts[0] == "slot":
+            slots.append(parts[1:])
+        else:
+            outs[int(parts[1])] = int(parts[2], 16)
+    M, k = 3, 3
+    ttr = np.full((M, k), -1, np.int64)
+    w = np.zeros((M, k), np.float32)
+    y = {}
+    for t, j, r, wh, yh in slots:
+        t, j, r = int(t), int(j), int(r)
+        ttr[t, j] = r
+        w[t, j] = np.array([int(wh, 16)], np.uint32).view(np.float32)[0]
+        if r >= 0:
+            y[r] = bf16_bits_to_f32(np.array([int(yh, 16)], np.uint16)).astype(np.float64)
+    out = oracle.combine(np.zeros((M, 1), np.uint16), y, w, ttr)
+    for t in range(M):
+        assert int(out[t, 0]) == outs[t], t
+
+
+def test_gap_to_unquantized_reference():
+    """The NVFP4 result stays close to the unquantized float64 MoE (three ~1-bit operands)."""
+    wl = WORKLOADS["tiny"]
+    p = _small_problem(wl)
+    out = bf16_bits_to_f32(_run(wl, p, 8)["out"]).astype(np.float64)
+    w1b, w2b = to_bits(p["w1"]), to_bits(p["w2"])
+    ref = oracle.unquantized_moe_f64(p["x"], lambda e: w1b[e], lambda e: w2b[e], p["ids"], p["w"],
+                                     wl.E, 0, wl.n_local, oracle.ACT_SWIGLU)
+    ref = np.stack([ref[t] for t in range(wl.M)])
+    gap = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert 0.02 < gap < 0.35, gap
