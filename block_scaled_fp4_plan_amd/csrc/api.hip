@@ -1,0 +1,398 @@
+// C entry points of the bfp4moe library: host-side validation, workspace sizing, launch
+// sequencing on the caller's stream, and the optional HIP-event kernel timer.
+// The contracts are documented in include/bfp4moe.h.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/bfp4moe.h"
+#include "runtime.h"
+
+namespace bfp4 {
+
+namespace {
+
+struct TimerState {
+  bool on = false;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<const char*> name;
+  int used = 0;
+  int launched = 0;
+};
+TimerState g_timer;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [lo, lo+n) and [lo2, lo2+n2) intersect (byte ranges, empty ranges never intersect)
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int device_check() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BFP4_ERR_DEVICE;
+  static int checked_dev = -1;
+  static int ok = 0;
+  if (checked_dev != dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BFP4_ERR_DEVICE;
+    ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    checked_dev = dev;
+  }
+  return ok ? BFP4_OK : BFP4_ERR_DEVICE;
+}
+
+inline int launched(hipError_t e) { return e == hipSuccess ? BFP4_OK : BFP4_ERR_LAUNCH; }
+
+inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool valid_block_m(int bm) { return bm >= 8 && bm % 8 == 0; }
+
+}  // namespace
+
+KernelTimer::KernelTimer(const char* name, hipStream_t stream) : slot_(-1), stream_(stream) {
+  if (!g_timer.on) return;
+  g_timer.launched++;
+  if (g_timer.used >= (int)g_timer.start.size()) return;
+  slot_ = g_timer.used++;
+  g_timer.name[slot_] = name;
+  hipEventRecord(g_timer.start[slot_], stream_);
+}
+
+KernelTimer::~KernelTimer() {
+  if (slot_ >= 0) hipEventRecord(g_timer.stop[slot_], stream_);
+}
+
+}  // namespace bfp4
+
+using namespace bfp4;
+
+extern "C" {
+
+const char* bfp4_status_string(int status) {
+  switch (status) {
+    case BFP4_OK: return "ok";
+    case BFP4_ERR_NULL: return "required pointer is NULL";
+    case BFP4_ERR_SHAPE: return "size out of range or not a required multiple";
+    case BFP4_ERR_ALIGN: return "pointer or stride misaligned";
+    case BFP4_ERR_BLOCK_M: return "block_m must be >= 8 and a multiple of 8";
+    case BFP4_ERR_CAPACITY: return "plan capacity too small";
+    case BFP4_ERR_WORKSPACE: return "workspace or panel buffer too small";
+    case BFP4_ERR_OVERLAP: return "output overlaps an input";
+    case BFP4_ERR_EXPERTS: return "invalid expert range";
+    case BFP4_ERR_MODE: return "unknown activation or scale mode";
+    case BFP4_ERR_SCALAR: return "scalar argument not finite or not positive";
+    case BFP4_ERR_DEVICE: return "no gfx950 HIP device";
+    case BFP4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* bfp4_version(void) { return "bfp4moe 0.1 (gfx950)"; }
+
+size_t bfp4_plan_capacity(int64_t M, int top_k, int num_local_experts, int block_m) {
+  if (M < 0 || top_k <= 0 || num_local_experts <= 0 || !valid_block_m(block_m)) return 0;
+  int64_t A = M * top_k;
+  int64_t ne = (int64_t)num_local_experts < A ? num_local_experts : A;
+  int64_t v = A + ne * (block_m - 1);
+  return (size_t)((v + block_m - 1) / block_m * block_m);
+}
+
+size_t bfp4_plan_workspace_size(int64_t M, int top_k, int num_local_experts) {
+  if (M < 0 || top_k <= 0 || num_local_experts <= 0) return 0;
+  int64_t A = M * top_k;
+  if (plan_uses_small_kernel(A)) return 0;
+  return (size_t)(plan_chunks(A) * num_local_experts * sizeof(int32_t));
+}
+
+int bfp4_moe_plan(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
+                  int local_expert_offset, int num_local_experts, int block_m,
+                  int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                  int32_t* token_to_row, size_t capacity, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
+  if (num_experts <= 0 || num_local_experts <= 0 || num_local_experts > 1024 ||
+      local_expert_offset < 0 || (int64_t)local_expert_offset + num_local_experts > num_experts)
+    return BFP4_ERR_EXPERTS;
+  size_t need = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
+  if (capacity < need || capacity % block_m || capacity >= (1ULL << 31)) return BFP4_ERR_CAPACITY;
+  if (!num_tokens_post_padded || (capacity && (!sorted_token_ids || !expert_ids)) ||
+      (M && (!topk_ids || !token_to_row)))
+    return BFP4_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_post_padded, 4) || !aligned(token_to_row, 4))
+    return BFP4_ERR_ALIGN;
+  size_t ws = bfp4_plan_workspace_size(M, top_k, num_local_experts);
+  if (workspace_bytes < ws || (ws && !workspace)) return BFP4_ERR_WORKSPACE;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_plan(topk_ids, M * top_k, top_k, num_experts, local_expert_offset,
+                              num_local_experts, block_m, sorted_token_ids, expert_ids,
+                              num_tokens_post_padded, token_to_row, (int64_t)capacity, workspace,
+                              (hipStream_t)stream));
+}
+
+size_t bfp4_quantize_workspace_size(int64_t rows, int mode, int64_t group_rows) {
+  if (mode != BFP4_SCALE_PER_GROUP || rows <= 0 || group_rows <= 0) return 0;
+  return (size_t)((rows / group_rows) * sizeof(uint32_t));
+}
+
+int bfp4_quantize_nvfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row_stride,
+                        int mode, int64_t group_rows, float fixed_encode_scale, uint8_t* q,
+                        uint8_t* sf, float* dec_scale, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (mode < 0 || mode > 2) return BFP4_ERR_MODE;
+  if (rows < 0 || cols <= 0 || cols % 32 || row_stride < cols || row_stride % 8 ||
+      rows >= (1LL << 31))
+    return BFP4_ERR_SHAPE;
+  if (mode == BFP4_SCALE_PER_GROUP && (group_rows <= 0 || rows % group_rows)) return BFP4_ERR_SHAPE;
+  if (mode == BFP4_SCALE_FIXED && !(isfinite(fixed_encode_scale) && fixed_encode_scale > 0.0f))
+    return BFP4_ERR_SCALAR;
+  if (rows == 0) return BFP4_OK;
+  if (!x_bf16 || !q || !sf || (mode != BFP4_SCALE_FIXED && !dec_scale)) return BFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q, 8) || !aligned(dec_scale, 4)) return BFP4_ERR_ALIGN;
+  size_t ws = bfp4_quantize_workspace_size(rows, mode, group_rows);
+  if (workspace_bytes < ws || (ws && !workspace)) return BFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return BFP4_ERR_ALIGN;
+  size_t xb = (size_t)((rows - 1) * row_stride + cols) * 2;
+  if (overlaps(x_bf16, xb, q, rows * cols / 2) || overlaps(x_bf16, xb, sf, rows * cols / 16))
+    return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_quantize(x_bf16, rows, cols, row_stride, mode, group_rows,
+                                  fixed_encode_scale, q, sf, dec_scale, workspace,
+                                  (hipStream_t)stream));
+}
+
+int bfp4_moe_permute(const uint8_t* q, const uint8_t* sf, const float* dec_scale, int64_t M,
+                     int64_t H, int top_k, const int32_t* sorted_token_ids,
+                     const int32_t* num_tokens_post_padded, size_t capacity, uint8_t* q_perm,
+                     uint8_t* sf_perm, float* s_perm, void* stream) {
+  if (M < 0 || H <= 0 || H % 32 || top_k <= 0 || capacity >= (1ULL << 31)) return BFP4_ERR_SHAPE;
+  if (capacity == 0) return BFP4_OK;
+  if (!sorted_token_ids || !num_tokens_post_padded || !q_perm || !sf_perm || !s_perm ||
+      (M && (!q || !sf || !dec_scale)))
+    return BFP4_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(sf, 16) || !aligned(q_perm, 16) || !aligned(sf_perm, 16) ||
+      !aligned(dec_scale, 4) || !aligned(s_perm, 4) || !aligned(sorted_token_ids, 4))
+    return BFP4_ERR_ALIGN;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_permute(q, sf, dec_scale, M, H, top_k, sorted_token_ids,
+                                 num_tokens_post_padded, (int64_t)capacity, q_perm, sf_perm,
+                                 s_perm, (hipStream_t)stream));
+}
+
+size_t bfp4_panel_bytes(int num_local_experts, int64_t H, int64_t I, int gated) {
+  if (num_local_experts <= 0 || H <= 0 || I <= 0 || H % 256 || I % 128) return 0;
+  int64_t N1 = gated ? 2 * I : I;
+  return (size_t)(panel_matrix_bytes(num_local_experts, N1, H) +
+                  panel_matrix_bytes(num_local_experts, H, I));
+}
+
+int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_t* w2_q,
+                         const uint8_t* w2_sf, int num_local_experts, int64_t H, int64_t I,
+                         int gated, void* panels, size_t panels_bytes, void* stream) {
+  if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
+  if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
+  if (!w1_q || !w1_sf || !w2_q || !w2_sf || !panels) return BFP4_ERR_NULL;
+  if (!aligned(w1_q, 16) || !aligned(w1_sf, 16) || !aligned(w2_q, 16) || !aligned(w2_sf, 16) ||
+      !aligned(panels, 16))
+    return BFP4_ERR_ALIGN;
+  if (panels_bytes < bfp4_panel_bytes(num_local_experts, H, I, gated)) return BFP4_ERR_WORKSPACE;
+  int dc = device_check();
+  if (dc) return dc;
+  int64_t N1 = gated ? 2 * I : I;
+  uint8_t* p1 = static_cast<uint8_t*>(panels);
+  uint8_t* p2 = p1 + panel_matrix_bytes(num_local_experts, N1, H);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_prepare(w1_q, w1_sf, num_local_experts, N1, H, gated ? (int)I : 0, p1, s);
+  if (e != hipSuccess) return BFP4_ERR_LAUNCH;
+  return launched(launch_prepare(w2_q, w2_sf, num_local_experts, H, I, 0, p2, s));
+}
+
+size_t bfp4_workspace_size(int64_t M, int64_t H, int64_t I, int top_k, int num_local_experts,
+                           int block_m, int do_finalize) {
+  size_t cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
+  if (H <= 0 || I <= 0) return 0;
+  size_t ws = align_up(cap * (size_t)(I / 2)) + align_up(cap * (size_t)(I / 16));
+  if (do_finalize) ws += align_up(cap * (size_t)H * 2);
+  return ws;
+}
+
+int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_dec,
+                         const void* panels, size_t panels_bytes, const float* alpha1_gate,
+                         const float* alpha1_up, const float* alpha2, float c2,
+                         const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                         const int32_t* num_tokens_post_padded, const int32_t* token_to_row,
+                         size_t capacity, const float* topk_weights, int64_t M, int64_t H,
+                         int64_t I, int num_local_experts, int top_k, int block_m, int act,
+                         float routed_scaling_factor, int do_finalize, uint16_t* out,
+                         uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (act != BFP4_ACT_SWIGLU && act != BFP4_ACT_RELU2) return BFP4_ERR_MODE;
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
+  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
+  if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
+  if (!(isfinite(c2) && c2 > 0.0f) || !isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
+  size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
+  if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
+    return BFP4_ERR_CAPACITY;
+  if (M == 0) return BFP4_OK;
+  if (!a_q || !a_sf || !a_dec || !panels || !alpha1_gate || !alpha1_up || !alpha2 ||
+      !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !token_to_row ||
+      !topk_weights || (do_finalize && !out) || (!do_finalize && !gemm2_out))
+    return BFP4_ERR_NULL;
+  if (!aligned(a_q, 16) || !aligned(a_sf, 16) || !aligned(panels, 16) || !aligned(out, 16) ||
+      !aligned(gemm2_out, 16) || !aligned(a_dec, 4) || !aligned(alpha1_gate, 4) ||
+      !aligned(alpha1_up, 4) || !aligned(alpha2, 4) || !aligned(topk_weights, 4) ||
+      !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) || !aligned(token_to_row, 4) ||
+      !aligned(workspace, 256))
+    return BFP4_ERR_ALIGN;
+  const int gated = act == BFP4_ACT_SWIGLU;
+  if (panels_bytes < bfp4_panel_bytes(num_local_experts, H, I, gated)) return BFP4_ERR_WORKSPACE;
+  size_t ws = bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize);
+  if (workspace_bytes < ws || !workspace) return BFP4_ERR_WORKSPACE;
+  const int64_t N1 = gated ? 2 * I : I;
+  if (debug) {
+    if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16) || !aligned(debug->inter_q, 8))
+      return BFP4_ERR_ALIGN;
+  }
+  if (do_finalize) {
+    size_t ob = (size_t)M * H * 2;
+    const size_t nl = (size_t)num_local_experts * 4, mk = (size_t)M * top_k * 4;
+    if (overlaps(out, ob, a_q, M * H / 2) || overlaps(out, ob, a_sf, M * H / 16) ||
+        overlaps(out, ob, a_dec, M * 4) || overlaps(out, ob, panels, panels_bytes) ||
+        overlaps(out, ob, alpha1_gate, nl) || overlaps(out, ob, alpha1_up, nl) ||
+        overlaps(out, ob, alpha2, nl) || overlaps(out, ob, sorted_token_ids, capacity * 4) ||
+        overlaps(out, ob, expert_ids, capacity / block_m * 4) ||
+        overlaps(out, ob, num_tokens_post_padded, 4) || overlaps(out, ob, token_to_row, mk) ||
+        overlaps(out, ob, topk_weights, mk) || overlaps(out, ob, workspace, ws))
+      return BFP4_ERR_OVERLAP;
+  }
+  int dc = device_check();
+  if (dc) return dc;
+
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  uint8_t* hq = (debug && debug->inter_q) ? debug->inter_q : w;
+  w += align_up(capacity * (size_t)(I / 2));
+  uint8_t* hsf = (debug && debug->inter_sf) ? debug->inter_sf : w;
+  w += align_up(capacity * (size_t)(I / 16));
+  uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
+
+  MoeGemmProblem p{};
+  p.a_q = a_q;
+  p.a_sf = a_sf;
+  p.a_dec = a_dec;
+  p.panel1 = static_cast<const uint8_t*>(panels);
+  p.panel2 = p.panel1 + panel_matrix_bytes(num_local_experts, N1, H);
+  p.alpha1_gate = alpha1_gate;
+  p.alpha1_up = alpha1_up;
+  p.alpha2 = alpha2;
+  p.c2 = c2;
+  p.sorted = sorted_token_ids;
+  p.eids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.cap = (int64_t)capacity;
+  p.M = M;
+  p.H = H;
+  p.I = I;
+  p.nloc = num_local_experts;
+  p.top_k = top_k;
+  p.block_m = block_m;
+  p.act = act;
+  p.hq = hq;
+  p.hsf = hsf;
+  p.y = y;
+  p.dbg_pre = debug ? debug->preact : nullptr;
+  p.dbg_inter = debug ? debug->inter : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_moe_gemms(p, s);
+  if (e != hipSuccess) return BFP4_ERR_LAUNCH;
+  if (!do_finalize) return BFP4_OK;
+  return launched(launch_finalize(y, topk_weights, token_to_row, M, H, top_k,
+                                  routed_scaling_factor, out, s));
+}
+
+int bfp4_moe_finalize(const uint16_t* gemm2_out, const float* topk_weights,
+                      const int32_t* token_to_row, int64_t M, int64_t H, int top_k,
+                      float routed_scaling_factor, uint16_t* out, void* stream) {
+  if (M < 0 || H <= 0 || H % 8 || top_k <= 0) return BFP4_ERR_SHAPE;
+  if (!isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
+  if (M == 0) return BFP4_OK;
+  if (!gemm2_out || !topk_weights || !token_to_row || !out) return BFP4_ERR_NULL;
+  if (!aligned(gemm2_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) ||
+      !aligned(token_to_row, 4))
+    return BFP4_ERR_ALIGN;
+  size_t ob = (size_t)M * H * 2, mk = (size_t)M * top_k * 4;
+  if (overlaps(out, ob, topk_weights, mk) || overlaps(out, ob, token_to_row, mk))
+    return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_finalize(gemm2_out, topk_weights, token_to_row, M, H, top_k,
+                                  routed_scaling_factor, out, (hipStream_t)stream));
+}
+
+int bfp4_profile_begin(int capacity) {
+  if (capacity <= 0 || capacity > (1 << 20)) return BFP4_ERR_SHAPE;
+  int dc = device_check();
+  if (dc) return dc;
+  TimerState& t = g_timer;
+  for (auto ev : t.start) hipEventDestroy(ev);
+  for (auto ev : t.stop) hipEventDestroy(ev);
+  t.start.assign(capacity, nullptr);
+  t.stop.assign(capacity, nullptr);
+  t.name.assign(capacity, nullptr);
+  for (int i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess)
+      return BFP4_ERR_LAUNCH;
+  }
+  t.used = 0;
+  t.launched = 0;
+  t.on = true;
+  return BFP4_OK;
+}
+
+int bfp4_profile_end(char* buf, size_t len) {
+  TimerState& t = g_timer;
+  if (!t.on) return BFP4_ERR_SHAPE;
+  t.on = false;
+  std::vector<std::string> names;
+  std::vector<double> total;
+  std::vector<int> count;
+  for (int i = 0; i < t.used; ++i) {
+    if (hipEventSynchronize(t.stop[i]) != hipSuccess) return BFP4_ERR_LAUNCH;
+    float ms = 0.0f;
+    hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+    size_t k = 0;
+    while (k < names.size() && names[k] != t.name[i]) ++k;
+    if (k == names.size()) {
+      names.push_back(t.name[i]);
+      total.push_back(0.0);
+      count.push_back(0);
+    }
+    total[k] += ms;
+    count[k] += 1;
+  }
+  std::string text;
+  char line[256];
+  for (size_t k = 0; k < names.size(); ++k) {
+    snprintf(line, sizeof(line), "%s %d %.6f\n", names[k].c_str(), count[k], total[k]);
+    text += line;
+  }
+  if (buf && len) {
+    size_t n = text.size() < len - 1 ? text.size() : len - 1;
+    memcpy(buf, text.data(), n);
+    buf[n] = 0;
+  }
+  return t.launched;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Device-side helpers shared by the bfp4moe kernels (gfx950 / CDNA4).
+//
+// Formats (FlashInfer "flashinfer.fused_moe.alphamoe_nvfp4_aligned_moe", layout paragraph;
+// Megatron-Core "core.inference.moe.flashinfer_nvfp4", module data):
+//   E2M1 code s.e1e0.m, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; two codes per byte, the even
+//   logical value in the low nibble.  E4M3FN block scales (bias 7, max 448), one per 16 values.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bfp4 {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE2M1Max = 6.0f;
+constexpr float kEncodeNumerator = 2688.0f;   // kE4M3Max * kE2M1Max, exact
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float -> BF16 bits, round to nearest even (finite inputs; overflow rounds to infinity).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E4M3FN byte -> float (sign bit ignored: block scales are non-negative).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// Non-negative finite float -> E4M3FN code: round to nearest even on the E4M3 grid, saturate at
+// 448 (code 0x7E).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  if (v >= kE4M3Max) return 0x7Eu;
+  if (v < 0x1p-6f) {                       // subnormal range: spacing 2^-9; 8 * 2^-9 is 2^-6
+    return (uint32_t)__builtin_rintf(v * 512.0f);
+  }
+  uint32_t u = __float_as_uint(v);
+  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);   // round the float mantissa to 3 bits
+  uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// float -> E2M1 code: nearest magnitude, ties to the even code, saturate at 6; sign bit copied.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
+  float a = __builtin_fabsf(y);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Quantize 16 values with encode scale s_enc (FP32 steps rounded separately, no FMA: the
+// library is compiled with -ffp-contract=off).  Returns the scale code; codes packed into
+// lo/hi (values 0..7 in lo, 8..15 in hi, even value in the low nibble of each byte).
+__device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float s_enc, uint32_t& lo,
+                                                  uint32_t& hi) {
+  float bmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bmax = __builtin_fmaxf(bmax, __builtin_fabsf(x[i]));
+  float v = (bmax * s_enc) / kE2M1Max;
+  uint32_t sf = f32_to_e4m3(v);
+  float sfv = e4m3_to_f32(sf);
+  float inv = (sfv == 0.0f) ? 0.0f : s_enc / sfv;
+  lo = 0u;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lo |= f32_to_e2m1(x[i] * inv) << (4 * i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hi |= f32_to_e2m1(x[8 + i] * inv) << (4 * i);
+  return sf;
+}
+
+// Encode scale from an FP32 amax: 2688 / amax, 1 when amax is 0, infinity clamped.
+__device__ __forceinline__ float encode_scale_from_amax(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  float s = kEncodeNumerator / amax;
+  return (s > 3.40282347e38f) ? 3.40282347e38f : s;
+}
+
+// Exact decode of NVFP4 operands to FP16.
+// Every E2M1 x E4M3 product has at most 6 significant bits and lies in [2^-10, 2688] (or is 0),
+// so it is exact in FP16 (normal range).  v_cvt_scalef32_pk_f16_fp4 converts two E2M1 codes of a
+// selected byte and multiplies by a power of two (only the exponent of its scale operand is
+// used); 256 is passed so that the E4M3 factor can be applied as the exact FP16 number
+// s * 2^-8, whose bit pattern is (code & 0x7F) << 7.
+__device__ __forceinline__ uint32_t e4m3_scale_h2(uint32_t sf_byte) {
+  uint32_t b = (sf_byte & 0x7Fu) << 7;
+  return b | (b << 16);
+}
+
+__device__ __forceinline__ uint32_t dec_pair(uint32_t w, h2_t s, int sel) {
+  h2_t p;
+  switch (sel) {   // the byte selector must be a compile-time constant
+    case 0: p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0); break;
+    case 1: p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1); break;
+    case 2: p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2); break;
+    default: p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3); break;
+  }
+  return __builtin_bit_cast(uint32_t, p * s);
+}
+
+// 8 E2M1 codes (one dword, code k in bits 4k..4k+3) times one E4M3 scale -> 8 exact FP16.
+__device__ __forceinline__ h8_t decode8(uint32_t w, uint32_t scale_h2_bits) {
+  h2_t s = __builtin_bit_cast(h2_t, scale_h2_bits);
+  u32x4_t r;
+  r[0] = dec_pair(w, s, 0);
+  r[1] = dec_pair(w, s, 1);
+  r[2] = dec_pair(w, s, 2);
+  r[3] = dec_pair(w, s, 3);
+  return __builtin_bit_cast(h8_t, r);
+}
+
+// Wave-wide (64 lanes) reductions.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// LDS barrier that leaves global loads in flight: wait for this wave's LDS operations only.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace bfp4

@@ -1,0 +1,227 @@
+// Expert-sorted routing plan (FlashInfer "flashinfer.fused_moe.alphamoe_nvfp4_aligned_moe",
+// plan paragraph: sorted_token_ids, expert_ids per block_m entries, num_tokens_post_padded;
+// "flashinfer.fused_moe.CudnnGroupedGemmNvfp4Config": expert-sorted permutation, masked
+// non-local experts).
+//
+// Plan contents: routed slots grouped by local expert (ascending), each group padded to a
+// multiple of block_m; inside a group the flat slot indices f = t*top_k + j ascend; padding and
+// the tail [extent, capacity) hold the sentinel M*top_k; expert_ids = local id per block, -1 past
+// the extent; token_to_row = plan row per slot or -1.
+//
+// Three phases: histogram of local expert ids; prefix sum of the padded counts; a stable scatter
+// in which one wavefront walks its slots 64 at a time and ranks equal ids with ballots (a lane's
+// rank among the lanes holding the same id is the popcount of the matching lanes below it).
+// Small inputs run all phases in one workgroup; large inputs split the slots into 1024-slot
+// chunks (per-chunk histograms, one scan over (expert, chunk), per-chunk scatter).
+#include "device.h"
+#include "runtime.h"
+
+namespace bfp4 {
+
+namespace {
+
+constexpr int kMaxLocal = 1024;
+constexpr int64_t kSmallMax = 2048;   // slots handled by the single-workgroup kernel
+constexpr int kChunk = 1024;          // slots per chunk in the multi-workgroup path
+
+__device__ __forceinline__ int local_id(int32_t id, int num_experts, int offset, int nloc) {
+  int e = id - offset;
+  return (id >= 0 && id < num_experts && e >= 0 && e < nloc) ? e : -1;
+}
+
+// Lanes of the current wave whose key equals this lane's key (keys < 2^nbits).
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits) {
+  uint64_t peers = __ballot(1);
+  for (int b = 0; b < nbits; ++b) {
+    uint32_t bit = (key >> b) & 1u;
+    uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ int key_bits(int nloc) {
+  int b = 1;
+  while ((1 << b) <= nloc) ++b;   // keys 0..nloc (nloc marks unrouted)
+  return b;
+}
+
+// One wave ranks slots [f0, f1) in order and scatters them.  run[e] holds, for each local
+// expert, the plan position of its next slot; it is advanced by the highest lane of each group.
+__device__ void scatter_wave(const int32_t* __restrict__ ids, int64_t f0, int64_t f1,
+                             int num_experts, int offset, int nloc, int* run,
+                             int32_t* __restrict__ sorted, int32_t* __restrict__ ttr) {
+  const int lane = threadIdx.x & 63;
+  const int nbits = key_bits(nloc);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = f0; base < f1; base += 64) {
+    int64_t f = base + lane;
+    if (f < f1) {
+      int e = local_id(ids[f], num_experts, offset, nloc);
+      uint32_t key = (e < 0) ? (uint32_t)nloc : (uint32_t)e;
+      uint64_t peers = match_any(key, nbits);
+      if (e >= 0) {
+        int rank = __popcll(peers & below);
+        int pos = run[e] + rank;
+        sorted[pos] = (int32_t)f;
+        ttr[f] = pos;
+        if ((peers >> lane) == 1ull) run[e] += __popcll(peers);   // highest lane of the group
+      } else {
+        ttr[f] = -1;
+      }
+    }
+  }
+}
+
+// Exclusive scan of one int per thread over a 1024-thread block; returns the total.
+__device__ int block_excl_scan_1024(int v, int* tmp, int& total) {
+  int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int add = (tid >= off) ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  int incl = tmp[tid];
+  total = tmp[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+// Writes num_tokens_post_padded, expert_ids and the sentinel entries, given each expert's
+// count (cnt) and segment start (start) in LDS.
+__device__ void write_plan_frame(const int* cnt, const int* start, int nloc, int block_m, int P,
+                                 int64_t cap, int32_t sentinel, int32_t* __restrict__ sorted,
+                                 int32_t* __restrict__ eids, int32_t* __restrict__ ntpp) {
+  int tid = threadIdx.x;
+  if (tid == 0) *ntpp = P;
+  if (tid < nloc) {
+    int c = cnt[tid];
+    if (c > 0) {
+      int seg = (c + block_m - 1) / block_m * block_m;
+      int s0 = start[tid];
+      for (int b = s0 / block_m; b < (s0 + seg) / block_m; ++b) eids[b] = tid;
+      for (int p = s0 + c; p < s0 + seg; ++p) sorted[p] = sentinel;
+    }
+  }
+  for (int64_t b = P / block_m + tid; b < cap / block_m; b += blockDim.x) eids[b] = -1;
+  for (int64_t p = P + tid; p < cap; p += blockDim.x) sorted[p] = sentinel;
+}
+
+__global__ __launch_bounds__(1024) void plan_small_kernel(
+    const int32_t* __restrict__ ids, int64_t A, int num_experts, int offset, int nloc,
+    int block_m, int32_t* __restrict__ sorted, int32_t* __restrict__ eids,
+    int32_t* __restrict__ ntpp, int32_t* __restrict__ ttr, int64_t cap) {
+  __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
+  int tid = threadIdx.x;
+  if (tid < nloc) cnt[tid] = 0;
+  __syncthreads();
+  for (int64_t f = tid; f < A; f += 1024) {
+    int e = local_id(ids[f], num_experts, offset, nloc);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  int seg = (tid < nloc) ? (cnt[tid] + block_m - 1) / block_m * block_m : 0;
+  int P;
+  int excl = block_excl_scan_1024(seg, tmp, P);
+  if (tid < nloc) start[tid] = excl;
+  __syncthreads();
+  write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
+  __syncthreads();
+  if (tid < 64) scatter_wave(ids, 0, A, num_experts, offset, nloc, start, sorted, ttr);
+}
+
+__global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restrict__ ids, int64_t A,
+                                                         int num_experts, int offset, int nloc,
+                                                         int32_t* __restrict__ hist) {
+  __shared__ int h[kMaxLocal];
+  for (int e = threadIdx.x; e < nloc; e += 256) h[e] = 0;
+  __syncthreads();
+  int64_t f0 = (int64_t)blockIdx.x * kChunk;
+  int64_t f1 = f0 + kChunk < A ? f0 + kChunk : A;
+  for (int64_t f = f0 + threadIdx.x; f < f1; f += 256) {
+    int e = local_id(ids[f], num_experts, offset, nloc);
+    if (e >= 0) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nloc; e += 256) hist[(int64_t)blockIdx.x * nloc + e] = h[e];
+}
+
+// Turns the per-chunk histograms into per-chunk starting positions (in place) and writes the
+// plan frame.
+__global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ hist, int64_t nchunks,
+                                                         int64_t A, int nloc, int block_m,
+                                                         int32_t* __restrict__ sorted,
+                                                         int32_t* __restrict__ eids,
+                                                         int32_t* __restrict__ ntpp, int64_t cap) {
+  __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
+  int tid = threadIdx.x;
+  int c = 0;
+  if (tid < nloc)
+    for (int64_t g = 0; g < nchunks; ++g) c += hist[g * nloc + tid];
+  if (tid < nloc) cnt[tid] = c;
+  int seg = (tid < nloc) ? (c + block_m - 1) / block_m * block_m : 0;
+  int P;
+  int excl = block_excl_scan_1024(seg, tmp, P);
+  if (tid < nloc) {
+    start[tid] = excl;
+    int pos = excl;
+    for (int64_t g = 0; g < nchunks; ++g) {
+      int v = hist[g * nloc + tid];
+      hist[g * nloc + tid] = pos;
+      pos += v;
+    }
+  }
+  __syncthreads();
+  write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
+}
+
+__global__ __launch_bounds__(64) void plan_scatter_kernel(const int32_t* __restrict__ ids, int64_t A,
+                                                          int num_experts, int offset, int nloc,
+                                                          const int32_t* __restrict__ pos0,
+                                                          int32_t* __restrict__ sorted,
+                                                          int32_t* __restrict__ ttr) {
+  __shared__ int run[kMaxLocal];
+  for (int e = threadIdx.x; e < nloc; e += 64) run[e] = pos0[(int64_t)blockIdx.x * nloc + e];
+  __syncthreads();
+  int64_t f0 = (int64_t)blockIdx.x * kChunk;
+  int64_t f1 = f0 + kChunk < A ? f0 + kChunk : A;
+  scatter_wave(ids, f0, f1, num_experts, offset, nloc, run, sorted, ttr);
+}
+
+}  // namespace
+
+bool plan_uses_small_kernel(int64_t A) { return A <= kSmallMax; }
+int64_t plan_chunks(int64_t A) { return (A + kChunk - 1) / kChunk; }
+
+hipError_t launch_plan(const int32_t* ids, int64_t A, int top_k, int num_experts, int offset,
+                       int nloc, int block_m, int32_t* sorted, int32_t* eids, int32_t* ntpp,
+                       int32_t* ttr, int64_t cap, void* ws, hipStream_t s) {
+  (void)top_k;
+  if (plan_uses_small_kernel(A)) {
+    KernelTimer t("plan_small", s);
+    hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(1024), 0, s, ids, A, num_experts, offset,
+                       nloc, block_m, sorted, eids, ntpp, ttr, cap);
+    return hipGetLastError();
+  }
+  int64_t nch = plan_chunks(A);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  {
+    KernelTimer t("plan_count", s);
+    hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)nch), dim3(256), 0, s, ids, A,
+                       num_experts, offset, nloc, hist);
+  }
+  {
+    KernelTimer t("plan_scan", s);
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nch, A, nloc, block_m,
+                       sorted, eids, ntpp, cap);
+  }
+  KernelTimer t("plan_scatter", s);
+  hipLaunchKernelGGL(plan_scatter_kernel, dim3((unsigned)nch), dim3(64), 0, s, ids, A, num_experts,
+                     offset, nloc, hist, sorted, ttr);
+  return hipGetLastError();
+}
+
+}  // namespace bfp4

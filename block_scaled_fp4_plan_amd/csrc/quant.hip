@@ -1,0 +1,240 @@
+// NVFP4 quantization, permutation into plan order, and the ordered FP32 combine (finalize).
+//
+// Quantization follows Megatron-Core "core.inference.moe.flashinfer_nvfp4" (one FP32 scale per
+// token or per expert matrix, block size 16, E2M1 max 6, E4M3 max 448), FlashInfer
+// "flashinfer.fused_moe.alphamoe_nvfp4_aligned_moe" (packing, linear scales) and vLLM
+// "flashinfer_utils" quantize_nvfp4_per_token_input (the FP32 scale returned is the decode
+// scale).  The combine follows FlashInfer "flashinfer.fused_moe.FrostLowLatencyConfig" (ordered,
+// separate FP32 multiplication and addition) and the alphamoe page's out parameter
+// (contributions added to out in FP32, one BF16 conversion).
+#include "device.h"
+#include "runtime.h"
+
+namespace bfp4 {
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+
+// Load one 16-value BF16 block as floats (two 16-byte loads).
+__device__ __forceinline__ void load_block16(const uint16_t* p, float (&x)[16]) {
+  uint4 a = *reinterpret_cast<const uint4*>(p);
+  uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+
+__device__ float block_max_256(float v, float* red) {
+  v = wave_max(v);
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// Row amax of each row, folded into its group's maximum with an integer atomic max (the bit
+// pattern of a non-negative float orders like the float).
+__global__ __launch_bounds__(kQuantThreads) void group_amax_kernel(const uint16_t* __restrict__ x,
+                                                                   int64_t cols, int64_t stride,
+                                                                   int64_t group_rows,
+                                                                   uint32_t* __restrict__ gmax) {
+  __shared__ float red[4];
+  int64_t r = blockIdx.x;
+  const uint16_t* xr = x + r * stride;
+  int64_t nblk = cols >> 4;
+  float m = 0.0f;
+  for (int64_t b = threadIdx.x; b < nblk; b += kQuantThreads) {
+    float v[16];
+    load_block16(xr + b * 16, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  }
+  m = block_max_256(m, red);
+  if (threadIdx.x == 0) atomicMax(gmax + r / group_rows, __float_as_uint(m));
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// One workgroup per row.  MODE 0: per-row scale from the row amax; 1: per-group scale from the
+// group maxima in gmax; 2: fixed encode scale.
+template <int MODE>
+__global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t cols, int64_t stride, int64_t group_rows, float fixed,
+    const uint32_t* __restrict__ gmax, uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+    float* __restrict__ dec) {
+  __shared__ float red[4];
+  int64_t r = blockIdx.x;
+  const uint16_t* xr = x + r * stride;
+  int64_t nblk = cols >> 4;
+  float s_enc;
+  if (MODE == 0) {
+    float m = 0.0f;
+    for (int64_t b = threadIdx.x; b < nblk; b += kQuantThreads) {
+      float v[16];
+      load_block16(xr + b * 16, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+    }
+    m = block_max_256(m, red);
+    s_enc = encode_scale_from_amax(m);
+    if (threadIdx.x == 0) dec[r] = 1.0f / s_enc;
+  } else if (MODE == 1) {
+    s_enc = encode_scale_from_amax(__uint_as_float(gmax[r / group_rows]));
+    if (threadIdx.x == 0 && (r % group_rows) == 0) dec[r / group_rows] = 1.0f / s_enc;
+  } else {
+    s_enc = fixed;
+    if (threadIdx.x == 0 && r == 0 && dec) dec[0] = 1.0f / s_enc;
+  }
+  uint8_t* qr = q + r * (cols >> 1);
+  uint8_t* sr = sf + r * nblk;
+  for (int64_t b = threadIdx.x; b < nblk; b += kQuantThreads) {
+    float v[16];
+    load_block16(xr + b * 16, v);
+    uint32_t lo, hi;
+    uint32_t s = quant_block16(v, s_enc, lo, hi);
+    *reinterpret_cast<uint2*>(qr + b * 8) = make_uint2(lo, hi);
+    sr[b] = (uint8_t)s;
+  }
+}
+
+// Permute: one workgroup of 64 threads per capacity row.
+__global__ __launch_bounds__(64) void permute_kernel(const uint8_t* __restrict__ q,
+                                                     const uint8_t* __restrict__ sf,
+                                                     const float* __restrict__ dec, int64_t M,
+                                                     int64_t H, int top_k,
+                                                     const int32_t* __restrict__ sorted,
+                                                     const int32_t* __restrict__ ntpp,
+                                                     uint8_t* __restrict__ qp,
+                                                     uint8_t* __restrict__ sp,
+                                                     float* __restrict__ spd) {
+  int64_t r = blockIdx.x;
+  int64_t P = *ntpp;
+  int64_t f = (r < P) ? (int64_t)sorted[r] : -1;
+  bool valid = f >= 0 && f < M * top_k;
+  int64_t t = valid ? f / top_k : 0;
+  int64_t qbytes = H >> 1, sbytes = H >> 4;
+  const uint4* srcq = reinterpret_cast<const uint4*>(q + t * qbytes);
+  uint4* dstq = reinterpret_cast<uint4*>(qp + r * qbytes);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int64_t i = threadIdx.x; i < qbytes / 16; i += 64) dstq[i] = valid ? srcq[i] : z;
+  const uint8_t* srcs = sf + t * sbytes;
+  uint8_t* dsts = sp + r * sbytes;
+  if ((sbytes & 15) == 0) {
+    for (int64_t i = threadIdx.x; i < sbytes / 16; i += 64)
+      reinterpret_cast<uint4*>(dsts)[i] = valid ? reinterpret_cast<const uint4*>(srcs)[i] : z;
+  } else {
+    for (int64_t i = threadIdx.x; i < sbytes; i += 64) dsts[i] = valid ? srcs[i] : (uint8_t)0;
+  }
+  if (threadIdx.x == 0) spd[r] = valid ? dec[t] : 0.0f;
+}
+
+// Finalize: one thread per (token, 8 consecutive hidden values).
+__global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restrict__ y,
+                                                       const float* __restrict__ w,
+                                                       const int32_t* __restrict__ ttr, int64_t M,
+                                                       int64_t H, int top_k, float rsf,
+                                                       uint16_t* __restrict__ out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t per_row = H >> 3;
+  if (i >= M * per_row) return;
+  int64_t t = i / per_row;
+  int64_t h = (i - t * per_row) * 8;
+  uint4 o = *reinterpret_cast<const uint4*>(out + t * H + h);
+  uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc[2 * k] = bf16_to_f32(ow[k] & 0xFFFFu);
+    acc[2 * k + 1] = bf16_to_f32(ow[k] >> 16);
+  }
+  const bool scaled = (rsf != 1.0f);
+  for (int j = 0; j < top_k; ++j) {
+    int32_t r = ttr[t * top_k + j];
+    if (r < 0) continue;                       // unrouted: weight never read
+    float wt = w[t * top_k + j];
+    uint4 yy = *reinterpret_cast<const uint4*>(y + (int64_t)r * H + h);
+    uint32_t yw[4] = {yy.x, yy.y, yy.z, yy.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float p0 = wt * bf16_to_f32(yw[k] & 0xFFFFu);
+      float p1 = wt * bf16_to_f32(yw[k] >> 16);
+      if (scaled) {
+        p0 = p0 * rsf;
+        p1 = p1 * rsf;
+      }
+      acc[2 * k] = acc[2 * k] + p0;
+      acc[2 * k + 1] = acc[2 * k + 1] + p1;
+    }
+  }
+  uint4 res;
+  res.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+  res.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+  res.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+  res.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(out + t * H + h) = res;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, int mode,
+                           int64_t group_rows, float fixed, uint8_t* q, uint8_t* sf, float* dec,
+                           void* ws, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)rows), block(kQuantThreads);
+  if (mode == 0) {
+    KernelTimer t("quantize_rows", s);
+    hipLaunchKernelGGL(quantize_rows_kernel<0>, grid, block, 0, s, x, cols, stride, group_rows,
+                       fixed, nullptr, q, sf, dec);
+  } else if (mode == 1) {
+    uint32_t* gmax = static_cast<uint32_t*>(ws);
+    int64_t ng = rows / group_rows;
+    {
+      KernelTimer t("fill_u32", s);
+      hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, s,
+                         gmax, ng, 0u);
+    }
+    {
+      KernelTimer t("group_amax", s);
+      hipLaunchKernelGGL(group_amax_kernel, grid, block, 0, s, x, cols, stride, group_rows, gmax);
+    }
+    KernelTimer t("quantize_rows_group", s);
+    hipLaunchKernelGGL(quantize_rows_kernel<1>, grid, block, 0, s, x, cols, stride, group_rows,
+                       fixed, gmax, q, sf, dec);
+  } else {
+    KernelTimer t("quantize_rows_fixed", s);
+    hipLaunchKernelGGL(quantize_rows_kernel<2>, grid, block, 0, s, x, cols, stride, group_rows,
+                       fixed, nullptr, q, sf, dec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const uint8_t* q, const uint8_t* sf, const float* dec, int64_t M,
+                          int64_t H, int top_k, const int32_t* sorted, const int32_t* ntpp,
+                          int64_t cap, uint8_t* qp, uint8_t* sp, float* spd, hipStream_t s) {
+  if (cap == 0) return hipSuccess;
+  KernelTimer t("permute", s);
+  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)cap), dim3(64), 0, s, q, sf, dec, M, H, top_k,
+                     sorted, ntpp, qp, sp, spd);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const uint16_t* y, const float* w, const int32_t* ttr, int64_t M,
+                           int64_t H, int top_k, float rsf, uint16_t* out, hipStream_t s) {
+  int64_t n = M * (H >> 3);
+  if (n == 0) return hipSuccess;
+  KernelTimer t("finalize", s);
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, w, ttr,
+                     M, H, top_k, rsf, out);
+  return hipGetLastError();
+}
+
+}  // namespace bfp4

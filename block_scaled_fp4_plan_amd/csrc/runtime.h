@@ -1,0 +1,69 @@
+// Host-side internals of the bfp4moe library: kernel launchers and the optional event timer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bfp4 {
+
+// Records a pair of HIP events around one kernel launch when timing is enabled
+// (bfp4_profile_begin); otherwise does nothing.
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t stream);
+  ~KernelTimer();
+
+ private:
+  int slot_;
+  hipStream_t stream_;
+};
+
+// ---- launchers (arguments already validated by the C entry points) ----
+hipError_t launch_plan(const int32_t* ids, int64_t A, int top_k, int num_experts, int offset,
+                       int nloc, int block_m, int32_t* sorted, int32_t* eids, int32_t* ntpp,
+                       int32_t* ttr, int64_t cap, void* ws, hipStream_t s);
+bool plan_uses_small_kernel(int64_t A);
+int64_t plan_chunks(int64_t A);
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, int mode,
+                           int64_t group_rows, float fixed, uint8_t* q, uint8_t* sf, float* dec,
+                           void* ws, hipStream_t s);
+
+hipError_t launch_permute(const uint8_t* q, const uint8_t* sf, const float* dec, int64_t M,
+                          int64_t H, int top_k, const int32_t* sorted, const int32_t* ntpp,
+                          int64_t cap, uint8_t* qp, uint8_t* sp, float* spd, hipStream_t s);
+
+hipError_t launch_finalize(const uint16_t* y, const float* w, const int32_t* ttr, int64_t M,
+                           int64_t H, int top_k, float rsf, uint16_t* out, hipStream_t s);
+
+// Weight panels: see gemm.hip for the layout.
+int64_t panel_matrix_bytes(int num_experts, int64_t rows, int64_t K);
+hipError_t launch_prepare(const uint8_t* w_q, const uint8_t* w_sf, int num_experts, int64_t rows,
+                          int64_t K, int gated_rows_half, uint8_t* panel, hipStream_t s);
+
+struct MoeGemmProblem {
+  const uint8_t* a_q;
+  const uint8_t* a_sf;
+  const float* a_dec;
+  const uint8_t* panel1;
+  const uint8_t* panel2;
+  const float* alpha1_gate;
+  const float* alpha1_up;
+  const float* alpha2;
+  float c2;
+  const int32_t* sorted;
+  const int32_t* eids;
+  const int32_t* ntpp;
+  int64_t cap;
+  int64_t M, H, I;
+  int nloc, top_k, block_m, act;
+  uint8_t* hq;      // [cap, I/2]
+  uint8_t* hsf;     // [cap, I/16]
+  uint16_t* y;      // [cap, H]
+  float* dbg_pre;
+  uint16_t* dbg_inter;
+};
+hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s);
+
+}  // namespace bfp4

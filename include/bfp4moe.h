@@ -1,0 +1,225 @@
+/*
+ * bfp4moe: NVFP4 routed mixture-of-experts expert computation on AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named as a device pointer refers to device memory owned by the
+ * caller; the library keeps no reference after a call returns, allocates no device memory on the
+ * paths below and never synchronizes the stream.  All work is enqueued asynchronously on
+ * `stream` (a hipStream_t handle; NULL means the default stream).
+ *
+ * Every entry point returns a bfp4_status.  Arguments are validated on the host from sizes,
+ * pointer values and alignment only (device memory is never read for validation), so an error
+ * is reported before anything is enqueued.  Device-side preconditions (documented per call) are
+ * not checked.
+ *
+ * Sources, cited by page title and section:
+ *   [cuDNN]   FlashInfer, "flashinfer.fused_moe.CudnnGroupedGemmNvfp4Config" (bullet list)
+ *   [MCore]   NVIDIA Megatron-Core, "core.inference.moe.flashinfer_nvfp4" (module text, data, API)
+ *   [Alpha]   FlashInfer, "flashinfer.fused_moe.alphamoe_nvfp4_aligned_moe" (signature, layout
+ *             paragraph, parameter list, notes)
+ *   [vLLM]    vLLM, "vllm.model_executor.layers.quantization.utils.flashinfer_utils"
+ *   [Frost]   FlashInfer, "flashinfer.fused_moe.FrostLowLatencyConfig" (numerics paragraphs)
+ *
+ * Formats shared by all calls:
+ *   NVFP4 row of C values = packed E2M1 bytes [C/2] (two values per byte, even logical value in
+ *   the low nibble [Alpha, layout]) + E4M3FN scale bytes [C/16], one per 16 consecutive values,
+ *   linear (not swizzled) [Alpha, layout] + one FP32 *decode* scale per row or matrix
+ *   [vLLM, quantize_nvfp4_per_token_input]; value = e2m1 * e4m3 * decode_scale.
+ *   BF16 values are passed as uint16_t bit patterns.
+ */
+#ifndef BFP4MOE_H
+#define BFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BFP4_OK = 0,
+  BFP4_ERR_NULL = -1,        /* a required pointer is NULL */
+  BFP4_ERR_SHAPE = -2,       /* a size is out of range or not a required multiple */
+  BFP4_ERR_ALIGN = -3,       /* a pointer or row stride is not aligned as required */
+  BFP4_ERR_BLOCK_M = -4,     /* block_m < 8 or not a multiple of 8 [Alpha, block_m] */
+  BFP4_ERR_CAPACITY = -5,    /* plan capacity below bfp4_plan_capacity() */
+  BFP4_ERR_WORKSPACE = -6,   /* workspace or panel buffer smaller than required */
+  BFP4_ERR_OVERLAP = -7,     /* out overlaps an input [Alpha, out] */
+  BFP4_ERR_EXPERTS = -8,     /* expert range invalid */
+  BFP4_ERR_MODE = -9,        /* unknown activation or scale mode */
+  BFP4_ERR_SCALAR = -10,     /* a scalar is not finite / not positive */
+  BFP4_ERR_DEVICE = -11,     /* no HIP device, or the current device is not gfx950 */
+  BFP4_ERR_LAUNCH = -12      /* a kernel launch failed */
+} bfp4_status;
+
+typedef enum { BFP4_ACT_SWIGLU = 0, BFP4_ACT_RELU2 = 1 } bfp4_act;
+typedef enum { BFP4_SCALE_PER_ROW = 0, BFP4_SCALE_PER_GROUP = 1, BFP4_SCALE_FIXED = 2 } bfp4_scale_mode;
+
+/* Human-readable name of a status code (static storage). */
+const char* bfp4_status_string(int status);
+
+/* Library version string (static storage). */
+const char* bfp4_version(void);
+
+/* ----------------------------------------------------------------------------------------------
+ * Routing plan [Alpha, plan paragraph and parameters sorted_token_ids / expert_ids /
+ * num_tokens_post_padded; cuDNN, permutation and expert-parallelism bullets].
+ *
+ * Slot (t, j) of topk_ids [M, top_k] is routed here when its id lies in
+ * [local_expert_offset, local_expert_offset + num_local_experts) (and in [0, num_experts));
+ * other ids, including -1, are unrouted [cuDNN EP bullet; MCore "-1 contribute zero"; Frost].
+ * The plan lists routed slots by local expert, ascending, each expert segment padded to a
+ * multiple of block_m; inside a segment the flat slot indices f = t*top_k + j ascend.
+ *   sorted_token_ids [capacity]: f for routed entries, M*top_k (sentinel) for padding and for
+ *                                every entry at or past the extent;
+ *   expert_ids [capacity / block_m]: local expert id of each block, -1 past the extent;
+ *   num_tokens_post_padded [1]: the extent P (a multiple of block_m);
+ *   token_to_row [M, top_k]: plan row of each slot, -1 when unrouted.
+ * capacity must be >= bfp4_plan_capacity(M, top_k, num_local_experts, block_m), a multiple of
+ * block_m; the extent never exceeds it.  Ids are int32, device pointers, contiguous.
+ * workspace: device scratch of at least bfp4_plan_workspace_size() bytes (may be NULL when that
+ * size is 0).  Device precondition: none (any id values are accepted; duplicates inside a token,
+ * which the pages forbid [cuDNN, topk_ids bullet], still give a valid stable plan).
+ * Limits: num_local_experts <= 1024, M*top_k < 2^31.
+ * ---------------------------------------------------------------------------------------------- */
+size_t bfp4_plan_capacity(int64_t M, int top_k, int num_local_experts, int block_m);
+size_t bfp4_plan_workspace_size(int64_t M, int top_k, int num_local_experts);
+int bfp4_moe_plan(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
+                  int local_expert_offset, int num_local_experts, int block_m,
+                  int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+                  int32_t* token_to_row, size_t capacity, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * NVFP4 quantization of a BF16 matrix x [rows, cols] (row stride in elements)
+ * [MCore: one FP32 scale per token / per expert matrix; cuDNN: intermediate with a global scale
+ * of one; vLLM: the returned scale is the decode scale; Alpha: packing and linear scales].
+ *   mode PER_ROW:   one scale per row (activations); dec_scale [rows].
+ *   mode PER_GROUP: one scale per group of group_rows consecutive rows (one expert matrix);
+ *                   dec_scale [rows / group_rows].
+ *   mode FIXED:     encode scale fixed_encode_scale for every row; dec_scale may be NULL, else
+ *                   receives [1] = 1/fixed_encode_scale.
+ * Arithmetic (FP32, round to nearest even, no fused multiply-add):
+ *   s_enc = 2688 / amax (1 when amax == 0, infinity clamped to FLT_MAX); dec = 1 / s_enc;
+ *   per 16-block: sf = e4m3_rne_sat((bmax * s_enc) / 6); inv = sf ? s_enc / sf : 0;
+ *   code = e2m1_rne_sat(x * inv), ties to the even code, sign bit copied from x.
+ * Outputs (device, contiguous): q [rows, cols/2], sf [rows, cols/16].
+ * Requirements: cols % 32 == 0; row_stride >= cols and % 8 == 0; x 16-byte aligned;
+ * workspace >= bfp4_quantize_workspace_size(rows, mode, group_rows) (PER_GROUP keeps the group
+ * maxima there).  Device preconditions: x finite; every row (group) maximum is 0 or >= 2^-106.
+ * ---------------------------------------------------------------------------------------------- */
+size_t bfp4_quantize_workspace_size(int64_t rows, int mode, int64_t group_rows);
+int bfp4_quantize_nvfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row_stride,
+                        int mode, int64_t group_rows, float fixed_encode_scale, uint8_t* q,
+                        uint8_t* sf, float* dec_scale, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * Permutation of quantized token rows into plan order [cuDNN, permutation bullet]:
+ * for plan row r < extent with entry f < M*top_k, row r of the outputs is token f / top_k
+ * (q_perm [capacity, H/2], sf_perm [capacity, H/16], s_perm [capacity]); sentinel rows and rows
+ * at or past the extent are zero.  Inputs: q [M, H/2], sf [M, H/16], dec_scale [M] (device).
+ * Requirements: H % 32 == 0; all byte pointers 16-byte aligned.  Device precondition: plan
+ * produced for this M and top_k.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_moe_permute(const uint8_t* q, const uint8_t* sf, const float* dec_scale, int64_t M,
+                     int64_t H, int top_k, const int32_t* sorted_token_ids,
+                     const int32_t* num_tokens_post_padded, size_t capacity, uint8_t* q_perm,
+                     uint8_t* sf_perm, float* s_perm, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * Expert weights [MCore prepare_routed_nvfp4_weights; Alpha gemm1/gemm2 weight layouts].
+ * Input: linear NVFP4 weights of num_local_experts experts, as bfp4_quantize_nvfp4 writes them
+ * with one scale per expert matrix:
+ *   w1_q [E, N1, H/2], w1_sf [E, N1, H/16] with N1 = 2*I in [gate; up] row order (gated) or I;
+ *   w2_q [E, H, I/2],  w2_sf [E, H, I/16].
+ * Output: `panels`, an opaque device buffer of bfp4_panel_bytes() bytes holding the same values
+ * rearranged for the gfx950 kernels (gate/up row groups interleaved, K-blocked 1 KiB tiles, scales
+ * grouped per 512 K values).  Requirements: H % 256 == 0, I % 128 == 0, all pointers 16-byte
+ * aligned.  Runs once at load; the raw weights are not needed afterwards.
+ * ---------------------------------------------------------------------------------------------- */
+size_t bfp4_panel_bytes(int num_local_experts, int64_t H, int64_t I, int gated);
+int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_t* w2_q,
+                         const uint8_t* w2_sf, int num_local_experts, int64_t H, int64_t I,
+                         int gated, void* panels, size_t panels_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * The fused expert computation [Alpha: gate/up GEMM, SwiGLU, requantization, down GEMM on a
+ * pre-aligned plan; cuDNN: pipeline, finalize / unfinalized triple; Frost: rounding points].
+ *
+ * Per valid plan row r (entry f < M*top_k, token t = f / top_k, local expert e of r's block):
+ *   pre[n] = (sum_h x[t,h] * W1_e[n,h]) * a_dec[t] * alpha1_{gate|up}[e]   (FP32 accumulate;
+ *            gate rows n < I use alpha1_gate, up rows alpha1_up; non-gated uses alpha1_up)
+ *   h[i]   = bf16(silu(pre[i]) * pre[I+i])  (SwiGLU)  or  bf16(max(pre[i],0)^2)  (ReLU^2)
+ *   hq     = NVFP4 of h with fixed encode scale c2 (the quantizer's FIXED mode)
+ *   y[k]   = bf16((sum_i hq[i] * W2_e[k,i]) * (1/c2) * alpha2[e])
+ * Finalize (do_finalize != 0): for every token t,
+ *   out[t,k] = bf16(f32(out[t,k]) + sum_{j ascending, token_to_row[t,j] >= 0}
+ *              fl32(fl32(w[t,j] * y[row,k]) [* rsf]))   -- each product and sum rounded to FP32,
+ *   no fused multiply-add; unrouted slots are skipped without reading their weights [Frost].
+ *   out accumulates: zero it first for a fresh result [Alpha, out].
+ * Unfinalized (do_finalize == 0): gemm2_out [capacity, H] receives y at every routed row (rows
+ *   not named by token_to_row are left unwritten); with topk_weights and token_to_row this is the
+ *   [gemm2_out, expert_weights, token_to_row] triple [cuDNN, finalize bullet]; out is untouched.
+ *
+ * Arguments (device pointers unless noted):
+ *   a_q [M, H/2], a_sf [M, H/16], a_dec [M]: NVFP4 activations (bfp4_quantize_nvfp4 PER_ROW);
+ *   panels: from bfp4_prepare_weights for (num_local_experts, H, I, gated);
+ *   alpha1_gate, alpha1_up, alpha2 [num_local_experts] FP32;  c2 (host) > 0, finite;
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded, token_to_row: a plan from
+ *   bfp4_moe_plan for the same M, top_k, num_local_experts and block_m, with this capacity;
+ *   topk_weights [M, top_k] FP32; routed_scaling_factor (host) finite;
+ *   out [M, H] BF16 (16-byte aligned, must not overlap any input) -- used when do_finalize;
+ *   gemm2_out [capacity, H] BF16 -- required when !do_finalize, else may be NULL;
+ *   debug (may be NULL): optional copies of internal values for verification.
+ *   workspace: >= bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize).
+ * Requirements: H % 256 == 0 and H >= 256 [Alpha, notes]; I % 128 == 0 [cuDNN, sizes bullet];
+ *   block_m >= 8, % 8 == 0 [Alpha, block_m]; pointers 16-byte aligned.
+ * Device preconditions: the plan's expert ids are < num_local_experts; token ids < M.
+ * ---------------------------------------------------------------------------------------------- */
+typedef struct {
+  float* preact;        /* [capacity, N1] FP32 pre-activations (logical W1 row order) or NULL */
+  uint16_t* inter;      /* [capacity, I] BF16 activation output or NULL */
+  uint8_t* inter_q;     /* [capacity, I/2] requantized intermediate or NULL */
+  uint8_t* inter_sf;    /* [capacity, I/16] its E4M3 scales or NULL */
+} bfp4_debug;
+
+size_t bfp4_workspace_size(int64_t M, int64_t H, int64_t I, int top_k, int num_local_experts,
+                           int block_m, int do_finalize);
+int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a_dec,
+                         const void* panels, size_t panels_bytes, const float* alpha1_gate,
+                         const float* alpha1_up, const float* alpha2, float c2,
+                         const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                         const int32_t* num_tokens_post_padded, const int32_t* token_to_row,
+                         size_t capacity, const float* topk_weights, int64_t M, int64_t H,
+                         int64_t I, int num_local_experts, int top_k, int block_m, int act,
+                         float routed_scaling_factor, int do_finalize, uint16_t* out,
+                         uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * Finalize an unfinalized triple [cuDNN finalize bullet; Frost combine contract]: the combine of
+ * bfp4_fused_moe_nvfp4 applied to gemm2_out [rows, H], topk_weights [M, top_k] and
+ * token_to_row [M, top_k], accumulating into out [M, H].  Bit-identical to the finalized path.
+ * Requirements: H % 8 == 0; pointers 16-byte aligned; out must not overlap the inputs.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_moe_finalize(const uint16_t* gemm2_out, const float* topk_weights,
+                      const int32_t* token_to_row, int64_t M, int64_t H, int top_k,
+                      float routed_scaling_factor, uint16_t* out, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * Kernel timing with HIP events (measurement support, off by default).
+ * bfp4_profile_begin(capacity) creates `capacity` event pairs and starts recording one pair
+ * around every kernel the library launches; bfp4_profile_end() stops recording, waits for the
+ * recorded events and writes one line per kernel name, "name count total_ms", into buf
+ * (NUL-terminated, truncated to len).  Returns the number of kernels launched while recording,
+ * or a negative status.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_profile_begin(int capacity);
+int bfp4_profile_end(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BFP4MOE_H */

@@ -16,8 +16,9 @@ The steps follow the pages' description of the format:
 Readings taken where the pages are silent (every FP32 step rounds to nearest even, as numpy
 float32 arithmetic does; no fused multiply-add):
 1. encode scale  s_enc = fl32(FLOAT8_E4M3_MAX * FLOAT4_E2M1_MAX / amax) = fl32(2688 / amax) over
-   the row (per-row) or the group of rows (per-group); s_enc = 1 when amax == 0; an overflow
-   to infinity is clamped to the largest finite float32.  Fixed mode uses s_enc = c.
+   the row (per-row) or the group of rows (per-group); s_enc = 1 when amax == 0.  A row or group
+   with 0 < amax < 2**-106 (about 1.2e-32) is outside the contract, like non-finite input: there
+   s_enc / sfv can overflow float32 for the smallest block scales.  Fixed mode uses s_enc = c.
    The decode scale returned is fl32(1 / s_enc).
 2. block scale  v = fl32(fl32(bmax * s_enc) / 6), code sf = e4m3_encode(v), value sfv.
 3. element  inv = 0 if sfv == 0 else fl32(s_enc / sfv);  code = e2m1_encode(fl32(x * inv)).
@@ -46,6 +47,8 @@ _F32_MAX = np.float32(np.finfo(np.float32).max)
 def _encode_scale(amax):
     """Step 1: FP32 encode scale from an FP32 amax (array)."""
     amax = np.asarray(amax, dtype=np.float32)
+    if np.any((amax > 0) & (amax < np.float32(2.0 ** -106))):
+        raise ValueError("0 < amax < 2**-106 is outside the quantizer's contract")
     num = np.float32(FLOAT8_E4M3_MAX) * np.float32(FLOAT4_E2M1_MAX)     # 2688, exact
     with np.errstate(divide="ignore", over="ignore"):
         s = num / np.where(amax == 0, np.float32(1), amax)               # float32 division

@@ -1,0 +1,356 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Bars (per workload): routing plan, permutation and quantization bit-exact; GEMM1
+pre-activation within 1e-5 relative Frobenius; final output within 2e-2 relative Frobenius;
+requantization of the GPU's own BF16 intermediate and the combine of the GPU's own expert outputs
+bit-exact; finalize(unfinalized) == finalized; two runs bit-identical.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.formats import bf16_bits_to_f32
+from synth import WORKLOADS
+from synth.workloads import Workload
+
+from gpu_common import Problem, np_bits, np_u8, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import block_scaled_fp4_plan_amd as bf
+    from block_scaled_fp4_plan_amd import runner
+
+
+# ----------------------------------------------------------------------------- quantization
+
+def _gpu_quant(x_bits, mode=0, group_rows=0, c=1.0):
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, sf, dec = runner.quantize(x, mode, group_rows, c)
+    torch.cuda.synchronize()
+    return np_u8(q), np_u8(sf), dec.cpu().numpy()
+
+
+def _check_quant(x_bits, mode=0, group_rows=0, c=1.0):
+    q, sf, dec = _gpu_quant(x_bits, mode, group_rows, c)
+    oq, osf, odec = oracle.quantize_nvfp4(bf16_bits_to_f32(x_bits), mode, group_rows or None, c)
+    assert np.array_equal(q, oq)
+    assert np.array_equal(sf, osf)
+    if mode == oracle.SCALE_FIXED:
+        assert dec[0] == odec[0]
+    else:
+        assert np.array_equal(dec[:len(odec)].view(np.uint32), odec.view(np.uint32))
+
+
+def test_quantize_per_row_workload_shapes():
+    for name in ("tiny", "decode_ll", "decode"):
+        wl = WORKLOADS[name]
+        say("quantize per-row", name)
+        from synth import make_activations
+        _check_quant(make_activations(wl, 0))
+
+
+def test_quantize_all_bf16_bit_patterns():
+    """Every finite BF16 value, in rows of 256, at several row magnitudes."""
+    say("quantize all bf16 patterns")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = bf16_bits_to_f32(bits)
+    bits = np.where(np.isfinite(v), bits, 0).astype(np.uint16)
+    rng = np.random.default_rng(0)
+
+    def in_contract(r):   # row amax 0 or >= 2**-106
+        a = np.abs(bf16_bits_to_f32(r)).max(axis=1)
+        return r[(a == 0) | (a >= 2.0 ** -106)]
+
+    rows = in_contract(bits.reshape(512, 128))     # each row: one sign, two exponents
+    assert rows.shape[0] > 460
+    _check_quant(rows)
+    _check_quant(in_contract(rng.permutation(bits).reshape(512, 128)))
+    _check_quant(bits.reshape(512, 128), oracle.SCALE_FIXED, 0, 1.0)
+    _check_quant(bits.reshape(1024, 64), oracle.SCALE_FIXED, 0, 0.37)
+
+
+def test_quantize_edge_rows():
+    say("quantize edge rows")
+    from synth import bf16_bits
+    x = np.zeros((6, 64))
+    x[1] = -0.0
+    x[2, :16] = 1e-40                       # BF16 subnormals next to a tiny in-contract amax
+    x[2, 20] = -2.0 ** -106
+    x[3] = np.linspace(-6, 6, 64)
+    x[4, 5] = 3.0e38
+    x[5, ::7] = -1e-30
+    b = bf16_bits(x)
+    b[1] = 0x8000
+    _check_quant(b)
+
+
+def test_quantize_per_group_and_fixed():
+    say("quantize per-group")
+    rng = np.random.default_rng(3)
+    from synth import bf16_bits
+    w = bf16_bits(rng.standard_normal((8 * 96, 256)) * rng.uniform(0.001, 10, (8 * 96, 1)))
+    _check_quant(w, oracle.SCALE_PER_GROUP, 96)
+    _check_quant(w, oracle.SCALE_PER_GROUP, 1)
+    say("quantize fixed")
+    _check_quant(w, oracle.SCALE_FIXED, 0, 1.0)
+
+
+# ----------------------------------------------------------------------------- plan / permute
+
+def _gpu_plan(ids, E, off, nloc, bm):
+    M, k = ids.shape
+    pb = runner.MoePlanBuffers(M, k, nloc, bm, "cuda")
+    pb.build(torch.from_numpy(ids).cuda(), E, off)
+    torch.cuda.synchronize()
+    return (pb.sorted_token_ids.cpu().numpy()[:pb.capacity], pb.expert_ids.cpu().numpy()[:pb.capacity // bm],
+            int(pb.num_tokens_post_padded.item()), pb.token_to_row.cpu().numpy()[:M])
+
+
+PLAN_CASES = [  # (M, top_k, E, offset, nloc, block_m, kind)
+    (16, 2, 8, 0, 8, 8, "distinct"), (16, 2, 8, 0, 8, 128, "distinct"),
+    (4, 10, 128, 0, 128, 8, "distinct"), (8, 8, 256, 0, 256, 8, "distinct"),
+    (300, 6, 288, 0, 144, 128, "zipf"), (37, 3, 8, 2, 4, 16, "noisy"),
+    (4096, 8, 256, 0, 256, 128, "distinct"), (16384, 6, 288, 0, 144, 128, "zipf"),
+    (2000, 4, 64, 16, 32, 24, "noisy"), (1, 1, 4, 0, 4, 8, "distinct"),
+]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=[str(c) for c in PLAN_CASES])
+def test_plan_bit_exact(case):
+    M, k, E, off, nloc, bm, kind = case
+    say("plan", case)
+    rng = np.random.default_rng(M * 7 + k)
+    if kind == "distinct":
+        ids = np.argsort(rng.random((M, E)), axis=1)[:, :k].astype(np.int32)
+    elif kind == "zipf":
+        from synth.workloads import make_routing
+        wl = Workload("z", M=M, H=256, I=128, E=E, top_k=k, block_m=bm, routing="zipf",
+                      num_local=nloc)
+        ids, _ = make_routing(wl, 0)
+    else:
+        ids = rng.integers(-2, E + 3, (M, k)).astype(np.int32)   # duplicates, -1, out of range
+    got = _gpu_plan(ids, E, off, nloc, bm)
+    want = oracle.moe_plan(ids, E, off, nloc, bm)
+    assert got[2] == want[2]
+    assert np.array_equal(got[0], want[0])
+    assert np.array_equal(got[1], want[1])
+    assert np.array_equal(got[3], want[3])
+
+
+def test_permute_bit_exact():
+    wl = WORKLOADS["decode_ll"]
+    say("permute", wl.name)
+    p = Problem(wl, M=48)
+    q, sf, dec = runner.quantize(p.x)
+    pb = runner.MoePlanBuffers(48, wl.top_k, wl.n_local, 8, "cuda").build(p.ids_d, wl.E)
+    cap = pb.capacity
+    qp = torch.empty((cap, wl.H // 2), dtype=torch.uint8, device="cuda")
+    sp = torch.empty((cap, wl.H // 16), dtype=torch.uint8, device="cuda")
+    spd = torch.empty(cap, dtype=torch.float32, device="cuda")
+    bf.bfp4_moe_permute(q, sf, dec, 48, wl.H, wl.top_k, pb.sorted_token_ids,
+                        pb.num_tokens_post_padded, cap, qp, sp, spd)
+    torch.cuda.synchronize()
+    srt, eids, P, ttr = oracle.moe_plan(p.ids, wl.E, 0, wl.n_local, 8)
+    oq, osf, odec = p.oracle_activations()
+    wq, wsf, wsd = oracle.moe_permute(oq, osf, odec, srt, P, wl.top_k)
+    assert np.array_equal(np_u8(qp), wq)
+    assert np.array_equal(np_u8(sp), wsf)
+    assert np.array_equal(spd.cpu().numpy().view(np.uint32), wsd.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- weights layout
+
+def test_prepare_weights_layout():
+    """Panels hold exactly the linear NVFP4 bytes, rearranged (layout re-derived here)."""
+    say("prepare layout")
+    rng = np.random.default_rng(5)
+    E, H, I = 2, 512, 384                     # K = 512 (one full superchunk), I = 384 (partial)
+    for gated in (1, 0):
+        N1 = 2 * I if gated else I
+        w1q = rng.integers(0, 256, (E, N1, H // 2), dtype=np.uint8)
+        w1s = rng.integers(0, 256, (E, N1, H // 16), dtype=np.uint8)
+        w2q = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+        w2s = rng.integers(0, 256, (E, H, I // 16), dtype=np.uint8)
+        nb = bf.bfp4_panel_bytes(E, H, I, gated)
+        panels = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        t = [torch.from_numpy(a).cuda() for a in (w1q, w1s, w2q, w2s)]
+        bf.bfp4_prepare_weights(*t, E, H, I, gated, panels, nb)
+        torch.cuda.synchronize()
+        got = np_u8(panels)
+        off = 0
+        for (q, s, rows, K, half) in ((w1q, w1s, N1, H, I if gated else 0), (w2q, w2s, H, I, 0)):
+            nch, ng = K // 64, rows // 32
+            nsc = (nch + 7) // 8
+            for e in range(E):
+                for g in range(ng):
+                    for rho in range(32):
+                        perm = 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3)
+                        lr = ((g & 1) * half + (g >> 1) * 32 + perm) if half else g * 32 + perm
+                        for hh in range(2):
+                            lane = hh * 32 + rho
+                            for c in range(nch):
+                                sc, j = divmod(c, 8)
+                                base = off + ((e * ng + g) * (nsc + nch) + sc * 9) * 1024
+                                d = base + 1024 * (1 + j) + lane * 16
+                                assert np.array_equal(got[d:d + 16], q[e, lr, 32 * c + 16 * hh: 32 * c + 16 * hh + 16])
+                                sidx = base + lane * 16 + 2 * j
+                                assert got[sidx] == s[e, lr, 4 * c + 2 * hh]
+                                assert got[sidx + 1] == s[e, lr, 4 * c + 2 * hh + 1]
+            off += E * ng * (nsc + nch) * 1024
+        assert off == nb
+
+
+# ----------------------------------------------------------------------------- full path
+
+SMALL_SKEWED = Workload("skewed_small", M=96, H=256, I=128, E=24, top_k=4, block_m=16,
+                        act="relu2", routing="zipf", local_offset=4, num_local=12)
+TINY_RELU2 = Workload("tiny_relu2", M=40, H=512, I=256, E=8, top_k=3, block_m=128, act="relu2")
+
+MOE_CASES = [
+    ("tiny", 8), ("tiny", 128), ("decode_ll", 8), ("skewed_small", 16), ("tiny_relu2", 128),
+    ("tiny", 32), ("tiny", 136),
+]
+
+
+def _workload(name):
+    return {"skewed_small": SMALL_SKEWED, "tiny_relu2": TINY_RELU2}.get(name) or WORKLOADS[name]
+
+
+def run_gpu_moe(p, block_m, do_finalize=True, debug=True, rsf=1.0):
+    wl = p.wl
+    pw, lin = runner.prepare_weights(p.w1, p.w2, gated=wl.gated, keep_linear=True)
+    fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, block_m, wl.local_offset, do_finalize)
+    cap = fwd.plan.capacity
+    dbg = None
+    if debug:
+        dbg = dict(preact=torch.full((cap, wl.N1), float("nan"), device="cuda"),
+                   inter=torch.zeros((cap, wl.I), dtype=torch.bfloat16, device="cuda"),
+                   inter_q=torch.zeros((cap, wl.I // 2), dtype=torch.uint8, device="cuda"),
+                   inter_sf=torch.zeros((cap, wl.I // 16), dtype=torch.uint8, device="cuda"))
+    res = fwd(p.x, p.ids_d, p.w_d, debug=dbg, routed_scaling_factor=rsf)
+    torch.cuda.synchronize()
+    return fwd, pw, lin, dbg, res
+
+
+@pytest.mark.parametrize("name,bm", MOE_CASES, ids=["%s-bm%d" % c for c in MOE_CASES])
+def test_fused_moe_matches_oracle(name, bm):
+    wl = _workload(name)
+    say("fused_moe", name, "block_m", bm)
+    p = Problem(wl)
+    fwd, pw, lin, dbg, out = run_gpu_moe(p, bm)
+    out_bits = np_bits(out)
+    M, k = p.M, wl.top_k
+    # activations and plan: bit-exact
+    oq, osf, odec = p.oracle_activations()
+    assert np.array_equal(np_u8(fwd.a_q), oq) and np.array_equal(np_u8(fwd.a_sf), osf)
+    assert np.array_equal(fwd.a_dec.cpu().numpy().view(np.uint32), odec.view(np.uint32))
+    srt, eids, P, ttr = p.oracle_plan(bm)
+    assert int(fwd.plan.num_tokens_post_padded.item()) == P
+    assert np.array_equal(fwd.plan.sorted_token_ids.cpu().numpy()[:len(srt)], srt)
+    assert np.array_equal(fwd.plan.token_to_row.cpu().numpy(), ttr)
+    # weights: the GPU's per-expert quantization is bit-exact for the routed experts
+    experts = sorted(set(int(e) for e in eids[:P // bm]))
+    for e in experts[:4]:
+        (q1, s1, q2, s2), a1, a2 = p.oracle_expert(e)
+        assert np.array_equal(np_u8(lin[0][e]), q1) and np.array_equal(np_u8(lin[1][e]), s1)
+        assert np.array_equal(np_u8(lin[2][e]), q2) and np.array_equal(np_u8(lin[3][e]), s2)
+        assert pw.alpha1_gate[e].item() == a1 and pw.alpha2[e].item() == a2
+    # oracle forward with its own quantized weights
+    a1, a2 = p.oracle_alphas(experts)
+    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    res = oracle.fused_moe_nvfp4(oq, osf, odec, lambda e: p.oracle_expert(e)[0], a1, a1, a2, 1.0,
+                                 srt, eids, P, ttr, p.w, k, bm, act)
+    rows = sorted(res["pre"].keys())
+    # GEMM1 pre-activation
+    pre_gpu = dbg["preact"].cpu().numpy()[rows]
+    pre_ref = np.stack([res["pre"][r] for r in rows])
+    e_pre = rel_fro(pre_gpu, pre_ref)
+    # requantization of the GPU's own BF16 intermediate
+    inter = np_bits(dbg["inter"])[rows]
+    rq, rsf_, _ = oracle.quantize_nvfp4(bf16_bits_to_f32(inter), oracle.SCALE_FIXED, None, 1.0)
+    assert np.array_equal(np_u8(dbg["inter_q"])[rows], rq)
+    assert np.array_equal(np_u8(dbg["inter_sf"])[rows], rsf_)
+    e_h = rel_fro(bf16_bits_to_f32(inter), np.stack([res["h"][r] for r in rows]))
+    # final output
+    out_ref = bf16_bits_to_f32(res["out"]).astype(np.float64)
+    e_out = rel_fro(bf16_bits_to_f32(out_bits), out_ref)
+    # NVFP4 vs unquantized FP64 gap of the oracle itself (reported)
+    ref64 = oracle.unquantized_moe_f64(p.x_bits, lambda e: p.host_weight_bits(e)[0],
+                                       lambda e: p.host_weight_bits(e)[1], p.ids, p.w, wl.E,
+                                       wl.local_offset, wl.n_local, act)
+    ref64 = np.stack([ref64[t] for t in range(M)])
+    gap = rel_fro(out_ref, ref64)
+    say("pre %.3e  h %.3e  out %.3e  oracle-vs-fp64 gap %.3f" % (e_pre, e_h, e_out, gap))
+    assert e_pre <= 1e-5
+    assert e_out <= 2e-2
+    # unfinalized triple -> finalize == finalized, bit for bit; run-twice determinism
+    fwd2 = runner.MoeForward(pw, p.M, k, wl.E, bm, wl.local_offset, do_finalize=False)
+    y, wts, ttr_d = fwd2(p.x, p.ids_d, p.w_d)
+    out2 = torch.zeros_like(out)
+    bf.bfp4_moe_finalize(y, wts, ttr_d, M, wl.H, k, 1.0, out2)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_bits(out2), out_bits)
+    # the combine of the GPU's own expert outputs is the oracle's combine, bit for bit
+    ttr_np = ttr_d.cpu().numpy()
+    ybits = np_bits(y)
+    ydict = {int(r): bf16_bits_to_f32(ybits[r]).astype(np.float64) for r in ttr_np.reshape(-1) if r >= 0}
+    comb = oracle.combine(np.zeros((M, wl.H), np.uint16), ydict, p.w, ttr_np)
+    assert np.array_equal(comb, out_bits)
+    out3 = fwd(p.x, p.ids_d, p.w_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_bits(out3), out_bits)
+
+
+def test_out_accumulates_and_rsf():
+    wl = WORKLOADS["tiny"]
+    say("out accumulation / routed_scaling_factor")
+    p = Problem(wl)
+    pw = runner.prepare_weights(p.w1, p.w2)
+    fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, 8)
+    rng = np.random.default_rng(1)
+    from synth import bf16_bits
+    o0 = bf16_bits(rng.standard_normal((p.M, wl.H)))
+    out = torch.from_numpy(o0.view(np.int16)).view(torch.bfloat16).cuda()
+    fwd(p.x, p.ids_d, p.w_d, out=out, routed_scaling_factor=0.75)
+    fwd2 = runner.MoeForward(pw, p.M, wl.top_k, wl.E, 8, do_finalize=False)
+    y, wts, ttr = fwd2(p.x, p.ids_d, p.w_d)
+    torch.cuda.synchronize()
+    ttr_np = ttr.cpu().numpy()
+    ybits = np_bits(y)
+    ydict = {int(r): bf16_bits_to_f32(ybits[r]).astype(np.float64) for r in ttr_np.reshape(-1) if r >= 0}
+    want = oracle.combine(o0, ydict, p.w, ttr_np, 0.75)
+    assert np.array_equal(np_bits(out), want)
+
+
+def test_masked_slots_nan_weights_and_all_masked_token():
+    wl = SMALL_SKEWED
+    say("masking with NaN weights")
+    p = Problem(wl)
+    pw = runner.prepare_weights(p.w1, p.w2, gated=False)
+    fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, wl.block_m, wl.local_offset)
+    base = np_bits(fwd(p.x, p.ids_d, p.w_d))
+    loc = p.ids - wl.local_offset
+    masked = (loc < 0) | (loc >= wl.n_local)
+    assert masked.any()
+    w = p.w.copy()
+    w[masked] = np.nan
+    ids = p.ids.copy()
+    ids[0, :] = -1
+    w[0, :] = np.inf
+    o0 = np.full((p.M, wl.H), 0x3F80, np.uint16)
+    out = torch.from_numpy(o0.view(np.int16)).view(torch.bfloat16).cuda()
+    fwd(p.x, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), out=out)
+    got = np_bits(out)
+    torch.cuda.synchronize()
+    assert np.all(got[0] == 0x3F80)
+    assert np.all(np.isfinite(bf16_bits_to_f32(got)))
+    # with all NaNs on masked slots, unmasked tokens match the plain run with out0 = 1.0 added
+    fwd_plain = runner.MoeForward(pw, p.M, wl.top_k, wl.E, wl.block_m, wl.local_offset)
+    out_b = torch.from_numpy(o0.view(np.int16)).view(torch.bfloat16).cuda()
+    fwd_plain(p.x, torch.from_numpy(ids).cuda(), p.w_d, out=out_b)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_bits(out_b), got)
+    assert base.shape == got.shape
