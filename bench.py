@@ -1,0 +1,258 @@
+"""Benchmark of the NVFP4 routed-MoE hot path on one MI355X.
+
+One step = the whole per-call path on one batch of synthetic input already resident in HBM:
+routing plan + per-token NVFP4 quantization of the activations + fused experts (GEMM1 with
+SwiGLU and requantization, GEMM2, ordered FP32 finalize).  Weight quantization and panel
+preparation happen once, before timing (offline in a serving system).
+
+Workloads (synthetic, seeded):
+  decode  : M=8,    H=7168, I=2048, E=256, top_k=8, block_m=8   (primary: value = tokens/s)
+  prefill : M=4096, H=7168, I=2048, E=256, top_k=8, block_m=128 (reported in "prefill")
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|both]
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-MoE tokens/s + HBM GB/s (M=8) and TFLOP/s (M=4096), % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA (the issued dtype)
+NVFP4_BYTES = 9.0 / 16.0       # 0.5 B data + 1/16 B E4M3 scale per element
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="both", choices=["decode", "prefill", "both"])
+    ap.add_argument("--replicas", type=int, default=2,
+                    help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "block_scaled_fp4_plan_amd", "csrc"))):
+        with open(os.path.join(ROOT, "block_scaled_fp4_plan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    ent = d.get("%s/%s" % (workload, kernel))
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent["bytes_per_launch"]
+
+
+class Setup:
+    def __init__(self, wl, replicas, seed=0):
+        import torch
+
+        from block_scaled_fp4_plan_amd import runner
+        from synth import make_activations, make_routing, make_weights
+
+        self.wl = wl
+        dev = "cuda"
+        self.x_bits = make_activations(wl, seed)
+        self.ids, self.w = make_routing(wl, seed)
+        self.x = torch.from_numpy(self.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.ids_d = torch.from_numpy(self.ids).to(dev)
+        self.w_d = torch.from_numpy(self.w).to(dev)
+        self.w1, self.w2 = make_weights(wl, seed, dev)
+        pw = runner.prepare_weights(self.w1, self.w2, gated=wl.gated)
+        self.weights = [pw]
+        for _ in range(replicas - 1):
+            self.weights.append(runner.PreparedWeights(pw.panels.clone(), pw.panels_bytes,
+                                                       pw.alpha1_gate, pw.alpha1_up, pw.alpha2,
+                                                       pw.num_local_experts, pw.H, pw.I,
+                                                       pw.gated))
+        self.fwd = runner.MoeForward(pw, wl.M, wl.top_k, wl.E, wl.block_m, wl.local_offset)
+        self.out = torch.zeros((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        loc = self.ids.reshape(-1) - wl.local_offset
+        ok = (loc >= 0) & (loc < wl.n_local)
+        self.A = int(ok.sum())                               # valid local assignments
+        self.touched = len(set(loc[ok].tolist()))            # distinct routed experts
+
+    def step(self, i):
+        self.fwd(self.x, self.ids_d, self.w_d, out=self.out,
+                 weights=self.weights[i % len(self.weights)])
+
+
+def time_workload(wl, steps, warmup, replicas):
+    import torch
+
+    import block_scaled_fp4_plan_amd as bf
+
+    s = Setup(wl, replicas)
+    for i in range(warmup):
+        s.step(i)
+    torch.cuda.synchronize()
+    bf.bfp4_profile_begin(steps * 16 + 64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s.step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launched, table = bf.bfp4_profile_end()
+    return s, dt, table
+
+
+def gemm_bytes(wl, touched, A, which):
+    H, I, N1 = wl.H, wl.I, wl.N1
+    if which == 1:   # W1 of routed experts + routed token rows + requantized intermediate
+        return (touched * N1 * H * NVFP4_BYTES + wl.M * (H * NVFP4_BYTES + 4) +
+                A * I * NVFP4_BYTES)
+    return touched * H * I * NVFP4_BYTES + A * I * NVFP4_BYTES + A * H * 2
+
+
+def step_bytes(wl, touched):
+    """Whole-step algorithmic HBM bytes: routed experts' weights, x, out read+write, ids+weights."""
+    return (touched * (wl.N1 * wl.H + wl.H * wl.I) * NVFP4_BYTES + wl.M * wl.H * 2 +
+            2 * wl.M * wl.H * 2 + wl.M * wl.top_k * 8)
+
+
+def step_flops(wl, A):
+    return 2.0 * A * wl.H * wl.N1 + 2.0 * A * wl.I * wl.H
+
+
+def kernel_ms(table, prefix):
+    for name, (cnt, tot) in table.items():
+        if name.startswith(prefix):
+            return tot / cnt, cnt, name
+    return None, 0, None
+
+
+def cpu_baseline(s, sample_tokens=1):
+    """The oracle (float64 numpy, as it stands) on a bounded sample: the per-call path for the
+    first token(s): activation quantization, plan, permutation, the token's experts (GEMM1,
+    activation, requantization, GEMM2) and the combine.  Weight quantization is offline on both
+    sides and excluded."""
+    import oracle
+    from oracle.formats import bf16_bits_to_f32
+    from synth import to_bits
+
+    wl = s.wl
+    T = sample_tokens
+    ids = s.ids[:T]
+    experts = sorted(set(int(e) for e in ids.reshape(-1)))
+    wq = {}
+    for e in experts:                                           # offline part (untimed)
+        q1, s1, a1 = oracle.quantize_expert_weights(to_bits(s.w1[e])[None])
+        q2, s2, a2 = oracle.quantize_expert_weights(to_bits(s.w2[e])[None])
+        wq[e] = ((q1[0], s1[0], q2[0], s2[0]), a1[0], a2[0])
+    a1v = np.zeros(wl.n_local, np.float32)
+    a2v = np.zeros(wl.n_local, np.float32)
+    for e in experts:
+        a1v[e], a2v[e] = wq[e][1], wq[e][2]
+    t0 = time.perf_counter()
+    aq, asf, adec = oracle.quantize_nvfp4(bf16_bits_to_f32(s.x_bits[:T]), oracle.SCALE_PER_ROW)
+    srt, eids, P, ttr = oracle.moe_plan(ids, wl.E, wl.local_offset, wl.n_local, wl.block_m)
+    res = oracle.fused_moe_nvfp4(aq, asf, adec, lambda e: wq[e][0], a1v, a1v, a2v, 1.0, srt, eids,
+                                 P, ttr, s.w[:T], wl.top_k, wl.block_m, oracle.ACT_SWIGLU)
+    dt = time.perf_counter() - t0
+    import torch
+
+    out = torch.zeros_like(s.out)                      # one fresh GPU forward for the comparison
+    s.fwd(s.x, s.ids_d, s.w_d, out=out, weights=s.weights[0])
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(to_bits(out[:T])).astype(np.float64)
+    ref = bf16_bits_to_f32(res["out"]).astype(np.float64)
+    err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    return dict(value=T / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample="%d token(s) of the %s workload (%d experts), per-call path without weight "
+                       "quantization; %.2f s; float64 numpy, single thread; GPU-vs-oracle rel. "
+                       "Frobenius error on the sample %.2e" % (T, wl.name, len(experts), dt, err))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU (expert parallelism is reduced to "
+              "masking non-local experts); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synth import WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    result = {}
+    if args.workload in ("decode", "both"):
+        wl = WORKLOADS["decode"]
+        s, dt, table = time_workload(wl, args.steps, args.warmup, args.replicas)
+        ms = dt / args.steps * 1e3
+        g1_ms, g1_n, g1_name = kernel_ms(table, "gemm1")
+        g1_bytes = gemm_bytes(wl, s.touched, s.A, 1)
+        ach = g1_bytes / (g1_ms * 1e-3) / 1e9
+        traffic = traffic_for(g1_name, "decode")
+        result.update(
+            metric=METRIC, value=wl.M / (ms * 1e-3), unit="tokens/s", n_gpus=1,
+            steps=args.steps, warmup=args.warmup, ms_per_step=ms, higher_is_better=True,
+            scaling="weak", vs_baseline=None, dtype="f16", data="synthetic",
+            config={"workload": "decode: M=8 H=7168 I=2048 E=256 top_k=8 block_m=8 SwiGLU NVFP4",
+                    "touched_experts": s.touched, "assignments": s.A,
+                    "step_hbm_gbs": step_bytes(wl, s.touched) / (ms * 1e-3) / 1e9,
+                    "step_hbm_frac": step_bytes(wl, s.touched) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "weight_replicas": args.replicas,
+                    "kernel_ms": {k: v[1] / v[0] for k, v in table.items()}},
+            roofline={"bound": "hbm", "kernel": g1_name, "achieved": ach, "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                      "bytes_per_launch": g1_bytes, "avg_launch_ms": g1_ms})
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(s)
+        del s
+        torch.cuda.empty_cache()
+    if args.workload in ("prefill", "both"):
+        wl = WORKLOADS["prefill"]
+        s, dt, table = time_workload(wl, args.steps, args.warmup, 1)
+        ms = dt / args.steps * 1e3
+        g1_ms, _, g1_name = kernel_ms(table, "gemm1")
+        g1_flops = 2.0 * s.A * wl.H * wl.N1
+        ach = g1_flops / (g1_ms * 1e-3) / 1e12
+        tf = step_flops(wl, s.A) / (ms * 1e-3) / 1e12
+        pre = dict(
+            value=wl.M / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, tflops=tf,
+            tflops_frac=tf / F16_MFMA_PEAK_TFLOPS,
+            config={"workload": "prefill: M=4096 H=7168 I=2048 E=256 top_k=8 block_m=128 SwiGLU "
+                                "NVFP4", "assignments": s.A,
+                    "padded_rows": int(s.fwd.plan.num_tokens_post_padded.item()),
+                    "kernel_ms": {k: v[1] / v[0] for k, v in table.items()}},
+            roofline={"bound": "mfma", "kernel": g1_name, "achieved": ach,
+                      "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": ach / F16_MFMA_PEAK_TFLOPS,
+                      "traffic": traffic_for(g1_name, "prefill"), "flops_per_launch": g1_flops,
+                      "avg_launch_ms": g1_ms})
+        if "value" in result:
+            result["prefill"] = pre
+        else:
+            result.update(metric=METRIC, value=pre["value"], unit="tokens/s", n_gpus=1,
+                          steps=args.steps, warmup=args.warmup, ms_per_step=ms,
+                          higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
+                          data="synthetic", config=pre["config"], roofline=pre["roofline"])
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
