@@ -55,6 +55,7 @@ from .moe import (  # noqa: F401
     moe_permute,
     moe_plan,
     plan_capacity,
+    quantize_expert_rows,
     quantize_expert_weights,
     unquantized_moe_f64,
 )

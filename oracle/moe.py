@@ -109,6 +109,20 @@ def quantize_expert_weights(w_bf16_bits):
     return q.reshape(E, R, C // 2), sf.reshape(E, R, C // 16), dec.astype(np.float32)
 
 
+def quantize_expert_rows(w_bf16_bits, rows):
+    """Selected rows of one expert matrix [R, C] quantized exactly as quantize_expert_weights
+    quantizes the whole matrix: the encode scale comes from the amax of the full matrix, and each
+    row is then quantized on its own (the per-block steps only read the row).
+    Returns (q [len(rows), C/2], sf [len(rows), C/16], alpha)."""
+    from .quant import _encode_scale, quantize_rows
+
+    w = bf16_bits_to_f32(w_bf16_bits)
+    s_enc = _encode_scale(np.max(np.abs(w)))
+    sel = w[np.asarray(rows)]
+    q, sf = quantize_rows(sel, np.full(sel.shape[0], s_enc, dtype=np.float32))
+    return q, sf, (np.float32(1) / s_enc).astype(np.float32)
+
+
 def _activation(pre, I, act):
     """Typed activation on float64 pre-activations [rows, N1].
 

@@ -1,0 +1,115 @@
+"""Full-size GPU parity, in the launch configuration bench.py times.
+
+For the decode (M=8), prefill (M=4096) and skewed squared-ReLU (M=16384, 144 of 288 experts
+local) workloads: the whole plan, the activation quantization, the combine of the GPU's own
+expert outputs and finalize(unfinalized) are checked over every element; the expert
+computation is checked on a sampled token against the oracle, which quantizes that token's
+experts itself (all W1 rows, sampled W2 rows):  pre-activation within 1e-5, requantization of
+the GPU's BF16 intermediate bit-exact, final output within 2e-2 (relative Frobenius).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.formats import bf16_bits_to_f32
+from synth import WORKLOADS
+
+from gpu_common import Problem, np_bits, np_u8, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import block_scaled_fp4_plan_amd as bf
+    from block_scaled_fp4_plan_amd import runner
+
+
+def _check(name, token, n_hidden=512):
+    wl = WORKLOADS[name]
+    say("full-size", name, "token", token)
+    p = Problem(wl)
+    M, k, H, I, N1 = wl.M, wl.top_k, wl.H, wl.I, wl.N1
+    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    pw, lin = runner.prepare_weights(p.w1, p.w2, gated=wl.gated, keep_linear=True)
+    fwd = runner.MoeForward(pw, M, k, wl.E, wl.block_m, wl.local_offset)
+    cap = fwd.plan.capacity
+    dbg = dict(preact=torch.empty((cap, N1), dtype=torch.float32, device="cuda"),
+               inter=torch.empty((cap, I), dtype=torch.bfloat16, device="cuda"),
+               inter_q=torch.empty((cap, I // 2), dtype=torch.uint8, device="cuda"),
+               inter_sf=torch.empty((cap, I // 16), dtype=torch.uint8, device="cuda"))
+    out = fwd(p.x, p.ids_d, p.w_d, debug=dbg)
+    fwd_u = runner.MoeForward(pw, M, k, wl.E, wl.block_m, wl.local_offset, do_finalize=False)
+    y, wts, ttr_d = fwd_u(p.x, p.ids_d, p.w_d)
+    out_u = torch.zeros_like(out)
+    bf.bfp4_moe_finalize(y, wts, ttr_d, M, H, k, 1.0, out_u)
+    torch.cuda.synchronize()
+    out_bits = np_bits(out)
+
+    say(name, "plan + activation quantization (all elements)")
+    srt, eids, P, ttr = p.oracle_plan(wl.block_m)
+    assert int(fwd.plan.num_tokens_post_padded.item()) == P
+    assert np.array_equal(fwd.plan.sorted_token_ids.cpu().numpy(), srt)
+    assert np.array_equal(fwd.plan.expert_ids.cpu().numpy(), eids)
+    assert np.array_equal(fwd.plan.token_to_row.cpu().numpy(), ttr)
+    aq, asf, adec = p.oracle_activations()
+    assert np.array_equal(np_u8(fwd.a_q), aq) and np.array_equal(np_u8(fwd.a_sf), asf)
+    assert np.array_equal(fwd.a_dec.cpu().numpy().view(np.uint32), adec.view(np.uint32))
+
+    say(name, "finalize(unfinalized) and the ordered combine (all elements)")
+    assert np.array_equal(np_bits(out_u), out_bits)
+    ybits = np_bits(y)
+    ydict = {int(r): bf16_bits_to_f32(ybits[r]).astype(np.float64) for r in ttr.reshape(-1) if r >= 0}
+    assert np.array_equal(oracle.combine(np.zeros((M, H), np.uint16), ydict, p.w, ttr), out_bits)
+
+    say(name, "expert computation of token", token)
+    rng = np.random.default_rng(token)
+    hs = np.sort(rng.choice(H, n_hidden, replace=False))
+    rows_t = [int(r) for r in ttr[token] if r >= 0]
+    assert rows_t, "sampled token has no routed slot"
+    inter_bits = np_bits(dbg["inter"][rows_t])
+    pre_gpu = dbg["preact"][rows_t].cpu().numpy()
+    pre_ref, ys = [], {}
+    for j in range(k):
+        r = int(ttr[token, j])
+        if r < 0:
+            continue
+        e = int(eids[r // wl.block_m])
+        b1, b2 = (np_bits(p.w1[e]), np_bits(p.w2[e]))
+        q1, s1, a1 = oracle.quantize_expert_rows(b1, np.arange(N1))
+        q2, s2, a2 = oracle.quantize_expert_rows(b2, hs)
+        # the GPU's weight quantization is the oracle's, bit for bit, on these rows
+        assert np.array_equal(np_u8(lin[0][e]), q1) and np.array_equal(np_u8(lin[1][e]), s1)
+        assert np.array_equal(np_u8(lin[2][e][torch.from_numpy(hs).cuda()]), q2)
+        assert pw.alpha1_gate[e].item() == float(a1) and pw.alpha2[e].item() == float(a2)
+        o = oracle.expert_rows_forward(aq[token:token + 1], asf[token:token + 1],
+                                       adec[token:token + 1], q1, s1, q2, s2, a1, a1, a2, 1.0, act)
+        pre_ref.append(o["pre"][0])
+        ys[r] = o["y"][0]
+    e_pre = rel_fro(pre_gpu, np.stack(pre_ref))
+    rq, rsf, _ = oracle.quantize_nvfp4(bf16_bits_to_f32(inter_bits), oracle.SCALE_FIXED, None, 1.0)
+    assert np.array_equal(np_u8(dbg["inter_q"][rows_t]), rq)
+    assert np.array_equal(np_u8(dbg["inter_sf"][rows_t]), rsf)
+    ref = oracle.combine(np.zeros((1, len(hs)), np.uint16), ys, p.w[token:token + 1],
+                         ttr[token:token + 1])
+    e_out = rel_fro(bf16_bits_to_f32(out_bits[token, hs]), bf16_bits_to_f32(ref[0]))
+    say("%s: pre %.3e  out(sampled) %.3e" % (name, e_pre, e_out))
+    assert e_pre <= 1e-5
+    assert e_out <= 2e-2
+
+
+def test_fullsize_decode_m8():
+    _check("decode", token=3)
+
+
+def test_fullsize_prefill_m4096():
+    _check("prefill", token=2731)
+
+
+def test_fullsize_skewed_relu2_m16384():
+    wl = WORKLOADS["skewed_relu2"]
+    from synth import make_routing
+    ids, _ = make_routing(wl, 0)
+    loc = (ids >= wl.local_offset) & (ids < wl.local_offset + wl.n_local)
+    token = int(np.nonzero(loc.sum(axis=1) >= 3)[0][7])
+    _check("skewed_relu2", token=token)

@@ -132,3 +132,14 @@ def test_dequantize_int_is_exact():
 def test_unpack_even_value_low_nibble():
     codes = unpack_codes(np.array([[0x21, 0xF7]], dtype=np.uint8))
     assert list(codes[0]) == [1, 2, 7, 15]
+
+
+def test_expert_rows_subset_matches_whole_matrix():
+    """Quantizing selected rows with the whole matrix's scale equals slicing the full result."""
+    rng = np.random.default_rng(8)
+    from synth import bf16_bits
+    w = bf16_bits(rng.standard_normal((64, 128)) * 0.02)
+    q, sf, a = oracle.quantize_expert_weights(w[None])
+    rows = [3, 17, 40, 63]
+    q2, sf2, a2 = oracle.quantize_expert_rows(w, rows)
+    assert np.array_equal(q2, q[0, rows]) and np.array_equal(sf2, sf[0, rows]) and a2 == a[0]
