@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/bfp4moe.h"
+#include "bfp4moe.h"
 #include "runtime.h"
 
 namespace bfp4 {
@@ -221,7 +221,8 @@ size_t bfp4_workspace_size(int64_t M, int64_t H, int64_t I, int top_k, int num_l
                            int block_m, int do_finalize) {
   size_t cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
   if (H <= 0 || I <= 0) return 0;
-  size_t ws = align_up(cap * (size_t)(I / 2)) + align_up(cap * (size_t)(I / 16));
+  size_t ws = align_up(cap * (size_t)(I / 2)) + align_up(cap * (size_t)(I / 16)) +
+              align_up(moe_gemm_tile_ws_bytes((int64_t)cap, block_m));
   if (do_finalize) ws += align_up(cap * (size_t)H * 2);
   return ws;
 }
@@ -285,6 +286,8 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   w += align_up(capacity * (size_t)(I / 2));
   uint8_t* hsf = (debug && debug->inter_sf) ? debug->inter_sf : w;
   w += align_up(capacity * (size_t)(I / 16));
+  uint8_t* tile_ws = w;
+  w += align_up(moe_gemm_tile_ws_bytes((int64_t)capacity, block_m));
   uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
 
   MoeGemmProblem p{};
@@ -313,6 +316,7 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   p.y = y;
   p.dbg_pre = debug ? debug->preact : nullptr;
   p.dbg_inter = debug ? debug->inter : nullptr;
+  p.tile_ws = tile_ws;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_moe_gemms(p, s);
   if (e != hipSuccess) return BFP4_ERR_LAUNCH;

@@ -121,6 +121,8 @@ struct GemmArgs {
   int64_t cap;
   int64_t sentinel;
   int top_k, block_m, n_sub, nloc;
+  const int2* tiles;         // nullptr: one tile per (block, sub-tile); else {first row, rows}
+  const int32_t* n_tiles;
   // weights
   const uint8_t* panel;
   int64_t expert_bytes, rg_bytes;
@@ -141,51 +143,372 @@ struct GemmArgs {
 
 enum { EPI_SWIGLU = 0, EPI_RELU2 = 1, EPI_DOWN = 2 };
 
-template <int FN, int FM, int EPI, int OCC>
-__global__ __launch_bounds__(256, OCC) void moe_gemm_kernel(GemmArgs a) {
-  constexpr int MT = 32 * FM;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* tok0 = smem;
-  uint8_t* tok1 = smem + MT * kTokPitch;
-  int* row_src = reinterpret_cast<int*>(smem + 2 * MT * kTokPitch);
-  float* row_scale = reinterpret_cast<float*>(row_src + MT);
-  int* sh_nvalid = reinterpret_cast<int*>(row_scale + MT);
 
+// Tiles of up to `tb` consecutive plan blocks of one expert segment (aligned to the segment's
+// first block), compacted into a list; run once per fused call by a single workgroup.
+__global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ eids,
+                                                         const int32_t* __restrict__ ntpp,
+                                                         int64_t cap, int block_m, int tb,
+                                                         int2* __restrict__ tiles,
+                                                         int32_t* __restrict__ n_tiles) {
+  __shared__ int scan[1024];
+  __shared__ int carry_start, carry_count;
+  const int tid = threadIdx.x;
+  int64_t P = *ntpp;
+  if (P > cap) P = cap;
+  if (P < 0) P = 0;
+  const int nblk = (int)(P / block_m);
+  if (tid == 0) {
+    carry_start = 0;
+    carry_count = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < nblk; base += 1024) {
+    const int b = base + tid;
+    const bool valid = b < nblk;
+    const int e = valid ? eids[b] : -2;
+    const bool seg_start = valid && (b == 0 || eids[b - 1] != e);
+    // inclusive max-scan of segment starts
+    scan[tid] = seg_start ? b : -1;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      int v = (tid >= off) ? scan[tid - off] : -1;
+      __syncthreads();
+      scan[tid] = max(scan[tid], v);
+      __syncthreads();
+    }
+    const int s0 = max(scan[tid], carry_start);
+    const bool is_tile = valid && ((b - s0) % tb == 0);
+    __syncthreads();
+    // exclusive prefix sum of tile starts
+    scan[tid] = is_tile ? 1 : 0;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      int v = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int incl = scan[tid];
+    const int total = scan[1023];
+    if (is_tile) {
+      int nb = 1;
+      while (nb < tb && b + nb < nblk && eids[b + nb] == e) ++nb;
+      tiles[carry_count + incl - 1] = make_int2(b * block_m, nb * block_m);
+    }
+    __syncthreads();                         // every thread has read carry_start/count
+    if (tid == min(1023, nblk - 1 - base)) carry_start = s0;
+    if (tid == 0) carry_count += total;
+    __syncthreads();
+  }
+  if (tid == 0) *n_tiles = carry_count;
+}
+
+struct Smem {
+  uint8_t* tok;         // two token stages, MT rows each
+  int* row_src;
+  float* row_scale;
+  int* sh_nvalid;
+};
+
+// LDS slot (16 bytes = 8 FP16) of the 8 token values a lane needs for chunk c, K half h, MFMA
+// step s of a stage.  The writer of 16-value block blk (blk = 4c + 2h + s/2) stores its two
+// halves at slots blk and 8 + blk, so eight consecutive writer lanes fill 128 contiguous bytes.
+__device__ __forceinline__ int tok_slot(int c, int h, int s) {
+  return ((s & 1) << 3) + 4 * c + 2 * h + (s >> 1);
+}
+
+// Epilogue of one token column held by this lane: the lane holds 16 consecutive output rows
+// (16h + 0..15 of each of its FN weight row groups) for plan row r.
+template <int FN, int EPI>
+__device__ __forceinline__ void epilogue_frag(const GemmArgs& a, const f32x16_t (&acc)[FN], int e,
+                                              int64_t g0, int h, float s_row, int64_t r) {
+  if (EPI == EPI_DOWN) {
+    const float a2 = a.alpha_a[e];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int64_t k0 = (g0 + fn) * kGroupRows + 16 * h;
+      uint32_t pk[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float y0 = (acc[fn][2 * v] * s_row) * a2;
+        const float y1 = (acc[fn][2 * v + 1] * s_row) * a2;
+        pk[v] = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(a.y + r * a.Hout + k0);
+      dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    }
+    return;
+  }
+  const float au = a.alpha_b[e];
+  const float ag = a.alpha_a[e];
+  constexpr int NOUT = (EPI == EPI_SWIGLU) ? FN / 2 : FN;
+#pragma unroll
+  for (int p = 0; p < NOUT; ++p) {
+    float hv[16];
+    int64_t i0;
+    if (EPI == EPI_SWIGLU) {
+      i0 = ((g0 + 2 * p) >> 1) * kGroupRows + 16 * h;
+      float gt[16], up[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        gt[v] = (acc[2 * p][v] * s_row) * ag;
+        up[v] = (acc[2 * p + 1][v] * s_row) * au;
+        hv[v] = (gt[v] / (1.0f + expf(-gt[v]))) * up[v];
+      }
+      if (a.dbg_pre) {
+        float4* dg = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + i0);
+        float4* du = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + a.I + i0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          dg[v] = make_float4(gt[4 * v], gt[4 * v + 1], gt[4 * v + 2], gt[4 * v + 3]);
+          du[v] = make_float4(up[4 * v], up[4 * v + 1], up[4 * v + 2], up[4 * v + 3]);
+        }
+      }
+    } else {
+      i0 = (g0 + p) * kGroupRows + 16 * h;
+      float pr[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        pr[v] = (acc[p][v] * s_row) * au;
+        const float q = pr[v] > 0.0f ? pr[v] : 0.0f;
+        hv[v] = q * q;
+      }
+      if (a.dbg_pre) {
+        float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * a.I + i0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          dp[v] = make_float4(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]);
+      }
+    }
+    uint32_t bb[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      bb[v] = f32_to_bf16(hv[v]);
+      hv[v] = bf16_to_f32(bb[v]);
+    }
+    if (a.dbg_inter) {
+      uint4* d = reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + i0);
+      d[0] = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
+                        bb[6] | (bb[7] << 16));
+      d[1] = make_uint4(bb[8] | (bb[9] << 16), bb[10] | (bb[11] << 16), bb[12] | (bb[13] << 16),
+                        bb[14] | (bb[15] << 16));
+    }
+    uint32_t lo, hi;
+    const uint32_t sfb = quant_block16(hv, a.c2, lo, hi);
+    *reinterpret_cast<uint2*>(a.hq + r * (a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
+    a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+  }
+}
+
+// One tile.  WAVES waves per workgroup: wave % 4 selects FN weight row groups, wave / 4 selects
+// the token fragments fm = j * WM + wave / 4 (j < NFW), WM = WAVES / 4.
+template <int FN, int FM, int NFW, int EPI, int WAVES, int RING>
+__device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int e, int nt,
+                                         int64_t row0) {
+  constexpr int MT = 32 * FM;
+  constexpr int WM = WAVES / 4;
+  constexpr int NT = 64 * WAVES;                 // threads
+  constexpr int ROWS = 32 * NFW * WM;            // token rows staged
+  constexpr int ITEMS = ROWS * 8 / NT;           // staging items per thread
+  static_assert(ROWS * 8 % NT == 0, "staging items must divide evenly");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_n = wave & 3, wave_m = wave >> 2;
   const int h = lane >> 5, col = lane & 31;
+  const int nst = a.nch / kStageChunks;
+  const int64_t sf_rowb = a.a_rowq >> 3;
+
+  const int64_t g0 = (int64_t)nt * (4 * FN) + (int64_t)wave_n * FN;
+  const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
+  // a wave past the last row group still loads (group 0) so that every load is unconditional
+  // and the compiler's wait counts stay exact; it skips the MFMAs and the epilogue
+  const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
+                         lane * 16;
+
+  // token loader: item = (row, 16-value block) of a 128-value stage; thread tid handles block
+  // tid % 8 of rows tid / 8 + it * NT / 8.  Rows without a routed slot are not staged: their
+  // LDS rows hold stale values, which only reach MFMA output columns that are discarded.
+  const int blk = tid & 7;
+  const int lds0 = (tid >> 3) * kTokPitch + blk * 16;
+  // rows without a routed slot load token row 0 (any valid row) instead of branching
+  int64_t it_src[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int src = sm.row_src[(tid >> 3) + it * (NT / 8)];
+    it_src[it] = src < 0 ? 0 : src;
+  }
+
+  f32x16_t acc[FN][NFW];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) acc[i][j] = f32x16_t{};
+
+  uint4 W[RING][kStageChunks][FN];
+  uint32_t S[RING][FN];
+  uint2 Tq[ITEMS];
+  uint32_t Ts[ITEMS];
+
+  auto load_w = [&](uint4 (&Wd)[kStageChunks][FN], uint32_t (&Sd)[FN], int st) {
+    const int64_t sc = st / (kSuperChunks / kStageChunks);
+    const int c0 = (st * kStageChunks) % kSuperChunks;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const uint8_t* base = wbase + fn * a.rg_bytes + sc * kSuperBytes;
+      Sd[fn] = *reinterpret_cast<const uint32_t*>(base + 2 * c0);
+#pragma unroll
+      for (int c = 0; c < kStageChunks; ++c)
+        Wd[c][fn] = *reinterpret_cast<const uint4*>(base + kUnit + (c0 + c) * kUnit);
+    }
+  };
+  auto load_t = [&](int st) {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int64_t src = it_src[it];
+      Tq[it] = *reinterpret_cast<const uint2*>(a.a_q + src * a.a_rowq + st * 64 + blk * 8);
+      Ts[it] = a.a_sf[src * sf_rowb + st * 8 + blk];
+    }
+  };
+  auto store_t = [&](uint8_t* buf) {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const uint32_t s2 = e4m3_scale_h2(Ts[it]);
+      uint8_t* d = buf + lds0 + it * (NT / 8) * kTokPitch;
+      *reinterpret_cast<h8_t*>(d) = decode8(Tq[it].x, s2);
+      *reinterpret_cast<h8_t*>(d + 128) = decode8(Tq[it].y, s2);
+    }
+  };
+  auto compute = [&](const uint4 (&Wd)[kStageChunks][FN], const uint32_t (&Sd)[FN],
+                     const uint8_t* buf) {
+    if (!wave_on) return;
+#pragma unroll
+    for (int c = 0; c < kStageChunks; ++c) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        h8_t T[NFW];
+#pragma unroll
+        for (int j = 0; j < NFW; ++j)
+          T[j] = *reinterpret_cast<const h8_t*>(buf + ((j * WM + wave_m) * 32 + col) * kTokPitch +
+                                                tok_slot(c, h, s) * 16);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const uint32_t wd = (s == 0) ? Wd[c][fn].x : (s == 1) ? Wd[c][fn].y
+                              : (s == 2) ? Wd[c][fn].z : Wd[c][fn].w;
+          const uint32_t sb = (Sd[fn] >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
+          const h8_t Wv = decode8(wd, e4m3_scale_h2(sb));
+#pragma unroll
+          for (int j = 0; j < NFW; ++j)
+            acc[fn][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wv, T[j], acc[fn][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- pipeline: weights RING-1 stages ahead in registers, tokens one stage ahead in LDS ----
+  // Loads are never conditional (stage indices are clamped; the extra loads at the end re-read
+  // the last stage), so the waits the compiler places before each use count exactly the loads
+  // issued after it and the prefetch stays in flight.  The caller guarantees nst % RING == 0.
+#pragma unroll
+  for (int d = 0; d < RING - 1; ++d) load_w(W[d], S[d], min(d, nst - 1));
+  load_t(0);
+  store_t(sm.tok);
+  lds_barrier();
+  for (int st0 = 0; st0 < nst; st0 += RING) {
+#pragma unroll
+    for (int d = 0; d < RING; ++d) {
+      const int st = st0 + d;
+      // token loads first: the wait for them at the end of this stage (vmcnt counts in issue
+      // order) must not also wait for the weight loads issued for a later stage
+      load_t(min(st + 1, nst - 1));
+      load_w(W[(d + RING - 1) % RING], S[(d + RING - 1) % RING], min(st + RING - 1, nst - 1));
+      compute(W[d], S[d], sm.tok + (st & 1) * (MT * kTokPitch));
+      store_t(sm.tok + ((st + 1) & 1) * (MT * kTokPitch));
+      lds_barrier();
+    }
+  }
+
+  // ---- epilogue ----
+  if (!wave_on) return;
+#pragma unroll
+  for (int j = 0; j < NFW; ++j) {
+    const int m = (j * WM + wave_m) * 32 + col;
+    if (sm.row_src[m] < 0) continue;
+    f32x16_t accj[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) accj[fn] = acc[fn][j];
+    epilogue_frag<FN, EPI>(a, accj, e, g0, h, sm.row_scale[m], row0 + m);
+  }
+}
+
+template <int FN, int FM, int EPI, int WAVES, int RING>
+__device__ __forceinline__ void run_nfw(const GemmArgs& a, const Smem& sm, int e, int nt,
+                                        int64_t row0, int nfw) {
+  if constexpr (FM == 1) {
+    run_tile<FN, FM, 1, EPI, WAVES, RING>(a, sm, e, nt, row0);
+  } else {
+    static_assert(FM / (WAVES / 4) == 4, "prefill tile: 4 token fragments per wave at most");
+    switch (nfw) {
+      case 1: run_tile<FN, FM, 1, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
+      case 2: run_tile<FN, FM, 2, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
+      case 3: run_tile<FN, FM, 3, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
+      default: run_tile<FN, FM, 4, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
+    }
+  }
+}
+
+template <int FN, int FM, int EPI, int OCC, int WAVES, int RING>
+__global__ __launch_bounds__(64 * WAVES, OCC) void moe_gemm_kernel(GemmArgs a) {
+  constexpr int MT = 32 * FM;
+  constexpr int WM = WAVES / 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  Smem sm;
+  sm.tok = smem;
+  sm.row_src = reinterpret_cast<int*>(smem + 2 * MT * kTokPitch);
+  sm.row_scale = reinterpret_cast<float*>(sm.row_src + MT);
+  sm.sh_nvalid = reinterpret_cast<int*>(sm.row_scale + MT);
+
+  const int tid = threadIdx.x;
   int64_t P = *a.ntpp;
   if (P > a.cap) P = a.cap;
   if (P < 0) P = 0;
-  const int64_t n_mt = (P / a.block_m) * a.n_sub;
+  const int64_t n_mt = a.tiles ? (int64_t)(*a.n_tiles) : (P / a.block_m) * a.n_sub;
   const int xcd = blockIdx.x & 7;
   const int64_t Q = gridDim.x >> 3;
   const int64_t li = blockIdx.x >> 3;
   const int64_t mts_here = (n_mt > xcd) ? (n_mt - xcd + 7) / 8 : 0;
   const int64_t ntask = mts_here * a.n_nt;
-  const int nst = a.nch / kStageChunks;
-  const int64_t sf_rowb = a.a_rowq >> 3;
 
   for (int64_t k = li; k < ntask; k += Q) {
     const int64_t mt = xcd + 8 * (k / a.n_nt);
     const int nt = (int)(k % a.n_nt);
-    const int64_t b = mt / a.n_sub;
-    const int sub = (int)(mt % a.n_sub);
-    const int64_t row0 = b * a.block_m + (int64_t)sub * MT;
-    const int rows_here = min(MT, a.block_m - sub * MT);
-    const int e = a.eids[b];
+    int64_t row0;
+    int rows_here;
+    if (a.tiles) {
+      const int2 t = a.tiles[mt];
+      row0 = t.x;
+      rows_here = min(MT, t.y);
+    } else {
+      const int64_t b = mt / a.n_sub;
+      const int sub = (int)(mt % a.n_sub);
+      row0 = b * a.block_m + (int64_t)sub * MT;
+      rows_here = min(MT, a.block_m - sub * MT);
+    }
+    if (row0 < 0 || row0 + rows_here > P) continue;
+    const int e = a.eids[row0 / a.block_m];
     if (e < 0 || e >= a.nloc) continue;
 
     __syncthreads();                         // the previous task is done with LDS
-    if (tid == 0) *sh_nvalid = 0;
+    if (tid == 0) *sm.sh_nvalid = 0;
     __syncthreads();
     if (tid < MT) {
       int src = -1;
       float sc = 0.0f;
       if (tid < rows_here) {
-        int64_t ent = a.sorted[row0 + tid];
+        const int64_t ent = a.sorted[row0 + tid];
         if (ent >= 0 && ent < a.sentinel) {
           if (a.gather) {
-            int64_t t = ent / a.top_k;
+            const int64_t t = ent / a.top_k;
             src = (int)t;
             sc = a.a_dec[t];
           } else {
@@ -194,217 +517,185 @@ __global__ __launch_bounds__(256, OCC) void moe_gemm_kernel(GemmArgs a) {
           }
         }
       }
-      row_src[tid] = src;
-      row_scale[tid] = sc;
-      if (src >= 0) atomicMax(sh_nvalid, tid + 1);
+      sm.row_src[tid] = src;
+      sm.row_scale[tid] = sc;
+      if (src >= 0) atomicMax(sm.sh_nvalid, tid + 1);
     }
     __syncthreads();
-    const int nvalid = *sh_nvalid;
+    const int nvalid = *sm.sh_nvalid;
     if (nvalid == 0) continue;
-    const int fm_eff = (nvalid + 31) >> 5;
+    // token fragments per wave: ceil(fragments holding a valid row / WM); a trailing fragment
+    // with no valid row is computed and discarded
+    const int nfw = (((nvalid + 31) >> 5) + WM - 1) / WM;
+    const int nst = a.nch / kStageChunks;
+    if (nst % RING == 0) {
+      run_nfw<FN, FM, EPI, WAVES, RING>(a, sm, e, nt, row0, nfw);
+    } else if (RING > 2 && nst % 2 == 0) {
+      run_nfw<FN, FM, EPI, WAVES, 2>(a, sm, e, nt, row0, nfw);
+    } else {
+      run_nfw<FN, FM, EPI, WAVES, 1>(a, sm, e, nt, row0, nfw);
+    }
+  }
+}
 
-    // ---- this wave's weight row groups ----
+// Decode-sized plan blocks (block_m <= 32).  A workgroup task is (plan block, 4*FN weight row
+// groups).  The block's routed token rows (at most 32) are copied once, still packed (NVFP4
+// bytes and scale bytes for the whole K), into LDS; after one barrier every wave streams its own
+// FN weight row groups from HBM RING-1 stages ahead in registers and reads its token operand
+// from LDS, with no further barrier, so the four weight streams never wait for each other.
+template <int FN, int EPI, int RING>
+__global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int* row_src = reinterpret_cast<int*>(smem);
+  float* row_scale = reinterpret_cast<float*>(smem + 32 * sizeof(int));
+  uint8_t* tok = smem + 64 * sizeof(int);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  // per staged row: K/2 packed bytes then K/16 scale bytes, rounded up to 16 bytes
+  const int64_t pitch = (a.a_rowq + (a.a_rowq >> 3) + 15) & ~(int64_t)15;
+  int64_t P = *a.ntpp;
+  if (P > a.cap) P = a.cap;
+  if (P < 0) P = 0;
+  const int64_t nblk = P / a.block_m;
+  const int64_t ntask = nblk * a.n_nt;
+  const int nst = a.nch / kStageChunks;
+  const int rows_max = min(a.block_m, 32);
+
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int64_t b = task / a.n_nt;
+    const int nt = (int)(task - b * a.n_nt);
+    const int e = a.eids[b];
+    if (e < 0 || e >= a.nloc) continue;
+    __syncthreads();                                   // previous task done with LDS
+    if (tid < 32) {
+      int src = -1;
+      float sc = 0.0f;
+      if (tid < rows_max) {
+        const int64_t ent = a.sorted[b * a.block_m + tid];
+        if (ent >= 0 && ent < a.sentinel) {
+          if (a.gather) {
+            src = (int)(ent / a.top_k);
+            sc = a.a_dec[src];
+          } else {
+            src = (int)(b * a.block_m + tid);
+            sc = a.a_const_scale;
+          }
+        }
+      }
+      row_src[tid] = src;
+      row_scale[tid] = sc;
+    }
+    __syncthreads();
+    // stage the routed rows: packed bytes in 16-byte units (K/2 is a multiple of 64), scale
+    // bytes in 8-byte units (K/16 is a multiple of 8)
+    const int64_t q16 = a.a_rowq >> 4, s8 = (a.a_rowq >> 3) >> 3;
+    for (int r = 0; r < rows_max; ++r) {
+      const int src = row_src[r];
+      if (src < 0) continue;
+      const uint4* sq = reinterpret_cast<const uint4*>(a.a_q + (int64_t)src * a.a_rowq);
+      const uint2* ss = reinterpret_cast<const uint2*>(a.a_sf + (int64_t)src * (a.a_rowq >> 3));
+      uint8_t* d = tok + r * pitch;
+      for (int64_t i = tid; i < q16; i += 256) reinterpret_cast<uint4*>(d)[i] = sq[i];
+      for (int64_t i = tid; i < s8; i += 256) reinterpret_cast<uint2*>(d + a.a_rowq)[i] = ss[i];
+    }
+    __syncthreads();
+
     const int64_t g0 = (int64_t)nt * (4 * FN) + (int64_t)wave * FN;
     const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
-    const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + g0 * a.rg_bytes + lane * 16;
+    const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
+                           lane * 16;
+    // lanes past the staged rows read row 0; their MFMA columns are discarded
+    const uint8_t* trow = tok + (col < rows_max ? col : 0) * pitch;
 
-    // ---- token loader: FM items per thread, item = (row, 16-value block) of a stage ----
-    int it_row[FM];
-    const uint8_t* it_q[FM];
-    const uint8_t* it_s[FM];
+    f32x16_t acc[FN];
 #pragma unroll
-    for (int it = 0; it < FM; ++it) {
-      int idx = tid + 256 * it;
-      int r = idx >> 3, blk = idx & 7;
-      it_row[it] = r * kTokPitch + blk * 32;
-      int src = row_src[r];
-      it_q[it] = (src >= 0) ? a.a_q + (int64_t)src * a.a_rowq + blk * 8 : nullptr;
-      it_s[it] = (src >= 0) ? a.a_sf + (int64_t)src * sf_rowb + blk : nullptr;
-    }
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x16_t{};
+    uint4 W[RING][kStageChunks][FN];
+    uint32_t S[RING][FN];
 
-    f32x16_t acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = f32x16_t{};
-
-    uint4 WA[kStageChunks][FN], WB[kStageChunks][FN];
-    uint32_t SA[FN], SB[FN];
-    uint2 TAq[FM], TBq[FM];
-    uint32_t TAs[FM], TBs[FM];
-
-    auto load_w = [&](uint4 (&W)[kStageChunks][FN], uint32_t (&S)[FN], int st) {
-      if (!wave_on) return;
+    auto load_w = [&](uint4 (&Wd)[kStageChunks][FN], uint32_t (&Sd)[FN], int st) {
       const int64_t sc = st / (kSuperChunks / kStageChunks);
       const int c0 = (st * kStageChunks) % kSuperChunks;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const uint8_t* base = wbase + fn * a.rg_bytes + sc * kSuperBytes;
-        S[fn] = *reinterpret_cast<const uint32_t*>(base + 2 * c0);
+        Sd[fn] = *reinterpret_cast<const uint32_t*>(base + 2 * c0);
 #pragma unroll
         for (int c = 0; c < kStageChunks; ++c)
-          W[c][fn] = *reinterpret_cast<const uint4*>(base + kUnit + (c0 + c) * kUnit);
+          Wd[c][fn] = *reinterpret_cast<const uint4*>(base + kUnit + (c0 + c) * kUnit);
       }
     };
-    auto load_t = [&](uint2 (&Tq)[FM], uint32_t (&Ts)[FM], int st) {
-#pragma unroll
-      for (int it = 0; it < FM; ++it) {
-        if (it_q[it]) {
-          Tq[it] = *reinterpret_cast<const uint2*>(it_q[it] + st * 64);
-          Ts[it] = it_s[it][st * 8];
-        } else {
-          Tq[it] = make_uint2(0, 0);
-          Ts[it] = 0;
-        }
-      }
-    };
-    auto store_t = [&](const uint2 (&Tq)[FM], const uint32_t (&Ts)[FM], uint8_t* buf) {
-#pragma unroll
-      for (int it = 0; it < FM; ++it) {
-        uint32_t s2 = e4m3_scale_h2(Ts[it]);
-        h8_t lo = decode8(Tq[it].x, s2);
-        h8_t hi = decode8(Tq[it].y, s2);
-        *reinterpret_cast<h8_t*>(buf + it_row[it]) = lo;
-        *reinterpret_cast<h8_t*>(buf + it_row[it] + 16) = hi;
-      }
-    };
-    auto compute = [&](const uint4 (&W)[kStageChunks][FN], const uint32_t (&S)[FN],
-                       const uint8_t* buf) {
-      if (!wave_on) return;
+    auto compute = [&](const uint4 (&Wd)[kStageChunks][FN], const uint32_t (&Sd)[FN], int st) {
+      const uint2 tsc = *reinterpret_cast<const uint2*>(trow + a.a_rowq + st * 8);
 #pragma unroll
       for (int c = 0; c < kStageChunks; ++c) {
+        const uint4 td4 = *reinterpret_cast<const uint4*>(trow + st * 64 + c * 32 + 16 * h);
+        const uint32_t tsw = (c == 0) ? tsc.x : tsc.y;      // scale bytes of blocks 4c..4c+3
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          h8_t T[FM];
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
-            if (fm < fm_eff)
-              T[fm] = *reinterpret_cast<const h8_t*>(buf + (fm * 32 + col) * kTokPitch + c * 128 +
-                                                     h * 64 + s * 16);
-          }
+          const uint32_t td = (s == 0) ? td4.x : (s == 1) ? td4.y : (s == 2) ? td4.z : td4.w;
+          const uint32_t tsb = (tsw >> (8 * (2 * h + (s >> 1)))) & 0xFFu;
+          const h8_t Tv = decode8(td, e4m3_scale_h2(tsb));
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
-            uint32_t wd = (s == 0) ? W[c][fn].x : (s == 1) ? W[c][fn].y : (s == 2) ? W[c][fn].z
-                                                                                   : W[c][fn].w;
-            uint32_t sb = (S[fn] >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
-            h8_t Wd = decode8(wd, e4m3_scale_h2(sb));
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-              if (fm < fm_eff)
-                acc[fn][fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wd, T[fm], acc[fn][fm], 0, 0, 0);
-            }
+            const uint32_t wd = (s == 0) ? Wd[c][fn].x : (s == 1) ? Wd[c][fn].y
+                                : (s == 2) ? Wd[c][fn].z : Wd[c][fn].w;
+            const uint32_t sb = (Sd[fn] >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
+            const h8_t Wv = decode8(wd, e4m3_scale_h2(sb));
+            acc[fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wv, Tv, acc[fn], 0, 0, 0);
           }
         }
       }
     };
 
-    // ---- pipeline: stage s+1 loads in flight while stage s computes ----
-    load_w(WA, SA, 0);
-    load_t(TAq, TAs, 0);
-    store_t(TAq, TAs, tok0);
-    lds_barrier();
-    for (int st = 0; st < nst; st += 2) {
-      if (st + 1 < nst) {
-        load_w(WB, SB, st + 1);
-        load_t(TBq, TBs, st + 1);
-      }
-      compute(WA, SA, tok0);
-      if (st + 1 < nst) store_t(TBq, TBs, tok1);
-      lds_barrier();
-      if (st + 1 >= nst) break;
-      if (st + 2 < nst) {
-        load_w(WA, SA, st + 2);
-        load_t(TAq, TAs, st + 2);
-      }
-      compute(WB, SB, tok1);
-      if (st + 2 < nst) store_t(TAq, TAs, tok0);
-      lds_barrier();
-    }
-
-    // ---- epilogue ----
-    if (!wave_on) continue;
+    // weight loads are unconditional (stage index clamped) so the compiler's waits count them
+    // exactly; the tail of the last ring pass leaves through the break
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      if (fm >= fm_eff) continue;
-      const int m = fm * 32 + col;
-      if (row_src[m] < 0) continue;
-      const float s_row = row_scale[m];
-      const int64_t r = row0 + m;
-      if (EPI == EPI_DOWN) {
-        const float a2 = a.alpha_a[e];
+    for (int d = 0; d < RING - 1; ++d) load_w(W[d], S[d], min(d, nst - 1));
+    for (int st0 = 0; st0 < nst; st0 += RING) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int64_t k0 = (g0 + fn) * kGroupRows + 16 * h;
-          uint32_t pk[8];
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            float y0 = (acc[fn][fm][2 * v] * s_row) * a2;
-            float y1 = (acc[fn][fm][2 * v + 1] * s_row) * a2;
-            pk[v] = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
-          }
-          uint4* dst = reinterpret_cast<uint4*>(a.y + r * a.Hout + k0);
-          dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-          dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-        }
-      } else {
-        const float au = a.alpha_b[e];
-        const float ag = a.alpha_a[e];
-        constexpr int NOUT = (EPI == EPI_SWIGLU) ? FN / 2 : FN;
-#pragma unroll
-        for (int p = 0; p < NOUT; ++p) {
-          float hv[16];
-          int64_t i0;
-          if (EPI == EPI_SWIGLU) {
-            i0 = ((g0 + 2 * p) >> 1) * kGroupRows + 16 * h;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              float gt = (acc[2 * p][fm][v] * s_row) * ag;
-              float up = (acc[2 * p + 1][fm][v] * s_row) * au;
-              if (a.dbg_pre) {
-                a.dbg_pre[r * (2 * a.I) + i0 + v] = gt;
-                a.dbg_pre[r * (2 * a.I) + a.I + i0 + v] = up;
-              }
-              float sg = gt / (1.0f + expf(-gt));
-              hv[v] = sg * up;
-            }
-          } else {
-            i0 = (g0 + p) * kGroupRows + 16 * h;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              float pr = (acc[p][fm][v] * s_row) * au;
-              if (a.dbg_pre) a.dbg_pre[r * a.I + i0 + v] = pr;
-              float q = pr > 0.0f ? pr : 0.0f;
-              hv[v] = q * q;
-            }
-          }
-          uint32_t bb[16];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            bb[v] = f32_to_bf16(hv[v]);
-            hv[v] = bf16_to_f32(bb[v]);
-          }
-          if (a.dbg_inter) {
-            uint4* d = reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + i0);
-            d[0] = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
-                              bb[6] | (bb[7] << 16));
-            d[1] = make_uint4(bb[8] | (bb[9] << 16), bb[10] | (bb[11] << 16),
-                              bb[12] | (bb[13] << 16), bb[14] | (bb[15] << 16));
-          }
-          uint32_t lo, hi;
-          uint32_t sfb = quant_block16(hv, a.c2, lo, hi);
-          *reinterpret_cast<uint2*>(a.hq + r * (a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
-          a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
-        }
+      for (int d = 0; d < RING; ++d) {
+        const int st = st0 + d;
+        if (st >= nst) break;
+        const int nd = (d + RING - 1) % RING;
+        load_w(W[nd], S[nd], min(st + RING - 1, nst - 1));
+        compute(W[d], S[d], st);
       }
     }
+    if (wave_on && col < rows_max && row_src[col] >= 0)
+      epilogue_frag<FN, EPI>(a, acc, e, g0, h, row_scale[col], b * a.block_m + col);
   }
 }
 
-template <int FN, int FM, int EPI, int OCC>
-hipError_t launch_gemm(const GemmArgs& a, int64_t cap_blocks, const char* name, hipStream_t s) {
+template <int FN, int EPI>
+hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, hipStream_t s) {
+  constexpr int RING = 3;
+  auto kern = moe_gemv_kernel<FN, EPI, RING>;
+  const int rows_max = a.block_m < 32 ? a.block_m : 32;
+  const size_t lds = 64 * sizeof(int) +
+                     (size_t)rows_max * ((a.a_rowq + (a.a_rowq >> 3) + 15) & ~(int64_t)15);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  static size_t attr_lds = 0;
+  if (lds > attr_lds) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    attr_lds = lds;
+  }
+  const int64_t tasks = cap_blocks * a.n_nt;
+  const int64_t max_wg = 256LL * 4;                  // resident workgroups (4 waves each)
+  const int64_t grid = tasks < max_wg ? tasks : max_wg;
+  if (grid == 0) return hipSuccess;
+  KernelTimer t(name, s);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int FN, int FM, int EPI, int OCC, int WAVES, int RING>
+hipError_t launch_gemm(const GemmArgs& a, int64_t max_tiles, const char* name, hipStream_t s) {
   constexpr int MT = 32 * FM;
   const size_t lds = 2 * (size_t)MT * kTokPitch + 2 * MT * sizeof(int) + 16;
-  auto kern = moe_gemm_kernel<FN, FM, EPI, OCC>;
+  auto kern = moe_gemm_kernel<FN, FM, EPI, OCC, WAVES, RING>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -412,13 +703,13 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t cap_blocks, const char* name, 
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  int64_t total = cap_blocks * a.n_sub * a.n_nt;
-  int64_t maxwg = 256LL * OCC;
+  const int64_t total = max_tiles * a.n_nt;
+  const int64_t maxwg = 256LL * OCC;
   int64_t grid = total < maxwg ? total : maxwg;
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   KernelTimer t(name, s);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, s, a);
   return hipGetLastError();
 }
 
@@ -442,9 +733,11 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   const bool gated = (p.act == 0);
   const int64_t N1 = gated ? 2 * p.I : p.I;
   const int64_t cap_blocks = p.cap / p.block_m;
+  // Decode tile: 32 plan rows (one plan block of <= 32 rows); prefill tile: 256 plan rows made
+  // of up to 256/block_m consecutive blocks of one expert (or 256-row slices of larger blocks).
   const bool small = p.block_m <= 32;
-  const int MT = small ? 32 : 128;
-  const int FN = small ? 2 : 4;
+  const int MT = small ? 32 : 256;
+  const int FN = 2;
 
   GemmArgs g1{};
   g1.a_q = p.a_q;
@@ -462,6 +755,21 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.block_m = p.block_m;
   g1.n_sub = (int)((p.block_m + MT - 1) / MT);
   g1.nloc = p.nloc;
+  int64_t max_tiles = cap_blocks * g1.n_sub;
+  if (!small && p.block_m < MT) {
+    // list of multi-block tiles, built on the device from the plan
+    const int tb = MT / p.block_m;
+    g1.tiles = reinterpret_cast<const int2*>(p.tile_ws);
+    g1.n_tiles = reinterpret_cast<const int32_t*>(p.tile_ws + cap_blocks * sizeof(int2));
+    g1.n_sub = 1;
+    max_tiles = cap_blocks;
+    KernelTimer t("tile_list", s);
+    hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, p.eids, p.ntpp, p.cap,
+                       p.block_m, tb, reinterpret_cast<int2*>(p.tile_ws),
+                       reinterpret_cast<int32_t*>(p.tile_ws + cap_blocks * sizeof(int2)));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   PanelGeom pg1 = panel_geom(N1, p.H);
   g1.panel = p.panel1;
   g1.expert_bytes = pg1.expert_bytes;
@@ -501,15 +809,19 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
 
   hipError_t err;
   if (small) {
-    err = gated ? launch_gemm<2, 1, EPI_SWIGLU, 4>(g1, cap_blocks, "gemm1_swiglu_decode", s)
-                : launch_gemm<2, 1, EPI_RELU2, 4>(g1, cap_blocks, "gemm1_relu2_decode", s);
+    err = gated ? launch_gemv<2, EPI_SWIGLU>(g1, cap_blocks, "gemm1_swiglu_decode", s)
+                : launch_gemv<2, EPI_RELU2>(g1, cap_blocks, "gemm1_relu2_decode", s);
     if (err != hipSuccess) return err;
-    return launch_gemm<2, 1, EPI_DOWN, 4>(g2, cap_blocks, "gemm2_down_decode", s);
+    return launch_gemv<2, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s);
   }
-  err = gated ? launch_gemm<4, 4, EPI_SWIGLU, 1>(g1, cap_blocks, "gemm1_swiglu_prefill", s)
-              : launch_gemm<4, 4, EPI_RELU2, 1>(g1, cap_blocks, "gemm1_relu2_prefill", s);
+  err = gated ? launch_gemm<2, 8, EPI_SWIGLU, 1, 8, 2>(g1, max_tiles, "gemm1_swiglu_prefill", s)
+              : launch_gemm<2, 8, EPI_RELU2, 1, 8, 2>(g1, max_tiles, "gemm1_relu2_prefill", s);
   if (err != hipSuccess) return err;
-  return launch_gemm<4, 4, EPI_DOWN, 1>(g2, cap_blocks, "gemm2_down_prefill", s);
+  return launch_gemm<2, 8, EPI_DOWN, 1, 8, 2>(g2, max_tiles, "gemm2_down_prefill", s);
+}
+
+size_t moe_gemm_tile_ws_bytes(int64_t cap, int block_m) {
+  return (size_t)(cap / block_m) * sizeof(int2) + 16;
 }
 
 }  // namespace bfp4

@@ -63,7 +63,9 @@ struct MoeGemmProblem {
   uint16_t* y;      // [cap, H]
   float* dbg_pre;
   uint16_t* dbg_inter;
+  uint8_t* tile_ws;  // moe_gemm_tile_ws_bytes() of scratch for the prefill tile list
 };
 hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s);
+size_t moe_gemm_tile_ws_bytes(int64_t cap, int block_m);
 
 }  // namespace bfp4

@@ -51,8 +51,9 @@ def test_status_strings_and_sizes():
     assert bf.bfp4_panel_bytes(1, 256, 128, 1) == (8 * (4 + 1) + 8 * (2 + 1)) * 1024
     assert bf.bfp4_panel_bytes(2, 7168, 2048, 1) == 2 * (128 * (112 + 14) + 224 * (32 + 4)) * 1024
     assert bf.bfp4_panel_bytes(1, 250, 128, 1) == 0
-    # hq [88, 64] + hsf [88, 8] (each rounded up to 256 B) + y [88, 256] BF16
-    assert bf.bfp4_workspace_size(16, 256, 128, 2, 8, 8, 1) == 5632 + 768 + 88 * 512
+    # hq [88, 64] + hsf [88, 8] + tile list [11 x 8 B + 16] (each rounded up to 256 B)
+    # + y [88, 256] BF16
+    assert bf.bfp4_workspace_size(16, 256, 128, 2, 8, 8, 1) == 5632 + 768 + 256 + 88 * 512
     assert bf.bfp4_quantize_workspace_size(64, bf.BFP4_SCALE_PER_GROUP, 16) == 16
 
 
