@@ -56,24 +56,37 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
   return c | ((__float_as_uint(y) >> 28) & 8u);
 }
 
-// Quantize 16 values with encode scale s_enc (FP32 steps rounded separately, no FMA: the
-// library is compiled with -ffp-contract=off).  Returns the scale code; codes packed into
-// lo/hi (values 0..7 in lo, 8..15 in hi, even value in the low nibble of each byte).
+// E4M3 block scale of a block whose largest magnitude is bmax, for encode scale s_enc (FP32
+// steps rounded separately, no FMA: the library is compiled with -ffp-contract=off).  Returns
+// the scale code and sets inv, the factor that maps the block's values onto the E2M1 grid.
+__device__ __forceinline__ uint32_t block_scale(float bmax, float s_enc, float& inv) {
+  const float v = (bmax * s_enc) / kE2M1Max;
+  const uint32_t sf = f32_to_e4m3(v);
+  const float sfv = e4m3_to_f32(sf);
+  inv = (sfv == 0.0f) ? 0.0f : s_enc / sfv;
+  return sf;
+}
+
+// 8 values -> 8 E2M1 codes in one dword (value i in bits 4i..4i+3: even value in the low
+// nibble of each byte).
+__device__ __forceinline__ uint32_t quant8(const float* x, float inv) {
+  uint32_t c = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c |= f32_to_e2m1(x[i] * inv) << (4 * i);
+  return c;
+}
+
+// Quantize 16 values with encode scale s_enc.  Returns the scale code; codes packed into lo/hi
+// (values 0..7 in lo, 8..15 in hi).
 __device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float s_enc, uint32_t& lo,
                                                   uint32_t& hi) {
   float bmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) bmax = __builtin_fmaxf(bmax, __builtin_fabsf(x[i]));
-  float v = (bmax * s_enc) / kE2M1Max;
-  uint32_t sf = f32_to_e4m3(v);
-  float sfv = e4m3_to_f32(sf);
-  float inv = (sfv == 0.0f) ? 0.0f : s_enc / sfv;
-  lo = 0u;
-  hi = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) lo |= f32_to_e2m1(x[i] * inv) << (4 * i);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) hi |= f32_to_e2m1(x[8 + i] * inv) << (4 * i);
+  float inv;
+  const uint32_t sf = block_scale(bmax, s_enc, inv);
+  lo = quant8(x, inv);
+  hi = quant8(x + 8, inv);
   return sf;
 }
 
@@ -115,6 +128,32 @@ __device__ __forceinline__ h8_t decode8(uint32_t w, uint32_t scale_h2_bits) {
   r[2] = dec_pair(w, s, 2);
   r[3] = dec_pair(w, s, 3);
   return __builtin_bit_cast(h8_t, r);
+}
+
+// Raw buffer resources and loads (gfx9 resource word 3; stride 0, range checked against `bytes`).
+// Offsets: per-lane `voff` (VGPR) plus wave-uniform `soff` (SGPR), both unsigned 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint32_t buffer_load_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                   uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                    uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint2 buffer_load_u64(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 buffer_load_u128(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Wave-wide (64 lanes) reductions.

@@ -12,18 +12,25 @@
 // How (gfx950 design):
 // * Operands are NVFP4 in memory and decoded exactly to FP16 in registers (every E2M1 x E4M3
 //   product is exact in FP16), then fed to v_mfma_f32_32x32x16_f16 with FP32 accumulation.
-// * MFMA A operand = 32 weight rows, B operand = 32 plan rows (tokens).  Each wave owns FN weight
-//   row groups and streams them from HBM straight into registers (no LDS), one 16-byte load per
-//   lane per 64 K values; the token tile (32*FM plan rows) is decoded once per workgroup into LDS
-//   as FP16 and shared by the four waves.
+// * MFMA A operand = 32 weight rows, B operand = 32 plan rows (tokens).  Weights stream from HBM
+//   straight into registers (no LDS), one 16-byte load per lane per 64 K values.
+// * Prefill: a workgroup of 8 waves (two per SIMD) owns a tile of up to 256 plan rows of one
+//   expert and 8 weight row groups; the tile's tokens are decoded once per 128-K stage into LDS
+//   as FP16 and shared by the 8 waves; each wave decodes its own row group once per tile and
+//   multiplies it by every token fragment of the tile.
+// * Decode: the few routed rows of a plan block are staged packed in LDS once; each wave then
+//   streams its weight row groups without further barriers.
 // * Weight panels put, for each 32-row group and each 64-value K chunk, exactly the 1 KiB a wave
 //   loads in one instruction (lane l: row l%32, K half l/32), scales grouped per 512 K values.
 // * Inside a 32-row group the rows are permuted so that each lane's 16 accumulator rows are 16
-//   consecutive output indices: the requantization block (16 values) is lane-local, and a GEMM2
-//   lane stores 32 contiguous bytes.  Gated W1 alternates gate and up row groups, so a wave
-//   holds gate and up of the same 32 intermediate indices.
+//   consecutive logical rows: the requantization block (16 values) stays within a lane pair, and
+//   a GEMM2 lane stores 32 contiguous bytes.  A gated W1 group holds the gate rows of 16
+//   intermediate indices in its first 16 logical rows and the up rows of the same indices in
+//   the last 16, so the SwiGLU epilogue pairs lane l with lane l + 32.
 // * Plan rows past the device-side extent, padding rows and 32-row token fragments with no valid
 //   row are skipped; a static schedule interleaves M tiles over the 8 XCDs.
+#include <type_traits>
+
 #include "device.h"
 #include "runtime.h"
 
@@ -38,6 +45,8 @@ constexpr int kUnit = 1024;
 constexpr int kSuperBytes = (kSuperChunks + 1) * kUnit;
 constexpr int kStageChunks = 2;     // chunks per pipeline stage (128 K values)
 constexpr int kTokPitch = 272;      // LDS bytes per token row per stage: 128 FP16 + 16 pad
+constexpr int kTileRows = 256;      // plan rows per prefill tile (8 token fragments)
+constexpr int kTileGroups = 8;      // weight row groups per prefill task (one per wave)
 
 // Logical row (within a 32-row group) held at physical row rho: the MFMA 32x32 accumulator of
 // lane l holds rows 8i + 4*(l/32) + j (i, j in 0..3); they are made logical rows
@@ -78,8 +87,9 @@ __global__ void prepare_kernel(const uint8_t* __restrict__ w_q, const uint8_t* _
   int64_t j = u - sc * (kSuperChunks + 1);
   int rho = lane & 31, h = lane >> 5;
   int64_t lr;
-  if (half_rows > 0) {          // gated W1: groups alternate gate (even) and up (odd)
-    lr = (grp & 1) * half_rows + (grp >> 1) * kGroupRows + group_perm(rho);
+  if (half_rows > 0) {          // gated W1: gate rows 16*grp.. then the up rows of the same indices
+    const int gp = group_perm(rho);
+    lr = (gp >= 16 ? half_rows : 0) + grp * 16 + (gp & 15);
   } else {
     lr = grp * kGroupRows + group_perm(rho);
   }
@@ -110,6 +120,7 @@ struct GemmArgs {
   // token operand
   const uint8_t* a_q;
   const uint8_t* a_sf;
+  int64_t a_rows;            // rows of a_q / a_sf
   const float* a_dec;        // per-token decode scale (gather) or nullptr
   float a_const_scale;       // decode scale when a_dec is nullptr
   int64_t a_rowq;            // bytes per packed token row (K/2)
@@ -120,9 +131,10 @@ struct GemmArgs {
   const int32_t* ntpp;
   int64_t cap;
   int64_t sentinel;
-  int top_k, block_m, n_sub, nloc;
-  const int2* tiles;         // nullptr: one tile per (block, sub-tile); else {first row, rows}
+  int top_k, block_m, nloc;
+  const int2* tiles;         // prefill tiles {first row, rows}, longest and shortest alternating
   const int32_t* n_tiles;
+  uint32_t* task_counter;    // prefill: next task to hand out (cleared by the tile list)
   // weights
   const uint8_t* panel;
   int64_t expert_bytes, rg_bytes;
@@ -144,24 +156,34 @@ struct GemmArgs {
 enum { EPI_SWIGLU = 0, EPI_RELU2 = 1, EPI_DOWN = 2 };
 
 
-// Tiles of up to `tb` consecutive plan blocks of one expert segment (aligned to the segment's
-// first block), compacted into a list; run once per fused call by a single workgroup.
-__global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ eids,
-                                                         const int32_t* __restrict__ ntpp,
-                                                         int64_t cap, int block_m, int tb,
-                                                         int2* __restrict__ tiles,
-                                                         int32_t* __restrict__ n_tiles) {
+// Prefill tile list, built on the device from the plan by one workgroup before GEMM1:
+//  1. tiles in plan order: for block_m < kTileRows, up to kTileRows / block_m consecutive plan
+//     blocks of one local expert segment (aligned to the segment's first block); otherwise
+//     kTileRows-row slices of each block of a local expert;
+//  2. each tile's token-fragment count (up to its last routed row), tiles ranked by it
+//     (counting sort) and interleaved longest / shortest for the dynamic schedule of the GEMMs;
+//  3. the GEMMs' task counters are cleared.
+// tmp holds max_tiles int2 + max_tiles int; tiles max_tiles int2.
+__global__ __launch_bounds__(1024) void tile_list_kernel(
+    const int32_t* __restrict__ eids, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ ntpp, int64_t cap, int block_m, int64_t sentinel, int nloc,
+    int2* __restrict__ tmp, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    uint32_t* __restrict__ counters) {
   __shared__ int scan[1024];
   __shared__ int carry_start, carry_count;
+  __shared__ int hist[9], offs[9];
   const int tid = threadIdx.x;
   int64_t P = *ntpp;
   if (P > cap) P = cap;
   if (P < 0) P = 0;
   const int nblk = (int)(P / block_m);
+  const int tb = block_m < kTileRows ? kTileRows / block_m : 1;
+  const int n_sub = block_m < kTileRows ? 1 : (block_m + kTileRows - 1) / kTileRows;
   if (tid == 0) {
     carry_start = 0;
     carry_count = 0;
   }
+  if (tid < 9) hist[tid] = 0;
   __syncthreads();
   for (int base = 0; base < nblk; base += 1024) {
     const int b = base + tid;
@@ -178,10 +200,11 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
       __syncthreads();
     }
     const int s0 = max(scan[tid], carry_start);
-    const bool is_tile = valid && ((b - s0) % tb == 0);
+    const bool local = valid && e >= 0 && e < nloc;
+    const int ntile = !local ? 0 : (tb > 1 ? ((b - s0) % tb == 0 ? 1 : 0) : n_sub);
     __syncthreads();
-    // exclusive prefix sum of tile starts
-    scan[tid] = is_tile ? 1 : 0;
+    // exclusive prefix sum of the tiles each block starts
+    scan[tid] = ntile;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
       int v = (tid >= off) ? scan[tid - off] : 0;
@@ -189,26 +212,72 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
       scan[tid] += v;
       __syncthreads();
     }
-    const int incl = scan[tid];
+    const int first = carry_count + scan[tid] - ntile;
     const int total = scan[1023];
-    if (is_tile) {
-      int nb = 1;
-      while (nb < tb && b + nb < nblk && eids[b + nb] == e) ++nb;
-      tiles[carry_count + incl - 1] = make_int2(b * block_m, nb * block_m);
+    if (ntile > 0) {
+      if (tb > 1) {
+        int nb = 1;
+        while (nb < tb && b + nb < nblk && eids[b + nb] == e) ++nb;
+        tmp[first] = make_int2(b * block_m, nb * block_m);
+      } else {
+        for (int u = 0; u < n_sub; ++u)
+          tmp[first + u] = make_int2(b * block_m + u * kTileRows,
+                                     min(kTileRows, block_m - u * kTileRows));
+      }
     }
     __syncthreads();                         // every thread has read carry_start/count
     if (tid == min(1023, nblk - 1 - base)) carry_start = s0;
     if (tid == 0) carry_count += total;
     __syncthreads();
   }
-  if (tid == 0) *n_tiles = carry_count;
+  const int nt_all = carry_count;
+  int* nfw_of = reinterpret_cast<int*>(tmp + nt_all);
+  __syncthreads();
+  for (int t = tid; t < nt_all; t += 1024) {
+    // last routed row by bisection (an expert segment holds its routed rows first, then the
+    // padding); the count only orders the tiles, the GEMMs find each tile's rows themselves
+    const int2 tl = tmp[t];
+    int lo = -1, hi = tl.y;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      const int ent = sorted[tl.x + mid];
+      if (ent >= 0 && ent < sentinel) lo = mid;
+      else hi = mid;
+    }
+    const int nfw = max(1, (lo + 32) >> 5);
+    nfw_of[t] = nfw;
+    atomicAdd(&hist[nfw], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int f = 8; f >= 1; --f) {             // rank 0: most fragments
+      offs[f] = acc;
+      acc += hist[f];
+    }
+    offs[0] = acc;
+    *n_tiles = acc;
+    counters[0] = 0u;
+    counters[1] = 0u;
+  }
+  __syncthreads();
+  // rank r in decreasing fragment count -> position: the longest and the shortest tiles
+  // alternate (r0, r(n-1), r1, r(n-2), ...), so that the tasks in flight at any time mix
+  // MFMA-bound and weight-streaming-bound tiles
+  const int n = offs[0];
+  for (int t = tid; t < nt_all; t += 1024) {
+    const int r = atomicAdd(&offs[nfw_of[t]], 1);
+    const int pos = (r < (n + 1) / 2) ? 2 * r : 2 * (n - 1 - r) + 1;
+    tiles[pos] = tmp[t];
+  }
 }
 
 struct Smem {
-  uint8_t* tok;         // two token stages, MT rows each
+  uint8_t* tok;         // two token stages of kTileRows rows
   int* row_src;
   float* row_scale;
   int* sh_nvalid;
+  int* sh_task;
 };
 
 // LDS slot (16 bytes = 8 FP16) of the 8 token values a lane needs for chunk c, K half h, MFMA
@@ -218,75 +287,48 @@ __device__ __forceinline__ int tok_slot(int c, int h, int s) {
   return ((s & 1) << 3) + 4 * c + 2 * h + (s >> 1);
 }
 
-// Epilogue of one token column held by this lane: the lane holds 16 consecutive output rows
-// (16h + 0..15 of each of its FN weight row groups) for plan row r.
-template <int FN, int EPI>
-__device__ __forceinline__ void epilogue_frag(const GemmArgs& a, const f32x16_t (&acc)[FN], int e,
-                                              int64_t g0, int h, float s_row, int64_t r) {
+// Epilogue of one weight row group g for the plan row r of this lane's token column; the lane
+// holds the group's logical rows 16h .. 16h + 15.
+//   down:    outputs 32g + 16h + v  ->  BF16, 32 contiguous bytes per lane
+//   ReLU^2:  intermediate 32g + 16h + v, one requantization block per lane
+//   SwiGLU:  h = 0 holds gate, h = 1 up of intermediate 16g + v; lane h = 0 keeps 16g + 0..7 and
+//            lane h = 1 keeps 16g + 8..15 after swapping halves with its partner (lane ^ 32);
+//            the requantization block is the pair's 16 values.
+template <int EPI>
+__device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t& acc, int e,
+                                               int64_t g, int h, float s_row, int64_t r) {
   if (EPI == EPI_DOWN) {
     const float a2 = a.alpha_a[e];
+    const int64_t k0 = g * kGroupRows + 16 * h;
+    uint32_t pk[8];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int64_t k0 = (g0 + fn) * kGroupRows + 16 * h;
-      uint32_t pk[8];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const float y0 = (acc[fn][2 * v] * s_row) * a2;
-        const float y1 = (acc[fn][2 * v + 1] * s_row) * a2;
-        pk[v] = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(a.y + r * a.Hout + k0);
-      dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    for (int v = 0; v < 8; ++v) {
+      const float y0 = (acc[2 * v] * s_row) * a2;
+      const float y1 = (acc[2 * v + 1] * s_row) * a2;
+      pk[v] = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
     }
+    uint4* dst = reinterpret_cast<uint4*>(a.y + r * a.Hout + k0);
+    dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
     return;
   }
-  const float au = a.alpha_b[e];
-  const float ag = a.alpha_a[e];
-  constexpr int NOUT = (EPI == EPI_SWIGLU) ? FN / 2 : FN;
-#pragma unroll
-  for (int p = 0; p < NOUT; ++p) {
-    float hv[16];
-    int64_t i0;
-    if (EPI == EPI_SWIGLU) {
-      i0 = ((g0 + 2 * p) >> 1) * kGroupRows + 16 * h;
-      float gt[16], up[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        gt[v] = (acc[2 * p][v] * s_row) * ag;
-        up[v] = (acc[2 * p + 1][v] * s_row) * au;
-        hv[v] = (gt[v] / (1.0f + expf(-gt[v]))) * up[v];
-      }
-      if (a.dbg_pre) {
-        float4* dg = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + i0);
-        float4* du = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + a.I + i0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          dg[v] = make_float4(gt[4 * v], gt[4 * v + 1], gt[4 * v + 2], gt[4 * v + 3]);
-          du[v] = make_float4(up[4 * v], up[4 * v + 1], up[4 * v + 2], up[4 * v + 3]);
-        }
-      }
-    } else {
-      i0 = (g0 + p) * kGroupRows + 16 * h;
-      float pr[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        pr[v] = (acc[p][v] * s_row) * au;
-        const float q = pr[v] > 0.0f ? pr[v] : 0.0f;
-        hv[v] = q * q;
-      }
-      if (a.dbg_pre) {
-        float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * a.I + i0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          dp[v] = make_float4(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]);
-      }
-    }
+  if (EPI == EPI_RELU2) {
+    const float au = a.alpha_b[e];
+    const int64_t i0 = g * kGroupRows + 16 * h;
+    float pr[16], hv[16];
     uint32_t bb[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      bb[v] = f32_to_bf16(hv[v]);
+      pr[v] = (acc[v] * s_row) * au;
+      const float q = pr[v] > 0.0f ? pr[v] : 0.0f;
+      bb[v] = f32_to_bf16(q * q);
       hv[v] = bf16_to_f32(bb[v]);
+    }
+    if (a.dbg_pre) {
+      float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * a.I + i0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dp[v] = make_float4(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]);
     }
     if (a.dbg_inter) {
       uint4* d = reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + i0);
@@ -299,218 +341,293 @@ __device__ __forceinline__ void epilogue_frag(const GemmArgs& a, const f32x16_t 
     const uint32_t sfb = quant_block16(hv, a.c2, lo, hi);
     *reinterpret_cast<uint2*>(a.hq + r * (a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
     a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+    return;
   }
+  // SwiGLU
+  const int64_t i0 = g * 16;
+  const float al = h ? a.alpha_b[e] : a.alpha_a[e];
+  float pre[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) pre[v] = (acc[v] * s_row) * al;
+  if (a.dbg_pre) {
+    float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + h * a.I + i0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      dp[v] = make_float4(pre[4 * v], pre[4 * v + 1], pre[4 * v + 2], pre[4 * v + 3]);
+  }
+  float hv[8];
+  uint32_t bb[8];
+  float bmax = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const float send = h ? pre[v] : pre[8 + v];
+    const float recv = __shfl_xor(send, 32, 64);
+    const float gt = h ? recv : pre[v];
+    const float up = h ? pre[8 + v] : recv;
+    bb[v] = f32_to_bf16((gt / (1.0f + expf(-gt))) * up);
+    hv[v] = bf16_to_f32(bb[v]);
+    bmax = __builtin_fmaxf(bmax, __builtin_fabsf(hv[v]));
+  }
+  const int64_t ih = i0 + 8 * h;
+  if (a.dbg_inter) {
+    *reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + ih) =
+        make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
+                   bb[6] | (bb[7] << 16));
+  }
+  bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  float inv;
+  const uint32_t sfb = block_scale(bmax, a.c2, inv);
+  *reinterpret_cast<uint32_t*>(a.hq + r * (a.I >> 1) + (ih >> 1)) = quant8(hv, inv);
+  if (h == 0) a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
 }
 
-// One tile.  WAVES waves per workgroup: wave % 4 selects FN weight row groups, wave / 4 selects
-// the token fragments fm = j * WM + wave / 4 (j < NFW), WM = WAVES / 4.
-template <int FN, int FM, int NFW, int EPI, int WAVES, int RING>
+// Prefetch depths of a prefill tile with NFW token fragments, in 128-K stages: the weights of
+// stage st + RW - 1 and the packed tokens of stage st + RT are loaded while stage st computes.
+// Short tiles have short stages and spare registers, so they look further ahead.
+template <int NFW> struct TileDepth {
+  static constexpr int RW = NFW <= 4 ? 4 : 2;
+  static constexpr int RT = NFW <= 2 ? 4 : 2;
+};
+
+// One prefill tile of up to kTileRows plan rows of one expert, against kTileGroups weight row
+// groups.  Eight waves, two per SIMD: wave w owns row group g = kTileGroups * nt + w and all NFW
+// token fragments of the tile (32 * NFW plan rows), so each weight fragment is decoded once per
+// tile and each token value once per workgroup.
+// Per 128-K stage: the token rows are staged in LDS as FP16 (double buffered, their packed bytes
+// loaded RT stages ahead into registers); the weights are loaded RW - 1 stages ahead into
+// registers.  Within a stage, step q (16 K values) issues the NFW MFMAs of step q, and right
+// behind each MFMA the LDS read of the same token fragment for step q + 1 into the register the
+// MFMA has just consumed, so every LDS read has a whole step to complete.  The weight fragment
+// of step q + 1 is decoded during step q, and the next stage's staging items are decoded and
+// stored in LDS in between.
+template <int NFW, int EPI>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int e, int nt,
                                          int64_t row0) {
-  constexpr int MT = 32 * FM;
-  constexpr int WM = WAVES / 4;
-  constexpr int NT = 64 * WAVES;                 // threads
-  constexpr int ROWS = 32 * NFW * WM;            // token rows staged
-  constexpr int ITEMS = ROWS * 8 / NT;           // staging items per thread
-  static_assert(ROWS * 8 % NT == 0, "staging items must divide evenly");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_n = wave & 3, wave_m = wave >> 2;
+  static_assert(NFW >= 1 && NFW <= 8, "at most 8 token fragments per tile");
+  constexpr int RW = TileDepth<NFW>::RW, RT = TileDepth<NFW>::RT;
+  static_assert((RW == 2 || RW == 4) && (RT == 2 || RT == 4), "ring depths of 2 or 4");
+  constexpr int PERIOD = (RW > RT) ? RW : RT;   // a multiple of 2, RW and RT
+  constexpr int ITEMS = (NFW + 1) / 2;    // staging items per thread and stage (<= 4)
+  constexpr int BUF = kTileRows * kTokPitch;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int nst = a.nch / kStageChunks;
-  const int64_t sf_rowb = a.a_rowq >> 3;
+  const uint32_t sf_rowb = (uint32_t)(a.a_rowq >> 3);
 
-  const int64_t g0 = (int64_t)nt * (4 * FN) + (int64_t)wave_n * FN;
-  const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
-  // a wave past the last row group still loads (group 0) so that every load is unconditional
-  // and the compiler's wait counts stay exact; it skips the MFMAs and the epilogue
-  const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
-                         lane * 16;
+  const int64_t g = (int64_t)nt * kTileGroups + wave;
+  const bool wave_on = (g + 1) * kGroupRows <= a.N;
+  // a wave past the last row group streams group 0 (every load and MFMA is unconditional) and
+  // skips the epilogue.  Weight loads go through a buffer resource over the wave's row group:
+  // lane offset in a VGPR, stage offsets in SGPRs.
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(
+      a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g : 0) * a.rg_bytes, (uint32_t)a.rg_bytes);
+  const int wlane = lane * 16;
 
-  // token loader: item = (row, 16-value block) of a 128-value stage; thread tid handles block
-  // tid % 8 of rows tid / 8 + it * NT / 8.  Rows without a routed slot are not staged: their
-  // LDS rows hold stale values, which only reach MFMA output columns that are discarded.
+  // staging item it: plan row (tid >> 3) + 64 it, 16-value block tid & 7 of a stage.  Rows
+  // without a routed slot read token row 0; their MFMA columns are discarded.  The token
+  // operand is smaller than 2^31 bytes (checked by the launcher), so offsets are 32-bit.
   const int blk = tid & 7;
   const int lds0 = (tid >> 3) * kTokPitch + blk * 16;
-  // rows without a routed slot load token row 0 (any valid row) instead of branching
-  int64_t it_src[ITEMS];
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.a_q, (uint32_t)(a.a_rows * a.a_rowq));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.a_sf, (uint32_t)(a.a_rows * sf_rowb));
+  uint32_t it_q[ITEMS], it_s[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
-    const int src = sm.row_src[(tid >> 3) + it * (NT / 8)];
-    it_src[it] = src < 0 ? 0 : src;
+    int src = sm.row_src[(tid >> 3) + 64 * it];
+    src = src < 0 ? 0 : src;
+    it_q[it] = (uint32_t)src * (uint32_t)a.a_rowq + blk * 8;
+    it_s[it] = (uint32_t)src * sf_rowb + blk;
   }
+  // LDS byte offset of this lane's token operand in fragment 0, step q of a stage buffer
+  auto t_off = [&](int q) { return col * kTokPitch + tok_slot(q >> 2, h, q & 3) * 16; };
 
-  f32x16_t acc[FN][NFW];
+  f32x16_t acc[NFW];
 #pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < NFW; ++j) acc[i][j] = f32x16_t{};
+  for (int j = 0; j < NFW; ++j) acc[j] = f32x16_t{};
 
-  uint4 W[RING][kStageChunks][FN];
-  uint32_t S[RING][FN];
-  uint2 Tq[ITEMS];
-  uint32_t Ts[ITEMS];
+  uint4 W[RW][kStageChunks];
+  uint32_t S[RW];
+  uint2 Tq[RT][ITEMS];
+  uint32_t Ts[RT][ITEMS];
+  h8_t T[NFW];
+  h8_t Wc;
 
-  auto load_w = [&](uint4 (&Wd)[kStageChunks][FN], uint32_t (&Sd)[FN], int st) {
-    const int64_t sc = st / (kSuperChunks / kStageChunks);
+  auto load_w = [&](uint4 (&Wd)[kStageChunks], uint32_t& Sd, int st) {
+    const int sc = st / (kSuperChunks / kStageChunks);
     const int c0 = (st * kStageChunks) % kSuperChunks;
+    const int so = sc * kSuperBytes;
+    Sd = buffer_load_u32(wrs, wlane, so + 2 * c0);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const uint8_t* base = wbase + fn * a.rg_bytes + sc * kSuperBytes;
-      Sd[fn] = *reinterpret_cast<const uint32_t*>(base + 2 * c0);
-#pragma unroll
-      for (int c = 0; c < kStageChunks; ++c)
-        Wd[c][fn] = *reinterpret_cast<const uint4*>(base + kUnit + (c0 + c) * kUnit);
-    }
+    for (int c = 0; c < kStageChunks; ++c)
+      Wd[c] = buffer_load_u128(wrs, wlane + (1 + c) * kUnit, so + c0 * kUnit);
   };
-  auto load_t = [&](int st) {
+  auto load_t = [&](uint2 (&Tqd)[ITEMS], uint32_t (&Tsd)[ITEMS], int st) {
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-      const int64_t src = it_src[it];
-      Tq[it] = *reinterpret_cast<const uint2*>(a.a_q + src * a.a_rowq + st * 64 + blk * 8);
-      Ts[it] = a.a_sf[src * sf_rowb + st * 8 + blk];
+      Tqd[it] = buffer_load_u64(qrs, it_q[it], st * 64);
+      Tsd[it] = buffer_load_u8(srs, it_s[it], st * 8);
     }
   };
-  auto store_t = [&](uint8_t* buf) {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const uint32_t s2 = e4m3_scale_h2(Ts[it]);
-      uint8_t* d = buf + lds0 + it * (NT / 8) * kTokPitch;
-      *reinterpret_cast<h8_t*>(d) = decode8(Tq[it].x, s2);
-      *reinterpret_cast<h8_t*>(d + 128) = decode8(Tq[it].y, s2);
-    }
+  auto store_item = [&](uint2 q, uint32_t sb, uint8_t* buf, int it) {
+    const uint32_t s2 = e4m3_scale_h2(sb);
+    uint8_t* d = buf + lds0 + it * 64 * kTokPitch;
+    *reinterpret_cast<h8_t*>(d) = decode8(q.x, s2);
+    *reinterpret_cast<h8_t*>(d + 128) = decode8(q.y, s2);
   };
-  auto compute = [&](const uint4 (&Wd)[kStageChunks][FN], const uint32_t (&Sd)[FN],
-                     const uint8_t* buf) {
-    if (!wave_on) return;
+  auto dec_w = [&](const uint4 (&Wd)[kStageChunks], uint32_t Sd, int q) {
+    const int c = q >> 2, s = q & 3;
+    const uint32_t wd = (s == 0) ? Wd[c].x : (s == 1) ? Wd[c].y : (s == 2) ? Wd[c].z : Wd[c].w;
+    const uint32_t sb = (Sd >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
+    return decode8(wd, e4m3_scale_h2(sb));
+  };
+  auto read_all = [&](const uint8_t* buf, int q) {
 #pragma unroll
-    for (int c = 0; c < kStageChunks; ++c) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        h8_t T[NFW];
-#pragma unroll
-        for (int j = 0; j < NFW; ++j)
-          T[j] = *reinterpret_cast<const h8_t*>(buf + ((j * WM + wave_m) * 32 + col) * kTokPitch +
-                                                tok_slot(c, h, s) * 16);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const uint32_t wd = (s == 0) ? Wd[c][fn].x : (s == 1) ? Wd[c][fn].y
-                              : (s == 2) ? Wd[c][fn].z : Wd[c][fn].w;
-          const uint32_t sb = (Sd[fn] >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
-          const h8_t Wv = decode8(wd, e4m3_scale_h2(sb));
-#pragma unroll
-          for (int j = 0; j < NFW; ++j)
-            acc[fn][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wv, T[j], acc[fn][j], 0, 0, 0);
-        }
-      }
-    }
+    for (int j = 0; j < NFW; ++j)
+      T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q));
   };
 
-  // ---- pipeline: weights RING-1 stages ahead in registers, tokens one stage ahead in LDS ----
-  // Loads are never conditional (stage indices are clamped; the extra loads at the end re-read
-  // the last stage), so the waits the compiler places before each use count exactly the loads
-  // issued after it and the prefetch stays in flight.  The caller guarantees nst % RING == 0.
+  // ---- prologue: tokens of stages 0 .. RT-1 (stage 0 staged), weights of 0 .. RW-2 ----
+  // Loads are never conditional (stage indices are clamped; the loads past the end re-read the
+  // last stage), so the waits the compiler places before each use count exactly the loads
+  // issued after it and the prefetch stays in flight.
+  load_t(Tq[0], Ts[0], 0);
 #pragma unroll
-  for (int d = 0; d < RING - 1; ++d) load_w(W[d], S[d], min(d, nst - 1));
-  load_t(0);
-  store_t(sm.tok);
+  for (int r = 0; r < RW - 1; ++r) load_w(W[r], S[r], min(r, nst - 1));
+#pragma unroll
+  for (int r = 1; r < RT; ++r) load_t(Tq[r], Ts[r], min(r, nst - 1));
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) store_item(Tq[0][it], Ts[0][it], sm.tok, it);
   lds_barrier();
-  for (int st0 = 0; st0 < nst; st0 += RING) {
+  read_all(sm.tok, 0);
+  Wc = dec_w(W[0], S[0], 0);
+
+  // One stage st; R = st % PERIOD gives the LDS buffer (R % 2), the weight slot (R % RW) and the
+  // token slot (R % RT) as compile-time indices.  Stage st refills the token slot it freed
+  // (stage st was staged during stage st - 1) with stage st + RT, and the weight slot freed by
+  // stage st - 1 with stage st + RW - 1.  Stages run in groups of PERIOD with the remainder
+  // after the loop: the loop has no early exit, which keeps the register allocation of the
+  // unrolled body flat.
+  auto stage = [&](auto RR, int st) {
+    constexpr int R = decltype(RR)::value;
+    constexpr int d = R & 1, rw = R % RW, rt = R % RT, rt1 = (R + 1) % RT;
+    const uint8_t* buf = sm.tok + d * BUF;
+    uint8_t* nbuf = sm.tok + (d ^ 1) * BUF;
+    load_t(Tq[rt], Ts[rt], min(st + RT, nst - 1));
+    load_w(W[(R + RW - 1) % RW], S[(R + RW - 1) % RW], min(st + RW - 1, nst - 1));
 #pragma unroll
-    for (int d = 0; d < RING; ++d) {
-      const int st = st0 + d;
-      // token loads first: the wait for them at the end of this stage (vmcnt counts in issue
-      // order) must not also wait for the weight loads issued for a later stage
-      load_t(min(st + 1, nst - 1));
-      load_w(W[(d + RING - 1) % RING], S[(d + RING - 1) % RING], min(st + RING - 1, nst - 1));
-      compute(W[d], S[d], sm.tok + (st & 1) * (MT * kTokPitch));
-      store_t(sm.tok + ((st + 1) & 1) * (MT * kTokPitch));
-      lds_barrier();
+    for (int q = 0; q < 8; ++q) {
+#pragma unroll
+      for (int j = 0; j < NFW; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc, T[j], acc[j], 0, 0, 0);
+        if (q < 7)
+          T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q + 1));
+      }
+      Wc = (q < 7) ? dec_w(W[rw], S[rw], q + 1) : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
+      // items of stage st + 1 at steps 0, 2, 4, 6
+      if ((q & 1) == 0 && (q >> 1) < ITEMS) store_item(Tq[rt1][q >> 1], Ts[rt1][q >> 1], nbuf, q >> 1);
+      // order within the step: each MFMA followed by the LDS read that refills its token
+      // register, the decode VALU work spread in between
+#pragma unroll
+      for (int j = 0; j < NFW; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        if (q < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    lds_barrier();
+    read_all(nbuf, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int st = 0;
+  if constexpr (PERIOD == 2) {
+    for (; st + 1 < nst; st += 2) {
+      stage(I0{}, st);
+      stage(I1{}, st + 1);
+    }
+    if (st < nst) stage(I0{}, st);
+  } else {
+    for (; st + 3 < nst; st += 4) {
+      stage(I0{}, st);
+      stage(I1{}, st + 1);
+      stage(I2{}, st + 2);
+      stage(I3{}, st + 3);
+    }
+    const int rem = nst - st;
+    if (rem >= 1) stage(I0{}, st);
+    if (rem >= 2) stage(I1{}, st + 1);
+    if (rem >= 3) stage(I2{}, st + 2);
   }
 
   // ---- epilogue ----
   if (!wave_on) return;
 #pragma unroll
   for (int j = 0; j < NFW; ++j) {
-    const int m = (j * WM + wave_m) * 32 + col;
+    const int m = j * 32 + col;
     if (sm.row_src[m] < 0) continue;
-    f32x16_t accj[FN];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) accj[fn] = acc[fn][j];
-    epilogue_frag<FN, EPI>(a, accj, e, g0, h, sm.row_scale[m], row0 + m);
+    epilogue_group<EPI>(a, acc[j], e, g, h, sm.row_scale[m], row0 + m);
   }
 }
 
-template <int FN, int FM, int EPI, int WAVES, int RING>
+template <int EPI>
 __device__ __forceinline__ void run_nfw(const GemmArgs& a, const Smem& sm, int e, int nt,
                                         int64_t row0, int nfw) {
-  if constexpr (FM == 1) {
-    run_tile<FN, FM, 1, EPI, WAVES, RING>(a, sm, e, nt, row0);
-  } else {
-    static_assert(FM / (WAVES / 4) == 4, "prefill tile: 4 token fragments per wave at most");
-    switch (nfw) {
-      case 1: run_tile<FN, FM, 1, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
-      case 2: run_tile<FN, FM, 2, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
-      case 3: run_tile<FN, FM, 3, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
-      default: run_tile<FN, FM, 4, EPI, WAVES, RING>(a, sm, e, nt, row0); break;
-    }
+  switch (nfw) {
+    case 1: run_tile<1, EPI>(a, sm, e, nt, row0); break;
+    case 2: run_tile<2, EPI>(a, sm, e, nt, row0); break;
+    case 3: run_tile<3, EPI>(a, sm, e, nt, row0); break;
+    case 4: run_tile<4, EPI>(a, sm, e, nt, row0); break;
+    case 5: run_tile<5, EPI>(a, sm, e, nt, row0); break;
+    case 6: run_tile<6, EPI>(a, sm, e, nt, row0); break;
+    case 7: run_tile<7, EPI>(a, sm, e, nt, row0); break;
+    default: run_tile<8, EPI>(a, sm, e, nt, row0); break;
   }
 }
 
-template <int FN, int FM, int EPI, int OCC, int WAVES, int RING>
-__global__ __launch_bounds__(64 * WAVES, OCC) void moe_gemm_kernel(GemmArgs a) {
-  constexpr int MT = 32 * FM;
-  constexpr int WM = WAVES / 4;
+// Prefill-sized plan blocks.  Persistent grid of one 8-wave workgroup per CU with a dynamic
+// schedule: a task is (tile, n-tile of kTileGroups weight row groups), task k = tile k / n_nt
+// of the tile list, n-tile k % n_nt; a workgroup takes its next task from a global counter
+// while it works on the current one.
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Smem sm;
   sm.tok = smem;
-  sm.row_src = reinterpret_cast<int*>(smem + 2 * MT * kTokPitch);
-  sm.row_scale = reinterpret_cast<float*>(sm.row_src + MT);
-  sm.sh_nvalid = reinterpret_cast<int*>(sm.row_scale + MT);
+  sm.row_src = reinterpret_cast<int*>(smem + 2 * kTileRows * kTokPitch);
+  sm.row_scale = reinterpret_cast<float*>(sm.row_src + kTileRows);
+  sm.sh_nvalid = reinterpret_cast<int*>(sm.row_scale + kTileRows);
+  sm.sh_task = sm.sh_nvalid + 1;
 
   const int tid = threadIdx.x;
-  int64_t P = *a.ntpp;
-  if (P > a.cap) P = a.cap;
-  if (P < 0) P = 0;
-  const int64_t n_mt = a.tiles ? (int64_t)(*a.n_tiles) : (P / a.block_m) * a.n_sub;
-  const int xcd = blockIdx.x & 7;
-  const int64_t Q = gridDim.x >> 3;
-  const int64_t li = blockIdx.x >> 3;
-  const int64_t mts_here = (n_mt > xcd) ? (n_mt - xcd + 7) / 8 : 0;
-  const int64_t ntask = mts_here * a.n_nt;
-
-  for (int64_t k = li; k < ntask; k += Q) {
-    const int64_t mt = xcd + 8 * (k / a.n_nt);
+  const int64_t ntask = (int64_t)(*a.n_tiles) * a.n_nt;
+  if (tid == 0) *sm.sh_task = (int)atomicAdd(a.task_counter, 1u);
+  __syncthreads();
+  int64_t k = *sm.sh_task;
+  while (k < ntask) {
+    uint32_t k_next = 0;
+    if (tid == 0) k_next = atomicAdd(a.task_counter, 1u);   // in flight during this task
+    const int2 t = a.tiles[k / a.n_nt];
     const int nt = (int)(k % a.n_nt);
-    int64_t row0;
-    int rows_here;
-    if (a.tiles) {
-      const int2 t = a.tiles[mt];
-      row0 = t.x;
-      rows_here = min(MT, t.y);
-    } else {
-      const int64_t b = mt / a.n_sub;
-      const int sub = (int)(mt % a.n_sub);
-      row0 = b * a.block_m + (int64_t)sub * MT;
-      rows_here = min(MT, a.block_m - sub * MT);
-    }
-    if (row0 < 0 || row0 + rows_here > P) continue;
+    const int64_t row0 = t.x;
+    const int rows_here = min(kTileRows, t.y);
     const int e = a.eids[row0 / a.block_m];
-    if (e < 0 || e >= a.nloc) continue;
-
     __syncthreads();                         // the previous task is done with LDS
     if (tid == 0) *sm.sh_nvalid = 0;
     __syncthreads();
-    if (tid < MT) {
+    if (tid < kTileRows) {
       int src = -1;
       float sc = 0.0f;
       if (tid < rows_here) {
         const int64_t ent = a.sorted[row0 + tid];
         if (ent >= 0 && ent < a.sentinel) {
           if (a.gather) {
-            const int64_t t = ent / a.top_k;
-            src = (int)t;
-            sc = a.a_dec[t];
+            const int64_t tk = ent / a.top_k;
+            src = (int)tk;
+            sc = a.a_dec[tk];
           } else {
             src = (int)(row0 + tid);
             sc = a.a_const_scale;
@@ -523,18 +640,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void moe_gemm_kernel(GemmArgs a) {
     }
     __syncthreads();
     const int nvalid = *sm.sh_nvalid;
-    if (nvalid == 0) continue;
-    // token fragments per wave: ceil(fragments holding a valid row / WM); a trailing fragment
-    // with no valid row is computed and discarded
-    const int nfw = (((nvalid + 31) >> 5) + WM - 1) / WM;
-    const int nst = a.nch / kStageChunks;
-    if (nst % RING == 0) {
-      run_nfw<FN, FM, EPI, WAVES, RING>(a, sm, e, nt, row0, nfw);
-    } else if (RING > 2 && nst % 2 == 0) {
-      run_nfw<FN, FM, EPI, WAVES, 2>(a, sm, e, nt, row0, nfw);
-    } else {
-      run_nfw<FN, FM, EPI, WAVES, 1>(a, sm, e, nt, row0, nfw);
-    }
+    // the tile list holds local experts and tiles with a routed row only
+    if (nvalid > 0 && e >= 0 && e < a.nloc) run_nfw<EPI>(a, sm, e, nt, row0, (nvalid + 31) >> 5);
+    __syncthreads();                         // every thread has read sh_task
+    if (tid == 0) *sm.sh_task = (int)k_next;
+    __syncthreads();
+    k = *sm.sh_task;
   }
 }
 
@@ -662,8 +773,11 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
         compute(W[d], S[d], st);
       }
     }
-    if (wave_on && col < rows_max && row_src[col] >= 0)
-      epilogue_frag<FN, EPI>(a, acc, e, g0, h, row_scale[col], b * a.block_m + col);
+    if (wave_on && col < rows_max && row_src[col] >= 0) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        epilogue_group<EPI>(a, acc[fn], e, g0 + fn, h, row_scale[col], b * a.block_m + col);
+    }
   }
 }
 
@@ -691,11 +805,10 @@ hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, 
   return hipGetLastError();
 }
 
-template <int FN, int FM, int EPI, int OCC, int WAVES, int RING>
+template <int EPI>
 hipError_t launch_gemm(const GemmArgs& a, int64_t max_tiles, const char* name, hipStream_t s) {
-  constexpr int MT = 32 * FM;
-  const size_t lds = 2 * (size_t)MT * kTokPitch + 2 * MT * sizeof(int) + 16;
-  auto kern = moe_gemm_kernel<FN, FM, EPI, OCC, WAVES, RING>;
+  const size_t lds = 2 * (size_t)kTileRows * kTokPitch + 2 * kTileRows * sizeof(int) + 16;
+  auto kern = moe_gemm_kernel<EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -704,12 +817,12 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t max_tiles, const char* name, h
     attr_set = true;
   }
   const int64_t total = max_tiles * a.n_nt;
-  const int64_t maxwg = 256LL * OCC;
+  const int64_t maxwg = 256;                         // one workgroup per CU
   int64_t grid = total < maxwg ? total : maxwg;
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   KernelTimer t(name, s);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, a);
   return hipGetLastError();
 }
 
@@ -733,15 +846,15 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   const bool gated = (p.act == 0);
   const int64_t N1 = gated ? 2 * p.I : p.I;
   const int64_t cap_blocks = p.cap / p.block_m;
-  // Decode tile: 32 plan rows (one plan block of <= 32 rows); prefill tile: 256 plan rows made
-  // of up to 256/block_m consecutive blocks of one expert (or 256-row slices of larger blocks).
+  // Decode: one plan block of <= 32 rows per task; prefill: tiles of up to kTileRows plan rows
+  // (several blocks of one expert, or slices of larger blocks) from the device-built tile list.
   const bool small = p.block_m <= 32;
-  const int MT = small ? 32 : 256;
   const int FN = 2;
 
   GemmArgs g1{};
   g1.a_q = p.a_q;
   g1.a_sf = p.a_sf;
+  g1.a_rows = p.M;
   g1.a_dec = p.a_dec;
   g1.a_const_scale = 0.0f;
   g1.a_rowq = p.H / 2;
@@ -753,20 +866,20 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.sentinel = p.M * p.top_k;
   g1.top_k = p.top_k;
   g1.block_m = p.block_m;
-  g1.n_sub = (int)((p.block_m + MT - 1) / MT);
   g1.nloc = p.nloc;
-  int64_t max_tiles = cap_blocks * g1.n_sub;
-  if (!small && p.block_m < MT) {
-    // list of multi-block tiles, built on the device from the plan
-    const int tb = MT / p.block_m;
-    g1.tiles = reinterpret_cast<const int2*>(p.tile_ws);
-    g1.n_tiles = reinterpret_cast<const int32_t*>(p.tile_ws + cap_blocks * sizeof(int2));
-    g1.n_sub = 1;
-    max_tiles = cap_blocks;
+  const int64_t max_tiles = moe_gemm_max_tiles(p.cap, p.block_m);
+  int2* tile_tmp = reinterpret_cast<int2*>(p.tile_ws);
+  int2* tiles = tile_tmp + 2 * max_tiles;     // after max_tiles int2 + max_tiles int (rounded up)
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(tiles + max_tiles);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(n_tiles + 1);
+  if (!small) {
+    g1.tiles = tiles;
+    g1.n_tiles = n_tiles;
+    g1.task_counter = counters;
     KernelTimer t("tile_list", s);
-    hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, p.eids, p.ntpp, p.cap,
-                       p.block_m, tb, reinterpret_cast<int2*>(p.tile_ws),
-                       reinterpret_cast<int32_t*>(p.tile_ws + cap_blocks * sizeof(int2)));
+    hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, p.eids, p.sorted, p.ntpp, p.cap,
+                       p.block_m, (int64_t)(p.M * p.top_k), p.nloc, tile_tmp, tiles, n_tiles,
+                       counters);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -789,8 +902,10 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   GemmArgs g2 = g1;
   g2.a_q = p.hq;
   g2.a_sf = p.hsf;
+  g2.a_rows = p.cap;
   g2.a_dec = nullptr;
   g2.a_const_scale = 1.0f / p.c2;
+  g2.task_counter = counters + 1;
   g2.a_rowq = p.I / 2;
   g2.gather = 0;
   PanelGeom pg2 = panel_geom(p.H, p.I);
@@ -814,14 +929,22 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
     if (err != hipSuccess) return err;
     return launch_gemv<2, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s);
   }
-  err = gated ? launch_gemm<2, 8, EPI_SWIGLU, 1, 8, 2>(g1, max_tiles, "gemm1_swiglu_prefill", s)
-              : launch_gemm<2, 8, EPI_RELU2, 1, 8, 2>(g1, max_tiles, "gemm1_relu2_prefill", s);
+  // the prefill kernels address token operands with 32-bit buffer offsets
+  if (p.M * (p.H / 2) >= (int64_t(1) << 31) || p.cap * (p.I / 2) >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  err = gated ? launch_gemm<EPI_SWIGLU>(g1, max_tiles, "gemm1_swiglu_prefill", s)
+              : launch_gemm<EPI_RELU2>(g1, max_tiles, "gemm1_relu2_prefill", s);
   if (err != hipSuccess) return err;
-  return launch_gemm<2, 8, EPI_DOWN, 1, 8, 2>(g2, max_tiles, "gemm2_down_prefill", s);
+  return launch_gemm<EPI_DOWN>(g2, max_tiles, "gemm2_down_prefill", s);
+}
+
+int64_t moe_gemm_max_tiles(int64_t cap, int block_m) {
+  return (cap / block_m) * ((block_m + kTileRows - 1) / kTileRows);
 }
 
 size_t moe_gemm_tile_ws_bytes(int64_t cap, int block_m) {
-  return (size_t)(cap / block_m) * sizeof(int2) + 16;
+  // tile list scratch (int2 + int per tile, as two int2), the ordered list, count, 2 counters
+  return (size_t)moe_gemm_max_tiles(cap, block_m) * 3 * sizeof(int2) + 16;
 }
 
 }  // namespace bfp4

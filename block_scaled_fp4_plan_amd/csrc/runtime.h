@@ -66,6 +66,7 @@ struct MoeGemmProblem {
   uint8_t* tile_ws;  // moe_gemm_tile_ws_bytes() of scratch for the prefill tile list
 };
 hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s);
+int64_t moe_gemm_max_tiles(int64_t cap, int block_m);
 size_t moe_gemm_tile_ws_bytes(int64_t cap, int block_m);
 
 }  // namespace bfp4

@@ -53,7 +53,8 @@ def test_status_strings_and_sizes():
     assert bf.bfp4_panel_bytes(1, 250, 128, 1) == 0
     # hq [88, 64] + hsf [88, 8] + tile list [11 x 8 B + 16] (each rounded up to 256 B)
     # + y [88, 256] BF16
-    assert bf.bfp4_workspace_size(16, 256, 128, 2, 8, 8, 1) == 5632 + 768 + 256 + 88 * 512
+    # hq | hsf | tile list (11 tiles x 24 bytes + 16) | y, each rounded up to 256 bytes
+    assert bf.bfp4_workspace_size(16, 256, 128, 2, 8, 8, 1) == 5632 + 768 + 512 + 88 * 512
     assert bf.bfp4_quantize_workspace_size(64, bf.BFP4_SCALE_PER_GROUP, 16) == 16
 
 

@@ -188,7 +188,9 @@ def test_prepare_weights_layout():
                 for g in range(ng):
                     for rho in range(32):
                         perm = 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3)
-                        lr = ((g & 1) * half + (g >> 1) * 32 + perm) if half else g * 32 + perm
+                        # gated W1: gate rows 16g.. in logical rows 0..15, up rows of the same
+                        # intermediate indices in logical rows 16..31
+                        lr = ((half if perm >= 16 else 0) + 16 * g + (perm & 15)) if half else g * 32 + perm
                         for hh in range(2):
                             lane = hh * 32 + rho
                             for c in range(nch):
