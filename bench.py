@@ -39,7 +39,24 @@ def parse():
     ap.add_argument("--replicas", type=int, default=2,
                     help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(copies=4):
+    """A plain device-to-device copy of 1 GiB, the known-size reference against which the
+    FETCH_SIZE / WRITE_SIZE counters of the kernels are scaled."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(copies):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": copies}))
 
 
 def kernel_source_digest():
@@ -198,6 +215,9 @@ def main():
     from synth import WORKLOADS
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     result = {}
     if args.workload in ("decode", "both"):
         wl = WORKLOADS["decode"]
