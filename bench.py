@@ -60,8 +60,9 @@ def calibrate_copy(copies=4):
 
 
 def kernel_source_digest():
+    """Digest of the sources that define the GEMM kernels (device helpers and gemm.hip)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "block_scaled_fp4_plan_amd", "csrc"))):
+    for f in ("device.h", "gemm.hip"):
         with open(os.path.join(ROOT, "block_scaled_fp4_plan_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

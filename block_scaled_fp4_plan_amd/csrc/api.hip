@@ -243,6 +243,9 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
   if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
   if (!(isfinite(c2) && c2 > 0.0f) || !isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
+  // the tiled (block_m > 32) GEMMs address their token operands with 32-bit offsets
+  if (block_m > 32 && (M * (H / 2) >= (1LL << 31) || (int64_t)capacity * (I / 2) >= (1LL << 31)))
+    return BFP4_ERR_SHAPE;
   size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
   if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
     return BFP4_ERR_CAPACITY;
