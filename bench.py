@@ -198,10 +198,16 @@ def cpu_baseline(s, sample_tokens=1):
     got = bf16_bits_to_f32(to_bits(out[:T])).astype(np.float64)
     ref = bf16_bits_to_f32(res["out"]).astype(np.float64)
     err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    # the oracle's own NVFP4-vs-unquantized gap on the same sample (reported, not gated)
+    u = oracle.unquantized_moe_f64(s.x_bits[:T], lambda e: to_bits(s.w1[e]), lambda e: to_bits(s.w2[e]),
+                                   ids, s.w[:T], wl.E, wl.local_offset, wl.n_local, oracle.ACT_SWIGLU)
+    u = np.stack([u[t] for t in range(T)])
+    gap = float(np.linalg.norm(ref - u) / np.linalg.norm(u))
     return dict(value=T / dt, unit="tokens/s", cores=1, kind="oracle",
                 sample="%d token(s) of the %s workload (%d experts), per-call path without weight "
                        "quantization; %.2f s; float64 numpy, single thread; GPU-vs-oracle rel. "
-                       "Frobenius error on the sample %.2e" % (T, wl.name, len(experts), dt, err))
+                       "Frobenius error on the sample %.2e" % (T, wl.name, len(experts), dt, err),
+                oracle_nvfp4_vs_fp64_gap=gap)
 
 
 def main():
