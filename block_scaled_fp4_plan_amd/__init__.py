@@ -83,7 +83,7 @@ _sig("bfp4_fused_moe_nvfp4", _I,
      [_P, _P, _P, _P, _SZ, _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _I64, _I64, _I64, _I, _I, _I,
       _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
 _sig("bfp4_moe_finalize", _I, [_P, _P, _P, _I64, _I64, _I, _F, _P, _P])
-_sig("bfp4_profile_begin", _I, [_I])
+_sig("bfp4_profile_begin", _I, [_I, ctypes.c_char_p])
 _sig("bfp4_profile_end", _I, [ctypes.c_char_p, _SZ])
 
 
@@ -192,8 +192,9 @@ def bfp4_moe_finalize(gemm2_out, topk_weights, token_to_row, M, H, top_k, routed
         _p(out), _s(stream)), "bfp4_moe_finalize")
 
 
-def bfp4_profile_begin(capacity):
-    return _check(_lib.bfp4_profile_begin(capacity), "bfp4_profile_begin")
+def bfp4_profile_begin(capacity, name_prefix=None):
+    pre = name_prefix.encode() if name_prefix else None
+    return _check(_lib.bfp4_profile_begin(capacity, pre), "bfp4_profile_begin")
 
 
 def bfp4_profile_end():

@@ -19,6 +19,7 @@ struct TimerState {
   bool on = false;
   std::vector<hipEvent_t> start, stop;
   std::vector<const char*> name;
+  std::string prefix;          // record only kernels whose name starts with it (empty: all)
   int used = 0;
   int launched = 0;
 };
@@ -58,6 +59,8 @@ bool valid_block_m(int bm) { return bm >= 8 && bm % 8 == 0; }
 KernelTimer::KernelTimer(const char* name, hipStream_t stream) : slot_(-1), stream_(stream) {
   if (!g_timer.on) return;
   g_timer.launched++;
+  if (!g_timer.prefix.empty() && strncmp(name, g_timer.prefix.c_str(), g_timer.prefix.size()) != 0)
+    return;
   if (g_timer.used >= (int)g_timer.start.size()) return;
   slot_ = g_timer.used++;
   g_timer.name[slot_] = name;
@@ -347,7 +350,7 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const float* topk_weights,
                                   routed_scaling_factor, out, (hipStream_t)stream));
 }
 
-int bfp4_profile_begin(int capacity) {
+int bfp4_profile_begin(int capacity, const char* name_prefix) {
   if (capacity <= 0 || capacity > (1 << 20)) return BFP4_ERR_SHAPE;
   int dc = device_check();
   if (dc) return dc;
@@ -361,6 +364,7 @@ int bfp4_profile_begin(int capacity) {
     if (hipEventCreate(&t.start[i]) != hipSuccess || hipEventCreate(&t.stop[i]) != hipSuccess)
       return BFP4_ERR_LAUNCH;
   }
+  t.prefix = name_prefix ? name_prefix : "";
   t.used = 0;
   t.launched = 0;
   t.on = true;

@@ -157,22 +157,36 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restric
     acc[2 * k + 1] = bf16_to_f32(ow[k] >> 16);
   }
   const bool scaled = (rsf != 1.0f);
-  for (int j = 0; j < top_k; ++j) {
-    int32_t r = ttr[t * top_k + j];
-    if (r < 0) continue;                       // unrouted: weight never read
-    float wt = w[t * top_k + j];
-    uint4 yy = *reinterpret_cast<const uint4*>(y + (int64_t)r * H + h);
-    uint32_t yw[4] = {yy.x, yy.y, yy.z, yy.w};
+  // slots in groups of 8: the group's rows, then its weights and expert-output rows are loaded
+  // together, then added in ascending slot order (unrouted slots: weight never read)
+  for (int j0 = 0; j0 < top_k; j0 += 8) {
+    int32_t r[8];
+    float wt[8];
+    uint4 yy[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float p0 = wt * bf16_to_f32(yw[k] & 0xFFFFu);
-      float p1 = wt * bf16_to_f32(yw[k] >> 16);
-      if (scaled) {
-        p0 = p0 * rsf;
-        p1 = p1 * rsf;
+    for (int u = 0; u < 8; ++u) r[u] = (j0 + u < top_k) ? ttr[t * top_k + j0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (r[u] >= 0) {
+        wt[u] = w[t * top_k + j0 + u];
+        yy[u] = *reinterpret_cast<const uint4*>(y + (int64_t)r[u] * H + h);
       }
-      acc[2 * k] = acc[2 * k] + p0;
-      acc[2 * k + 1] = acc[2 * k + 1] + p1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (r[u] < 0) continue;
+      const uint32_t yw[4] = {yy[u].x, yy[u].y, yy[u].z, yy[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float p0 = wt[u] * bf16_to_f32(yw[k] & 0xFFFFu);
+        float p1 = wt[u] * bf16_to_f32(yw[k] >> 16);
+        if (scaled) {
+          p0 = p0 * rsf;
+          p1 = p1 * rsf;
+        }
+        acc[2 * k] = acc[2 * k] + p0;
+        acc[2 * k + 1] = acc[2 * k + 1] + p1;
+      }
     }
   }
   uint4 res;

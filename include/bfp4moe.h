@@ -211,13 +211,16 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const float* topk_weights,
 
 /* ----------------------------------------------------------------------------------------------
  * Kernel timing with HIP events (measurement support, off by default).
- * bfp4_profile_begin(capacity) creates `capacity` event pairs and starts recording one pair
- * around every kernel the library launches; bfp4_profile_end() stops recording, waits for the
+ * bfp4_profile_begin(capacity, name_prefix) creates `capacity` event pairs and starts recording
+ * one pair around every kernel the library launches whose name starts with name_prefix (host
+ * string; NULL or "" for every kernel): plan_*, quantize_*, permute, prepare_weights, tile_list,
+ * gemm1_{swiglu,relu2}_{decode,prefill}, gemm2_down_{decode,prefill}, finalize.
+ * bfp4_profile_end() stops recording, waits for the
  * recorded events and writes one line per kernel name, "name count total_ms", into buf
  * (NUL-terminated, truncated to len).  Returns the number of kernels launched while recording,
  * or a negative status.
  * ---------------------------------------------------------------------------------------------- */
-int bfp4_profile_begin(int capacity);
+int bfp4_profile_begin(int capacity, const char* name_prefix);
 int bfp4_profile_end(char* buf, size_t len);
 
 #ifdef __cplusplus
