@@ -226,6 +226,8 @@ size_t bfp4_workspace_size(int64_t M, int64_t H, int64_t I, int top_k, int num_l
   if (H <= 0 || I <= 0) return 0;
   size_t ws = align_up(cap * (size_t)(I / 2)) + align_up(cap * (size_t)(I / 16)) +
               align_up(moe_gemm_tile_ws_bytes((int64_t)cap, block_m));
+  // tiled prefill kernels: FP16 copies of the activations and of the requantized intermediate
+  if (block_m > 32) ws += align_up((size_t)M * H * 2) + align_up(cap * (size_t)I * 2);
   if (do_finalize) ws += align_up(cap * (size_t)H * 2);
   return ws;
 }
@@ -246,8 +248,8 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
   if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
   if (!(isfinite(c2) && c2 > 0.0f) || !isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
-  // the tiled (block_m > 32) GEMMs address their token operands with 32-bit offsets
-  if (block_m > 32 && (M * (H / 2) >= (1LL << 31) || (int64_t)capacity * (I / 2) >= (1LL << 31)))
+  // the tiled (block_m > 32) GEMMs address their FP16 token operands with 32-bit offsets
+  if (block_m > 32 && (M * H * 2 >= (1LL << 31) || (int64_t)capacity * I * 2 >= (1LL << 31)))
     return BFP4_ERR_SHAPE;
   size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
   if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
@@ -294,6 +296,14 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   w += align_up(capacity * (size_t)(I / 16));
   uint8_t* tile_ws = w;
   w += align_up(moe_gemm_tile_ws_bytes((int64_t)capacity, block_m));
+  uint16_t* a16 = nullptr;
+  uint16_t* h16 = nullptr;
+  if (block_m > 32) {
+    a16 = reinterpret_cast<uint16_t*>(w);
+    w += align_up((size_t)M * H * 2);
+    h16 = reinterpret_cast<uint16_t*>(w);
+    w += align_up(capacity * (size_t)I * 2);
+  }
   uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
 
   MoeGemmProblem p{};
@@ -323,6 +333,8 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   p.dbg_pre = debug ? debug->preact : nullptr;
   p.dbg_inter = debug ? debug->inter : nullptr;
   p.tile_ws = tile_ws;
+  p.a16 = a16;
+  p.h16 = h16;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_moe_gemms(p, s);
   if (e != hipSuccess) return BFP4_ERR_LAUNCH;

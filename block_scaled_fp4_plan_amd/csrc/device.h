@@ -156,6 +156,23 @@ __device__ __forceinline__ uint4 buffer_load_u128(__amdgpu_buffer_rsrc_t r, uint
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Direct buffer -> LDS load of 16 bytes per lane: lane l's bytes land at lds_wave_base + 16*l
+// (lds_wave_base is wave-uniform).  Completion is counted by vmcnt like any vector load.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,
+                                                  uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only: at most N of this wave's vector memory
+// operations still outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Wave-wide (64 lanes) reductions.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

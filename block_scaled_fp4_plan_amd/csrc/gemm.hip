@@ -44,7 +44,8 @@ constexpr int kSuperChunks = 8;     // chunks sharing one 1 KiB scale unit
 constexpr int kUnit = 1024;
 constexpr int kSuperBytes = (kSuperChunks + 1) * kUnit;
 constexpr int kStageChunks = 2;     // chunks per pipeline stage (128 K values)
-constexpr int kTokPitch = 272;      // LDS bytes per token row per stage: 128 FP16 + 16 pad
+constexpr int kTokPitch = 256;      // LDS bytes per token row per stage: 128 FP16, 16-byte slots swizzled
+constexpr int kTokRegion = 128 * 1024;   // LDS bytes of prefill token stage buffers
 constexpr int kTileRows = 256;      // plan rows per prefill tile (8 token fragments)
 constexpr int kTileGroups = 8;      // weight row groups per prefill task (one per wave)
 
@@ -120,7 +121,9 @@ struct GemmArgs {
   // token operand
   const uint8_t* a_q;
   const uint8_t* a_sf;
-  int64_t a_rows;            // rows of a_q / a_sf
+  int64_t a_rows;            // rows of a_q / a_sf (and of t16)
+  const uint16_t* t16;       // prefill: exact FP16 copy of the token operand [a_rows, K]
+  int64_t t16_rowb;          // bytes per t16 row (2 K)
   const float* a_dec;        // per-token decode scale (gather) or nullptr
   float a_const_scale;       // decode scale when a_dec is nullptr
   int64_t a_rowq;            // bytes per packed token row (K/2)
@@ -146,6 +149,7 @@ struct GemmArgs {
   int64_t I;
   uint8_t* hq;
   uint8_t* hsf;
+  uint16_t* h16;             // prefill: FP16 copy of the requantized intermediate [cap, I] or null
   float* dbg_pre;
   uint16_t* dbg_inter;
   // GEMM2 epilogue
@@ -272,20 +276,27 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(
   }
 }
 
+// Exact FP16 copy of NVFP4 rows (E2M1 x E4M3, without the row's FP32 decode scale): one thread
+// per 8 values.
+__global__ void decode_rows_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sf,
+                                   int64_t n8, int64_t cols, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t v0 = i * 8;                   // first value; 8 values never straddle a row
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(q + (v0 >> 1));
+  const uint32_t sb = sf[v0 >> 4];
+  (void)cols;
+  *reinterpret_cast<h8_t*>(out + v0) = decode8(w, e4m3_scale_h2(sb));
+}
+
 struct Smem {
-  uint8_t* tok;         // two token stages of kTileRows rows
+  uint8_t* tok;         // token stage buffers (kTokRegion bytes)
   int* row_src;
   float* row_scale;
   int* sh_nvalid;
   int* sh_task;
 };
 
-// LDS slot (16 bytes = 8 FP16) of the 8 token values a lane needs for chunk c, K half h, MFMA
-// step s of a stage.  The writer of 16-value block blk (blk = 4c + 2h + s/2) stores its two
-// halves at slots blk and 8 + blk, so eight consecutive writer lanes fill 128 contiguous bytes.
-__device__ __forceinline__ int tok_slot(int c, int h, int s) {
-  return ((s & 1) << 3) + 4 * c + 2 * h + (s >> 1);
-}
 
 // Epilogue of one weight row group g for the plan row r of this lane's token column; the lane
 // holds the group's logical rows 16h .. 16h + 15.
@@ -341,6 +352,11 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     const uint32_t sfb = quant_block16(hv, a.c2, lo, hi);
     *reinterpret_cast<uint2*>(a.hq + r * (a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
     a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+    if (a.h16) {                 // the same values, E2M1 x E4M3 exactly in FP16
+      h8_t* d = reinterpret_cast<h8_t*>(a.h16 + r * a.I + i0);
+      d[0] = decode8(lo, e4m3_scale_h2(sfb));
+      d[1] = decode8(hi, e4m3_scale_h2(sfb));
+    }
     return;
   }
   // SwiGLU
@@ -377,43 +393,50 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
   bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 32, 64));
   float inv;
   const uint32_t sfb = block_scale(bmax, a.c2, inv);
-  *reinterpret_cast<uint32_t*>(a.hq + r * (a.I >> 1) + (ih >> 1)) = quant8(hv, inv);
+  const uint32_t codes = quant8(hv, inv);
+  *reinterpret_cast<uint32_t*>(a.hq + r * (a.I >> 1) + (ih >> 1)) = codes;
   if (h == 0) a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+  if (a.h16)                     // the same values, E2M1 x E4M3 exactly in FP16
+    *reinterpret_cast<h8_t*>(a.h16 + r * a.I + ih) = decode8(codes, e4m3_scale_h2(sfb));
 }
 
 // Prefetch depths of a prefill tile with NFW token fragments, in 128-K stages: the weights of
-// stage st + RW - 1 and the packed tokens of stage st + RT are loaded while stage st computes.
-// Short tiles have short stages and spare registers, so they look further ahead.
+// stage st + RW - 1 are loaded into registers and the FP16 token rows of stage st + NB - 1 into
+// LDS while stage st computes.  A stage of token rows takes NFW * 8 KiB of the 128 KiB region,
+// so short tiles (short stages) look further ahead.
 template <int NFW> struct TileDepth {
   static constexpr int RW = NFW <= 4 ? 4 : 2;
-  static constexpr int RT = NFW <= 2 ? 4 : 2;
+  static constexpr int NB0 = kTokRegion / (NFW * 32 * kTokPitch);
+  static constexpr int NB = NB0 > 8 ? 8 : NB0;
 };
 
 // One prefill tile of up to kTileRows plan rows of one expert, against kTileGroups weight row
 // groups.  Eight waves, two per SIMD: wave w owns row group g = kTileGroups * nt + w and all NFW
 // token fragments of the tile (32 * NFW plan rows), so each weight fragment is decoded once per
-// tile and each token value once per workgroup.
-// Per 128-K stage: the token rows are staged in LDS as FP16 (double buffered, their packed bytes
-// loaded RT stages ahead into registers); the weights are loaded RW - 1 stages ahead into
-// registers.  Within a stage, step q (16 K values) issues the NFW MFMAs of step q, and right
-// behind each MFMA the LDS read of the same token fragment for step q + 1 into the register the
-// MFMA has just consumed, so every LDS read has a whole step to complete.  The weight fragment
-// of step q + 1 is decoded during step q, and the next stage's staging items are decoded and
-// stored in LDS in between.
+// tile.  The token operand comes from an exact FP16 copy (the decoded activations for GEMM1,
+// the dequantized intermediate for GEMM2) and is copied into LDS by direct buffer-to-LDS loads:
+// per 128-K stage each wave moves 4 rows of every fragment (one 1 KiB load per fragment), into
+// a ring of NB stage buffers.  Inside a buffer row r's 16-byte slot u (K values 8u .. 8u+7 of the
+// stage) sits at slot u ^ (r & 15), so the MFMA operand reads are free of bank conflicts.
+// Per 16-K step a wave issues its NFW MFMAs, each followed by the LDS read that refills the same
+// token register for the next step, and decodes its weight fragment of the next step.
 template <int NFW, int EPI>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int e, int nt,
                                          int64_t row0) {
   static_assert(NFW >= 1 && NFW <= 8, "at most 8 token fragments per tile");
-  constexpr int RW = TileDepth<NFW>::RW, RT = TileDepth<NFW>::RT;
-  static_assert((RW == 2 || RW == 4) && (RT == 2 || RT == 4), "ring depths of 2 or 4");
-  constexpr int PERIOD = (RW > RT) ? RW : RT;   // a multiple of 2, RW and RT
-  constexpr int ITEMS = (NFW + 1) / 2;    // staging items per thread and stage (<= 4)
-  constexpr int BUF = kTileRows * kTokPitch;
+  constexpr int RW = TileDepth<NFW>::RW, NB = TileDepth<NFW>::NB;
+  static_assert(RW == 2 || RW == 4, "weight ring of 2 or 4 stages");
+  static_assert(NB >= 2, "at least two token stage buffers");
+  constexpr int SBUF = NFW * 32 * kTokPitch;      // bytes of one stage buffer
+  // vector memory operations a wave issues per stage: NFW token loads, then 3 weight loads
+  constexpr int VM_STAGE = NFW + 3;
+  // loads issued after the prologue's token load of stage 1: NB - 3 token stages, RW - 1 weight
+  // stages, then stage 0's NFW + 3 (the fewest behind any prologue-loaded stage)
+  constexpr int kEarlyWait = NB >= 3 ? (NB - 3) * NFW + 3 * (RW - 1) + VM_STAGE : 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int nst = a.nch / kStageChunks;
-  const uint32_t sf_rowb = (uint32_t)(a.a_rowq >> 3);
 
   const int64_t g = (int64_t)nt * kTileGroups + wave;
   const bool wave_on = (g + 1) * kGroupRows <= a.N;
@@ -424,23 +447,28 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
       a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g : 0) * a.rg_bytes, (uint32_t)a.rg_bytes);
   const int wlane = lane * 16;
 
-  // staging item it: plan row (tid >> 3) + 64 it, 16-value block tid & 7 of a stage.  Rows
-  // without a routed slot read token row 0; their MFMA columns are discarded.  The token
-  // operand is smaller than 2^31 bytes (checked by the launcher), so offsets are 32-bit.
-  const int blk = tid & 7;
-  const int lds0 = (tid >> 3) * kTokPitch + blk * 16;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(a.a_q, (uint32_t)(a.a_rows * a.a_rowq));
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.a_sf, (uint32_t)(a.a_rows * sf_rowb));
-  uint32_t it_q[ITEMS], it_s[ITEMS];
+  // token rows: this lane moves row 32 i + 4 wave + lane / 16 of fragment i, physical slot
+  // lane % 16, i.e. logical slot u_l; rows without a routed slot read row 0 (their MFMA columns
+  // are discarded).  The FP16 token operand is smaller than 2^31 bytes (checked at the entry
+  // point), so offsets are 32-bit.
+  const int trow = 4 * wave + (lane >> 4);
+  const uint32_t u_l = (uint32_t)((lane & 15) ^ (trow & 15));
+  const uint32_t rowb = (uint32_t)a.t16_rowb;
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(a.t16, (uint32_t)(a.a_rows * (int64_t)rowb));
+  uint32_t t_voff[NFW];
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    int src = sm.row_src[(tid >> 3) + 64 * it];
+  for (int i = 0; i < NFW; ++i) {
+    int src = sm.row_src[32 * i + trow];
     src = src < 0 ? 0 : src;
-    it_q[it] = (uint32_t)src * (uint32_t)a.a_rowq + blk * 8;
-    it_s[it] = (uint32_t)src * sf_rowb + blk;
+    t_voff[i] = (uint32_t)src * rowb + u_l * 16;
   }
-  // LDS byte offset of this lane's token operand in fragment 0, step q of a stage buffer
-  auto t_off = [&](int q) { return col * kTokPitch + tok_slot(q >> 2, h, q & 3) * 16; };
+  uint8_t* const tok_wave = sm.tok + 4 * wave * kTokPitch;       // row 4 * wave of a buffer
+  // LDS byte offset of this lane's operand in fragment 0, step q of a stage buffer
+  const int swz = col & 15;
+  auto t_off = [&](int q) {
+    const int u = 8 * (q >> 2) + 4 * h + (q & 3);
+    return col * kTokPitch + ((u ^ swz) << 4);
+  };
 
   f32x16_t acc[NFW];
 #pragma unroll
@@ -448,8 +476,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
 
   uint4 W[RW][kStageChunks];
   uint32_t S[RW];
-  uint2 Tq[RT][ITEMS];
-  uint32_t Ts[RT][ITEMS];
   h8_t T[NFW];
   h8_t Wc;
 
@@ -462,18 +488,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
     for (int c = 0; c < kStageChunks; ++c)
       Wd[c] = buffer_load_u128(wrs, wlane + (1 + c) * kUnit, so + c0 * kUnit);
   };
-  auto load_t = [&](uint2 (&Tqd)[ITEMS], uint32_t (&Tsd)[ITEMS], int st) {
+  // token rows of stage st into stage buffer b
+  auto load_t = [&](int b, int st) {
+    uint8_t* dst = tok_wave + b * SBUF;
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      Tqd[it] = buffer_load_u64(qrs, it_q[it], st * 64);
-      Tsd[it] = buffer_load_u8(srs, it_s[it], st * 8);
-    }
-  };
-  auto store_item = [&](uint2 q, uint32_t sb, uint8_t* buf, int it) {
-    const uint32_t s2 = e4m3_scale_h2(sb);
-    uint8_t* d = buf + lds0 + it * 64 * kTokPitch;
-    *reinterpret_cast<h8_t*>(d) = decode8(q.x, s2);
-    *reinterpret_cast<h8_t*>(d + 128) = decode8(q.y, s2);
+    for (int i = 0; i < NFW; ++i)
+      buffer_load_lds16(trs, dst + i * 32 * kTokPitch, t_voff[i], (uint32_t)st * kTokPitch);
   };
   auto dec_w = [&](const uint4 (&Wd)[kStageChunks], uint32_t Sd, int q) {
     const int c = q >> 2, s = q & 3;
@@ -487,34 +507,34 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
       T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q));
   };
 
-  // ---- prologue: tokens of stages 0 .. RT-1 (stage 0 staged), weights of 0 .. RW-2 ----
-  // Loads are never conditional (stage indices are clamped; the loads past the end re-read the
-  // last stage), so the waits the compiler places before each use count exactly the loads
-  // issued after it and the prefetch stays in flight.
-  load_t(Tq[0], Ts[0], 0);
+  // ---- prologue: token stages 0 .. NB-2 into buffers 0 .. NB-2, weights of 0 .. RW-2 ----
+  // Every load is unconditional (stage indices clamped; the loads past the end re-read the last
+  // stage into buffers nobody reads again), and token loads and weight loads are issued in a
+  // fixed order, so the explicit waits below count exactly.
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b) load_t(b, min(b, nst - 1));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < RW - 1; ++r) load_w(W[r], S[r], min(r, nst - 1));
-#pragma unroll
-  for (int r = 1; r < RT; ++r) load_t(Tq[r], Ts[r], min(r, nst - 1));
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it) store_item(Tq[0][it], Ts[0][it], sm.tok, it);
+  __builtin_amdgcn_sched_barrier(0);
+  // stage 0's rows have landed once at most the later loads are outstanding
+  wait_vmcnt<(NB - 2) * NFW + 3 * (RW - 1)>();
   lds_barrier();
   read_all(sm.tok, 0);
   Wc = dec_w(W[0], S[0], 0);
 
-  // One stage st; R = st % PERIOD gives the LDS buffer (R % 2), the weight slot (R % RW) and the
-  // token slot (R % RT) as compile-time indices.  Stage st refills the token slot it freed
-  // (stage st was staged during stage st - 1) with stage st + RT, and the weight slot freed by
-  // stage st - 1 with stage st + RW - 1.  Stages run in groups of PERIOD with the remainder
-  // after the loop: the loop has no early exit, which keeps the register allocation of the
-  // unrolled body flat.
+  // One stage st; R = st % RW gives the weight slot as a compile-time index; the LDS stage
+  // buffer is st % NB.  Stage st refills buffer (st - 1) % NB (read by stage st - 1, released by
+  // the barrier that ended it) with stage st + NB - 1, and the weight slot freed by stage st - 1
+  // with stage st + RW - 1.  Stages run in groups of RW with the remainder after the loop.
   auto stage = [&](auto RR, int st) {
     constexpr int R = decltype(RR)::value;
-    constexpr int d = R & 1, rw = R % RW, rt = R % RT, rt1 = (R + 1) % RT;
-    const uint8_t* buf = sm.tok + d * BUF;
-    uint8_t* nbuf = sm.tok + (d ^ 1) * BUF;
-    load_t(Tq[rt], Ts[rt], min(st + RT, nst - 1));
+    const uint8_t* buf = sm.tok + (st % NB) * SBUF;
+    const uint8_t* nbuf = sm.tok + ((st + 1) % NB) * SBUF;
+    load_t((st + NB - 1) % NB, min(st + NB - 1, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
     load_w(W[(R + RW - 1) % RW], S[(R + RW - 1) % RW], min(st + RW - 1, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
 #pragma unroll
@@ -523,19 +543,23 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
         if (q < 7)
           T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q + 1));
       }
-      Wc = (q < 7) ? dec_w(W[rw], S[rw], q + 1) : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
-      // items of stage st + 1 at steps 0, 2, 4, 6
-      if ((q & 1) == 0 && (q >> 1) < ITEMS) store_item(Tq[rt1][q >> 1], Ts[rt1][q >> 1], nbuf, q >> 1);
+      Wc = (q < 7) ? dec_w(W[R], S[R], q + 1) : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
       // order within the step: each MFMA followed by the LDS read that refills its token
-      // register, the decode VALU work spread in between
+      // register, the weight decode spread in between
 #pragma unroll
       for (int j = 0; j < NFW; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
         if (q < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);      // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // stage st + 1's rows have landed once at most the loads issued after them are
+    // outstanding.  In the steady state they were loaded NB - 1 stages ago, followed by that
+    // stage's 3 weight loads and NB - 2 full stages; while st + 1 <= NB - 2 they came from the
+    // prologue, followed by fewer loads (the smallest count is at st = 0).
+    if (st + 1 > NB - 2) wait_vmcnt<3 + (NB - 2) * VM_STAGE>();
+    else wait_vmcnt<kEarlyWait>();
     lds_barrier();
     read_all(nbuf, 0);
   };
@@ -544,7 +568,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   int st = 0;
-  if constexpr (PERIOD == 2) {
+  if constexpr (RW == 2) {
     for (; st + 1 < nst; st += 2) {
       stage(I0{}, st);
       stage(I1{}, st + 1);
@@ -562,6 +586,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
     if (rem >= 2) stage(I1{}, st + 1);
     if (rem >= 3) stage(I2{}, st + 2);
   }
+  // the clamped token loads of the last stages must land before LDS is reused
+  wait_vmcnt<0>();
 
   // ---- epilogue ----
   if (!wave_on) return;
@@ -597,7 +623,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Smem sm;
   sm.tok = smem;
-  sm.row_src = reinterpret_cast<int*>(smem + 2 * kTileRows * kTokPitch);
+  sm.row_src = reinterpret_cast<int*>(smem + kTokRegion);
   sm.row_scale = reinterpret_cast<float*>(sm.row_src + kTileRows);
   sm.sh_nvalid = reinterpret_cast<int*>(sm.row_scale + kTileRows);
   sm.sh_task = sm.sh_nvalid + 1;
@@ -807,7 +833,7 @@ hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, 
 
 template <int EPI>
 hipError_t launch_gemm(const GemmArgs& a, int64_t max_tiles, const char* name, hipStream_t s) {
-  const size_t lds = 2 * (size_t)kTileRows * kTokPitch + 2 * kTileRows * sizeof(int) + 16;
+  const size_t lds = (size_t)kTokRegion + 2 * kTileRows * sizeof(int) + 16;
   auto kern = moe_gemm_kernel<EPI>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -876,6 +902,14 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
     g1.tiles = tiles;
     g1.n_tiles = n_tiles;
     g1.task_counter = counters;
+    const int64_t n8 = p.M * (p.H / 8);
+    if (n8 > 0) {
+      KernelTimer t("decode_tokens", s);
+      hipLaunchKernelGGL(decode_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                         p.a_q, p.a_sf, n8, p.H, p.a16);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
     KernelTimer t("tile_list", s);
     hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, p.eids, p.sorted, p.ntpp, p.cap,
                        p.block_m, (int64_t)(p.M * p.top_k), p.nloc, tile_tmp, tiles, n_tiles,
@@ -896,6 +930,9 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.I = p.I;
   g1.hq = p.hq;
   g1.hsf = p.hsf;
+  g1.t16 = small ? nullptr : p.a16;
+  g1.t16_rowb = p.H * 2;
+  g1.h16 = small ? nullptr : p.h16;
   g1.dbg_pre = p.dbg_pre;
   g1.dbg_inter = p.dbg_inter;
 
@@ -905,6 +942,9 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g2.a_rows = p.cap;
   g2.a_dec = nullptr;
   g2.a_const_scale = 1.0f / p.c2;
+  g2.t16 = small ? nullptr : p.h16;
+  g2.t16_rowb = p.I * 2;
+  g2.h16 = nullptr;
   g2.task_counter = counters + 1;
   g2.a_rowq = p.I / 2;
   g2.gather = 0;
@@ -929,8 +969,8 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
     if (err != hipSuccess) return err;
     return launch_gemv<2, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s);
   }
-  // the prefill kernels address token operands with 32-bit buffer offsets
-  if (p.M * (p.H / 2) >= (int64_t(1) << 31) || p.cap * (p.I / 2) >= (int64_t(1) << 31))
+  // the prefill kernels address their FP16 token operands with 32-bit buffer offsets
+  if (p.M * p.H * 2 >= (int64_t(1) << 31) || p.cap * p.I * 2 >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
   err = gated ? launch_gemm<EPI_SWIGLU>(g1, max_tiles, "gemm1_swiglu_prefill", s)
               : launch_gemm<EPI_RELU2>(g1, max_tiles, "gemm1_relu2_prefill", s);

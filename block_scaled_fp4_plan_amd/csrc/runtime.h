@@ -64,6 +64,8 @@ struct MoeGemmProblem {
   float* dbg_pre;
   uint16_t* dbg_inter;
   uint8_t* tile_ws;  // moe_gemm_tile_ws_bytes() of scratch for the prefill tile list
+  uint16_t* a16;     // block_m > 32: [M, H] FP16 copy of the activations
+  uint16_t* h16;     // block_m > 32: [cap, I] FP16 copy of the requantized intermediate
 };
 hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s);
 int64_t moe_gemm_max_tiles(int64_t cap, int block_m);

@@ -155,7 +155,7 @@ def test_fused_validation():
     assert _fused(out=A + (1 << 16) + 64) == "BFP4_ERR_OVERLAP"  # out over a_sf
     assert _fused(out=A + (50 << 16) + 512) == "BFP4_ERR_OVERLAP"  # out over workspace
     assert _fused(num_local_experts=0) == "BFP4_ERR_EXPERTS"
-    # tiled kernels (block_m > 32) address token operands with 32-bit offsets: M*H/2 < 2^31
+    # tiled kernels (block_m > 32) read FP16 token copies with 32-bit offsets: M*H*2 < 2^31
     assert _fused(M=1 << 24, top_k=1, block_m=128) == "BFP4_ERR_SHAPE"
 
 
