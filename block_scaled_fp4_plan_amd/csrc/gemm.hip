@@ -48,6 +48,7 @@ constexpr int kTokPitch = 256;      // LDS bytes per token row per stage: 128 FP
 constexpr int kTokRegion = 128 * 1024;   // LDS bytes of prefill token stage buffers
 constexpr int kTileRows = 256;      // plan rows per prefill tile (8 token fragments)
 constexpr int kTileGroups = 8;      // weight row groups per prefill task (one per wave)
+constexpr int kXcds = 8;            // accelerator complex dies (each with its own L2)
 
 // Logical row (within a 32-row group) held at physical row rho: the MFMA 32x32 accumulator of
 // lane l holds rows 8i + 4*(l/32) + j (i, j in 0..3); they are made logical rows
@@ -137,7 +138,7 @@ struct GemmArgs {
   int top_k, block_m, nloc;
   const int2* tiles;         // prefill tiles {first row, rows}, longest and shortest alternating
   const int32_t* n_tiles;
-  uint32_t* task_counter;    // prefill: next task to hand out (cleared by the tile list)
+  uint32_t* task_counter;    // prefill: one ticket counter per XCD queue (cleared by the tile list)
   // weights
   const uint8_t* panel;
   int64_t expert_bytes, rg_bytes;
@@ -166,7 +167,7 @@ enum { EPI_SWIGLU = 0, EPI_RELU2 = 1, EPI_DOWN = 2 };
 //     kTileRows-row slices of each block of a local expert;
 //  2. each tile's token-fragment count (up to its last routed row), tiles ranked by it
 //     (counting sort) and interleaved longest / shortest for the dynamic schedule of the GEMMs;
-//  3. the GEMMs' task counters are cleared.
+//  3. the GEMMs' per-XCD ticket counters are cleared.
 // tmp holds max_tiles int2 + max_tiles int; tiles max_tiles int2.
 __global__ __launch_bounds__(1024) void tile_list_kernel(
     const int32_t* __restrict__ eids, const int32_t* __restrict__ sorted,
@@ -261,8 +262,7 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(
     }
     offs[0] = acc;
     *n_tiles = acc;
-    counters[0] = 0u;
-    counters[1] = 0u;
+    for (int c = 0; c < 2 * kXcds; ++c) counters[c] = 0u;
   }
   __syncthreads();
   // rank r in decreasing fragment count -> position: the longest and the shortest tiles
@@ -629,13 +629,35 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   sm.sh_task = sm.sh_nvalid + 1;
 
   const int tid = threadIdx.x;
-  const int64_t ntask = (int64_t)(*a.n_tiles) * a.n_nt;
-  if (tid == 0) *sm.sh_task = (int)atomicAdd(a.task_counter, 1u);
+  const int n_tiles = *a.n_tiles;
+  // queue x holds tiles x, x + 8, ... (the tile list alternates long and short tiles, so every
+  // queue gets a similar mix); workgroups of XCD x (dispatch places workgroup i on XCD i % 8)
+  // take tasks from queue x, so a tile's n-tile tasks share one L2, and move on to the next
+  // queues when theirs is empty.  Thread 0 keeps the current queue in q.
+  auto q_tasks = [&](int qq) -> int64_t {
+    return n_tiles > qq ? (int64_t)((n_tiles - qq + kXcds - 1) / kXcds) * a.n_nt : 0;
+  };
+  // resolve a ticket of queue q into a task (tile * n_nt + n-tile), moving on while queues are
+  // exhausted; -1 when every queue is
+  auto resolve = [&](int& qq, uint32_t ticket) -> int {
+    for (int tries = 0; tries < kXcds; ++tries) {
+      if ((int64_t)ticket < q_tasks(qq)) {
+        const int tile = qq + kXcds * (int)(ticket / a.n_nt);
+        return tile * a.n_nt + (int)(ticket % a.n_nt);
+      }
+      if (tries == kXcds - 1) break;
+      qq = (qq + 1) % kXcds;
+      ticket = atomicAdd(a.task_counter + qq, 1u);
+    }
+    return -1;
+  };
+  int q = (int)(blockIdx.x % kXcds);
+  if (tid == 0) *sm.sh_task = resolve(q, atomicAdd(a.task_counter + q, 1u));
   __syncthreads();
   int64_t k = *sm.sh_task;
-  while (k < ntask) {
-    uint32_t k_next = 0;
-    if (tid == 0) k_next = atomicAdd(a.task_counter, 1u);   // in flight during this task
+  while (k >= 0) {
+    uint32_t ticket = 0;
+    if (tid == 0) ticket = atomicAdd(a.task_counter + q, 1u);   // in flight during this task
     const int2 t = a.tiles[k / a.n_nt];
     const int nt = (int)(k % a.n_nt);
     const int64_t row0 = t.x;
@@ -669,7 +691,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
     // the tile list holds local experts and tiles with a routed row only
     if (nvalid > 0 && e >= 0 && e < a.nloc) run_nfw<EPI>(a, sm, e, nt, row0, (nvalid + 31) >> 5);
     __syncthreads();                         // every thread has read sh_task
-    if (tid == 0) *sm.sh_task = (int)k_next;
+    if (tid == 0) *sm.sh_task = resolve(q, ticket);
     __syncthreads();
     k = *sm.sh_task;
   }
@@ -945,7 +967,7 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g2.t16 = small ? nullptr : p.h16;
   g2.t16_rowb = p.I * 2;
   g2.h16 = nullptr;
-  g2.task_counter = counters + 1;
+  g2.task_counter = counters + kXcds;
   g2.a_rowq = p.I / 2;
   g2.gather = 0;
   PanelGeom pg2 = panel_geom(p.H, p.I);
@@ -983,8 +1005,9 @@ int64_t moe_gemm_max_tiles(int64_t cap, int block_m) {
 }
 
 size_t moe_gemm_tile_ws_bytes(int64_t cap, int block_m) {
-  // tile list scratch (int2 + int per tile, as two int2), the ordered list, count, 2 counters
-  return (size_t)moe_gemm_max_tiles(cap, block_m) * 3 * sizeof(int2) + 16;
+  // tile list scratch (int2 + int per tile, as two int2), the ordered list, the count and the
+  // two GEMMs' per-XCD ticket counters
+  return (size_t)moe_gemm_max_tiles(cap, block_m) * 3 * sizeof(int2) + 4 + 2 * kXcds * 4;
 }
 
 }  // namespace bfp4
