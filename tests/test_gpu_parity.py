@@ -356,3 +356,66 @@ def test_masked_slots_nan_weights_and_all_masked_token():
     torch.cuda.synchronize()
     assert np.array_equal(np_bits(out_b), got)
     assert base.shape == got.shape
+
+
+# ----------------------------------------------------------------------------- exact GEMM1 case
+
+EXACT_GRID = Workload("exact_grid", M=48, H=2048, I=256, E=4, top_k=2, block_m=8)
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _grid_rows(rng, rows, cols, big_rows, zero_blocks, big_block, pow2):
+    """Values on the NVFP4 grid: every 16-value block holds E2M1 values with block scale 1 and
+    one element of magnitude 6, except zero_blocks (all zero) and, in big_rows, big_block (block
+    scale 448, so the row maximum is 6 * 448); all times 2**pow2."""
+    v = _E2M1[rng.integers(0, 8, (rows, cols))] * rng.choice([-1.0, 1.0], (rows, cols))
+    v = v.reshape(rows, cols // 16, 16)
+    v[:, :, 0] = 6.0 * rng.choice([-1.0, 1.0], (rows, cols // 16))
+    for b in zero_blocks:
+        v[:, b, :] = 0.0
+    for r in big_rows:
+        v[r, big_block, :] *= 448.0
+    return (v.reshape(rows, cols) * 2.0 ** pow2)
+
+
+@pytest.mark.parametrize("bm", [8, 128])
+def test_gemm1_exact_on_grid(bm):
+    """GEMM1 pre-activation bit-exact in a case where FP32 accumulation is exact.
+
+    Activations and W1 lie on the NVFP4 grid with power-of-two token and expert scales (row
+    maxima 2688 * 2^-9 and 2688 * 2^-10, so the decode scales are 2^-9 and 2^-10); the scale-448
+    blocks of activations (K block 0) and of W1 (K block 1, row 0) meet only zeros, so every
+    surviving product is a multiple of 1/4 of magnitude <= 36 and every partial sum over
+    K = 2048 is an exact FP32 number in any order.  The GPU's pre-activation must then equal the
+    oracle's exact value bit for bit, on the decode (block_m 8) and the tiled (block_m 128)
+    kernels."""
+    from synth import bf16_bits
+    wl = EXACT_GRID
+    say("exact GEMM1 on grid, block_m", bm)
+    rng = np.random.default_rng(11)
+    p = Problem(wl)
+    x = _grid_rows(rng, wl.M, wl.H, range(wl.M), [1], 0, -9)
+    p.x_bits = bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(p.x_bits).astype(np.float64), x)   # exact in BF16
+    p.x = torch.from_numpy(p.x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    w1 = np.stack([_grid_rows(rng, wl.N1, wl.H, [0], [0], 1, -10) for _ in range(wl.E)])
+    wb = bf16_bits(w1)
+    assert np.array_equal(bf16_bits_to_f32(wb).astype(np.float64), w1)
+    p.w1 = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).cuda()
+    p._host_w = {}
+    fwd, pw, lin, dbg, out = run_gpu_moe(p, bm)
+    oq, osf, odec = p.oracle_activations()
+    assert np.all(odec == np.float32(2.0 ** -9))
+    srt, eids, P, ttr = p.oracle_plan(bm)
+    experts = sorted(set(int(e) for e in eids[:P // bm]))
+    a1, a2 = p.oracle_alphas(experts)
+    assert all(a1[e] == np.float32(2.0 ** -10) for e in experts)
+    res = oracle.fused_moe_nvfp4(oq, osf, odec, lambda e: p.oracle_expert(e)[0], a1, a1, a2, 1.0,
+                                 srt, eids, P, ttr, p.w, wl.top_k, bm, oracle.ACT_SWIGLU)
+    rows = sorted(res["pre"].keys())
+    pre_ref = np.stack([res["pre"][r] for r in rows])
+    assert np.array_equal(pre_ref.astype(np.float32).astype(np.float64), pre_ref)  # FP32-exact
+    pre_gpu = dbg["preact"].cpu().numpy()[rows].astype(np.float64)
+    bad = int(np.count_nonzero(pre_gpu != pre_ref))
+    say("exact GEMM1 block_m %d: %d of %d pre-activations differ" % (bm, bad, pre_ref.size))
+    assert bad == 0
