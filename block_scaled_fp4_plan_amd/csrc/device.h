@@ -47,13 +47,18 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// float -> E2M1 code: nearest magnitude, ties to the even code, saturate at 6; sign bit copied.
-__device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
-  float a = __builtin_fabsf(y);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-               (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
+// float -> E2M1 code: nearest magnitude, ties to the even code, saturate at 6, sign bit copied
+// (so -0.0 and small negatives give code 0x8).  gfx950's v_cvt_scalef32_pk_fp4_f32 with a scale
+// of 1 implements exactly this rule: it was compared with a compare-chain encoder of the rule on
+// every finite FP32 bit pattern and on both infinities, with no difference.  It converts two
+// values per instruction, the first into the low nibble of the selected byte.
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float lo, float hi, int sel) {
+  switch (sel) {   // the byte selector must be a compile-time constant
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, 3);
+  }
 }
 
 // E4M3 block scale of a block whose largest magnitude is bmax, for encode scale s_enc (FP32
@@ -67,12 +72,12 @@ __device__ __forceinline__ uint32_t block_scale(float bmax, float s_enc, float& 
   return sf;
 }
 
-// 8 values -> 8 E2M1 codes in one dword (value i in bits 4i..4i+3: even value in the low
-// nibble of each byte).
+// 8 values -> 8 E2M1 codes of fl32(x * inv) in one dword (value i in bits 4i..4i+3: even value
+// in the low nibble of each byte).
 __device__ __forceinline__ uint32_t quant8(const float* x, float inv) {
   uint32_t c = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c |= f32_to_e2m1(x[i] * inv) << (4 * i);
+  for (int j = 0; j < 4; ++j) c = e2m1_pack2(c, x[2 * j] * inv, x[2 * j + 1] * inv, j);
   return c;
 }
 

@@ -298,6 +298,14 @@ struct Smem {
 };
 
 
+// SiLU x / (1 + e^-x) with the hardware exponential (2^y) and reciprocal, each within a few ulp
+// of FP32: the result is rounded to BF16 next.  Saturates to -0 for large negative x (e^-x
+// overflows to infinity, whose reciprocal is 0) and to x for large positive x.
+__device__ __forceinline__ float silu(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896341f);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Epilogue of one weight row group g for the plan row r of this lane's token column; the lane
 // holds the group's logical rows 16h .. 16h + 15.
 //   down:    outputs 32g + 16h + v  ->  BF16, 32 contiguous bytes per lane
@@ -380,7 +388,7 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     const float recv = __shfl_xor(send, 32, 64);
     const float gt = h ? recv : pre[v];
     const float up = h ? pre[8 + v] : recv;
-    bb[v] = f32_to_bf16((gt / (1.0f + expf(-gt))) * up);
+    bb[v] = f32_to_bf16(silu(gt) * up);
     hv[v] = bf16_to_f32(bb[v]);
     bmax = __builtin_fmaxf(bmax, __builtin_fabsf(hv[v]));
   }
