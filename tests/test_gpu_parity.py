@@ -419,3 +419,38 @@ def test_gemm1_exact_on_grid(bm):
     bad = int(np.count_nonzero(pre_gpu != pre_ref))
     say("exact GEMM1 block_m %d: %d of %d pre-activations differ" % (bm, bad, pre_ref.size))
     assert bad == 0
+
+
+# ----------------------------------------------------------------------------- empty inputs
+
+@pytest.mark.parametrize("bm", [8, 128])
+def test_nothing_local_and_empty_batch(bm):
+    """No routed slot is local (every expert id below the local range): the plan is empty, out
+    keeps its previous contents bit for bit and the unfinalized triple names no row.  M = 0: every
+    call succeeds and touches nothing."""
+    wl = WORKLOADS["tiny"]
+    say("nothing local / empty batch, block_m", bm)
+    p = Problem(wl)
+    half = wl.E // 2                     # local experts [half, E); every routed id below half
+    pw = runner.prepare_weights(p.w1[half:], p.w2[half:], gated=True)
+    ids = torch.from_numpy(p.ids % half).cuda()
+    fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, bm, local_expert_offset=half)
+    o0 = np.random.default_rng(2).integers(0, 0x3F00, (p.M, wl.H)).astype(np.uint16)
+    out = torch.from_numpy(o0.view(np.int16)).view(torch.bfloat16).cuda()
+    fwd(p.x, ids, p.w_d, out=out)
+    torch.cuda.synchronize()
+    assert int(fwd.plan.num_tokens_post_padded.item()) == 0
+    assert np.array_equal(np_bits(out), o0)
+    fwd_u = runner.MoeForward(pw, p.M, wl.top_k, wl.E, bm, local_expert_offset=half,
+                              do_finalize=False)
+    y, wts, ttr = fwd_u(p.x, ids, p.w_d)
+    torch.cuda.synchronize()
+    assert np.all(ttr.cpu().numpy() == -1)
+    # an empty batch
+    fwd0 = runner.MoeForward(pw, 0, wl.top_k, wl.E, bm)
+    x0 = torch.empty((0, wl.H), dtype=torch.bfloat16, device="cuda")
+    out0 = torch.empty((0, wl.H), dtype=torch.bfloat16, device="cuda")
+    fwd0(x0, torch.empty((0, wl.top_k), dtype=torch.int32, device="cuda"),
+         torch.empty((0, wl.top_k), dtype=torch.float32, device="cuda"), out=out0)
+    torch.cuda.synchronize()
+    assert int(fwd0.plan.num_tokens_post_padded.item()) == 0
