@@ -30,6 +30,7 @@
 // * Plan rows past the device-side extent, padding rows and 32-row token fragments with no valid
 //   row are skipped; a static schedule interleaves M tiles over the 8 XCDs.
 #include <type_traits>
+#include <utility>
 
 #include "device.h"
 #include "runtime.h"
@@ -408,6 +409,12 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     *reinterpret_cast<h8_t*>(a.h16 + r * a.I + ih) = decode8(codes, e4m3_scale_h2(sfb));
 }
 
+// f(integral_constant<int, I>) for I = 0, 1, ... in order
+template <typename F, int... Is>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+
 // Prefetch depths of a prefill tile with NFW token fragments, in 128-K stages: the weights of
 // stage st + RW - 1 are loaded into registers and the FP16 token rows of stage st + NB - 1 into
 // LDS while stage st computes.  A stage of token rows takes NFW * 8 KiB of the 128 KiB region,
@@ -433,7 +440,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
                                          int64_t row0) {
   static_assert(NFW >= 1 && NFW <= 8, "at most 8 token fragments per tile");
   constexpr int RW = TileDepth<NFW>::RW, NB = TileDepth<NFW>::NB;
-  static_assert(RW == 2 || RW == 4, "weight ring of 2 or 4 stages");
+  static_assert(RW >= 2 && RW <= 8, "weight ring of 2 to 8 stages");
   static_assert(NB >= 2, "at least two token stage buffers");
   constexpr int SBUF = NFW * 32 * kTokPitch;      // bytes of one stage buffer
   // vector memory operations a wave issues per stage: NFW token loads, then 3 weight loads
@@ -571,29 +578,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
     lds_barrier();
     read_all(nbuf, 0);
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
   int st = 0;
-  if constexpr (RW == 2) {
-    for (; st + 1 < nst; st += 2) {
-      stage(I0{}, st);
-      stage(I1{}, st + 1);
-    }
-    if (st < nst) stage(I0{}, st);
-  } else {
-    for (; st + 3 < nst; st += 4) {
-      stage(I0{}, st);
-      stage(I1{}, st + 1);
-      stage(I2{}, st + 2);
-      stage(I3{}, st + 3);
-    }
-    const int rem = nst - st;
-    if (rem >= 1) stage(I0{}, st);
-    if (rem >= 2) stage(I1{}, st + 1);
-    if (rem >= 3) stage(I2{}, st + 2);
-  }
+  for (; st + RW - 1 < nst; st += RW)
+    unroll_seq([&](auto RR) { stage(RR, st + decltype(RR)::value); },
+               std::make_integer_sequence<int, RW>{});
+  const int rem = nst - st;
+  unroll_seq([&](auto RR) { if (decltype(RR)::value < rem) stage(RR, st + decltype(RR)::value); },
+             std::make_integer_sequence<int, RW - 1>{});
+  // The explicit waits count three weight loads in every stage, also in the last stages whose
+  // weight registers are never read again; this use keeps the compiler from deleting those loads.
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, W[r][0])),
+                 "v"(__builtin_bit_cast(u32x4_t, W[r][1])), "v"(S[r]));
   // the clamped token loads of the last stages must land before LDS is reused
   wait_vmcnt<0>();
 
