@@ -50,6 +50,10 @@ constexpr int kTokRegion = 128 * 1024;   // LDS bytes of prefill token stage buf
 constexpr int kTileRows = 256;      // plan rows per prefill tile (8 token fragments)
 constexpr int kTileGroups = 8;      // weight row groups per prefill task (one per wave)
 constexpr int kXcds = 8;            // accelerator complex dies (each with its own L2)
+#ifndef BFP4_SPREAD_STEPS
+#define BFP4_SPREAD_STEPS 4
+#endif
+constexpr int kSpreadSteps = BFP4_SPREAD_STEPS;   // 16-K steps of a stage its token loads span
 
 // Logical row (within a 32-row group) held at physical row rho: the MFMA 32x32 accumulator of
 // lane l holds rows 8i + 4*(l/32) + j (i, j in 0..3); they are made logical rows
@@ -443,10 +447,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   static_assert(RW >= 2 && RW <= 8, "weight ring of 2 to 8 stages");
   static_assert(NB >= 2, "at least two token stage buffers");
   constexpr int SBUF = NFW * 32 * kTokPitch;      // bytes of one stage buffer
-  // vector memory operations a wave issues per stage: NFW token loads, then 3 weight loads
+  // vector memory operations a wave issues per stage: 3 weight loads, then NFW token loads
   constexpr int VM_STAGE = NFW + 3;
   // loads issued after the prologue's token load of stage 1: NB - 3 token stages, RW - 1 weight
-  // stages, then stage 0's NFW + 3 (the fewest behind any prologue-loaded stage)
+  // stages, then stage 0's NFW + 3 (the fewest behind any prologue-loaded stage).  The prologue
+  // issues its token stages before its weight stages.
   constexpr int kEarlyWait = NB >= 3 ? (NB - 3) * NFW + 3 * (RW - 1) + VM_STAGE : 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -494,21 +499,31 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   h8_t T[NFW];
   h8_t Wc;
 
-  auto load_w = [&](uint4 (&Wd)[kStageChunks], uint32_t& Sd, int st) {
+  // weights of stage st: the scale dword (load_s) and 64-value chunk c (load_w1)
+  auto load_s = [&](int st) {
     const int sc = st / (kSuperChunks / kStageChunks);
     const int c0 = (st * kStageChunks) % kSuperChunks;
-    const int so = sc * kSuperBytes;
-    Sd = buffer_load_u32(wrs, wlane, so + 2 * c0);
-#pragma unroll
-    for (int c = 0; c < kStageChunks; ++c)
-      Wd[c] = buffer_load_u128(wrs, wlane + (1 + c) * kUnit, so + c0 * kUnit);
+    return buffer_load_u32(wrs, wlane, sc * kSuperBytes + 2 * c0);
   };
-  // token rows of stage st into stage buffer b
-  auto load_t = [&](int b, int st) {
-    uint8_t* dst = tok_wave + b * SBUF;
+  auto load_w1 = [&](int st, int c) {
+    const int sc = st / (kSuperChunks / kStageChunks);
+    const int c0 = (st * kStageChunks) % kSuperChunks;
+    return buffer_load_u128(wrs, wlane + (1 + c) * kUnit, sc * kSuperBytes + c0 * kUnit);
+  };
+  auto load_w = [&](uint4 (&Wd)[kStageChunks], uint32_t& Sd, int st) {
+    Sd = load_s(st);
 #pragma unroll
-    for (int i = 0; i < NFW; ++i)
-      buffer_load_lds16(trs, dst + i * 32 * kTokPitch, t_voff[i], (uint32_t)st * kTokPitch);
+    for (int c = 0; c < kStageChunks; ++c) Wd[c] = load_w1(st, c);
+  };
+  // token rows of fragment i (load_t1) or of every fragment (load_t) of stage st into stage
+  // buffer b
+  auto load_t1 = [&](int b, int st, int i) {
+    buffer_load_lds16(trs, tok_wave + b * SBUF + i * 32 * kTokPitch, t_voff[i],
+                      (uint32_t)st * kTokPitch);
+  };
+  auto load_t = [&](int b, int st) {
+#pragma unroll
+    for (int i = 0; i < NFW; ++i) load_t1(b, st, i);
   };
   auto dec_w = [&](const uint4 (&Wd)[kStageChunks], uint32_t Sd, int q) {
     const int c = q >> 2, s = q & 3;
@@ -546,34 +561,39 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
     constexpr int R = decltype(RR)::value;
     const uint8_t* buf = sm.tok + (st % NB) * SBUF;
     const uint8_t* nbuf = sm.tok + ((st + 1) % NB) * SBUF;
-    load_t((st + NB - 1) % NB, min(st + NB - 1, nst - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(W[(R + RW - 1) % RW], S[(R + RW - 1) % RW], min(st + RW - 1, nst - 1));
-    __builtin_amdgcn_sched_barrier(0);
+    const int tb = (st + NB - 1) % NB, ts = min(st + NB - 1, nst - 1);
+    const int wslot = (R + RW - 1) % RW, ws = min(st + RW - 1, nst - 1);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
+      const h8_t Wn = (q < 7) ? dec_w(W[R], S[R], q + 1) : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
 #pragma unroll
       for (int j = 0; j < NFW; ++j) {
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc, T[j], acc[j], 0, 0, 0);
         if (q < 7)
           T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q + 1));
-      }
-      Wc = (q < 7) ? dec_w(W[R], S[R], q + 1) : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
-      // order within the step: each MFMA followed by the LDS read that refills its token
-      // register, the weight decode spread in between
+        // The stage's vector memory operations go out in a fixed order: its three weight loads
+        // after the first MFMA, then the token rows one at a time between the MFMAs of the
+        // first half of the stage: a wave stalled issuing a burst of them behind other waves'
+        // requests would have no MFMA in flight.  Only VALU and SALU work crosses these points.
+        const int m = q * NFW + j;
+        if (m == 0) {
+          S[wslot] = load_s(ws);
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-        if (q < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);      // VALU
+          for (int c = 0; c < kStageChunks; ++c) W[wslot][c] = load_w1(ws, c);
+        }
+#pragma unroll
+        for (int i = 0; i < NFW; ++i)
+          if (m == 1 + (i * (kSpreadSteps * NFW - 1)) / NFW) load_t1(tb, ts, i);
+        if (m == 0) __builtin_amdgcn_sched_barrier(0);
+        else __builtin_amdgcn_sched_barrier(0x006);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      Wc = Wn;
     }
     // stage st + 1's rows have landed once at most the loads issued after them are
-    // outstanding.  In the steady state they were loaded NB - 1 stages ago, followed by that
-    // stage's 3 weight loads and NB - 2 full stages; while st + 1 <= NB - 2 they came from the
-    // prologue, followed by fewer loads (the smallest count is at st = 0).
-    if (st + 1 > NB - 2) wait_vmcnt<3 + (NB - 2) * VM_STAGE>();
+    // outstanding.  In the steady state they were the last loads of the stage NB - 1 stages
+    // ago, followed by NB - 2 full stages; while st + 1 <= NB - 2 they came from the prologue,
+    // followed by fewer loads (the smallest count is at st = 0).
+    if (st + 1 > NB - 2) wait_vmcnt<(NB - 2) * VM_STAGE>();
     else wait_vmcnt<kEarlyWait>();
     lds_barrier();
     read_all(nbuf, 0);
