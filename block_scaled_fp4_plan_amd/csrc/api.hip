@@ -251,6 +251,11 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   // the tiled (block_m > 32) GEMMs address their FP16 token operands with 32-bit offsets
   if (block_m > 32 && (M * H * 2 >= (1LL << 31) || (int64_t)capacity * I * 2 >= (1LL << 31)))
     return BFP4_ERR_SHAPE;
+  // ... and an expert's weight panels with 32-bit offsets
+  if (block_m > 32 &&
+      (panel_matrix_bytes(1, act == BFP4_ACT_SWIGLU ? 2 * I : I, H) >= (1LL << 31) ||
+       panel_matrix_bytes(1, H, I) >= (1LL << 31)))
+    return BFP4_ERR_SHAPE;
   size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
   if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
     return BFP4_ERR_CAPACITY;

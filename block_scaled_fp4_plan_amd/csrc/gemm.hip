@@ -54,6 +54,15 @@ constexpr int kXcds = 8;            // accelerator complex dies (each with its o
 #define BFP4_SPREAD_STEPS 4
 #endif
 constexpr int kSpreadSteps = BFP4_SPREAD_STEPS;   // 16-K steps of a stage its token loads span
+#ifndef BFP4_CHAIN1
+#define BFP4_CHAIN1 1
+#endif
+#ifndef BFP4_CHAIN2
+#define BFP4_CHAIN2 4
+#endif
+constexpr int kChainGemm1 = BFP4_CHAIN1;          // prefill n-tiles per task, gate/up GEMM
+static_assert(kChainGemm1 == 1, "the gate/up GEMM kernel runs one n-tile per task");
+constexpr int kChainGemm2 = BFP4_CHAIN2;          // prefill n-tiles per task, down GEMM
 
 // Logical row (within a 32-row group) held at physical row rho: the MFMA 32x32 accumulator of
 // lane l holds rows 8i + 4*(l/32) + j (i, j in 0..3); they are made logical rows
@@ -148,6 +157,7 @@ struct GemmArgs {
   const uint8_t* panel;
   int64_t expert_bytes, rg_bytes;
   int nch, N, n_nt;
+  int chain, n_ct;           // prefill: n-tiles per task and tasks per tile (ceil(n_nt / chain))
   const float* alpha_a;      // GEMM1: alpha1_gate; GEMM2: alpha2
   const float* alpha_b;      // GEMM1: alpha1_up
   // GEMM1 epilogue
@@ -318,11 +328,20 @@ __device__ __forceinline__ float silu(float x) {
 //   SwiGLU:  h = 0 holds gate, h = 1 up of intermediate 16g + v; lane h = 0 keeps 16g + 0..7 and
 //            lane h = 1 keeps 16g + 8..15 after swapping halves with its partner (lane ^ 32);
 //            the requantization block is the pair's 16 values.
+// al is the lane's per-expert output scale (lane_alpha), read before the main loop so that its
+// load latency is hidden.
 template <int EPI>
-__device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t& acc, int e,
+__device__ __forceinline__ float lane_alpha(const GemmArgs& a, int e, int h) {
+  if (EPI == EPI_DOWN) return a.alpha_a[e];
+  if (EPI == EPI_RELU2) return a.alpha_b[e];
+  return h ? a.alpha_b[e] : a.alpha_a[e];
+}
+
+template <int EPI>
+__device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t& acc, float al,
                                                int64_t g, int h, float s_row, int64_t r) {
   if (EPI == EPI_DOWN) {
-    const float a2 = a.alpha_a[e];
+    const float a2 = al;
     const int64_t k0 = g * kGroupRows + 16 * h;
     uint32_t pk[8];
 #pragma unroll
@@ -337,7 +356,7 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     return;
   }
   if (EPI == EPI_RELU2) {
-    const float au = a.alpha_b[e];
+    const float au = al;
     const int64_t i0 = g * kGroupRows + 16 * h;
     float pr[16], hv[16];
     uint32_t bb[16];
@@ -374,7 +393,6 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
   }
   // SwiGLU
   const int64_t i0 = g * 16;
-  const float al = h ? a.alpha_b[e] : a.alpha_a[e];
   float pre[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) pre[v] = (acc[v] * s_row) * al;
@@ -440,8 +458,8 @@ template <int NFW> struct TileDepth {
 // Per 16-K step a wave issues its NFW MFMAs, each followed by the LDS read that refills the same
 // token register for the next step, and decodes its weight fragment of the next step.
 template <int NFW, int EPI>
-__device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int e, int nt,
-                                         int64_t row0) {
+__device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int e, int nt0,
+                                         int nchain, int64_t row0) {
   static_assert(NFW >= 1 && NFW <= 8, "at most 8 token fragments per tile");
   constexpr int RW = TileDepth<NFW>::RW, NB = TileDepth<NFW>::NB;
   static_assert(RW >= 2 && RW <= 8, "weight ring of 2 to 8 stages");
@@ -458,14 +476,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   const int h = lane >> 5, col = lane & 31;
   const int nst = a.nch / kStageChunks;
 
-  const int64_t g = (int64_t)nt * kTileGroups + wave;
-  const bool wave_on = (g + 1) * kGroupRows <= a.N;
-  // a wave past the last row group streams group 0 (every load and MFMA is unconditional) and
-  // skips the epilogue.  Weight loads go through a buffer resource over the wave's row group:
-  // lane offset in a VGPR, stage offsets in SGPRs.
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(
-      a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g : 0) * a.rg_bytes, (uint32_t)a.rg_bytes);
+  // Weight loads go through a buffer resource over the expert's panel: lane offset in a VGPR,
+  // row-group and stage offsets in SGPRs.  A wave past the last row group of its n-tile streams
+  // group 0 (every load and MFMA is unconditional) and skips that n-tile's epilogue.
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(a.panel + (int64_t)e * a.expert_bytes, (uint32_t)a.expert_bytes);
   const int wlane = lane * 16;
+  auto group_of = [&](int nt) { return nt * kTileGroups + wave; };
+  auto group_on = [&](int nt) { return (group_of(nt) + 1) * kGroupRows <= a.N; };
 
   // token rows: this lane moves row 32 i + 4 wave + lane / 16 of fragment i, physical slot
   // lane % 16, i.e. logical slot u_l; rows without a routed slot read row 0 (their MFMA columns
@@ -490,6 +508,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
     return col * kTokPitch + ((u ^ swz) << 4);
   };
 
+  const float al = lane_alpha<EPI>(a, e, h);
   f32x16_t acc[NFW];
 #pragma unroll
   for (int j = 0; j < NFW; ++j) acc[j] = f32x16_t{};
@@ -499,21 +518,17 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   h8_t T[NFW];
   h8_t Wc;
 
-  // weights of stage st: the scale dword (load_s) and 64-value chunk c (load_w1)
-  auto load_s = [&](int st) {
+  // weights of local stage st of row-group offset go (bytes): the scale dword (load_s) and
+  // 64-value chunk c (load_w1)
+  auto load_s = [&](int go, int st) {
     const int sc = st / (kSuperChunks / kStageChunks);
     const int c0 = (st * kStageChunks) % kSuperChunks;
-    return buffer_load_u32(wrs, wlane, sc * kSuperBytes + 2 * c0);
+    return buffer_load_u32(wrs, wlane, go + sc * kSuperBytes + 2 * c0);
   };
-  auto load_w1 = [&](int st, int c) {
+  auto load_w1 = [&](int go, int st, int c) {
     const int sc = st / (kSuperChunks / kStageChunks);
     const int c0 = (st * kStageChunks) % kSuperChunks;
-    return buffer_load_u128(wrs, wlane + (1 + c) * kUnit, sc * kSuperBytes + c0 * kUnit);
-  };
-  auto load_w = [&](uint4 (&Wd)[kStageChunks], uint32_t& Sd, int st) {
-    Sd = load_s(st);
-#pragma unroll
-    for (int c = 0; c < kStageChunks; ++c) Wd[c] = load_w1(st, c);
+    return buffer_load_u128(wrs, wlane + (1 + c) * kUnit, go + sc * kSuperBytes + c0 * kUnit);
   };
   // token rows of fragment i (load_t1) or of every fragment (load_t) of stage st into stage
   // buffer b
@@ -537,112 +552,150 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
       T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q));
   };
 
-  // ---- prologue: token stages 0 .. NB-2 into buffers 0 .. NB-2, weights of 0 .. RW-2 ----
-  // Every load is unconditional (stage indices clamped; the loads past the end re-read the last
-  // stage into buffers nobody reads again), and token loads and weight loads are issued in a
-  // fixed order, so the explicit waits below count exactly.
+  // n-tiles nt0 .. nt0 + nchain - 1 of the tile run as one stream of nchain * nst stages when
+  // the weight ring divides nst (then every n-tile starts in weight slot 0); otherwise one
+  // stream per n-tile.  Inside a stream the loads of the next n-tile's first stages are in flight
+  // while the previous n-tile's epilogue runs.  Only the down GEMM streams several n-tiles: the
+  // larger gate/up epilogues inside the stage loop would push its registers past the file.
+  constexpr bool kStream = EPI == EPI_DOWN;
+  const int cc = (kStream && nst % RW == 0) ? nchain : 1;
+  for (int c0 = 0; c0 < nchain; c0 += cc) {
+    const int ntb = nt0 + c0, cnt = kStream ? min(cc, nchain - c0) : 1;
+    const int NS = cnt * nst;                 // stages of this stream
+    // weight row-group byte offset of the n-tile of global stage gs, and its local stage
+    auto wgo = [&](int gs) {
+      const int nt = kStream ? ntb + gs / nst : ntb;
+      return (group_on(nt) ? group_of(nt) : 0) * (int)a.rg_bytes;
+    };
+    auto local = [&](int gs) { return kStream ? gs % nst : gs; };
+    auto load_w = [&](uint4 (&Wd)[kStageChunks], uint32_t& Sd, int gs) {
+      const int go = wgo(gs), ls = local(gs);
+      Sd = load_s(go, ls);
 #pragma unroll
-  for (int b = 0; b < NB - 1; ++b) load_t(b, min(b, nst - 1));
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int r = 0; r < RW - 1; ++r) load_w(W[r], S[r], min(r, nst - 1));
-  __builtin_amdgcn_sched_barrier(0);
-  // stage 0's rows have landed once at most the later loads are outstanding
-  wait_vmcnt<(NB - 2) * NFW + 3 * (RW - 1)>();
-  lds_barrier();
-  read_all(sm.tok, 0);
-  Wc = dec_w(W[0], S[0], 0);
+      for (int c = 0; c < kStageChunks; ++c) Wd[c] = load_w1(go, ls, c);
+    };
 
-  // One stage st; R = st % RW gives the weight slot as a compile-time index; the LDS stage
-  // buffer is st % NB.  Stage st refills buffer (st - 1) % NB (read by stage st - 1, released by
-  // the barrier that ended it) with stage st + NB - 1, and the weight slot freed by stage st - 1
-  // with stage st + RW - 1.  Stages run in groups of RW with the remainder after the loop.
-  auto stage = [&](auto RR, int st) {
-    constexpr int R = decltype(RR)::value;
-    const uint8_t* buf = sm.tok + (st % NB) * SBUF;
-    const uint8_t* nbuf = sm.tok + ((st + 1) % NB) * SBUF;
-    const int tb = (st + NB - 1) % NB, ts = min(st + NB - 1, nst - 1);
-    const int wslot = (R + RW - 1) % RW, ws = min(st + RW - 1, nst - 1);
+    // ---- prologue: token stages 0 .. NB-2 into buffers 0 .. NB-2, weights of 0 .. RW-2 ----
+    // Every load is unconditional (stage indices clamped; the loads past the end re-read the
+    // last stage into buffers nobody reads again), and token loads and weight loads are issued
+    // in a fixed order, so the explicit waits below count exactly.
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const h8_t Wn = (q < 7) ? dec_w(W[R], S[R], q + 1) : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
+    for (int b = 0; b < NB - 1; ++b) load_t(b, local(min(b, NS - 1)));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) {
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc, T[j], acc[j], 0, 0, 0);
-        if (q < 7)
-          T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q + 1));
-        // The stage's vector memory operations go out in a fixed order: its three weight loads
-        // after the first MFMA, then the token rows one at a time between the MFMAs of the
-        // first half of the stage: a wave stalled issuing a burst of them behind other waves'
-        // requests would have no MFMA in flight.  Only VALU and SALU work crosses these points.
-        const int m = q * NFW + j;
-        if (m == 0) {
-          S[wslot] = load_s(ws);
-#pragma unroll
-          for (int c = 0; c < kStageChunks; ++c) W[wslot][c] = load_w1(ws, c);
-        }
-#pragma unroll
-        for (int i = 0; i < NFW; ++i)
-          if (m == 1 + (i * (kSpreadSteps * NFW - 1)) / NFW) load_t1(tb, ts, i);
-        if (m == 0) __builtin_amdgcn_sched_barrier(0);
-        else __builtin_amdgcn_sched_barrier(0x006);
-      }
-      Wc = Wn;
-    }
-    // stage st + 1's rows have landed once at most the loads issued after them are
-    // outstanding.  In the steady state they were the last loads of the stage NB - 1 stages
-    // ago, followed by NB - 2 full stages; while st + 1 <= NB - 2 they came from the prologue,
-    // followed by fewer loads (the smallest count is at st = 0).
-    if (st + 1 > NB - 2) wait_vmcnt<(NB - 2) * VM_STAGE>();
-    else wait_vmcnt<kEarlyWait>();
+    for (int r = 0; r < RW - 1; ++r) load_w(W[r], S[r], min(r, NS - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 0's rows have landed once at most the later loads are outstanding
+    wait_vmcnt<(NB - 2) * NFW + 3 * (RW - 1)>();
     lds_barrier();
-    read_all(nbuf, 0);
-  };
-  int st = 0;
-  for (; st + RW - 1 < nst; st += RW)
-    unroll_seq([&](auto RR) { stage(RR, st + decltype(RR)::value); },
-               std::make_integer_sequence<int, RW>{});
-  const int rem = nst - st;
-  unroll_seq([&](auto RR) { if (decltype(RR)::value < rem) stage(RR, st + decltype(RR)::value); },
-             std::make_integer_sequence<int, RW - 1>{});
-  // The explicit waits count three weight loads in every stage, also in the last stages whose
-  // weight registers are never read again; this use keeps the compiler from deleting those loads.
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-    asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, W[r][0])),
-                 "v"(__builtin_bit_cast(u32x4_t, W[r][1])), "v"(S[r]));
-  // the clamped token loads of the last stages must land before LDS is reused
-  wait_vmcnt<0>();
+    read_all(sm.tok, 0);
+    Wc = dec_w(W[0], S[0], 0);
 
-  // ---- epilogue ----
-  if (!wave_on) return;
+    // One stage st of the stream; R = st % RW gives the weight slot as a compile-time index;
+    // the LDS stage buffer is st % NB.  Stage st refills buffer (st - 1) % NB (read by stage
+    // st - 1, released by the barrier that ended it) with stage st + NB - 1, and the weight slot
+    // freed by stage st - 1 with stage st + RW - 1.  Stages run in groups of RW.
+    auto stage = [&](auto RR, int st) {
+      constexpr int R = decltype(RR)::value;
+      const uint8_t* buf = sm.tok + (st % NB) * SBUF;
+      const uint8_t* nbuf = sm.tok + ((st + 1) % NB) * SBUF;
+      const int tb = (st + NB - 1) % NB, ts = local(min(st + NB - 1, NS - 1));
+      const int wslot = (R + RW - 1) % RW, wgs = min(st + RW - 1, NS - 1);
+      const int wgo_s = wgo(wgs), ws = local(wgs);
 #pragma unroll
-  for (int j = 0; j < NFW; ++j) {
-    const int m = j * 32 + col;
-    if (sm.row_src[m] < 0) continue;
-    epilogue_group<EPI>(a, acc[j], e, g, h, sm.row_scale[m], row0 + m);
+      for (int q = 0; q < 8; ++q) {
+        const h8_t Wn = (q < 7) ? dec_w(W[R], S[R], q + 1)
+                                : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc, T[j], acc[j], 0, 0, 0);
+          if (q < 7)
+            T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q + 1));
+          // The stage's vector memory operations go out in a fixed order: its three weight
+          // loads after the first MFMA, then the token rows one at a time between the MFMAs of
+          // the first half of the stage: a wave stalled issuing a burst of them behind other
+          // waves' requests would have no MFMA in flight.  Only VALU and SALU work crosses these
+          // points.
+          const int m = q * NFW + j;
+          if (m == 0) {
+            S[wslot] = load_s(wgo_s, ws);
+#pragma unroll
+            for (int c = 0; c < kStageChunks; ++c) W[wslot][c] = load_w1(wgo_s, ws, c);
+          }
+#pragma unroll
+          for (int i = 0; i < NFW; ++i)
+            if (m == 1 + (i * (kSpreadSteps * NFW - 1)) / NFW) load_t1(tb, ts, i);
+          if (m == 0) __builtin_amdgcn_sched_barrier(0);
+          else __builtin_amdgcn_sched_barrier(0x006);
+        }
+        Wc = Wn;
+      }
+      // stage st + 1's rows have landed once at most the loads issued after them are
+      // outstanding.  In the steady state they were the last loads of the stage NB - 1 stages
+      // ago, followed by NB - 2 full stages (and possibly an epilogue's stores, which only make
+      // the wait stricter); while st + 1 <= NB - 2 they came from the prologue, followed by
+      // fewer loads (the smallest count is at st = 0).
+      if (st + 1 > NB - 2) wait_vmcnt<(NB - 2) * VM_STAGE>();
+      else wait_vmcnt<kEarlyWait>();
+      lds_barrier();
+      read_all(nbuf, 0);
+    };
+    for (int c = 0; c < cnt; ++c) {
+      const int s0 = c * nst;
+      int ls = 0;
+      for (; ls + RW - 1 < nst; ls += RW)
+        unroll_seq([&](auto RR) { stage(RR, s0 + ls + decltype(RR)::value); },
+                   std::make_integer_sequence<int, RW>{});
+      const int rem = nst - ls;                // only when the stream is a single n-tile
+      unroll_seq([&](auto RR) {
+        if (decltype(RR)::value < rem) stage(RR, s0 + ls + decltype(RR)::value);
+      }, std::make_integer_sequence<int, RW - 1>{});
+      if (c == cnt - 1) {
+        // The explicit waits count three weight loads in every stage, also in the last stages
+        // whose weight registers are never read again; this use keeps the compiler from
+        // deleting those loads.
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+          asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, W[r][0])),
+                       "v"(__builtin_bit_cast(u32x4_t, W[r][1])), "v"(S[r]));
+        // the clamped token loads of the last stages must land before LDS is reused
+        wait_vmcnt<0>();
+      }
+      // ---- epilogue of n-tile ntb + c ----
+      const int nt = ntb + c;
+      if (group_on(nt)) {
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) {
+          const int m = j * 32 + col;
+          if (sm.row_src[m] < 0) continue;
+          epilogue_group<EPI>(a, acc[j], al, group_of(nt), h, sm.row_scale[m], row0 + m);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NFW; ++j) acc[j] = f32x16_t{};
+    }
   }
 }
 
 template <int EPI>
 __device__ __forceinline__ void run_nfw(const GemmArgs& a, const Smem& sm, int e, int nt,
-                                        int64_t row0, int nfw) {
+                                        int nchain, int64_t row0, int nfw) {
   switch (nfw) {
-    case 1: run_tile<1, EPI>(a, sm, e, nt, row0); break;
-    case 2: run_tile<2, EPI>(a, sm, e, nt, row0); break;
-    case 3: run_tile<3, EPI>(a, sm, e, nt, row0); break;
-    case 4: run_tile<4, EPI>(a, sm, e, nt, row0); break;
-    case 5: run_tile<5, EPI>(a, sm, e, nt, row0); break;
-    case 6: run_tile<6, EPI>(a, sm, e, nt, row0); break;
-    case 7: run_tile<7, EPI>(a, sm, e, nt, row0); break;
-    default: run_tile<8, EPI>(a, sm, e, nt, row0); break;
+    case 1: run_tile<1, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 2: run_tile<2, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 3: run_tile<3, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 4: run_tile<4, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 5: run_tile<5, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 6: run_tile<6, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 7: run_tile<7, EPI>(a, sm, e, nt, nchain, row0); break;
+    default: run_tile<8, EPI>(a, sm, e, nt, nchain, row0); break;
   }
 }
 
 // Prefill-sized plan blocks.  Persistent grid of one 8-wave workgroup per CU with a dynamic
-// schedule: a task is (tile, n-tile of kTileGroups weight row groups), task k = tile k / n_nt
-// of the tile list, n-tile k % n_nt; a workgroup takes its next task from a global counter
-// while it works on the current one.
+// schedule: a task is (tile, chain of up to `chain` consecutive n-tiles of kTileGroups weight
+// row groups), task k = tile k / n_ct of the tile list, n-tiles from (k % n_ct) * chain; a
+// workgroup takes its next task from a global counter while it works on the current one.
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -660,15 +713,15 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   // take tasks from queue x, so a tile's n-tile tasks share one L2, and move on to the next
   // queues when theirs is empty.  Thread 0 keeps the current queue in q.
   auto q_tasks = [&](int qq) -> int64_t {
-    return n_tiles > qq ? (int64_t)((n_tiles - qq + kXcds - 1) / kXcds) * a.n_nt : 0;
+    return n_tiles > qq ? (int64_t)((n_tiles - qq + kXcds - 1) / kXcds) * a.n_ct : 0;
   };
-  // resolve a ticket of queue q into a task (tile * n_nt + n-tile), moving on while queues are
+  // resolve a ticket of queue q into a task (tile * n_ct + chain), moving on while queues are
   // exhausted; -1 when every queue is
   auto resolve = [&](int& qq, uint32_t ticket) -> int {
     for (int tries = 0; tries < kXcds; ++tries) {
       if ((int64_t)ticket < q_tasks(qq)) {
-        const int tile = qq + kXcds * (int)(ticket / a.n_nt);
-        return tile * a.n_nt + (int)(ticket % a.n_nt);
+        const int tile = qq + kXcds * (int)(ticket / a.n_ct);
+        return tile * a.n_ct + (int)(ticket % a.n_ct);
       }
       if (tries == kXcds - 1) break;
       qq = (qq + 1) % kXcds;
@@ -683,8 +736,9 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   while (k >= 0) {
     uint32_t ticket = 0;
     if (tid == 0) ticket = atomicAdd(a.task_counter + q, 1u);   // in flight during this task
-    const int2 t = a.tiles[k / a.n_nt];
-    const int nt = (int)(k % a.n_nt);
+    const int2 t = a.tiles[k / a.n_ct];
+    const int nt = (int)(k % a.n_ct) * a.chain;
+    const int nchain = EPI == EPI_DOWN ? min(a.chain, a.n_nt - nt) : 1;
     const int64_t row0 = t.x;
     const int rows_here = min(kTileRows, t.y);
     const int e = a.eids[row0 / a.block_m];
@@ -714,7 +768,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
     __syncthreads();
     const int nvalid = *sm.sh_nvalid;
     // the tile list holds local experts and tiles with a routed row only
-    if (nvalid > 0 && e >= 0 && e < a.nloc) run_nfw<EPI>(a, sm, e, nt, row0, (nvalid + 31) >> 5);
+    if (nvalid > 0 && e >= 0 && e < a.nloc) run_nfw<EPI>(a, sm, e, nt, nchain, row0, (nvalid + 31) >> 5);
     __syncthreads();                         // every thread has read sh_task
     if (tid == 0) *sm.sh_task = resolve(q, ticket);
     __syncthreads();
@@ -791,6 +845,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
     // lanes past the staged rows read row 0; their MFMA columns are discarded
     const uint8_t* trow = tok + (col < rows_max ? col : 0) * pitch;
 
+    const float al = lane_alpha<EPI>(a, e, h);
     f32x16_t acc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x16_t{};
@@ -849,7 +904,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
     if (wave_on && col < rows_max && row_src[col] >= 0) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
-        epilogue_group<EPI>(a, acc[fn], e, g0 + fn, h, row_scale[col], b * a.block_m + col);
+        epilogue_group<EPI>(a, acc[fn], al, g0 + fn, h, row_scale[col], b * a.block_m + col);
     }
   }
 }
@@ -889,7 +944,7 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t max_tiles, const char* name, h
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  const int64_t total = max_tiles * a.n_nt;
+  const int64_t total = max_tiles * a.n_ct;
   const int64_t maxwg = 256;                         // one workgroup per CU
   int64_t grid = total < maxwg ? total : maxwg;
   grid = (grid + 7) / 8 * 8;
@@ -971,6 +1026,8 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.nch = (int)pg1.nch;
   g1.N = (int)N1;
   g1.n_nt = (int)((N1 + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g1.chain = kChainGemm1;
+  g1.n_ct = (g1.n_nt + g1.chain - 1) / g1.chain;
   g1.alpha_a = p.alpha1_gate;
   g1.alpha_b = p.alpha1_up;
   g1.c2 = p.c2;
@@ -1002,6 +1059,8 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g2.nch = (int)pg2.nch;
   g2.N = (int)p.H;
   g2.n_nt = (int)((p.H + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g2.chain = kChainGemm2;
+  g2.n_ct = (g2.n_nt + g2.chain - 1) / g2.chain;
   g2.alpha_a = p.alpha2;
   g2.alpha_b = nullptr;
   g2.y = p.y;

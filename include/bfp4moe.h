@@ -176,8 +176,9 @@ int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_
  * Requirements: H % 256 == 0 and H >= 256 [Alpha, notes]; I % 128 == 0 [cuDNN, sizes bullet];
  *   block_m >= 8, % 8 == 0 [Alpha, block_m]; pointers 16-byte aligned.  With block_m > 32 (the
  *   tiled prefill kernels, which read exact FP16 copies of their token operands through 32-bit
- *   buffer offsets) also M*H*2 < 2^31 and capacity*I*2 < 2^31 bytes, else BFP4_ERR_SHAPE
- *   (split such a batch into several calls).
+ *   buffer offsets) also M*H*2 < 2^31 and capacity*I*2 < 2^31 bytes, and one expert's panel
+ *   of each matrix (bfp4_panel_bytes(1, ...) splits into the two) below 2^31 bytes, else
+ *   BFP4_ERR_SHAPE (split such a batch into several calls).
  * Device preconditions: the plan's expert ids are < num_local_experts; token ids < M.
  * ---------------------------------------------------------------------------------------------- */
 typedef struct {

@@ -213,16 +213,18 @@ TINY_RELU2 = Workload("tiny_relu2", M=40, H=512, I=256, E=8, top_k=3, block_m=12
 # K = 1280 and 640: 10 and 5 stages of 128, not a multiple of any prefill prefetch depth (2 to 8
 # stages), with skewed expert loads giving tiles of 1 to 8 token fragments
 RAGGED_K = Workload("ragged_k", M=384, H=1280, I=640, E=6, top_k=3, block_m=128, routing="zipf")
+# down GEMM with 4 n-tiles of 4 stages: each tile's n-tiles run as one stage stream
+CHAIN_N = Workload("chain_n", M=320, H=1024, I=512, E=5, top_k=2, block_m=128, routing="zipf")
 
 MOE_CASES = [
     ("tiny", 8), ("tiny", 128), ("decode_ll", 8), ("skewed_small", 16), ("tiny_relu2", 128),
-    ("tiny", 32), ("tiny", 136), ("ragged_k", 128),
+    ("tiny", 32), ("tiny", 136), ("ragged_k", 128), ("chain_n", 128),
 ]
 
 
 def _workload(name):
-    return ({"skewed_small": SMALL_SKEWED, "tiny_relu2": TINY_RELU2, "ragged_k": RAGGED_K}.get(name)
-            or WORKLOADS[name])
+    return ({"skewed_small": SMALL_SKEWED, "tiny_relu2": TINY_RELU2, "ragged_k": RAGGED_K,
+             "chain_n": CHAIN_N}.get(name) or WORKLOADS[name])
 
 
 def run_gpu_moe(p, block_m, do_finalize=True, debug=True, rsf=1.0):
