@@ -54,10 +54,24 @@ __device__ void scatter_wave(const int32_t* __restrict__ ids, int64_t f0, int64_
   const int lane = threadIdx.x & 63;
   const int nbits = key_bits(nloc);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // the ids of kIdBatch rounds of 64 slots are loaded together (independent loads in flight)
+  constexpr int kIdBatch = 16;
+  int32_t idv[kIdBatch];
   for (int64_t base = f0; base < f1; base += 64) {
+    const int rb = (int)(((base - f0) >> 6) % kIdBatch);
+    if (rb == 0) {
+#pragma unroll
+      for (int i = 0; i < kIdBatch; ++i) {
+        const int64_t fi = base + 64 * i + lane;
+        idv[i] = fi < f1 ? ids[fi] : -1;
+      }
+    }
+    int32_t id = idv[0];
+#pragma unroll
+    for (int i = 1; i < kIdBatch; ++i) id = rb == i ? idv[i] : id;
     int64_t f = base + lane;
     if (f < f1) {
-      int e = local_id(ids[f], num_experts, offset, nloc);
+      int e = local_id(id, num_experts, offset, nloc);
       uint32_t key = (e < 0) ? (uint32_t)nloc : (uint32_t)e;
       uint64_t peers = match_any(key, nbits);
       if (e >= 0) {
@@ -73,21 +87,29 @@ __device__ void scatter_wave(const int32_t* __restrict__ ids, int64_t f0, int64_
   }
 }
 
-// Exclusive scan of one int per thread over a 1024-thread block; returns the total.
+// Exclusive scan of one int per thread over a 1024-thread block (16 waves); returns the
+// total.  Each wave scans its 64 values with lane shuffles; one barrier publishes the wave
+// totals.
 __device__ int block_excl_scan_1024(int v, int* tmp, int& total) {
-  int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int add = (tid >= off) ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  int incl = tmp[tid];
-  total = tmp[1023];
+  if (lane == 63) tmp[w] = x;
   __syncthreads();
-  return incl - v;
+  int pre = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = tmp[i];
+    pre += i < w ? t : 0;
+    all += t;
+  }
+  total = all;
+  __syncthreads();                       // tmp may be reused by the caller
+  return pre + x - v;
 }
 
 // Writes num_tokens_post_padded, expert_ids and the sentinel entries, given each expert's
@@ -158,20 +180,34 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ h
                                                          int32_t* __restrict__ ntpp, int64_t cap) {
   __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
   int tid = threadIdx.x;
+  // the chunk histograms are read kBatch at a time (independent loads in flight together)
+  constexpr int kBatch = 16;
   int c = 0;
-  if (tid < nloc)
-    for (int64_t g = 0; g < nchunks; ++g) c += hist[g * nloc + tid];
-  if (tid < nloc) cnt[tid] = c;
+  if (tid < nloc) {
+    for (int64_t g0 = 0; g0 < nchunks; g0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = g0 + i < nchunks ? hist[(g0 + i) * nloc + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) c += v[i];
+    }
+    cnt[tid] = c;
+  }
   int seg = (tid < nloc) ? (c + block_m - 1) / block_m * block_m : 0;
   int P;
   int excl = block_excl_scan_1024(seg, tmp, P);
   if (tid < nloc) {
     start[tid] = excl;
     int pos = excl;
-    for (int64_t g = 0; g < nchunks; ++g) {
-      int v = hist[g * nloc + tid];
-      hist[g * nloc + tid] = pos;
-      pos += v;
+    for (int64_t g0 = 0; g0 < nchunks; g0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = g0 + i < nchunks ? hist[(g0 + i) * nloc + tid] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (g0 + i < nchunks) hist[(g0 + i) * nloc + tid] = pos;
+        pos += v[i];
+      }
     }
   }
   __syncthreads();

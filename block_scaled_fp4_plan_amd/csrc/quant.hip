@@ -76,9 +76,24 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
   const uint16_t* xr = x + r * stride;
   int64_t nblk = cols >> 4;
   float s_enc;
+  // the first kCached blocks of this thread stay in registers between the amax and the
+  // quantization pass (all of them for rows up to kCached * 4096 values)
+  constexpr int kCached = 2;
+  static_assert(kCached == 2, "the quantization pass below selects between two cached blocks");
+  float vc[kCached][16];
   if (MODE == 0) {
     float m = 0.0f;
-    for (int64_t b = threadIdx.x; b < nblk; b += kQuantThreads) {
+#pragma unroll
+    for (int i = 0; i < kCached; ++i) {
+      const int64_t b = threadIdx.x + (int64_t)i * kQuantThreads;
+      if (b < nblk) {
+        load_block16(xr + b * 16, vc[i]);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(vc[i][k]));
+      }
+    }
+    for (int64_t b = threadIdx.x + (int64_t)kCached * kQuantThreads; b < nblk;
+         b += kQuantThreads) {
       float v[16];
       load_block16(xr + b * 16, v);
 #pragma unroll
@@ -96,9 +111,14 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
   }
   uint8_t* qr = q + r * (cols >> 1);
   uint8_t* sr = sf + r * nblk;
-  for (int64_t b = threadIdx.x; b < nblk; b += kQuantThreads) {
+  for (int64_t b = threadIdx.x, i = 0; b < nblk; b += kQuantThreads, ++i) {
     float v[16];
-    load_block16(xr + b * 16, v);
+    if (MODE == 0 && i < kCached) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = i == 0 ? vc[0][k] : vc[kCached - 1][k];
+    } else {
+      load_block16(xr + b * 16, v);
+    }
     uint32_t lo, hi;
     uint32_t s = quant_block16(v, s_enc, lo, hi);
     *reinterpret_cast<uint2*>(qr + b * 8) = make_uint2(lo, hi);
