@@ -337,9 +337,17 @@ __device__ __forceinline__ float lane_alpha(const GemmArgs& a, int e, int h) {
   return h ? a.alpha_b[e] : a.alpha_a[e];
 }
 
-template <int EPI>
+// O32: the intermediate's element offsets (r * I) fit in 32 bits (the tiled kernels' operands are
+// checked to be below 2^31 bytes), so they are formed with 32-bit products.
+template <int EPI, bool O32 = false>
 __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t& acc, float al,
                                                int64_t g, int h, float s_row, int64_t r) {
+  // r * I / 16 (I is a multiple of 128); with O32, r < 2^23 (r * I * 2 < 2^31, I >= 128), so a
+  // 24-bit product
+  const int64_t r16 = O32 ? (int64_t)__umul24((uint32_t)r, (uint32_t)(a.I >> 4)) : r * (a.I >> 4);
+  auto roff = [&](int64_t stride) -> int64_t {   // stride is I / 2, I / 16 or I
+    return stride == (a.I >> 1) ? r16 << 3 : stride == (a.I >> 4) ? r16 : r16 << 4;
+  };
   if (EPI == EPI_DOWN) {
     const float a2 = al;
     const int64_t k0 = g * kGroupRows + 16 * h;
@@ -382,10 +390,10 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     }
     uint32_t lo, hi;
     const uint32_t sfb = quant_block16(hv, a.c2, lo, hi);
-    *reinterpret_cast<uint2*>(a.hq + r * (a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
-    a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+    *reinterpret_cast<uint2*>(a.hq + roff(a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
+    a.hsf[roff(a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
     if (a.h16) {                 // the same values, E2M1 x E4M3 exactly in FP16
-      h8_t* d = reinterpret_cast<h8_t*>(a.h16 + r * a.I + i0);
+      h8_t* d = reinterpret_cast<h8_t*>(a.h16 + roff(a.I) + i0);
       d[0] = decode8(lo, e4m3_scale_h2(sfb));
       d[1] = decode8(hi, e4m3_scale_h2(sfb));
     }
@@ -407,10 +415,13 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
   float bmax = 0.0f;
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
-    const float send = h ? pre[v] : pre[8 + v];
-    const float recv = __shfl_xor(send, 32, 64);
-    const float gt = h ? recv : pre[v];
-    const float up = h ? pre[8 + v] : recv;
+    // one lane swap gives every lane its gate and up value: lanes 0..31 keep pre[v] (gate of
+    // 16g + v) and take their partner's pre[v] (up of 16g + v); lanes 32..63 take their
+    // partner's pre[8 + v] (gate of 16g + 8 + v) and keep pre[8 + v] (up)
+    const auto gu = __builtin_amdgcn_permlane32_swap(__float_as_uint(pre[v]),
+                                                     __float_as_uint(pre[8 + v]), false, false);
+    const float gt = __uint_as_float(gu[0]);
+    const float up = __uint_as_float(gu[1]);
     bb[v] = f32_to_bf16(silu(gt) * up);
     hv[v] = bf16_to_f32(bb[v]);
     bmax = __builtin_fmaxf(bmax, __builtin_fabsf(hv[v]));
@@ -421,14 +432,18 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
         make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
                    bb[6] | (bb[7] << 16));
   }
-  bmax = __builtin_fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  {
+    const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax),
+                                                     false, false);
+    bmax = __builtin_fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));   // this lane, partner
+  }
   float inv;
   const uint32_t sfb = block_scale(bmax, a.c2, inv);
   const uint32_t codes = quant8(hv, inv);
-  *reinterpret_cast<uint32_t*>(a.hq + r * (a.I >> 1) + (ih >> 1)) = codes;
-  if (h == 0) a.hsf[r * (a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+  *reinterpret_cast<uint32_t*>(a.hq + roff(a.I >> 1) + (ih >> 1)) = codes;
+  if (h == 0) a.hsf[roff(a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
   if (a.h16)                     // the same values, E2M1 x E4M3 exactly in FP16
-    *reinterpret_cast<h8_t*>(a.h16 + r * a.I + ih) = decode8(codes, e4m3_scale_h2(sfb));
+    *reinterpret_cast<h8_t*>(a.h16 + roff(a.I) + ih) = decode8(codes, e4m3_scale_h2(sfb));
 }
 
 // f(integral_constant<int, I>) for I = 0, 1, ... in order
@@ -668,7 +683,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
         for (int j = 0; j < NFW; ++j) {
           const int m = j * 32 + col;
           if (sm.row_src[m] < 0) continue;
-          epilogue_group<EPI>(a, acc[j], al, group_of(nt), h, sm.row_scale[m], row0 + m);
+          epilogue_group<EPI, true>(a, acc[j], al, group_of(nt), h, sm.row_scale[m], row0 + m);
         }
       }
 #pragma unroll
