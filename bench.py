@@ -14,6 +14,7 @@ Prints one JSON line.
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -60,11 +61,15 @@ def calibrate_copy(copies=4):
 
 
 def kernel_source_digest():
-    """Digest of the sources that define the GEMM kernels (device helpers and gemm.hip)."""
+    """Digest of the code (comments and whitespace removed) of the sources that define the GEMM
+    kernels: device helpers and gemm.hip."""
     h = hashlib.sha256()
     for f in ("device.h", "gemm.hip"):
-        with open(os.path.join(ROOT, "block_scaled_fp4_plan_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_scaled_fp4_plan_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

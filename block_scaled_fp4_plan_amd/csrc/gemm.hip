@@ -15,9 +15,10 @@
 // * MFMA A operand = 32 weight rows, B operand = 32 plan rows (tokens).  Weights stream from HBM
 //   straight into registers (no LDS), one 16-byte load per lane per 64 K values.
 // * Prefill: a workgroup of 8 waves (two per SIMD) owns a tile of up to 256 plan rows of one
-//   expert and 8 weight row groups; the tile's tokens are decoded once per 128-K stage into LDS
-//   as FP16 and shared by the 8 waves; each wave decodes its own row group once per tile and
-//   multiplies it by every token fragment of the tile.
+//   expert and 8 weight row groups (one n-tile; the down GEMM streams up to 4 n-tiles of a tile
+//   through one pipeline); the tile's token rows are copied per 128-K stage from an exact FP16
+//   copy into LDS by direct buffer-to-LDS loads and shared by the 8 waves; each wave decodes its
+//   own row group once per tile and multiplies it by every token fragment of the tile.
 // * Decode: the few routed rows of a plan block are staged packed in LDS once; each wave then
 //   streams its weight row groups without further barriers.
 // * Weight panels put, for each 32-row group and each 64-value K chunk, exactly the 1 KiB a wave
@@ -28,7 +29,8 @@
 //   intermediate indices in its first 16 logical rows and the up rows of the same indices in
 //   the last 16, so the SwiGLU epilogue pairs lane l with lane l + 32.
 // * Plan rows past the device-side extent, padding rows and 32-row token fragments with no valid
-//   row are skipped; a static schedule interleaves M tiles over the 8 XCDs.
+//   row are skipped.  Prefill tasks are handed out dynamically from one ticket queue per XCD;
+//   the decode grid covers (plan block, row groups) tasks with a static stride.
 #include <type_traits>
 #include <utility>
 
@@ -50,19 +52,10 @@ constexpr int kTokRegion = 128 * 1024;   // LDS bytes of prefill token stage buf
 constexpr int kTileRows = 256;      // plan rows per prefill tile (8 token fragments)
 constexpr int kTileGroups = 8;      // weight row groups per prefill task (one per wave)
 constexpr int kXcds = 8;            // accelerator complex dies (each with its own L2)
-#ifndef BFP4_SPREAD_STEPS
-#define BFP4_SPREAD_STEPS 4
-#endif
-constexpr int kSpreadSteps = BFP4_SPREAD_STEPS;   // 16-K steps of a stage its token loads span
-#ifndef BFP4_CHAIN1
-#define BFP4_CHAIN1 1
-#endif
-#ifndef BFP4_CHAIN2
-#define BFP4_CHAIN2 4
-#endif
-constexpr int kChainGemm1 = BFP4_CHAIN1;          // prefill n-tiles per task, gate/up GEMM
+constexpr int kSpreadSteps = 4;     // 16-K steps of a stage over which its token loads go out
+constexpr int kChainGemm1 = 1;      // prefill n-tiles per task, gate/up GEMM
 static_assert(kChainGemm1 == 1, "the gate/up GEMM kernel runs one n-tile per task");
-constexpr int kChainGemm2 = BFP4_CHAIN2;          // prefill n-tiles per task, down GEMM
+constexpr int kChainGemm2 = 4;      // prefill n-tiles per task, down GEMM
 
 // Logical row (within a 32-row group) held at physical row rho: the MFMA 32x32 accumulator of
 // lane l holds rows 8i + 4*(l/32) + j (i, j in 0..3); they are made logical rows
