@@ -919,7 +919,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
 
 template <int FN, int EPI>
 hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, hipStream_t s) {
-  constexpr int RING = 3;
+  constexpr int RING = 2;
   auto kern = moe_gemv_kernel<FN, EPI, RING>;
   const int rows_max = a.block_m < 32 ? a.block_m : 32;
   const size_t lds = 64 * sizeof(int) +
