@@ -449,8 +449,10 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is.
 // stage st + RW - 1 are loaded into registers and the FP16 token rows of stage st + NB - 1 into
 // LDS while stage st computes.  A stage of token rows takes NFW * 8 KiB of the 128 KiB region,
 // so short tiles (short stages) look further ahead.
-template <int NFW> struct TileDepth {
-  static constexpr int RW = NFW <= 4 ? 4 : 2;
+template <int NFW, int EPI> struct TileDepth {
+  // 3 stages for short gate/up tiles measured faster than 4; the down GEMM keeps 4, which
+  // divides its 16 stages per n-tile so that n-tiles stream through one pipeline
+  static constexpr int RW = NFW <= 4 ? (EPI == EPI_DOWN ? 4 : 3) : 2;
   static constexpr int NB0 = kTokRegion / (NFW * 32 * kTokPitch);
   static constexpr int NB = NB0 > 8 ? 8 : NB0;
 };
@@ -469,7 +471,7 @@ template <int NFW, int EPI>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int e, int nt0,
                                          int nchain, int64_t row0) {
   static_assert(NFW >= 1 && NFW <= 8, "at most 8 token fragments per tile");
-  constexpr int RW = TileDepth<NFW>::RW, NB = TileDepth<NFW>::NB;
+  constexpr int RW = TileDepth<NFW, EPI>::RW, NB = TileDepth<NFW, EPI>::NB;
   static_assert(RW >= 2 && RW <= 8, "weight ring of 2 to 8 stages");
   static_assert(NB >= 2, "at least two token stage buffers");
   constexpr int SBUF = NFW * 32 * kTokPitch;      // bytes of one stage buffer
