@@ -119,13 +119,17 @@ __device__ void write_plan_frame(const int* cnt, const int* start, int nloc, int
                                  int32_t* __restrict__ eids, int32_t* __restrict__ ntpp) {
   int tid = threadIdx.x;
   if (tid == 0) *ntpp = P;
-  if (tid < nloc) {
-    int c = cnt[tid];
+  // blockDim / nloc threads per expert (at least one: nloc <= kMaxLocal = blockDim) write its
+  // block ids and padding sentinels
+  const int per = (int)blockDim.x / nloc;
+  if (tid < per * nloc) {
+    const int e = tid % nloc, part = tid / nloc;
+    int c = cnt[e];
     if (c > 0) {
       int seg = (c + block_m - 1) / block_m * block_m;
-      int s0 = start[tid];
-      for (int b = s0 / block_m; b < (s0 + seg) / block_m; ++b) eids[b] = tid;
-      for (int p = s0 + c; p < s0 + seg; ++p) sorted[p] = sentinel;
+      int s0 = start[e];
+      for (int b = s0 / block_m + part; b < (s0 + seg) / block_m; b += per) eids[b] = e;
+      for (int p = s0 + c + part; p < s0 + seg; p += per) sorted[p] = sentinel;
     }
   }
   for (int64_t b = P / block_m + tid; b < cap / block_m; b += blockDim.x) eids[b] = -1;
@@ -220,7 +224,18 @@ __global__ __launch_bounds__(64) void plan_scatter_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ sorted,
                                                           int32_t* __restrict__ ttr) {
   __shared__ int run[kMaxLocal];
-  for (int e = threadIdx.x; e < nloc; e += 64) run[e] = pos0[(int64_t)blockIdx.x * nloc + e];
+  // the chunk's starting positions, 4 loads in flight per lane
+  for (int e0 = threadIdx.x; e0 < nloc; e0 += 4 * 64) {
+    int v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 64 * i;
+      v[i] = e < nloc ? pos0[(int64_t)blockIdx.x * nloc + e] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e0 + 64 * i < nloc) run[e0 + 64 * i] = v[i];
+  }
   __syncthreads();
   int64_t f0 = (int64_t)blockIdx.x * kChunk;
   int64_t f1 = f0 + kChunk < A ? f0 + kChunk : A;
