@@ -48,7 +48,7 @@ __device__ __forceinline__ int key_bits(int nloc) {
 
 // One wave ranks slots [f0, f1) in order and scatters them.  run[e] holds, for each local
 // expert, the plan position of its next slot; it is advanced by the highest lane of each group.
-__device__ void scatter_wave(const int32_t* __restrict__ ids, int64_t f0, int64_t f1,
+__device__ void scatter_wave(const int32_t* ids, int64_t f0, int64_t f1,
                              int num_experts, int offset, int nloc, int* run,
                              int32_t* __restrict__ sorted, int32_t* __restrict__ ttr) {
   const int lane = threadIdx.x & 63;
@@ -141,11 +141,14 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
     int block_m, int32_t* __restrict__ sorted, int32_t* __restrict__ eids,
     int32_t* __restrict__ ntpp, int32_t* __restrict__ ttr, int64_t cap) {
   __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
+  __shared__ int32_t sid[kSmallMax];          // the ids, read from memory once
   int tid = threadIdx.x;
   if (tid < nloc) cnt[tid] = 0;
   __syncthreads();
   for (int64_t f = tid; f < A; f += 1024) {
-    int e = local_id(ids[f], num_experts, offset, nloc);
+    const int32_t id = ids[f];
+    sid[f] = id;
+    int e = local_id(id, num_experts, offset, nloc);
     if (e >= 0) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   __syncthreads();
   write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
   __syncthreads();
-  if (tid < 64) scatter_wave(ids, 0, A, num_experts, offset, nloc, start, sorted, ttr);
+  if (tid < 64) scatter_wave(sid, 0, A, num_experts, offset, nloc, start, sorted, ttr);
 }
 
 __global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restrict__ ids, int64_t A,
