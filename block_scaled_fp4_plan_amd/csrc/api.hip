@@ -64,11 +64,15 @@ KernelTimer::KernelTimer(const char* name, hipStream_t stream) : slot_(-1), stre
   if (g_timer.used >= (int)g_timer.start.size()) return;
   slot_ = g_timer.used++;
   g_timer.name[slot_] = name;
-  hipEventRecord(g_timer.start[slot_], stream_);
+  if (hipEventRecord(g_timer.start[slot_], stream_) != hipSuccess) {
+    g_timer.name[slot_] = nullptr;                   // slot left out of the report
+    slot_ = -1;
+  }
 }
 
 KernelTimer::~KernelTimer() {
-  if (slot_ >= 0) hipEventRecord(g_timer.stop[slot_], stream_);
+  if (slot_ >= 0 && hipEventRecord(g_timer.stop[slot_], stream_) != hipSuccess)
+    g_timer.name[slot_] = nullptr;
 }
 
 }  // namespace bfp4
@@ -372,8 +376,8 @@ int bfp4_profile_begin(int capacity, const char* name_prefix) {
   int dc = device_check();
   if (dc) return dc;
   TimerState& t = g_timer;
-  for (auto ev : t.start) hipEventDestroy(ev);
-  for (auto ev : t.stop) hipEventDestroy(ev);
+  for (auto ev : t.start) (void)hipEventDestroy(ev);   // a failed destroy only leaks the event
+  for (auto ev : t.stop) (void)hipEventDestroy(ev);
   t.start.assign(capacity, nullptr);
   t.stop.assign(capacity, nullptr);
   t.name.assign(capacity, nullptr);
@@ -396,9 +400,10 @@ int bfp4_profile_end(char* buf, size_t len) {
   std::vector<double> total;
   std::vector<int> count;
   for (int i = 0; i < t.used; ++i) {
+    if (t.name[i] == nullptr) continue;              // an event of this slot was not recorded
     if (hipEventSynchronize(t.stop[i]) != hipSuccess) return BFP4_ERR_LAUNCH;
     float ms = 0.0f;
-    hipEventElapsedTime(&ms, t.start[i], t.stop[i]);
+    if (hipEventElapsedTime(&ms, t.start[i], t.stop[i]) != hipSuccess) return BFP4_ERR_LAUNCH;
     size_t k = 0;
     while (k < names.size() && names[k] != t.name[i]) ++k;
     if (k == names.size()) {
