@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=2,
                     help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the achievable-peak context (read stream, vendor BF16 GEMM)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -161,6 +163,78 @@ def time_workload(wl, steps, warmup, replicas, timed_prefix="gemm1"):
     return s, dt, dt_ev, table, breakdown
 
 
+def time_graph(s, steps, warmup):
+    """The same step captured once per weight replica in a HIP graph (plan, activation
+    quantization, fused experts, finalize: the library allocates nothing and never synchronizes,
+    so the capture holds exactly the eager step's kernels), then `steps` replays timed."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for r in range(len(s.weights)):
+            s.step(r)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(len(s.weights)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.step(r)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    del graphs
+    return dt
+
+
+def achievable_context(reps=5):
+    """Achievable-peak context on this GPU: a plain read stream (torch's sum over 4 GiB of FP32),
+    a device copy, and a BF16 GEMM of the prefill's GEMM1 shape through torch.matmul (the vendor
+    BLAS)."""
+    import torch
+
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    x.sum()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        x.sum()
+    torch.cuda.synchronize()
+    read_gbs = x.numel() * 4 * reps / (time.perf_counter() - t0) / 1e9
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * x.numel() * 4 * reps / (time.perf_counter() - t0) / 1e9
+    del x, y
+    m, n, k = 4096, 4096, 7168
+    a = torch.randn(m, k, device="cuda").to(torch.bfloat16)
+    b = torch.randn(k, n, device="cuda").to(torch.bfloat16)
+    (a @ b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps * 4):
+        (a @ b)
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * m * n * k * reps * 4 / (time.perf_counter() - t0) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"read_stream_gbs": read_gbs, "read_stream": "torch sum over 4 GiB FP32",
+            "copy_gbs": copy_gbs, "copy": "torch copy of 4 GiB, bytes read + written",
+            "bf16_gemm_tflops": gemm_tf,
+            "bf16_gemm": "torch.matmul BF16 %dx%dx%d (vendor BLAS)" % (m, n, k)}
+
+
 def gemm_bytes(wl, touched, A, which):
     H, I, N1 = wl.H, wl.I, wl.N1
     if which == 1:   # W1 of routed experts + routed token rows + requantized intermediate
@@ -273,6 +347,9 @@ def main():
             roofline={"bound": "hbm", "kernel": g1_name, "achieved": ach, "peak": HBM_PEAK_GBS,
                       "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                       "bytes_per_launch": g1_bytes, "avg_launch_ms": g1_ms})
+        gdt = time_graph(s, args.steps, args.warmup)
+        result["config"]["graph_replay_ms_per_step"] = gdt / args.steps * 1e3
+        result["config"]["graph_replay_tokens_per_s"] = wl.M / (gdt / args.steps)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(s)
         del s
@@ -281,6 +358,7 @@ def main():
         wl = WORKLOADS["prefill"]
         s, dt, dt_ev, table, breakdown = time_workload(wl, args.steps, args.warmup, 1)
         ms = dt / args.steps * 1e3
+        gdt = time_graph(s, args.steps, args.warmup)
         g1_ms, _, g1_name = kernel_ms(table, "gemm1")
         g1_flops = 2.0 * s.A * wl.H * wl.N1
         ach = g1_flops / (g1_ms * 1e-3) / 1e12
@@ -292,6 +370,8 @@ def main():
                                 "NVFP4", "assignments": s.A,
                     "padded_rows": int(s.fwd.plan.num_tokens_post_padded.item()),
                     "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
+                    "graph_replay_ms_per_step": gdt / args.steps * 1e3,
+                    "graph_replay_tokens_per_s": wl.M / (gdt / args.steps),
                     "kernel_ms": {k: v[1] / v[0] for k, v in breakdown.items()}},
             roofline={"bound": "mfma", "kernel": g1_name, "achieved": ach,
                       "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -305,6 +385,8 @@ def main():
                           steps=args.steps, warmup=args.warmup, ms_per_step=ms,
                           higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
                           data="synthetic", config=pre["config"], roofline=pre["roofline"])
+    if not args.no_context:
+        result["context"] = achievable_context()
     print(json.dumps(result))
 
 
