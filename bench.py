@@ -243,6 +243,40 @@ def gemm_bytes(wl, touched, A, which):
     return touched * H * I * NVFP4_BYTES + A * I * NVFP4_BYTES + A * H * 2
 
 
+def kernel_rooflines(wl, s, breakdown):
+    """Every kernel of the step against its own roofline: the average duration from the breakdown
+    pass and the algorithmic bytes (HBM- and latency-bound kernels) or flops (the tiled GEMMs) of
+    one launch, as in the kernel table of the design notes."""
+    M, H, I, N1, k, A, q = wl.M, wl.H, wl.I, wl.N1, wl.top_k, s.A, NVFP4_BYTES
+    work = {
+        "plan": ("latency", M * k * 12),                  # id read, plan entry, token_to_row
+        "quantize_rows": ("hbm", M * H * 2 + M * H * q + M * 4),
+        "decode_tokens": ("hbm", M * H * (q + 2)),
+        "tile_list": ("latency", 0),
+        "gemm1_swiglu_decode": ("hbm", gemm_bytes(wl, s.touched, A, 1)),
+        "gemm2_down_decode": ("hbm", gemm_bytes(wl, s.touched, A, 2)),
+        "gemm1_swiglu_prefill": ("mfma", 2.0 * A * H * N1),
+        "gemm2_down_prefill": ("mfma", 2.0 * A * H * I),
+        "finalize": ("hbm", A * H * 2 + 2 * M * H * 2 + M * k * 8),
+    }
+    out = {}
+    for name, (cnt, tot) in breakdown.items():
+        ms = tot / cnt
+        key = "plan" if name.startswith("plan_") else name
+        ent = {"ms": ms}
+        if key in work:
+            bound, units = work[key]
+            ent["bound"] = bound
+            if bound == "mfma":
+                ach = units / (ms * 1e-3) / 1e12
+                ent.update(achieved=ach, unit="TFLOP/s", frac=ach / F16_MFMA_PEAK_TFLOPS)
+            elif units:
+                ach = units / (ms * 1e-3) / 1e9
+                ent.update(achieved=ach, unit="GB/s", frac=ach / HBM_PEAK_GBS)
+        out[name] = ent
+    return out
+
+
 def step_bytes(wl, touched):
     """Whole-step algorithmic HBM bytes: routed experts' weights, x, out read+write, ids+weights."""
     return (touched * (wl.N1 * wl.H + wl.H * wl.I) * NVFP4_BYTES + wl.M * wl.H * 2 +
@@ -343,7 +377,7 @@ def main():
                     "step_hbm_frac": step_bytes(wl, s.touched) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "weight_replicas": args.replicas,
                     "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
-                    "kernel_ms": {k: v[1] / v[0] for k, v in breakdown.items()}},
+                    "kernels": kernel_rooflines(wl, s, breakdown)},
             roofline={"bound": "hbm", "kernel": g1_name, "achieved": ach, "peak": HBM_PEAK_GBS,
                       "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                       "bytes_per_launch": g1_bytes, "avg_launch_ms": g1_ms})
@@ -372,7 +406,7 @@ def main():
                     "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
                     "graph_replay_ms_per_step": gdt / args.steps * 1e3,
                     "graph_replay_tokens_per_s": wl.M / (gdt / args.steps),
-                    "kernel_ms": {k: v[1] / v[0] for k, v in breakdown.items()}},
+                    "kernels": kernel_rooflines(wl, s, breakdown)},
             roofline={"bound": "mfma", "kernel": g1_name, "achieved": ach,
                       "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": ach / F16_MFMA_PEAK_TFLOPS,
