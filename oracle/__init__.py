@@ -7,7 +7,8 @@ The HIP library never uses it and shares no code, tables or helpers with it.
 What it computes follows these web pages (cited by page title and section):
 
 * FlashInfer, "flashinfer.fused_moe.CudnnGroupedGemmNvfp4Config": the pipeline order
-  (expert-sorted permutation, GEMM1, typed activation, GEMM2, finalize), 128-row segment
+  (expert-sorted permutation, GEMM1, typed activation, GEMM2, finalize), the activation list
+  (SwiGLU, GeGLU, GELU, ReLU, SiLU, Identity), 128-row segment
   padding, BF16 intermediate re-quantized to NVFP4 with a global scale of one, one global
   scale per expert, masking of non-local experts, the unfinalized output triple.
 * Megatron-Core, "core.inference.moe.flashinfer_nvfp4": per-token NVFP4 x NVFP4 SwiGLU and
@@ -46,8 +47,15 @@ from .formats import (  # noqa: F401
 )
 from .quant import SCALE_FIXED, SCALE_PER_GROUP, SCALE_PER_ROW, dequantize_nvfp4, quantize_nvfp4  # noqa: F401
 from .moe import (  # noqa: F401
+    ACT_GEGLU,
+    ACT_GELU,
+    ACT_IDENTITY,
+    ACT_RELU,
     ACT_RELU2,
+    ACT_SILU,
     ACT_SWIGLU,
+    ACTS,
+    is_gated,
     combine,
     dense_loop_moe,
     expert_rows_forward,

@@ -12,8 +12,21 @@ import numpy as np
 from .formats import bf16_bits_to_f32, round_to_bf16
 from .quant import SCALE_FIXED, SCALE_PER_GROUP, dequantize_int, quantize_nvfp4
 
+# Typed activations.  CudnnGroupedGemmNvfp4Config, activation bullet: SwiGLU with default
+# scalars, GeGLU, GELU, ReLU, SiLU and Identity; Megatron-Core flashinfer_nvfp4: squared ReLU.
+# The two GLU forms are gated (W1 rows [gate; up], N1 = 2 I); the others take one projection.
 ACT_SWIGLU = 0
 ACT_RELU2 = 1
+ACT_GEGLU = 2
+ACT_GELU = 3
+ACT_RELU = 4
+ACT_SILU = 5
+ACT_IDENTITY = 6
+ACTS = (ACT_SWIGLU, ACT_RELU2, ACT_GEGLU, ACT_GELU, ACT_RELU, ACT_SILU, ACT_IDENTITY)
+
+
+def is_gated(act):
+    return act in (ACT_SWIGLU, ACT_GEGLU)
 
 _TWO_M20 = 2.0 ** -20
 
@@ -123,20 +136,48 @@ def quantize_expert_rows(w_bf16_bits, rows):
     return q, sf, (np.float32(1) / s_enc).astype(np.float32)
 
 
+def _silu(x):
+    """silu(x) = x / (1 + e^-x) (x * logistic(x))."""
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def _gelu(x):
+    """GELU in its exact form x * Phi(x) = x / 2 * (1 + erf(x / sqrt(2))), Phi the standard
+    normal CDF.  Reading taken: the pages list GELU and GeGLU beside a separate tanh variant
+    (GeGLUTanh), so the plain names are the erf form."""
+    return 0.5 * x * (1.0 + _erf(x / np.sqrt(2.0)))
+
+
+def _erf(x):
+    from scipy.special import erf
+
+    return erf(x)
+
+
 def _activation(pre, I, act):
     """Typed activation on float64 pre-activations [rows, N1].
 
-    SwiGLU with default scalars (CudnnGroupedGemmNvfp4Config activation bullet): W1 rows are
-    [gate; up] (alphamoe page: "conventional [gate; up] row order"), h = silu(gate) * up with
-    silu(g) = g / (1 + exp(-g)).  Squared ReLU (Megatron-Core module): h = max(pre, 0)**2.
+    Gated forms split W1's rows as [gate; up] (alphamoe page: "conventional [gate; up] row
+    order"): SwiGLU with default scalars (CudnnGroupedGemmNvfp4Config activation bullet)
+    h = silu(gate) * up; GeGLU h = gelu(gate) * up.  One-projection forms: squared ReLU
+    (Megatron-Core module) h = max(pre, 0)**2; ReLU max(pre, 0); SiLU silu(pre); GELU gelu(pre);
+    Identity h = pre.
     """
     if act == ACT_SWIGLU:
-        g = pre[:, :I]
-        u = pre[:, I:2 * I]
-        with np.errstate(over="ignore"):
-            return g / (1.0 + np.exp(-g)) * u
+        return _silu(pre[:, :I]) * pre[:, I:2 * I]
+    if act == ACT_GEGLU:
+        return _gelu(pre[:, :I]) * pre[:, I:2 * I]
     if act == ACT_RELU2:
         return np.maximum(pre, 0.0) ** 2
+    if act == ACT_RELU:
+        return np.maximum(pre, 0.0)
+    if act == ACT_SILU:
+        return _silu(pre)
+    if act == ACT_GELU:
+        return _gelu(pre)
+    if act == ACT_IDENTITY:
+        return pre.copy()
     raise ValueError("unknown activation")
 
 
@@ -160,7 +201,7 @@ def expert_rows_forward(a_q, a_sf, a_dec, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate,
     R = a_q.shape[0]
     N1 = w1_q.shape[0]
     I = w2_q.shape[1] * 2
-    gated = (act == ACT_SWIGLU)
+    gated = is_gated(act)
     if N1 != (2 * I if gated else I):
         raise ValueError("W1 rows do not match the activation")
     s1 = dequantize_int(a_q, a_sf) @ dequantize_int(w1_q, w1_sf).T          # exact int64

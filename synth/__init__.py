@@ -7,6 +7,7 @@ their inputs from here.
 """
 
 from .workloads import (  # noqa: F401
+    ACT_NAMES,
     WORKLOADS,
     Workload,
     bf16_bits,

@@ -19,6 +19,10 @@ from dataclasses import dataclass, field
 import numpy as np
 
 
+# Activation names in the order of their codes in the C ABI and in the oracle.
+ACT_NAMES = ("swiglu", "relu2", "geglu", "gelu", "relu", "silu", "identity")
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -28,7 +32,7 @@ class Workload:
     E: int
     top_k: int
     block_m: int
-    act: str = "swiglu"              # "swiglu" (gated) or "relu2" (non-gated)
+    act: str = "swiglu"              # one of ACT_NAMES; "swiglu" and "geglu" are gated
     routing: str = "softmax"         # "softmax", "softmax_bias", "zipf"
     local_offset: int = 0
     num_local: int = -1              # -1: all experts are local
@@ -42,7 +46,11 @@ class Workload:
 
     @property
     def gated(self):
-        return self.act == "swiglu"
+        return self.act in ("swiglu", "geglu")
+
+    @property
+    def act_code(self):
+        return ACT_NAMES.index(self.act)
 
     @property
     def N1(self):

@@ -30,7 +30,7 @@ def _check(name, token, n_hidden=512):
     say("full-size", name, "token", token)
     p = Problem(wl)
     M, k, H, I, N1 = wl.M, wl.top_k, wl.H, wl.I, wl.N1
-    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    act = wl.act_code
     pw, lin = runner.prepare_weights(p.w1, p.w2, gated=wl.gated, keep_linear=True)
     fwd = runner.MoeForward(pw, M, k, wl.E, wl.block_m, wl.local_offset)
     cap = fwd.plan.capacity

@@ -268,7 +268,7 @@ def test_fused_moe_matches_oracle(name, bm):
         assert pw.alpha1_gate[e].item() == a1 and pw.alpha2[e].item() == a2
     # oracle forward with its own quantized weights
     a1, a2 = p.oracle_alphas(experts)
-    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    act = wl.act_code
     res = oracle.fused_moe_nvfp4(oq, osf, odec, lambda e: p.oracle_expert(e)[0], a1, a1, a2, 1.0,
                                  srt, eids, P, ttr, p.w, k, bm, act)
     rows = sorted(res["pre"].keys())

@@ -9,6 +9,7 @@ separate FP32 multiply/add combine, unrouted slots ignored with their scores),
 Megatron-Core "core.inference.moe.flashinfer_nvfp4" (-1 routing entries contribute zero).
 """
 
+import dataclasses
 import math
 import os
 from fractions import Fraction
@@ -144,12 +145,24 @@ def _exact_matrix(q, sf):
     return out
 
 
-@pytest.mark.parametrize("act", [oracle.ACT_SWIGLU, oracle.ACT_RELU2])
+def _act_ref(act, g, u=None):
+    """Textbook activations on one float (math module only): silu(x) = x / (1 + e^-x),
+    gelu(x) = x * Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2."""
+    silu = lambda x: x / (1 + math.exp(-x))                       # noqa: E731
+    gelu = lambda x: x * 0.5 * (1 + math.erf(x / math.sqrt(2)))    # noqa: E731
+    return {oracle.ACT_SWIGLU: lambda: silu(g) * u, oracle.ACT_GEGLU: lambda: gelu(g) * u,
+            oracle.ACT_RELU2: lambda: max(g, 0.0) ** 2, oracle.ACT_RELU: lambda: max(g, 0.0),
+            oracle.ACT_SILU: lambda: silu(g), oracle.ACT_GELU: lambda: gelu(g),
+            oracle.ACT_IDENTITY: lambda: g}[act]()
+
+
+@pytest.mark.parametrize("act", oracle.ACTS)
 def test_expert_projection_brute_force(act):
     """pre, h and y against exact rational arithmetic on a tiny expert (H=32, I=16)."""
     rng = np.random.default_rng(11 + act)
     R, H, I = 3, 32, 16
-    N1 = 2 * I if act == oracle.ACT_SWIGLU else I
+    gated = oracle.is_gated(act)
+    N1 = 2 * I if gated else I
     aq, asf = _rand_nvfp4(rng, R, H)
     w1q, w1sf = _rand_nvfp4(rng, N1, H)
     w2q, w2sf = _rand_nvfp4(rng, H, I)
@@ -162,18 +175,14 @@ def test_expert_projection_brute_force(act):
         pre = []
         for n in range(N1):
             s = sum(A[r][h] * W1[n][h] for h in range(H))
-            alpha = (ag if n < I else au) if act == oracle.ACT_SWIGLU else au
+            alpha = (ag if n < I else au) if gated else au
             pre.append(s * Fraction(float(adec[r])) * Fraction(float(alpha)))
         got = o["pre"][r]
         for n in range(N1):
             assert abs(got[n] - float(pre[n])) <= 4e-16 * abs(float(pre[n])) + 1e-300
         # activation from the exact pre-activation with math.exp: gate rows first, then up
         for i in range(I):
-            if act == oracle.ACT_SWIGLU:
-                g, u = float(pre[i]), float(pre[I + i])
-                h = g / (1 + math.exp(-g)) * u
-            else:
-                h = max(float(pre[i]), 0.0) ** 2
+            h = _act_ref(act, float(pre[i]), float(pre[I + i]) if gated else None)
             hb = o["h"][r, i]
             assert abs(hb - h) <= abs(h) * 2.0 ** -8 * 1.0001 + 1e-300
     # the intermediate is requantized with the fixed encode scale 1 (CudnnGroupedGemmNvfp4Config:
@@ -194,6 +203,31 @@ def test_expert_projection_brute_force(act):
             s = sum(HQ[r][i] * W2[hh][i] for i in range(I)) * Fraction(float(a2))
             ref = float(s)
             assert abs(o["y"][r, hh] - ref) <= abs(ref) * 2.0 ** -8 * 1.0001 + 1e-300
+
+
+def test_activation_closed_forms():
+    """Values of the typed activations fixed by their definitions: Phi(1) = 0.841344746068543,
+    Phi(2) = 0.977249868051821 (standard normal CDF); the odd parts gelu(x) - gelu(-x) = x and
+    silu(x) - silu(-x) = x; logistic(1) = 1 / (1 + 1/e); gated forms take the gate half first."""
+    act = oracle.moe._activation
+    x = np.array([[1.0, -1.0, 2.0, 0.0, 10.0]])
+    assert np.allclose(act(x, 5, oracle.ACT_GELU),
+                       [[0.8413447460685429, -0.15865525393145707, 1.9544997361036416, 0.0, 10.0]],
+                       rtol=1e-15, atol=0)
+    assert np.allclose(act(x, 5, oracle.ACT_SILU)[0, 0], 0.7310585786300049, rtol=1e-15)
+    v = np.linspace(-8, 8, 33).reshape(1, -1)
+    for a in (oracle.ACT_GELU, oracle.ACT_SILU):
+        assert np.allclose(act(v, 33, a) - act(-v, 33, a), v, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(act(v, 33, oracle.ACT_RELU), np.maximum(v, 0))
+    assert np.array_equal(act(v, 33, oracle.ACT_RELU2), np.maximum(v, 0) ** 2)
+    assert np.array_equal(act(v, 33, oracle.ACT_IDENTITY), v)
+    gu = np.array([[1.0, 3.0]])                  # I = 1: gate 1, up 3
+    assert np.isclose(act(gu, 1, oracle.ACT_SWIGLU)[0, 0], 3 * 0.7310585786300049, rtol=1e-15)
+    assert np.isclose(act(gu, 1, oracle.ACT_GEGLU)[0, 0], 3 * 0.8413447460685429, rtol=1e-15)
+    assert np.isclose(act(gu[:, ::-1], 1, oracle.ACT_GEGLU)[0, 0], 0.9986501019683699 * 3,
+                      rtol=1e-15)                # gelu(3) * 1 = 3 Phi(3)
+    with pytest.raises(ValueError):
+        act(v, 33, 7)
 
 
 def test_gemm1_exact_grid_case():
@@ -229,7 +263,7 @@ def _small_problem(wl, seed=0, M=None):
 def _run(wl, p, bm, out0=None, ids=None, w=None, rsf=1.0):
     ids = p["ids"] if ids is None else ids
     w = p["w"] if w is None else w
-    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    act = wl.act_code
     srt, eids, P, ttr = oracle.moe_plan(ids, wl.E, wl.local_offset, wl.n_local, bm)
     return oracle.fused_moe_nvfp4(p["aq"], p["asf"], p["adec"], p["W"], p["a1"], p["a1"], p["a2"],
                                   1.0, srt, eids, P, ttr, w, wl.top_k, bm, act, rsf, out0)
@@ -239,10 +273,18 @@ SHRUNK_SKEWED = Workload("skewed_small", M=48, H=128, I=64, E=24, top_k=4, block
                          act="relu2", routing="zipf", local_offset=4, num_local=12)
 
 
-@pytest.mark.parametrize("wl", [WORKLOADS["tiny"], SHRUNK_SKEWED], ids=["tiny", "skewed_small"])
+ACT_VARIANTS = [WORKLOADS["tiny"], SHRUNK_SKEWED,
+                dataclasses.replace(WORKLOADS["tiny"], name="tiny_geglu", act="geglu"),
+                dataclasses.replace(SHRUNK_SKEWED, name="skewed_gelu", act="gelu"),
+                dataclasses.replace(SHRUNK_SKEWED, name="skewed_silu", act="silu"),
+                dataclasses.replace(SHRUNK_SKEWED, name="skewed_relu", act="relu"),
+                dataclasses.replace(SHRUNK_SKEWED, name="skewed_identity", act="identity")]
+
+
+@pytest.mark.parametrize("wl", ACT_VARIANTS, ids=[w.name for w in ACT_VARIANTS])
 def test_dense_loop_equals_plan_path(wl):
     p = _small_problem(wl)
-    act = oracle.ACT_SWIGLU if wl.gated else oracle.ACT_RELU2
+    act = wl.act_code
     res = _run(wl, p, wl.block_m)
     dense = oracle.dense_loop_moe(p["aq"], p["asf"], p["adec"], p["W"], p["a1"], p["a1"], p["a2"],
                                   1.0, p["ids"], p["w"], wl.E, wl.local_offset, wl.n_local, act)
