@@ -24,6 +24,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 BFP4_ACT_SWIGLU = 0
 BFP4_ACT_RELU2 = 1
+BFP4_ACT_GEGLU = 2
+BFP4_ACT_GELU = 3
+BFP4_ACT_RELU = 4
+BFP4_ACT_SILU = 5
+BFP4_ACT_IDENTITY = 6
+GATED_ACTS = (BFP4_ACT_SWIGLU, BFP4_ACT_GEGLU)
 BFP4_SCALE_PER_ROW = 0
 BFP4_SCALE_PER_GROUP = 1
 BFP4_SCALE_FIXED = 2

@@ -246,7 +246,8 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          float routed_scaling_factor, int do_finalize, uint16_t* out,
                          uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (act != BFP4_ACT_SWIGLU && act != BFP4_ACT_RELU2) return BFP4_ERR_MODE;
+  if (act < BFP4_ACT_SWIGLU || act > BFP4_ACT_IDENTITY) return BFP4_ERR_MODE;
+  const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
   if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
   if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
   if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
@@ -257,7 +258,7 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
     return BFP4_ERR_SHAPE;
   // ... and an expert's weight panels with 32-bit offsets
   if (block_m > 32 &&
-      (panel_matrix_bytes(1, act == BFP4_ACT_SWIGLU ? 2 * I : I, H) >= (1LL << 31) ||
+      (panel_matrix_bytes(1, gated ? 2 * I : I, H) >= (1LL << 31) ||
        panel_matrix_bytes(1, H, I) >= (1LL << 31)))
     return BFP4_ERR_SHAPE;
   size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
@@ -274,7 +275,6 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
       !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) || !aligned(token_to_row, 4) ||
       !aligned(workspace, 256))
     return BFP4_ERR_ALIGN;
-  const int gated = act == BFP4_ACT_SWIGLU;
   if (panels_bytes < bfp4_panel_bytes(num_local_experts, H, I, gated)) return BFP4_ERR_WORKSPACE;
   size_t ws = bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize);
   if (workspace_bytes < ws || !workspace) return BFP4_ERR_WORKSPACE;

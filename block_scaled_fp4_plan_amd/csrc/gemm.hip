@@ -34,6 +34,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "bfp4moe.h"
 #include "device.h"
 #include "runtime.h"
 
@@ -154,6 +155,7 @@ struct GemmArgs {
   const float* alpha_a;      // GEMM1: alpha1_gate; GEMM2: alpha2
   const float* alpha_b;      // GEMM1: alpha1_up
   // GEMM1 epilogue
+  int act;                   // activation code (EPI_ACT picks GELU, ReLU, SiLU or Identity by it)
   float c2;
   int64_t I;
   uint8_t* hq;
@@ -166,7 +168,12 @@ struct GemmArgs {
   int64_t Hout;
 };
 
-enum { EPI_SWIGLU = 0, EPI_RELU2 = 1, EPI_DOWN = 2 };
+// Epilogues: the two GEMM1 forms the hot paths use (SwiGLU, squared ReLU), the down GEMM, GeGLU,
+// and the remaining one-projection activations (GELU, ReLU, SiLU, Identity) chosen at run time.
+enum { EPI_SWIGLU = 0, EPI_RELU2 = 1, EPI_DOWN = 2, EPI_GEGLU = 3, EPI_ACT = 4 };
+
+// GEMM1 epilogues whose intermediate value i comes from one pre-activation (no gate/up pairs)
+constexpr bool one_projection(int epi) { return epi == EPI_RELU2 || epi == EPI_ACT; }
 
 
 // Prefill tile list, built on the device from the plan by one workgroup before GEMM1:
@@ -314,6 +321,21 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// GELU in its erf form, x * Phi(x) with Phi(x) = erfc(-x / sqrt 2) / 2: the complementary error
+// function keeps Phi's relative accuracy for large negative x, where 1 + erf(x / sqrt 2) would
+// cancel.
+__device__ __forceinline__ float gelu(float x) {
+  return 0.5f * x * erfcf(x * -0.70710678118654752f);
+}
+
+// The one-projection activations other than squared ReLU, by activation code.
+__device__ __forceinline__ float act_one(float x, int act) {
+  if (act == BFP4_ACT_GELU) return gelu(x);
+  if (act == BFP4_ACT_RELU) return x > 0.0f ? x : 0.0f;
+  if (act == BFP4_ACT_SILU) return silu(x);
+  return x;                                        // Identity
+}
+
 // Epilogue of one weight row group g for the plan row r of this lane's token column; the lane
 // holds the group's logical rows 16h .. 16h + 15.
 //   down:    outputs 32g + 16h + v  ->  BF16, 32 contiguous bytes per lane
@@ -326,7 +348,7 @@ __device__ __forceinline__ float silu(float x) {
 template <int EPI>
 __device__ __forceinline__ float lane_alpha(const GemmArgs& a, int e, int h) {
   if (EPI == EPI_DOWN) return a.alpha_a[e];
-  if (EPI == EPI_RELU2) return a.alpha_b[e];
+  if (one_projection(EPI)) return a.alpha_b[e];
   return h ? a.alpha_b[e] : a.alpha_a[e];
 }
 
@@ -356,7 +378,7 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
     return;
   }
-  if (EPI == EPI_RELU2) {
+  if (one_projection(EPI)) {
     const float au = al;
     const int64_t i0 = g * kGroupRows + 16 * h;
     float pr[16], hv[16];
@@ -364,8 +386,12 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       pr[v] = (acc[v] * s_row) * au;
-      const float q = pr[v] > 0.0f ? pr[v] : 0.0f;
-      bb[v] = f32_to_bf16(q * q);
+      if (EPI == EPI_RELU2) {
+        const float q = pr[v] > 0.0f ? pr[v] : 0.0f;
+        bb[v] = f32_to_bf16(q * q);
+      } else {
+        bb[v] = f32_to_bf16(act_one(pr[v], a.act));
+      }
       hv[v] = bf16_to_f32(bb[v]);
     }
     if (a.dbg_pre) {
@@ -392,7 +418,7 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     }
     return;
   }
-  // SwiGLU
+  // SwiGLU, GeGLU
   const int64_t i0 = g * 16;
   float pre[16];
 #pragma unroll
@@ -415,7 +441,7 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
                                                      __float_as_uint(pre[8 + v]), false, false);
     const float gt = __uint_as_float(gu[0]);
     const float up = __uint_as_float(gu[1]);
-    bb[v] = f32_to_bf16(silu(gt) * up);
+    bb[v] = f32_to_bf16((EPI == EPI_GEGLU ? gelu(gt) : silu(gt)) * up);
     hv[v] = bf16_to_f32(bb[v]);
     bmax = __builtin_fmaxf(bmax, __builtin_fabsf(hv[v]));
   }
@@ -981,7 +1007,7 @@ hipError_t launch_prepare(const uint8_t* w_q, const uint8_t* w_sf, int num_exper
 }
 
 hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
-  const bool gated = (p.act == 0);
+  const bool gated = p.act == BFP4_ACT_SWIGLU || p.act == BFP4_ACT_GEGLU;
   const int64_t N1 = gated ? 2 * p.I : p.I;
   const int64_t cap_blocks = p.cap / p.block_m;
   // Decode: one plan block of <= 32 rows per task; prefill: tiles of up to kTileRows plan rows
@@ -1040,6 +1066,7 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.n_ct = (g1.n_nt + g1.chain - 1) / g1.chain;
   g1.alpha_a = p.alpha1_gate;
   g1.alpha_b = p.alpha1_up;
+  g1.act = p.act;
   g1.c2 = p.c2;
   g1.I = p.I;
   g1.hq = p.hq;
@@ -1080,16 +1107,28 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
 
   hipError_t err;
   if (small) {
-    err = gated ? launch_gemv<2, EPI_SWIGLU>(g1, cap_blocks, "gemm1_swiglu_decode", s)
-                : launch_gemv<2, EPI_RELU2>(g1, cap_blocks, "gemm1_relu2_decode", s);
+    static const char* const kName[] = {
+        "gemm1_swiglu_decode", "gemm1_relu2_decode", "gemm1_geglu_decode", "gemm1_gelu_decode",
+        "gemm1_relu_decode", "gemm1_silu_decode", "gemm1_identity_decode"};
+    const char* nm = kName[p.act];
+    err = p.act == BFP4_ACT_SWIGLU ? launch_gemv<2, EPI_SWIGLU>(g1, cap_blocks, nm, s)
+        : p.act == BFP4_ACT_RELU2  ? launch_gemv<2, EPI_RELU2>(g1, cap_blocks, nm, s)
+        : p.act == BFP4_ACT_GEGLU  ? launch_gemv<2, EPI_GEGLU>(g1, cap_blocks, nm, s)
+                              : launch_gemv<2, EPI_ACT>(g1, cap_blocks, nm, s);
     if (err != hipSuccess) return err;
     return launch_gemv<2, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s);
   }
   // the prefill kernels address their FP16 token operands with 32-bit buffer offsets
   if (p.M * p.H * 2 >= (int64_t(1) << 31) || p.cap * p.I * 2 >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
-  err = gated ? launch_gemm<EPI_SWIGLU>(g1, max_tiles, "gemm1_swiglu_prefill", s)
-              : launch_gemm<EPI_RELU2>(g1, max_tiles, "gemm1_relu2_prefill", s);
+  static const char* const kName[] = {
+      "gemm1_swiglu_prefill", "gemm1_relu2_prefill", "gemm1_geglu_prefill", "gemm1_gelu_prefill",
+      "gemm1_relu_prefill", "gemm1_silu_prefill", "gemm1_identity_prefill"};
+  const char* nm = kName[p.act];
+  err = p.act == BFP4_ACT_SWIGLU ? launch_gemm<EPI_SWIGLU>(g1, max_tiles, nm, s)
+      : p.act == BFP4_ACT_RELU2  ? launch_gemm<EPI_RELU2>(g1, max_tiles, nm, s)
+      : p.act == BFP4_ACT_GEGLU  ? launch_gemm<EPI_GEGLU>(g1, max_tiles, nm, s)
+                            : launch_gemm<EPI_ACT>(g1, max_tiles, nm, s);
   if (err != hipSuccess) return err;
   return launch_gemm<EPI_DOWN>(g2, max_tiles, "gemm2_down_prefill", s);
 }

@@ -10,6 +10,7 @@ import torch
 from . import (
     BFP4_ACT_RELU2,
     BFP4_ACT_SWIGLU,
+    GATED_ACTS,
     BFP4_SCALE_PER_GROUP,
     BFP4_SCALE_PER_ROW,
     bfp4_fused_moe_nvfp4,
@@ -101,7 +102,13 @@ class MoeForward:
     """One forward: plan, per-token activation quantization, fused experts (+ finalize)."""
 
     def __init__(self, weights: PreparedWeights, M, top_k, num_experts, block_m,
-                 local_expert_offset=0, do_finalize=True, device="cuda"):
+                 local_expert_offset=0, do_finalize=True, device="cuda", act=None):
+        """act: a BFP4_ACT_* code; by default SwiGLU for gated weights, squared ReLU otherwise."""
+        if act is None:
+            act = BFP4_ACT_SWIGLU if weights.gated else BFP4_ACT_RELU2
+        if (act in GATED_ACTS) != bool(weights.gated):
+            raise ValueError("activation %d does not match the weights' gating" % act)
+        self.act = act
         self.w = weights
         self.M, self.top_k, self.E, self.block_m = M, top_k, num_experts, block_m
         self.offset = local_expert_offset
@@ -128,7 +135,9 @@ class MoeForward:
                             self.a_sf, self.a_dec, None, 0, stream)
         if out is None and self.do_finalize:
             out = torch.zeros((M, H), dtype=torch.bfloat16, device=x_bf16.device)
-        act = BFP4_ACT_SWIGLU if w.gated else BFP4_ACT_RELU2
+        act = self.act
+        if (act in GATED_ACTS) != bool(w.gated):
+            raise ValueError("activation %d does not match the weights' gating" % act)
         pl = self.plan
         bfp4_fused_moe_nvfp4(self.a_q, self.a_sf, self.a_dec, w.panels, w.panels_bytes,
                              w.alpha1_gate, w.alpha1_up, w.alpha2, c2, pl.sorted_token_ids,

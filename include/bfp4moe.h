@@ -52,7 +52,19 @@ typedef enum {
   BFP4_ERR_LAUNCH = -12      /* a kernel launch failed */
 } bfp4_status;
 
-typedef enum { BFP4_ACT_SWIGLU = 0, BFP4_ACT_RELU2 = 1 } bfp4_act;
+/* Typed activations [cuDNN, activation bullet: SwiGLU with default scalars, GeGLU, GELU, ReLU,
+ * SiLU, Identity; Megatron-Core flashinfer_nvfp4: squared ReLU].  SWIGLU and GEGLU are gated:
+ * W1 holds [gate; up] (N1 = 2*I) and h = act(gate) * up; the others use one projection (N1 = I).
+ * silu(x) = x / (1 + e^-x); gelu(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), the erf form. */
+typedef enum {
+  BFP4_ACT_SWIGLU = 0,    /* silu(gate) * up */
+  BFP4_ACT_RELU2 = 1,     /* max(x, 0)^2 */
+  BFP4_ACT_GEGLU = 2,     /* gelu(gate) * up */
+  BFP4_ACT_GELU = 3,      /* gelu(x) */
+  BFP4_ACT_RELU = 4,      /* max(x, 0) */
+  BFP4_ACT_SILU = 5,      /* silu(x) */
+  BFP4_ACT_IDENTITY = 6   /* x */
+} bfp4_act;
 typedef enum { BFP4_SCALE_PER_ROW = 0, BFP4_SCALE_PER_GROUP = 1, BFP4_SCALE_FIXED = 2 } bfp4_scale_mode;
 
 /* Human-readable name of a status code (static storage). */
@@ -150,7 +162,8 @@ int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_
  * Per valid plan row r (entry f < M*top_k, token t = f / top_k, local expert e of r's block):
  *   pre[n] = (sum_h x[t,h] * W1_e[n,h]) * a_dec[t] * alpha1_{gate|up}[e]   (FP32 accumulate;
  *            gate rows n < I use alpha1_gate, up rows alpha1_up; non-gated uses alpha1_up)
- *   h[i]   = bf16(silu(pre[i]) * pre[I+i])  (SwiGLU)  or  bf16(max(pre[i],0)^2)  (ReLU^2)
+ *   h[i]   = bf16(act(pre[i]) * pre[I+i])  (gated: SwiGLU, GeGLU)  or  bf16(act(pre[i]))
+ *            (ReLU^2, GELU, ReLU, SiLU, Identity); act is the bfp4_act code
  *   hq     = NVFP4 of h with fixed encode scale c2 (the quantizer's FIXED mode)
  *   y[k]   = bf16((sum_i hq[i] * W2_e[k,i]) * (1/c2) * alpha2[e])
  * Finalize (do_finalize != 0): for every token t,
@@ -164,7 +177,8 @@ int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_
  *
  * Arguments (device pointers unless noted):
  *   a_q [M, H/2], a_sf [M, H/16], a_dec [M]: NVFP4 activations (bfp4_quantize_nvfp4 PER_ROW);
- *   panels: from bfp4_prepare_weights for (num_local_experts, H, I, gated);
+ *   panels: from bfp4_prepare_weights for (num_local_experts, H, I, gated), gated matching act
+ *   (panels_bytes below the size for act gives BFP4_ERR_WORKSPACE);
  *   alpha1_gate, alpha1_up, alpha2 [num_local_experts] FP32;  c2 (host) > 0, finite;
  *   sorted_token_ids, expert_ids, num_tokens_post_padded, token_to_row: a plan from
  *   bfp4_moe_plan for the same M, top_k, num_local_experts and block_m, with this capacity;

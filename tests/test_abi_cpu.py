@@ -142,7 +142,10 @@ def test_fused_validation():
     assert _fused(H=128) == "BFP4_ERR_SHAPE"                   # H >= 256 and % 256
     assert _fused(I=96) == "BFP4_ERR_SHAPE"                    # I % 128
     assert _fused(block_m=9) == "BFP4_ERR_BLOCK_M"
-    assert _fused(act=5) == "BFP4_ERR_MODE"
+    assert _fused(act=7) == "BFP4_ERR_MODE"
+    assert _fused(act=-1) == "BFP4_ERR_MODE"
+    # a gated activation (GeGLU) needs the larger, gated panels
+    assert _fused(act=2, panels_bytes=bf.bfp4_panel_bytes(8, 256, 128, 0)) == "BFP4_ERR_WORKSPACE"
     assert _fused(c2=0.0) == "BFP4_ERR_SCALAR"
     assert _fused(routed_scaling_factor=float("nan")) == "BFP4_ERR_SCALAR"
     assert _fused(capacity=80) == "BFP4_ERR_CAPACITY"
@@ -162,6 +165,9 @@ def test_fused_validation():
 @cpu_only
 def test_fused_valid_args_without_device():
     assert _fused() == "BFP4_ERR_DEVICE"
+    for act in range(7):                         # every activation code is accepted
+        nb = bf.bfp4_panel_bytes(8, 256, 128, int(act in bf.GATED_ACTS))
+        assert _fused(act=act, panels_bytes=nb) == "BFP4_ERR_DEVICE"
 
 
 def test_finalize_and_prepare_validation():

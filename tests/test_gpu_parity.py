@@ -6,6 +6,8 @@ requantization of the GPU's own BF16 intermediate and the combine of the GPU's o
 bit-exact; finalize(unfinalized) == finalized; two runs bit-identical.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -216,21 +218,37 @@ RAGGED_K = Workload("ragged_k", M=384, H=1280, I=640, E=6, top_k=3, block_m=128,
 # down GEMM with 4 n-tiles of 4 stages: each tile's n-tiles run as one stage stream
 CHAIN_N = Workload("chain_n", M=320, H=1024, I=512, E=5, top_k=2, block_m=128, routing="zipf")
 
+# the other activations, on the decode (block_m 8, 16) and the tiled (block_m 128) kernels
+ACT_WORKLOADS = {
+    "tiny_geglu": dataclasses.replace(WORKLOADS["tiny"], name="tiny_geglu", act="geglu"),
+    "ll_geglu": dataclasses.replace(WORKLOADS["decode_ll"], name="ll_geglu", act="geglu"),
+    "ragged_geglu": dataclasses.replace(RAGGED_K, name="ragged_geglu", act="geglu"),
+    "gelu": dataclasses.replace(TINY_RELU2, name="gelu", act="gelu"),
+    "relu": dataclasses.replace(TINY_RELU2, name="relu", act="relu"),
+    "silu": dataclasses.replace(TINY_RELU2, name="silu", act="silu"),
+    "identity": dataclasses.replace(TINY_RELU2, name="identity", act="identity"),
+    "skewed_gelu": dataclasses.replace(SMALL_SKEWED, name="skewed_gelu", act="gelu"),
+}
+
 MOE_CASES = [
     ("tiny", 8), ("tiny", 128), ("decode_ll", 8), ("skewed_small", 16), ("tiny_relu2", 128),
     ("tiny", 32), ("tiny", 136), ("ragged_k", 128), ("chain_n", 128),
+    ("tiny_geglu", 8), ("tiny_geglu", 128), ("ll_geglu", 8), ("ragged_geglu", 128),
+    ("gelu", 8), ("gelu", 128), ("relu", 16), ("relu", 128), ("silu", 8), ("silu", 128),
+    ("identity", 8), ("identity", 128), ("skewed_gelu", 16),
 ]
 
 
 def _workload(name):
     return ({"skewed_small": SMALL_SKEWED, "tiny_relu2": TINY_RELU2, "ragged_k": RAGGED_K,
-             "chain_n": CHAIN_N}.get(name) or WORKLOADS[name])
+             "chain_n": CHAIN_N, **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
 
 
 def run_gpu_moe(p, block_m, do_finalize=True, debug=True, rsf=1.0):
     wl = p.wl
     pw, lin = runner.prepare_weights(p.w1, p.w2, gated=wl.gated, keep_linear=True)
-    fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, block_m, wl.local_offset, do_finalize)
+    fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, block_m, wl.local_offset, do_finalize,
+                            act=wl.act_code)
     cap = fwd.plan.capacity
     dbg = None
     if debug:
@@ -293,9 +311,14 @@ def test_fused_moe_matches_oracle(name, bm):
     gap = rel_fro(out_ref, ref64)
     say("pre %.3e  h %.3e  out %.3e  oracle-vs-fp64 gap %.3f" % (e_pre, e_h, e_out, gap))
     assert e_pre <= 1e-5
+    # the activation itself: both sides round act(pre) to BF16 from pre-activations 1e-5 apart,
+    # so an element differs by at most one BF16 step (2^-8 relative) and rarely; 2e-3 would take
+    # a quarter of the elements a step apart, a wrong activation is ~1e-1 off
+    assert e_h <= 2e-3
     assert e_out <= 2e-2
     # unfinalized triple -> finalize == finalized, bit for bit; run-twice determinism
-    fwd2 = runner.MoeForward(pw, p.M, k, wl.E, bm, wl.local_offset, do_finalize=False)
+    fwd2 = runner.MoeForward(pw, p.M, k, wl.E, bm, wl.local_offset, do_finalize=False,
+                             act=wl.act_code)
     y, wts, ttr_d = fwd2(p.x, p.ids_d, p.w_d)
     out2 = torch.zeros_like(out)
     bf.bfp4_moe_finalize(y, wts, ttr_d, M, wl.H, k, 1.0, out2)
