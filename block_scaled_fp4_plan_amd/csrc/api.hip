@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 #include <vector>
 
@@ -34,18 +35,22 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// The current device is a gfx950; the answer is kept per device (0 unknown, 1 yes, 2 no), so a
+// call after the first makes no device query (none inside a stream capture either).
 int device_check() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return BFP4_ERR_DEVICE;
-  static int checked_dev = -1;
-  static int ok = 0;
-  if (checked_dev != dev) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> state[kMaxDevices];
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  int st = cached ? state[dev].load(std::memory_order_relaxed) : 0;
+  if (st == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BFP4_ERR_DEVICE;
-    ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    checked_dev = dev;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (cached) state[dev].store(st, std::memory_order_relaxed);
   }
-  return ok ? BFP4_OK : BFP4_ERR_DEVICE;
+  return st == 1 ? BFP4_OK : BFP4_ERR_DEVICE;
 }
 
 inline int launched(hipError_t e) { return e == hipSuccess ? BFP4_OK : BFP4_ERR_LAUNCH; }

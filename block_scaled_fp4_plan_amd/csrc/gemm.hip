@@ -31,6 +31,7 @@
 // * Plan rows past the device-side extent, padding rows and 32-row token fragments with no valid
 //   row are skipped.  Prefill tasks are handed out dynamically from one ticket queue per XCD;
 //   the decode grid covers (plan block, row groups) tasks with a static stride.
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -945,6 +946,27 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
   }
 }
 
+constexpr int kMaxDevices = 64;
+
+// Raises fn's dynamic LDS limit to at least `lds` bytes on the current device, once per device
+// (done[dev] holds the largest limit set so far); several threads may race here harmlessly, since
+// setting the same attribute twice is idempotent.
+hipError_t ensure_dynamic_lds(const void* fn, size_t lds, std::atomic<size_t>* done) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::atomic<size_t>* slot = (dev >= 0 && dev < kMaxDevices) ? &done[dev] : nullptr;
+  if (slot && slot->load(std::memory_order_acquire) >= lds) return hipSuccess;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  if (slot) {
+    size_t cur = slot->load(std::memory_order_acquire);
+    while (cur < lds && !slot->compare_exchange_weak(cur, lds, std::memory_order_acq_rel)) {
+    }
+  }
+  return hipSuccess;
+}
+
 template <int FN, int EPI>
 hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, hipStream_t s) {
   constexpr int RING = 2;
@@ -953,13 +975,9 @@ hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, 
   const size_t lds = 64 * sizeof(int) +
                      (size_t)rows_max * ((a.a_rowq + (a.a_rowq >> 3) + 15) & ~(int64_t)15);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static size_t attr_lds = 0;
-  if (lds > attr_lds) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    attr_lds = lds;
-  }
+  static std::atomic<size_t> lds_set[kMaxDevices];
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
+  if (err != hipSuccess) return err;
   const int64_t tasks = cap_blocks * a.n_nt;
   const int64_t max_wg = 256LL * 4;                  // resident workgroups (4 waves each)
   const int64_t grid = tasks < max_wg ? tasks : max_wg;
@@ -973,13 +991,9 @@ template <int EPI>
 hipError_t launch_gemm(const GemmArgs& a, int64_t max_tiles, const char* name, hipStream_t s) {
   const size_t lds = (size_t)kTokRegion + 2 * kTileRows * sizeof(int) + 16;
   auto kern = moe_gemm_kernel<EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<size_t> lds_set[kMaxDevices];
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
+  if (err != hipSuccess) return err;
   const int64_t total = max_tiles * a.n_ct;
   const int64_t maxwg = 256;                         // one workgroup per CU
   int64_t grid = total < maxwg ? total : maxwg;

@@ -230,7 +230,9 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const float* topk_weights,
  * bfp4_profile_begin(capacity, name_prefix) creates `capacity` event pairs and starts recording
  * one pair around every kernel the library launches whose name starts with name_prefix (host
  * string; NULL or "" for every kernel): plan_*, quantize_*, permute, prepare_weights, tile_list,
- * gemm1_{swiglu,relu2}_{decode,prefill}, gemm2_down_{decode,prefill}, finalize.
+ * decode_tokens, gemm1_<activation>_{decode,prefill} (activation swiglu, relu2, geglu, gelu, relu,
+ * silu or identity), gemm2_down_{decode,prefill}, finalize.  The timer is process-wide state:
+ * record from one host thread at a time, and not while a stream is being captured.
  * bfp4_profile_end() stops recording, waits for the
  * recorded events and writes one line per kernel name, "name count total_ms", into buf
  * (NUL-terminated, truncated to len).  Returns the number of kernels launched while recording,
