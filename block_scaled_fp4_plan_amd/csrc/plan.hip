@@ -12,7 +12,9 @@
 // in which one wavefront walks its slots 64 at a time and ranks equal ids with ballots (a lane's
 // rank among the lanes holding the same id is the popcount of the matching lanes below it).
 // Small inputs run all phases in one workgroup; large inputs split the slots into 1024-slot
-// chunks (per-chunk histograms, one scan over (expert, chunk), per-chunk scatter).
+// chunks (per-chunk histograms, one scan over (expert, chunk), per-chunk scatter).  The scatter
+// is a serial chain of ballot rounds per wave, so spreading the chunks over many workgroups
+// (one wave each, on different CUs) is faster than running more waves in one workgroup.
 #include "device.h"
 #include "runtime.h"
 
@@ -48,40 +50,41 @@ __device__ __forceinline__ int key_bits(int nloc) {
 
 // One wave ranks slots [f0, f1) in order and scatters them.  run[e] holds, for each local
 // expert, the plan position of its next slot; it is advanced by the highest lane of each group.
+// The ids of kIdBatch rounds of 64 slots are loaded together before any of those rounds
+// scatters: the vector-memory counter covers loads and stores in issue order, so a load issued
+// after a round's stores could only be waited for behind them, one store round trip per round.
 __device__ void scatter_wave(const int32_t* ids, int64_t f0, int64_t f1,
                              int num_experts, int offset, int nloc, int* run,
                              int32_t* __restrict__ sorted, int32_t* __restrict__ ttr) {
   const int lane = threadIdx.x & 63;
   const int nbits = key_bits(nloc);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // the ids of kIdBatch rounds of 64 slots are loaded together (independent loads in flight)
   constexpr int kIdBatch = 16;
-  int32_t idv[kIdBatch];
-  for (int64_t base = f0; base < f1; base += 64) {
-    const int rb = (int)(((base - f0) >> 6) % kIdBatch);
-    if (rb == 0) {
+  for (int64_t b0 = f0; b0 < f1; b0 += 64 * kIdBatch) {
+    int32_t idv[kIdBatch];
 #pragma unroll
-      for (int i = 0; i < kIdBatch; ++i) {
-        const int64_t fi = base + 64 * i + lane;
-        idv[i] = fi < f1 ? ids[fi] : -1;
-      }
+    for (int i = 0; i < kIdBatch; ++i) {
+      const int64_t fi = b0 + 64 * i + lane;
+      idv[i] = fi < f1 ? ids[fi] : -1;
     }
-    int32_t id = idv[0];
 #pragma unroll
-    for (int i = 1; i < kIdBatch; ++i) id = rb == i ? idv[i] : id;
-    int64_t f = base + lane;
-    if (f < f1) {
-      int e = local_id(id, num_experts, offset, nloc);
-      uint32_t key = (e < 0) ? (uint32_t)nloc : (uint32_t)e;
-      uint64_t peers = match_any(key, nbits);
-      if (e >= 0) {
-        int rank = __popcll(peers & below);
-        int pos = run[e] + rank;
-        sorted[pos] = (int32_t)f;
-        ttr[f] = pos;
-        if ((peers >> lane) == 1ull) run[e] += __popcll(peers);   // highest lane of the group
-      } else {
-        ttr[f] = -1;
+    for (int i = 0; i < kIdBatch; ++i) {
+      const int64_t base = b0 + 64 * i;
+      if (base >= f1) break;
+      const int64_t f = base + lane;
+      if (f < f1) {
+        const int e = local_id(idv[i], num_experts, offset, nloc);
+        const uint32_t key = (e < 0) ? (uint32_t)nloc : (uint32_t)e;
+        const uint64_t peers = match_any(key, nbits);
+        if (e >= 0) {
+          const int rank = __popcll(peers & below);
+          const int pos = run[e] + rank;
+          sorted[pos] = (int32_t)f;
+          ttr[f] = pos;
+          if ((peers >> lane) == 1ull) run[e] += __popcll(peers);   // highest lane of the group
+        } else {
+          ttr[f] = -1;
+        }
       }
     }
   }

@@ -117,6 +117,10 @@ PLAN_CASES = [  # (M, top_k, E, offset, nloc, block_m, kind)
     (300, 6, 288, 0, 144, 128, "zipf"), (37, 3, 8, 2, 4, 16, "noisy"),
     (4096, 8, 256, 0, 256, 128, "distinct"), (16384, 6, 288, 0, 144, 128, "zipf"),
     (2000, 4, 64, 16, 32, 24, "noisy"), (1, 1, 4, 0, 4, 8, "distinct"),
+    # 65536 and 65544 slots, 512 and 513 local experts, just past the one-workgroup kernel
+    (8192, 8, 256, 0, 256, 128, "distinct"), (8193, 8, 256, 0, 256, 128, "distinct"),
+    (700, 8, 600, 40, 512, 8, "noisy"), (700, 8, 600, 40, 513, 8, "noisy"),
+    (257, 8, 64, 0, 64, 16, "distinct"),
 ]
 
 
