@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=2,
                     help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (for counter-collection runs)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the achievable-peak context (read stream, vendor BF16 GEMM)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -381,9 +383,10 @@ def main():
             roofline={"bound": "hbm", "kernel": g1_name, "achieved": ach, "peak": HBM_PEAK_GBS,
                       "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                       "bytes_per_launch": g1_bytes, "avg_launch_ms": g1_ms})
-        gdt = time_graph(s, args.steps, args.warmup)
-        result["config"]["graph_replay_ms_per_step"] = gdt / args.steps * 1e3
-        result["config"]["graph_replay_tokens_per_s"] = wl.M / (gdt / args.steps)
+        if not args.no_graph:
+            gdt = time_graph(s, args.steps, args.warmup)
+            result["config"]["graph_replay_ms_per_step"] = gdt / args.steps * 1e3
+            result["config"]["graph_replay_tokens_per_s"] = wl.M / (gdt / args.steps)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(s)
         del s
@@ -392,7 +395,7 @@ def main():
         wl = WORKLOADS["prefill"]
         s, dt, dt_ev, table, breakdown = time_workload(wl, args.steps, args.warmup, 1)
         ms = dt / args.steps * 1e3
-        gdt = time_graph(s, args.steps, args.warmup)
+        gdt = None if args.no_graph else time_graph(s, args.steps, args.warmup)
         g1_ms, _, g1_name = kernel_ms(table, "gemm1")
         g1_flops = 2.0 * s.A * wl.H * wl.N1
         ach = g1_flops / (g1_ms * 1e-3) / 1e12
@@ -404,8 +407,8 @@ def main():
                                 "NVFP4", "assignments": s.A,
                     "padded_rows": int(s.fwd.plan.num_tokens_post_padded.item()),
                     "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
-                    "graph_replay_ms_per_step": gdt / args.steps * 1e3,
-                    "graph_replay_tokens_per_s": wl.M / (gdt / args.steps),
+                    "graph_replay_ms_per_step": gdt and gdt / args.steps * 1e3,
+                    "graph_replay_tokens_per_s": gdt and wl.M / (gdt / args.steps),
                     "kernels": kernel_rooflines(wl, s, breakdown)},
             roofline={"bound": "mfma", "kernel": g1_name, "achieved": ach,
                       "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
