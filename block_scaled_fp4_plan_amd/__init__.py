@@ -33,6 +33,8 @@ GATED_ACTS = (BFP4_ACT_SWIGLU, BFP4_ACT_GEGLU)
 BFP4_SCALE_PER_ROW = 0
 BFP4_SCALE_PER_GROUP = 1
 BFP4_SCALE_FIXED = 2
+BFP4_WEIGHTS_F32 = 0
+BFP4_WEIGHTS_BF16 = 1
 
 STATUS = {
     0: "BFP4_OK", -1: "BFP4_ERR_NULL", -2: "BFP4_ERR_SHAPE", -3: "BFP4_ERR_ALIGN",
@@ -86,9 +88,9 @@ _sig("bfp4_panel_bytes", _SZ, [_I, _I64, _I64, _I])
 _sig("bfp4_prepare_weights", _I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _P, _SZ, _P])
 _sig("bfp4_workspace_size", _SZ, [_I64, _I64, _I64, _I, _I, _I, _I])
 _sig("bfp4_fused_moe_nvfp4", _I,
-     [_P, _P, _P, _P, _SZ, _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _I64, _I64, _I64, _I, _I, _I,
-      _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
-_sig("bfp4_moe_finalize", _I, [_P, _P, _P, _I64, _I64, _I, _F, _P, _P])
+     [_P, _P, _P, _P, _SZ, _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I,
+      _I, _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
+_sig("bfp4_moe_finalize", _I, [_P, _P, _I, _P, _I64, _I64, _I, _F, _P, _P])
 _sig("bfp4_profile_begin", _I, [_I, ctypes.c_char_p])
 _sig("bfp4_profile_end", _I, [ctypes.c_char_p, _SZ])
 
@@ -176,9 +178,9 @@ def bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize)
 
 def bfp4_fused_moe_nvfp4(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, alpha1_up, alpha2,
                          c2, sorted_token_ids, expert_ids, num_tokens_post_padded, token_to_row,
-                         capacity, topk_weights, M, H, I, num_local_experts, top_k, block_m, act,
-                         routed_scaling_factor, do_finalize, out, gemm2_out, debug, workspace,
-                         workspace_bytes, stream=None):
+                         capacity, topk_weights, weights_dtype, M, H, I, num_local_experts, top_k,
+                         block_m, act, routed_scaling_factor, do_finalize, out, gemm2_out, debug,
+                         workspace, workspace_bytes, stream=None):
     dbg = None
     if debug is not None:
         dbg = ctypes.byref(bfp4_debug(*(_p(debug.get(k)) for k in
@@ -186,16 +188,17 @@ def bfp4_fused_moe_nvfp4(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, al
     return _check(_lib.bfp4_fused_moe_nvfp4(
         _p(a_q), _p(a_sf), _p(a_dec), _p(panels), panels_bytes, _p(alpha1_gate), _p(alpha1_up),
         _p(alpha2), c2, _p(sorted_token_ids), _p(expert_ids), _p(num_tokens_post_padded),
-        _p(token_to_row), capacity, _p(topk_weights), M, H, I, num_local_experts, top_k, block_m,
+        _p(token_to_row), capacity, _p(topk_weights), weights_dtype, M, H, I, num_local_experts,
+        top_k, block_m,
         act, routed_scaling_factor, do_finalize, _p(out), _p(gemm2_out), dbg, _p(workspace),
         workspace_bytes, _s(stream)), "bfp4_fused_moe_nvfp4")
 
 
-def bfp4_moe_finalize(gemm2_out, topk_weights, token_to_row, M, H, top_k, routed_scaling_factor,
-                      out, stream=None):
+def bfp4_moe_finalize(gemm2_out, topk_weights, weights_dtype, token_to_row, M, H, top_k,
+                      routed_scaling_factor, out, stream=None):
     return _check(_lib.bfp4_moe_finalize(
-        _p(gemm2_out), _p(topk_weights), _p(token_to_row), M, H, top_k, routed_scaling_factor,
-        _p(out), _s(stream)), "bfp4_moe_finalize")
+        _p(gemm2_out), _p(topk_weights), weights_dtype, _p(token_to_row), M, H, top_k,
+        routed_scaling_factor, _p(out), _s(stream)), "bfp4_moe_finalize")
 
 
 def bfp4_profile_begin(capacity, name_prefix=None):

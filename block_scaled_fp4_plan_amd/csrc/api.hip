@@ -246,12 +246,15 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          const float* alpha1_up, const float* alpha2, float c2,
                          const int32_t* sorted_token_ids, const int32_t* expert_ids,
                          const int32_t* num_tokens_post_padded, const int32_t* token_to_row,
-                         size_t capacity, const float* topk_weights, int64_t M, int64_t H,
-                         int64_t I, int num_local_experts, int top_k, int block_m, int act,
+                         size_t capacity, const void* topk_weights, int weights_dtype,
+                         int64_t M, int64_t H, int64_t I, int num_local_experts, int top_k,
+                         int block_m, int act,
                          float routed_scaling_factor, int do_finalize, uint16_t* out,
                          uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (act < BFP4_ACT_SWIGLU || act > BFP4_ACT_IDENTITY) return BFP4_ERR_MODE;
+  if (weights_dtype != BFP4_WEIGHTS_F32 && weights_dtype != BFP4_WEIGHTS_BF16) return BFP4_ERR_MODE;
+  const size_t wsz = weights_dtype == BFP4_WEIGHTS_BF16 ? 2 : 4;
   const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
   if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
   if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
@@ -276,7 +279,7 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
     return BFP4_ERR_NULL;
   if (!aligned(a_q, 16) || !aligned(a_sf, 16) || !aligned(panels, 16) || !aligned(out, 16) ||
       !aligned(gemm2_out, 16) || !aligned(a_dec, 4) || !aligned(alpha1_gate, 4) ||
-      !aligned(alpha1_up, 4) || !aligned(alpha2, 4) || !aligned(topk_weights, 4) ||
+      !aligned(alpha1_up, 4) || !aligned(alpha2, 4) || !aligned(topk_weights, wsz) ||
       !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) || !aligned(token_to_row, 4) ||
       !aligned(workspace, 256))
     return BFP4_ERR_ALIGN;
@@ -297,7 +300,8 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
         overlaps(out, ob, alpha2, nl) || overlaps(out, ob, sorted_token_ids, capacity * 4) ||
         overlaps(out, ob, expert_ids, capacity / block_m * 4) ||
         overlaps(out, ob, num_tokens_post_padded, 4) || overlaps(out, ob, token_to_row, mk) ||
-        overlaps(out, ob, topk_weights, mk) || overlaps(out, ob, workspace, ws))
+        overlaps(out, ob, topk_weights, (size_t)M * top_k * wsz) ||
+        overlaps(out, ob, workspace, ws))
       return BFP4_ERR_OVERLAP;
   }
   int dc = device_check();
@@ -353,27 +357,31 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   hipError_t e = launch_moe_gemms(p, s);
   if (e != hipSuccess) return BFP4_ERR_LAUNCH;
   if (!do_finalize) return BFP4_OK;
-  return launched(launch_finalize(y, topk_weights, token_to_row, M, H, top_k,
-                                  routed_scaling_factor, out, s));
+  return launched(launch_finalize(y, topk_weights, weights_dtype == BFP4_WEIGHTS_BF16,
+                                  token_to_row, M, H, top_k, routed_scaling_factor, out, s));
 }
 
-int bfp4_moe_finalize(const uint16_t* gemm2_out, const float* topk_weights,
+int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int weights_dtype,
                       const int32_t* token_to_row, int64_t M, int64_t H, int top_k,
                       float routed_scaling_factor, uint16_t* out, void* stream) {
+  if (weights_dtype != BFP4_WEIGHTS_F32 && weights_dtype != BFP4_WEIGHTS_BF16) return BFP4_ERR_MODE;
+  const size_t wsz = weights_dtype == BFP4_WEIGHTS_BF16 ? 2 : 4;
   if (M < 0 || H <= 0 || H % 8 || top_k <= 0) return BFP4_ERR_SHAPE;
   if (!isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
   if (M == 0) return BFP4_OK;
   if (!gemm2_out || !topk_weights || !token_to_row || !out) return BFP4_ERR_NULL;
-  if (!aligned(gemm2_out, 16) || !aligned(out, 16) || !aligned(topk_weights, 4) ||
+  if (!aligned(gemm2_out, 16) || !aligned(out, 16) || !aligned(topk_weights, wsz) ||
       !aligned(token_to_row, 4))
     return BFP4_ERR_ALIGN;
   size_t ob = (size_t)M * H * 2, mk = (size_t)M * top_k * 4;
-  if (overlaps(out, ob, topk_weights, mk) || overlaps(out, ob, token_to_row, mk))
+  if (overlaps(out, ob, topk_weights, (size_t)M * top_k * wsz) ||
+      overlaps(out, ob, token_to_row, mk))
     return BFP4_ERR_OVERLAP;
   int dc = device_check();
   if (dc) return dc;
-  return launched(launch_finalize(gemm2_out, topk_weights, token_to_row, M, H, top_k,
-                                  routed_scaling_factor, out, (hipStream_t)stream));
+  return launched(launch_finalize(gemm2_out, topk_weights, weights_dtype == BFP4_WEIGHTS_BF16,
+                                  token_to_row, M, H, top_k, routed_scaling_factor, out,
+                                  (hipStream_t)stream));
 }
 
 int bfp4_profile_begin(int capacity, const char* name_prefix) {

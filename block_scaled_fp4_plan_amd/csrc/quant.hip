@@ -158,8 +158,10 @@ __global__ __launch_bounds__(64) void permute_kernel(const uint8_t* __restrict__
 }
 
 // Finalize: one thread per (token, 8 consecutive hidden values).
+// WBF16: the routing weights are BF16 bit patterns, used as their exact FP32 values
+template <bool WBF16>
 __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restrict__ y,
-                                                       const float* __restrict__ w,
+                                                       const void* __restrict__ w,
                                                        const int32_t* __restrict__ ttr, int64_t M,
                                                        int64_t H, int top_k, float rsf,
                                                        uint16_t* __restrict__ out) {
@@ -188,7 +190,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restric
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (r[u] >= 0) {
-        wt[u] = w[t * top_k + j0 + u];
+        const int64_t wi = t * top_k + j0 + u;
+        wt[u] = WBF16 ? bf16_to_f32(static_cast<const uint16_t*>(w)[wi])
+                      : static_cast<const float*>(w)[wi];
         yy[u] = *reinterpret_cast<const uint4*>(y + (int64_t)r[u] * H + h);
       }
     }
@@ -261,13 +265,19 @@ hipError_t launch_permute(const uint8_t* q, const uint8_t* sf, const float* dec,
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const uint16_t* y, const float* w, const int32_t* ttr, int64_t M,
-                           int64_t H, int top_k, float rsf, uint16_t* out, hipStream_t s) {
+hipError_t launch_finalize(const uint16_t* y, const void* w, bool w_bf16, const int32_t* ttr,
+                           int64_t M, int64_t H, int top_k, float rsf, uint16_t* out,
+                           hipStream_t s) {
   int64_t n = M * (H >> 3);
   if (n == 0) return hipSuccess;
   KernelTimer t("finalize", s);
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, w, ttr,
-                     M, H, top_k, rsf, out);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (w_bf16)
+    hipLaunchKernelGGL(finalize_kernel<true>, grid, dim3(256), 0, s, y, w, ttr, M, H, top_k, rsf,
+                       out);
+  else
+    hipLaunchKernelGGL(finalize_kernel<false>, grid, dim3(256), 0, s, y, w, ttr, M, H, top_k, rsf,
+                       out);
   return hipGetLastError();
 }
 

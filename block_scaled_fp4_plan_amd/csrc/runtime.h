@@ -34,7 +34,7 @@ hipError_t launch_permute(const uint8_t* q, const uint8_t* sf, const float* dec,
                           int64_t H, int top_k, const int32_t* sorted, const int32_t* ntpp,
                           int64_t cap, uint8_t* qp, uint8_t* sp, float* spd, hipStream_t s);
 
-hipError_t launch_finalize(const uint16_t* y, const float* w, const int32_t* ttr, int64_t M,
+hipError_t launch_finalize(const uint16_t* y, const void* w, bool w_bf16, const int32_t* ttr, int64_t M,
                            int64_t H, int top_k, float rsf, uint16_t* out, hipStream_t s);
 
 // Weight panels: see gemm.hip for the layout.

@@ -8,6 +8,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (
+    BFP4_WEIGHTS_BF16,
+    BFP4_WEIGHTS_F32,
     BFP4_ACT_RELU2,
     BFP4_ACT_SWIGLU,
     GATED_ACTS,
@@ -23,6 +25,15 @@ from . import (
     bfp4_quantize_workspace_size,
     bfp4_workspace_size,
 )
+
+
+def weights_dtype(topk_weights):
+    """BFP4_WEIGHTS_* code of a routing-weight tensor (FP32 or BF16)."""
+    if topk_weights.dtype == torch.float32:
+        return BFP4_WEIGHTS_F32
+    if topk_weights.dtype == torch.bfloat16:
+        return BFP4_WEIGHTS_BF16
+    raise TypeError("routing weights must be float32 or bfloat16, not %s" % topk_weights.dtype)
 
 
 def _bytes(n, device):
@@ -142,7 +153,8 @@ class MoeForward:
         bfp4_fused_moe_nvfp4(self.a_q, self.a_sf, self.a_dec, w.panels, w.panels_bytes,
                              w.alpha1_gate, w.alpha1_up, w.alpha2, c2, pl.sorted_token_ids,
                              pl.expert_ids, pl.num_tokens_post_padded, pl.token_to_row,
-                             pl.capacity, topk_weights, M, H, I, w.num_local_experts,
+                             pl.capacity, topk_weights, weights_dtype(topk_weights), M, H, I,
+                             w.num_local_experts,
                              self.top_k, self.block_m, act, routed_scaling_factor,
                              int(self.do_finalize), out, self.gemm2_out, debug, self.ws,
                              self.ws_bytes, stream)

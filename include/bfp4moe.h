@@ -66,6 +66,9 @@ typedef enum {
   BFP4_ACT_IDENTITY = 6   /* x */
 } bfp4_act;
 typedef enum { BFP4_SCALE_PER_ROW = 0, BFP4_SCALE_PER_GROUP = 1, BFP4_SCALE_FIXED = 2 } bfp4_scale_mode;
+/* Routing weights [cuDNN, routing weights bullet: unpacked FP32 or BF16]: FP32 values, or BF16
+ * bit patterns, which the combine uses as their exact FP32 values. */
+typedef enum { BFP4_WEIGHTS_F32 = 0, BFP4_WEIGHTS_BF16 = 1 } bfp4_weights_dtype;
 
 /* Human-readable name of a status code (static storage). */
 const char* bfp4_status_string(int status);
@@ -182,7 +185,9 @@ int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_
  *   alpha1_gate, alpha1_up, alpha2 [num_local_experts] FP32;  c2 (host) > 0, finite;
  *   sorted_token_ids, expert_ids, num_tokens_post_padded, token_to_row: a plan from
  *   bfp4_moe_plan for the same M, top_k, num_local_experts and block_m, with this capacity;
- *   topk_weights [M, top_k] FP32; routed_scaling_factor (host) finite;
+ *   topk_weights [M, top_k] FP32 (weights_dtype BFP4_WEIGHTS_F32, 4-byte aligned) or BF16
+ *   (BFP4_WEIGHTS_BF16, 2-byte aligned); another weights_dtype gives BFP4_ERR_MODE;
+ *   routed_scaling_factor (host) finite;
  *   out [M, H] BF16 (16-byte aligned, must not overlap any input) -- used when do_finalize;
  *   gemm2_out [capacity, H] BF16 -- required when !do_finalize, else may be NULL;
  *   debug (may be NULL): optional copies of internal values for verification.
@@ -209,19 +214,22 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          const float* alpha1_up, const float* alpha2, float c2,
                          const int32_t* sorted_token_ids, const int32_t* expert_ids,
                          const int32_t* num_tokens_post_padded, const int32_t* token_to_row,
-                         size_t capacity, const float* topk_weights, int64_t M, int64_t H,
-                         int64_t I, int num_local_experts, int top_k, int block_m, int act,
+                         size_t capacity, const void* topk_weights, int weights_dtype,
+                         int64_t M, int64_t H, int64_t I, int num_local_experts, int top_k,
+                         int block_m, int act,
                          float routed_scaling_factor, int do_finalize, uint16_t* out,
                          uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------------------------
  * Finalize an unfinalized triple [cuDNN finalize bullet; Frost combine contract]: the combine of
- * bfp4_fused_moe_nvfp4 applied to gemm2_out [rows, H], topk_weights [M, top_k] and
- * token_to_row [M, top_k], accumulating into out [M, H].  Bit-identical to the finalized path.
- * Requirements: H % 8 == 0; pointers 16-byte aligned; out must not overlap the inputs.
+ * bfp4_fused_moe_nvfp4 applied to gemm2_out [rows, H], topk_weights [M, top_k] (FP32 or BF16 by
+ * weights_dtype, as in bfp4_fused_moe_nvfp4) and token_to_row [M, top_k], accumulating into
+ * out [M, H].  Bit-identical to the finalized path.
+ * Requirements: H % 8 == 0; gemm2_out and out 16-byte aligned, token_to_row 4-byte, the weights
+ * aligned to their element size; out must not overlap the inputs.
  * ---------------------------------------------------------------------------------------------- */
-int bfp4_moe_finalize(const uint16_t* gemm2_out, const float* topk_weights,
+int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int weights_dtype,
                       const int32_t* token_to_row, int64_t M, int64_t H, int top_k,
                       float routed_scaling_factor, uint16_t* out, void* stream);
 

@@ -127,7 +127,7 @@ def _fused(**kw):
                 alpha1_up=A + (41 << 16), alpha2=A + (42 << 16), c2=1.0,
                 sorted_token_ids=A + (43 << 16), expert_ids=A + (44 << 16),
                 num_tokens_post_padded=A + (45 << 16), token_to_row=A + (46 << 16), capacity=88,
-                topk_weights=A + (47 << 16), M=16, H=256, I=128, num_local_experts=8, top_k=2,
+                topk_weights=A + (47 << 16), weights_dtype=0, M=16, H=256, I=128, num_local_experts=8, top_k=2,
                 block_m=8, act=0, routed_scaling_factor=1.0, do_finalize=1, out=A + (48 << 16),
                 gemm2_out=None, debug=None, workspace=A + (50 << 16),
                 workspace_bytes=bf.bfp4_workspace_size(16, 256, 128, 2, 8, 8, 1), stream=0)
@@ -143,6 +143,8 @@ def test_fused_validation():
     assert _fused(I=96) == "BFP4_ERR_SHAPE"                    # I % 128
     assert _fused(block_m=9) == "BFP4_ERR_BLOCK_M"
     assert _fused(act=7) == "BFP4_ERR_MODE"
+    assert _fused(weights_dtype=2) == "BFP4_ERR_MODE"
+    assert _fused(topk_weights=A + (47 << 16) + 2) == "BFP4_ERR_ALIGN"      # FP32 needs 4 bytes
     assert _fused(act=-1) == "BFP4_ERR_MODE"
     # a gated activation (GeGLU) needs the larger, gated panels
     assert _fused(act=2, panels_bytes=bf.bfp4_panel_bytes(8, 256, 128, 0)) == "BFP4_ERR_WORKSPACE"
@@ -168,15 +170,23 @@ def test_fused_valid_args_without_device():
     for act in range(7):                         # every activation code is accepted
         nb = bf.bfp4_panel_bytes(8, 256, 128, int(act in bf.GATED_ACTS))
         assert _fused(act=act, panels_bytes=nb) == "BFP4_ERR_DEVICE"
+    # BF16 routing weights need 2-byte alignment only
+    assert _fused(weights_dtype=1, topk_weights=A + (47 << 16) + 2) == "BFP4_ERR_DEVICE"
 
 
 def test_finalize_and_prepare_validation():
     with pytest.raises(Bfp4Error) as ei:
-        bf.bfp4_moe_finalize(A, A + 4096, A + 8192, 4, 12, 2, 1.0, A + (1 << 16), 0)
+        bf.bfp4_moe_finalize(A, A + 4096, 0, A + 8192, 4, 12, 2, 1.0, A + (1 << 16), 0)
     assert bf.STATUS[ei.value.status] == "BFP4_ERR_SHAPE"
     with pytest.raises(Bfp4Error) as ei:
-        bf.bfp4_moe_finalize(A, A + 4096, A + 8192, 4, 256, 2, 1.0, A + 4096, 0)
+        bf.bfp4_moe_finalize(A, A + 4096, 0, A + 8192, 4, 256, 2, 1.0, A + 4096, 0)
     assert bf.STATUS[ei.value.status] == "BFP4_ERR_OVERLAP"
+    with pytest.raises(Bfp4Error) as ei:                       # unknown routing-weight dtype
+        bf.bfp4_moe_finalize(A, A + 4096, 3, A + 8192, 4, 256, 2, 1.0, A + (1 << 16), 0)
+    assert bf.STATUS[ei.value.status] == "BFP4_ERR_MODE"
+    with pytest.raises(Bfp4Error) as ei:                       # FP32 weights 2-byte aligned
+        bf.bfp4_moe_finalize(A, A + 4098, 0, A + 8192, 4, 256, 2, 1.0, A + (1 << 16), 0)
+    assert bf.STATUS[ei.value.status] == "BFP4_ERR_ALIGN"
     with pytest.raises(Bfp4Error) as ei:
         bf.bfp4_prepare_weights(A, A, A, A, 1, 256, 100, 1, A, 1 << 20, 0)
     assert bf.STATUS[ei.value.status] == "BFP4_ERR_SHAPE"

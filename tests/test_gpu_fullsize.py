@@ -42,7 +42,7 @@ def _check(name, token, n_hidden=512):
     fwd_u = runner.MoeForward(pw, M, k, wl.E, wl.block_m, wl.local_offset, do_finalize=False)
     y, wts, ttr_d = fwd_u(p.x, p.ids_d, p.w_d)
     out_u = torch.zeros_like(out)
-    bf.bfp4_moe_finalize(y, wts, ttr_d, M, H, k, 1.0, out_u)
+    bf.bfp4_moe_finalize(y, wts, runner.weights_dtype(wts), ttr_d, M, H, k, 1.0, out_u)
     torch.cuda.synchronize()
     out_bits = np_bits(out)
 

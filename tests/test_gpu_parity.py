@@ -325,7 +325,7 @@ def test_fused_moe_matches_oracle(name, bm):
                              act=wl.act_code)
     y, wts, ttr_d = fwd2(p.x, p.ids_d, p.w_d)
     out2 = torch.zeros_like(out)
-    bf.bfp4_moe_finalize(y, wts, ttr_d, M, wl.H, k, 1.0, out2)
+    bf.bfp4_moe_finalize(y, wts, runner.weights_dtype(wts), ttr_d, M, wl.H, k, 1.0, out2)
     torch.cuda.synchronize()
     assert np.array_equal(np_bits(out2), out_bits)
     # the combine of the GPU's own expert outputs is the oracle's combine, bit for bit
@@ -358,6 +358,40 @@ def test_out_accumulates_and_rsf():
     ydict = {int(r): bf16_bits_to_f32(ybits[r]).astype(np.float64) for r in ttr_np.reshape(-1) if r >= 0}
     want = oracle.combine(o0, ydict, p.w, ttr_np, 0.75)
     assert np.array_equal(np_bits(out), want)
+
+
+@pytest.mark.parametrize("bm", [8, 128])
+def test_bf16_routing_weights(bm):
+    """BF16 routing weights ([cuDNN] routing weights bullet) combine as their exact FP32 values:
+    the finalized output equals the FP32-weight call on those values and the oracle's combine of
+    the GPU's expert outputs, bit for bit; the unfinalized triple returns the BF16 weights and
+    bfp4_moe_finalize with them reproduces the finalized output."""
+    wl = WORKLOADS["tiny"]
+    say("bf16 routing weights, block_m", bm)
+    p = Problem(wl)
+    pw = runner.prepare_weights(p.w1, p.w2)
+    w_bf = p.w_d.to(torch.bfloat16)
+    w_exact = w_bf.float()
+    fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, bm)
+    out_bf = fwd(p.x, p.ids_d, w_bf)
+    torch.cuda.synchronize()
+    out_f32 = fwd(p.x, p.ids_d, w_exact)
+    torch.cuda.synchronize()
+    assert torch.equal(out_bf.view(torch.int16), out_f32.view(torch.int16))
+    fwd_u = runner.MoeForward(pw, p.M, wl.top_k, wl.E, bm, do_finalize=False)
+    y, wts, ttr_d = fwd_u(p.x, p.ids_d, w_bf)
+    out2 = torch.zeros_like(out_bf)
+    bf.bfp4_moe_finalize(y, wts, bf.BFP4_WEIGHTS_BF16, ttr_d, p.M, wl.H, wl.top_k, 1.0, out2)
+    torch.cuda.synchronize()
+    assert wts.dtype == torch.bfloat16 and torch.equal(wts, w_bf)
+    assert torch.equal(out2.view(torch.int16), out_bf.view(torch.int16))
+    ttr_np = ttr_d.cpu().numpy()
+    ybits = np_bits(y)
+    ydict = {int(r): bf16_bits_to_f32(ybits[r]).astype(np.float64)
+             for r in ttr_np.reshape(-1) if r >= 0}
+    comb = oracle.combine(np.zeros((p.M, wl.H), np.uint16), ydict, w_exact.cpu().numpy(), ttr_np)
+    assert np.array_equal(comb, np_bits(out_bf))
+    assert np.any(comb != 0)
 
 
 def test_masked_slots_nan_weights_and_all_masked_token():
