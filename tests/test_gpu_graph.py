@@ -81,3 +81,53 @@ def test_graph_replay_matches_eager(name, bm, fin):
             rows = rows[rows >= 0].long()
             assert rows.numel() > 0
             assert torch.equal(_bits(y_g[rows]), _bits(y_e[rows])), seed
+
+
+@pytest.mark.parametrize("bm", [8, 128])
+def test_graph_stable_dispatcher_buffer(bm):
+    """Bounded execution over a graph-stable dispatcher buffer ([MCore] flashinfer_routed_nvfp4_moe:
+    rows whose routing entries are -1 contribute zero; with a token capacity only that fixed prefix
+    is processed and rows past it are left untouched in out).  One graph is captured over a
+    48-row buffer with a 32-row prefix; each replay routes a different number of leading rows and
+    marks the rest -1.  Routed rows equal the eager call on the same rows, unrouted prefix rows
+    keep their previous out values, and rows past the prefix are never written."""
+    wl = WORKLOADS["tiny"]
+    rows_buf, cap_rows = 48, 32
+    say("graph dispatcher buffer, block_m", bm)
+    p = Problem(wl, M=rows_buf)
+    pw = runner.prepare_weights(p.w1, p.w2, gated=wl.gated)
+    fwd_g = runner.MoeForward(pw, cap_rows, wl.top_k, wl.E, bm)
+    fwd_e = runner.MoeForward(pw, cap_rows, wl.top_k, wl.E, bm)
+    x, ids, w = p.x.clone(), p.ids_d.clone(), p.w_d.clone()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    out0 = torch.randn((rows_buf, wl.H), device="cuda", generator=g).to(torch.bfloat16)
+    out = out0.clone()
+
+    def call(f, xs, idss, ws, o):
+        return f(xs[:cap_rows], idss[:cap_rows], ws[:cap_rows], out=o[:cap_rows])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(fwd_g, x, ids, w, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(fwd_g, x, ids, w, out)
+
+    for n_routed in (32, 5, 0, 17):
+        xs, idss, ws = _inputs(wl, n_routed + 1, rows_buf)
+        idss[n_routed:] = -1
+        x.copy_(xs)
+        ids.copy_(idss)
+        w.copy_(ws)
+        out.copy_(out0)
+        graph.replay()
+        ref = out0.clone()
+        call(fwd_e, xs, idss, ws, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref)), n_routed
+        assert torch.equal(_bits(out[n_routed:]), _bits(out0[n_routed:])), n_routed
+        if n_routed:
+            assert not torch.equal(_bits(out[:n_routed]), _bits(out0[:n_routed]))
