@@ -264,6 +264,10 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   // the tiled (block_m > 32) GEMMs address their FP16 token operands with 32-bit offsets
   if (block_m > 32 && (M * H * 2 >= (1LL << 31) || (int64_t)capacity * I * 2 >= (1LL << 31)))
     return BFP4_ERR_SHAPE;
+  // the decode kernels (block_m <= 32) stage a plan block's token rows whole in LDS
+  if (block_m <= 32 && (moe_gemv_lds_bytes(block_m, H) > kMaxLdsBytes ||
+                        moe_gemv_lds_bytes(block_m, I) > kMaxLdsBytes))
+    return BFP4_ERR_SHAPE;
   // ... and an expert's weight panels with 32-bit offsets
   if (block_m > 32 &&
       (panel_matrix_bytes(1, gated ? 2 * I : I, H) >= (1LL << 31) ||

@@ -971,10 +971,8 @@ template <int FN, int EPI>
 hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, hipStream_t s) {
   constexpr int RING = 2;
   auto kern = moe_gemv_kernel<FN, EPI, RING>;
-  const int rows_max = a.block_m < 32 ? a.block_m : 32;
-  const size_t lds = 64 * sizeof(int) +
-                     (size_t)rows_max * ((a.a_rowq + (a.a_rowq >> 3) + 15) & ~(int64_t)15);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  const size_t lds = moe_gemv_lds_bytes(a.block_m, 2 * a.a_rowq);
+  if (lds > kMaxLdsBytes) return hipErrorInvalidValue;
   static std::atomic<size_t> lds_set[kMaxDevices];
   hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
   if (err != hipSuccess) return err;
@@ -1145,6 +1143,13 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
                             : launch_gemm<EPI_ACT>(g1, max_tiles, nm, s);
   if (err != hipSuccess) return err;
   return launch_gemm<EPI_DOWN>(g2, max_tiles, "gemm2_down_prefill", s);
+}
+
+// row sources and scales (64 words), then each staged row: K/2 packed bytes and K/16 scale
+// bytes, rounded up to 16 bytes
+size_t moe_gemv_lds_bytes(int block_m, int64_t K) {
+  const int64_t rows_max = block_m < 32 ? block_m : 32;
+  return 64 * sizeof(int) + (size_t)rows_max * ((K / 2 + K / 16 + 15) & ~(int64_t)15);
 }
 
 int64_t moe_gemm_max_tiles(int64_t cap, int block_m) {

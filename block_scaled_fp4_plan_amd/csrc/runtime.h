@@ -70,5 +70,8 @@ struct MoeGemmProblem {
 hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s);
 int64_t moe_gemm_max_tiles(int64_t cap, int block_m);
 size_t moe_gemm_tile_ws_bytes(int64_t cap, int block_m);
+// LDS bytes of a decode-GEMM workgroup (block_m <= 32) whose token rows have K values
+size_t moe_gemv_lds_bytes(int block_m, int64_t K);
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 }  // namespace bfp4

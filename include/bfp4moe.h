@@ -197,7 +197,11 @@ int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_
  *   tiled prefill kernels, which read exact FP16 copies of their token operands through 32-bit
  *   buffer offsets) also M*H*2 < 2^31 and capacity*I*2 < 2^31 bytes, and one expert's panel
  *   of each matrix (bfp4_panel_bytes(1, ...) splits into the two) below 2^31 bytes, else
- *   BFP4_ERR_SHAPE (split such a batch into several calls).
+ *   BFP4_ERR_SHAPE (split such a batch into several calls).  With block_m <= 32 (the decode
+ *   kernels, which stage a plan block's routed rows whole in LDS) min(block_m, 32) rows of
+ *   K/2 + K/16 bytes (rounded up to 16) plus 256 bytes must fit in 160 KiB for K = H and K = I
+ *   (for H a multiple of 256: H <= 8960 at block_m 32, 18176 at 16, 36352 at 8), else
+ *   BFP4_ERR_SHAPE.
  * Device preconditions: the plan's expert ids are < num_local_experts; token ids < M.
  * ---------------------------------------------------------------------------------------------- */
 typedef struct {

@@ -160,6 +160,9 @@ def test_fused_validation():
     assert _fused(out=A + (1 << 16) + 64) == "BFP4_ERR_OVERLAP"  # out over a_sf
     assert _fused(out=A + (50 << 16) + 512) == "BFP4_ERR_OVERLAP"  # out over workspace
     assert _fused(num_local_experts=0) == "BFP4_ERR_EXPERTS"
+    # decode kernels (block_m <= 32) stage a block's rows whole in LDS: H <= 8960 at block_m 32
+    assert _fused(H=9216, block_m=32, capacity=bf.bfp4_plan_capacity(16, 2, 8, 32),
+                  panels_bytes=bf.bfp4_panel_bytes(8, 9216, 128, 1)) == "BFP4_ERR_SHAPE"
     # tiled kernels (block_m > 32) read FP16 token copies with 32-bit offsets: M*H*2 < 2^31
     assert _fused(M=1 << 24, top_k=1, block_m=128) == "BFP4_ERR_SHAPE"
 
@@ -170,6 +173,11 @@ def test_fused_valid_args_without_device():
     for act in range(7):                         # every activation code is accepted
         nb = bf.bfp4_panel_bytes(8, 256, 128, int(act in bf.GATED_ACTS))
         assert _fused(act=act, panels_bytes=nb) == "BFP4_ERR_DEVICE"
+    # the largest decode-kernel shape at block_m 32 passes validation
+    assert _fused(H=8960, block_m=32, capacity=bf.bfp4_plan_capacity(16, 2, 8, 32),
+                  panels_bytes=bf.bfp4_panel_bytes(8, 8960, 128, 1),
+                  workspace_bytes=bf.bfp4_workspace_size(16, 8960, 128, 2, 8, 32, 1),
+                  out=1 << 40) == "BFP4_ERR_DEVICE"
     # BF16 routing weights need 2-byte alignment only
     assert _fused(weights_dtype=1, topk_weights=A + (47 << 16) + 2) == "BFP4_ERR_DEVICE"
 
