@@ -21,7 +21,8 @@ What it computes follows these web pages (cited by page title and section):
 * vLLM, "vllm.model_executor.layers.quantization.utils.flashinfer_utils":
   quantize_nvfp4_per_token_input returns one FP32 *decode* scale per token.
 * FlashInfer, "flashinfer.fused_moe.FrostLowLatencyConfig": BF16 rounding of the activation
-  output and of expert outputs; combine by ordered, separate FP32 multiply and add; expert
+  output and of expert outputs; the FP4 weight-only mode (BF16 input, pre-activation and
+  intermediate rounding); combine by ordered, separate FP32 multiply and add; expert
   ids outside the routed range are ignored together with their scores.
 
 Where the pages are silent the reading taken is stated next to the code that takes it.
@@ -59,7 +60,9 @@ from .moe import (  # noqa: F401
     combine,
     dense_loop_moe,
     expert_rows_forward,
+    expert_rows_forward_w16,
     fused_moe_nvfp4,
+    fused_moe_w4a16,
     moe_permute,
     moe_plan,
     plan_capacity,

@@ -337,6 +337,76 @@ def dense_loop_moe(a_q, a_sf, a_dec, weights, alpha1_gate, alpha1_up, alpha2, c2
     return (r.view(np.uint32) >> 16).astype(np.uint16)
 
 
+def expert_rows_forward_w16(x_bits, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate, alpha1_up, alpha2, act):
+    """One expert in the NVFP4 weight-only mode on BF16 rows (FrostLowLatencyConfig, FP4
+    weight-only paragraph: canonical E2M1 payloads with linear E4M3 K16 scales, BF16 input,
+    pre-activation and intermediate rounding, BF16 expert outputs).
+
+    x_bits: BF16 bit patterns [R, H] of the rows routed to this expert.  Steps:
+      pre   = (sum_h x deq(W1)) * alpha1            (float64; gate rows alpha1_gate, up rows
+                                                     alpha1_up, one-projection alpha1_up)
+      pre_b = bf16(pre)                              (pre-activation rounding)
+      h     = bf16(activation(pre_b))                (intermediate rounding)
+      y     = bf16((sum_i h deq(W2)) * alpha2)       (BF16 expert output)
+    Reading taken: the expert's FP32 global weight scale multiplies the sum before the rounding,
+    as in the NVFP4 x NVFP4 mode.  Each product of a BF16 value and a dequantized weight is exact
+    in float64 and the sums are float64.  Returns dict(pre, pre_b, h, y) as float64 arrays.
+    """
+    x = bf16_bits_to_f32(np.asarray(x_bits, np.uint16)).astype(np.float64)
+    N1 = w1_q.shape[0]
+    I = w2_q.shape[1] * 2
+    gated = is_gated(act)
+    if N1 != (2 * I if gated else I):
+        raise ValueError("W1 rows do not match the activation")
+    w1 = dequantize_int(w1_q, w1_sf).astype(np.float64) * 2.0 ** -10
+    w2 = dequantize_int(w2_q, w2_sf).astype(np.float64) * 2.0 ** -10
+    alpha_rows = np.full(N1, float(alpha1_up), dtype=np.float64)
+    if gated:
+        alpha_rows[:I] = float(alpha1_gate)
+    pre = (x @ w1.T) * alpha_rows.reshape(1, N1)
+    pre_b = round_to_bf16(pre)
+    h = round_to_bf16(_activation(pre_b, I, act))
+    y = round_to_bf16((h @ w2.T) * float(alpha2))
+    return dict(pre=pre, pre_b=pre_b, h=h, y=y)
+
+
+def fused_moe_w4a16(x_bits, weights, alpha1_gate, alpha1_up, alpha2, sorted_token_ids,
+                    expert_ids, num_tokens_post_padded, token_to_row, topk_weights, top_k, block_m,
+                    act, routed_scaling_factor=1.0, out0_bits=None, do_finalize=True):
+    """Plan-driven NVFP4 weight-only forward on BF16 activations: every valid plan row r of
+    expert e takes token t = entry // top_k through expert_rows_forward_w16, then the same
+    ordered combine as the NVFP4 mode (or the unfinalized triple).
+    Returns dict(out, y {row}, pre {row}, h {row}, unfinalized)."""
+    get = _experts_from(weights)
+    xb = np.asarray(x_bits, np.uint16)
+    M, H = xb.shape
+    ent = np.asarray(sorted_token_ids, dtype=np.int64)
+    eids = np.asarray(expert_ids, dtype=np.int64)
+    by_expert = {}
+    for b in range(num_tokens_post_padded // block_m):
+        for r in range(b * block_m, (b + 1) * block_m):
+            if ent[r] < M * top_k:                     # padding rows contribute nothing
+                by_expert.setdefault(int(eids[b]), []).append(r)
+    res = dict(y={}, pre={}, h={})
+    for e, rs in sorted(by_expert.items()):
+        w1q, w1s, w2q, w2s = get(e)
+        rs = np.array(rs)
+        o = expert_rows_forward_w16(xb[ent[rs] // top_k], w1q, w1s, w2q, w2s, alpha1_gate[e],
+                                    alpha1_up[e], alpha2[e], act)
+        for i, r in enumerate(rs):
+            res["y"][int(r)] = o["y"][i]
+            res["pre"][int(r)] = o["pre"][i]
+            res["h"][int(r)] = o["h"][i]
+    res["unfinalized"] = (res["y"], np.asarray(topk_weights, np.float32), np.asarray(token_to_row))
+    res["out"] = None
+    if do_finalize:
+        if out0_bits is None:
+            out0_bits = np.zeros((M, H), dtype=np.uint16)
+        res["out"] = combine(out0_bits, res["y"], topk_weights, token_to_row,
+                             routed_scaling_factor)
+    return res
+
+
 def unquantized_moe_f64(x_bits, w1_bits_of, w2_bits_of, topk_ids, topk_weights, num_experts,
                         local_expert_offset, num_local_experts, act, routed_scaling_factor=1.0,
                         tokens=None):

@@ -396,3 +396,95 @@ def test_gap_to_unquantized_reference():
     ref = np.stack([ref[t] for t in range(wl.M)])
     gap = np.linalg.norm(out - ref) / np.linalg.norm(ref)
     assert 0.02 < gap < 0.35, gap
+
+
+# ----------------------------------------------------------------------------- weight-only mode
+
+@pytest.mark.parametrize("act", [oracle.ACT_SWIGLU, oracle.ACT_GEGLU, oracle.ACT_RELU2,
+                                 oracle.ACT_IDENTITY])
+def test_w16_expert_brute_force(act):
+    """NVFP4 weight-only expert on BF16 rows (FrostLowLatencyConfig, FP4 weight-only paragraph)
+    against exact rational arithmetic: pre from Fractions of the BF16 inputs and the exactly
+    decoded weights; the BF16 rounding of pre and of the activation; y from the oracle's own
+    BF16 intermediate, exactly."""
+    rng = np.random.default_rng(31 + act)
+    R, H, I = 3, 32, 16
+    gated = oracle.is_gated(act)
+    N1 = 2 * I if gated else I
+    x_bits = to_bits(torch.from_numpy(rng.standard_normal((R, H))).to(torch.bfloat16))
+    w1q, w1sf = _rand_nvfp4(rng, N1, H)
+    w2q, w2sf = _rand_nvfp4(rng, H, I)
+    ag, au, a2 = np.float32(0.03), np.float32(0.05), np.float32(0.07)
+    o = oracle.expert_rows_forward_w16(x_bits, w1q, w1sf, w2q, w2sf, ag, au, a2, act)
+    X = [[Fraction(float(v)) for v in row] for row in bf16_bits_to_f32(x_bits)]
+    W1 = _exact_matrix(w1q, w1sf)
+    W2 = _exact_matrix(w2q, w2sf)
+    for r in range(R):
+        pre = [sum(X[r][h] * W1[n][h] for h in range(H)) *
+               Fraction(float((ag if n < I else au) if gated else au)) for n in range(N1)]
+        for n in range(N1):
+            assert abs(o["pre"][r, n] - float(pre[n])) <= 1e-15 * abs(float(pre[n])) + 1e-300
+            # pre-activation rounded to BF16: within half a BF16 step of the exact value
+            assert abs(o["pre_b"][r, n] - float(pre[n])) <= abs(float(pre[n])) * 2.0 ** -8 + 1e-300
+            assert o["pre_b"][r, n] == oracle.round_to_bf16(np.array([float(pre[n])]))[0]
+        for i in range(I):
+            h = _act_ref(act, float(o["pre_b"][r, i]),
+                         float(o["pre_b"][r, I + i]) if gated else None)
+            assert abs(o["h"][r, i] - h) <= abs(h) * 2.0 ** -8 * 1.0001 + 1e-300
+        for hh in range(H):
+            s = sum(Fraction(float(o["h"][r, i])) * W2[hh][i] for i in range(I)) * Fraction(float(a2))
+            assert abs(o["y"][r, hh] - float(s)) <= abs(float(s)) * 2.0 ** -8 * 1.0001 + 1e-300
+    # every rounded value is a BF16 value
+    for k in ("pre_b", "h", "y"):
+        v = o[k].astype(np.float32)
+        assert np.array_equal(v.view(np.uint32) & 0xFFFF, np.zeros_like(v.view(np.uint32)))
+
+
+def test_w16_unit_vector_reads_weight_column():
+    """A BF16 row equal to the unit vector e_k gives pre = alpha1 * W1[:, k] (exact), and with the
+    identity activation and alpha = 1 the intermediate is the BF16 of that column."""
+    rng = np.random.default_rng(7)
+    H, I = 64, 16
+    w1q, w1sf = _rand_nvfp4(rng, I, H)
+    w2q, w2sf = _rand_nvfp4(rng, H, I)
+    w1 = oracle.dequantize_nvfp4(w1q, w1sf)
+    for k in (0, 17, 63):
+        x = np.zeros((1, H))
+        x[0, k] = 1.0
+        o = oracle.expert_rows_forward_w16(oracle.f64_to_bf16_bits(x), w1q, w1sf, w2q, w2sf,
+                                           np.float32(1), np.float32(1), np.float32(1),
+                                           oracle.ACT_IDENTITY)
+        assert np.array_equal(o["pre"][0], w1[:, k])
+        assert np.array_equal(o["h"][0], w1[:, k])          # E2M1 x E4M3 values are BF16 values
+
+
+@pytest.mark.parametrize("wl", [WORKLOADS["tiny"], SHRUNK_SKEWED], ids=["tiny", "skewed_small"])
+def test_w16_plan_path_equals_per_token_loop(wl):
+    """The plan-driven weight-only forward equals a per-token loop over the routed slots (each
+    slot's row through its expert, then the ordered combine), and block_m 8 / 16 / 32 give the
+    same output bit for bit (padding rows contribute nothing)."""
+    p = _small_problem(wl)
+    act = wl.act_code
+    outs = []
+    for bm in (8, 16, 32):
+        srt, eids, P, ttr = oracle.moe_plan(p["ids"], wl.E, wl.local_offset, wl.n_local, bm)
+        res = oracle.fused_moe_w4a16(p["x"], p["W"], p["a1"], p["a1"], p["a2"], srt, eids, P, ttr,
+                                     p["w"], wl.top_k, bm, act)
+        outs.append(res["out"])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    # per-token loop
+    M, k = p["ids"].shape
+    get = lambda e: (p["W"][0][e], p["W"][1][e], p["W"][2][e], p["W"][3][e])   # noqa: E731
+    acc = np.zeros((M, wl.H), np.float32)
+    for t in range(M):
+        for j in range(k):
+            e = int(p["ids"][t, j]) - wl.local_offset
+            if not (0 <= int(p["ids"][t, j]) < wl.E and 0 <= e < wl.n_local):
+                continue
+            o = oracle.expert_rows_forward_w16(p["x"][t:t + 1], *get(e), p["a1"][e], p["a1"][e],
+                                               p["a2"][e], act)
+            prod = np.float32(p["w"][t, j]) * o["y"][0].astype(np.float32)
+            acc[t] = (acc[t] + prod).astype(np.float32)
+    dense = oracle.f64_to_bf16_bits(acc.astype(np.float64))
+    assert np.array_equal(outs[0], dense)
+    assert np.any(outs[0] != 0)
