@@ -5,7 +5,7 @@ routing plan + per-token NVFP4 quantization of the activations + fused experts (
 SwiGLU and requantization, GEMM2, ordered FP32 finalize).  Weight quantization and panel
 preparation happen once, before timing (offline in a serving system).
 
-Workloads (synthetic, seeded):
+Workloads (synthetic, seeded inputs from synth/):
   decode  : M=8,    H=7168, I=2048, E=256, top_k=8, block_m=8   (primary: value = tokens/s)
   prefill : M=4096, H=7168, I=2048, E=256, top_k=8, block_m=128 (reported in "prefill")
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|both]

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libbfp4moe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libbfp4moe.so is not built; run `python -m block_scaled_fp4_plan_amd.build` "
+        "libbfp4moe.so is not built; run `python block_scaled_fp4_plan_amd/build.py` "
         "(or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -46,7 +46,8 @@ EXPORTS = [
     "bfp4_status_string", "bfp4_version", "bfp4_plan_capacity", "bfp4_plan_workspace_size",
     "bfp4_moe_plan", "bfp4_quantize_workspace_size", "bfp4_quantize_nvfp4", "bfp4_moe_permute",
     "bfp4_panel_bytes", "bfp4_prepare_weights", "bfp4_workspace_size", "bfp4_fused_moe_nvfp4",
-    "bfp4_moe_finalize", "bfp4_profile_begin", "bfp4_profile_end",
+    "bfp4_moe_finalize", "bfp4_profile_begin", "bfp4_profile_end", "bfp4_workspace_size_w4a16",
+    "bfp4_fused_moe_w4a16",
 ]
 
 
@@ -91,6 +92,10 @@ _sig("bfp4_fused_moe_nvfp4", _I,
      [_P, _P, _P, _P, _SZ, _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I,
       _I, _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
 _sig("bfp4_moe_finalize", _I, [_P, _P, _I, _P, _I64, _I64, _I, _F, _P, _P])
+_sig("bfp4_workspace_size_w4a16", _SZ, [_I64, _I64, _I64, _I, _I, _I, _I])
+_sig("bfp4_fused_moe_w4a16", _I,
+     [_P, _I64, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I, _I,
+      _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
 _sig("bfp4_profile_begin", _I, [_I, ctypes.c_char_p])
 _sig("bfp4_profile_end", _I, [ctypes.c_char_p, _SZ])
 
@@ -192,6 +197,28 @@ def bfp4_fused_moe_nvfp4(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, al
         top_k, block_m,
         act, routed_scaling_factor, do_finalize, _p(out), _p(gemm2_out), dbg, _p(workspace),
         workspace_bytes, _s(stream)), "bfp4_fused_moe_nvfp4")
+
+
+def bfp4_workspace_size_w4a16(M, H, I, top_k, num_local_experts, block_m, do_finalize):
+    return _lib.bfp4_workspace_size_w4a16(M, H, I, top_k, num_local_experts, block_m, do_finalize)
+
+
+def bfp4_fused_moe_w4a16(x_bf16, row_stride, panels, panels_bytes, alpha1_gate, alpha1_up,
+                         alpha2, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                         token_to_row, capacity, topk_weights, weights_dtype, M, H, I,
+                         num_local_experts, top_k, block_m, act, routed_scaling_factor,
+                         do_finalize, out, gemm2_out, debug, workspace, workspace_bytes,
+                         stream=None):
+    dbg = None
+    if debug is not None:
+        dbg = ctypes.byref(bfp4_debug(*(_p(debug.get(k)) for k in
+                                        ("preact", "inter", "inter_q", "inter_sf"))))
+    return _check(_lib.bfp4_fused_moe_w4a16(
+        _p(x_bf16), row_stride, _p(panels), panels_bytes, _p(alpha1_gate), _p(alpha1_up),
+        _p(alpha2), _p(sorted_token_ids), _p(expert_ids), _p(num_tokens_post_padded),
+        _p(token_to_row), capacity, _p(topk_weights), weights_dtype, M, H, I, num_local_experts,
+        top_k, block_m, act, routed_scaling_factor, do_finalize, _p(out), _p(gemm2_out), dbg,
+        _p(workspace), workspace_bytes, _s(stream)), "bfp4_fused_moe_w4a16")
 
 
 def bfp4_moe_finalize(gemm2_out, topk_weights, weights_dtype, token_to_row, M, H, top_k,

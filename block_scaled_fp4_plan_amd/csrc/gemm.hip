@@ -167,6 +167,11 @@ struct GemmArgs {
   // GEMM2 epilogue
   uint16_t* y;
   int64_t Hout;
+  // weight-only mode (BF16 token operand): token rows (x for GEMM1, the BF16 intermediate for
+  // GEMM2) with their row stride in elements, and GEMM1's BF16 intermediate output [cap, I]
+  const uint16_t* w16_x;
+  int64_t w16_stride;
+  uint16_t* w16_h;
 };
 
 // Epilogues: the two GEMM1 forms the hot paths use (SwiGLU, squared ReLU), the down GEMM, GeGLU,
@@ -946,6 +951,223 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// NVFP4 weight-only mode on BF16 activations, decode-sized plan blocks (block_m <= 32).
+// Same tasks and weight stream as moe_gemv_kernel; the token operand is BF16 as given, read by
+// each lane straight from memory (the block's few rows stay in L2), so nothing is staged in LDS
+// but the row sources; each weight fragment is decoded exactly (E2M1 x E4M3 has at most 6
+// significant bits) to BF16 and fed to v_mfma_f32_32x32x16_bf16.
+
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+
+// 8 exact FP16 weights -> the same 8 values in BF16 (FP16 -> FP32 is exact, and the values need
+// at most 8 significant bits, so the high half of each FP32 is the BF16 value)
+__device__ __forceinline__ bf8_t h8_to_bf8(h8_t v) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = __float_as_uint((float)v[2 * i]);
+    const uint32_t hi = __float_as_uint((float)v[2 * i + 1]);
+    r[i] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // {hi[31:16], lo[31:16]}
+  }
+  return __builtin_bit_cast(bf8_t, r);
+}
+
+// GEMM1 epilogue of the weight-only mode: pre = acc * alpha (FP32, reported to dbg_pre), rounded
+// to BF16; the activation of the rounded values, rounded to BF16, is the intermediate h [cap, I]
+// (GEMM2's BF16 token operand).  Gated forms exchange halves between lanes l and l + 32 as the
+// NVFP4 epilogue does; one-projection forms keep 16 consecutive values per lane.
+template <int EPI>
+__device__ __forceinline__ void epilogue_w16(const GemmArgs& a, const f32x16_t& acc, float al,
+                                             int64_t g, int h, int64_t r) {
+  if (one_projection(EPI)) {
+    const int64_t i0 = g * kGroupRows + 16 * h;
+    float pr[16];
+    uint32_t bb[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      pr[v] = acc[v] * al;
+      const float pb = bf16_to_f32(f32_to_bf16(pr[v]));
+      float hv;
+      if (EPI == EPI_RELU2) {
+        const float q = pb > 0.0f ? pb : 0.0f;
+        hv = q * q;
+      } else {
+        hv = act_one(pb, a.act);
+      }
+      bb[v] = f32_to_bf16(hv);
+    }
+    if (a.dbg_pre) {
+      float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * a.I + i0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dp[v] = make_float4(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]);
+    }
+    const uint4 w0 = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16),
+                                bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16));
+    const uint4 w1 = make_uint4(bb[8] | (bb[9] << 16), bb[10] | (bb[11] << 16),
+                                bb[12] | (bb[13] << 16), bb[14] | (bb[15] << 16));
+    uint4* d = reinterpret_cast<uint4*>(a.w16_h + r * a.I + i0);
+    d[0] = w0;
+    d[1] = w1;
+    if (a.dbg_inter) {
+      uint4* dd = reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + i0);
+      dd[0] = w0;
+      dd[1] = w1;
+    }
+    return;
+  }
+  // SwiGLU, GeGLU
+  const int64_t i0 = g * 16;
+  float pre[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) pre[v] = acc[v] * al;
+  if (a.dbg_pre) {
+    float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + h * a.I + i0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      dp[v] = make_float4(pre[4 * v], pre[4 * v + 1], pre[4 * v + 2], pre[4 * v + 3]);
+  }
+  uint32_t bb[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const auto gu = __builtin_amdgcn_permlane32_swap(__float_as_uint(pre[v]),
+                                                     __float_as_uint(pre[8 + v]), false, false);
+    const float gt = bf16_to_f32(f32_to_bf16(__uint_as_float(gu[0])));
+    const float up = bf16_to_f32(f32_to_bf16(__uint_as_float(gu[1])));
+    bb[v] = f32_to_bf16((EPI == EPI_GEGLU ? gelu(gt) : silu(gt)) * up);
+  }
+  const int64_t ih = i0 + 8 * h;
+  const uint4 w = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
+                             bb[6] | (bb[7] << 16));
+  *reinterpret_cast<uint4*>(a.w16_h + r * a.I + ih) = w;
+  if (a.dbg_inter) *reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + ih) = w;
+}
+
+template <int FN, int EPI, int RING>
+__global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
+  __shared__ int row_src[32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  int64_t P = *a.ntpp;
+  if (P > a.cap) P = a.cap;
+  if (P < 0) P = 0;
+  const int64_t nblk = P / a.block_m;
+  const int nst = a.nch / kStageChunks;
+  const int rows_max = min(a.block_m, 32);
+  const int64_t ntask = nblk * a.n_nt;
+
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int64_t b = task / a.n_nt;
+    const int nt = (int)(task - b * a.n_nt);
+    const int e = a.eids[b];
+    if (e < 0 || e >= a.nloc) continue;
+    __syncthreads();                                   // previous task done with row_src
+    if (tid < 32) {
+      int src = -1;
+      if (tid < rows_max) {
+        const int64_t ent = a.sorted[b * a.block_m + tid];
+        if (ent >= 0 && ent < a.sentinel) src = a.gather ? (int)(ent / a.top_k)
+                                                         : (int)(b * a.block_m + tid);
+      }
+      row_src[tid] = src;
+    }
+    __syncthreads();
+
+    const int64_t g0 = (int64_t)nt * (4 * FN) + (int64_t)wave * FN;
+    const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
+    const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
+                           lane * 16;
+    // lanes past the routed rows read row 0's source (valid memory); their columns are dropped
+    const int my_src = row_src[col < rows_max ? col : 0];
+    const int src = my_src >= 0 ? my_src : 0;
+    const uint16_t* trow = a.w16_x + (int64_t)src * a.w16_stride + 32 * h;
+
+    const float al = lane_alpha<EPI>(a, e, h);
+    f32x16_t acc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x16_t{};
+    uint4 W[RING][kStageChunks][FN];
+    uint32_t S[RING][FN];
+
+    auto load_w = [&](uint4 (&Wd)[kStageChunks][FN], uint32_t (&Sd)[FN], int st) {
+      const int64_t sc = st / (kSuperChunks / kStageChunks);
+      const int c0 = (st * kStageChunks) % kSuperChunks;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const uint8_t* base = wbase + fn * a.rg_bytes + sc * kSuperBytes;
+        Sd[fn] = *reinterpret_cast<const uint32_t*>(base + 2 * c0);
+#pragma unroll
+        for (int c = 0; c < kStageChunks; ++c)
+          Wd[c][fn] = *reinterpret_cast<const uint4*>(base + kUnit + (c0 + c) * kUnit);
+      }
+    };
+    // token operand of one 64-value chunk: lane (col, h) holds values 32h .. 32h + 31 of the
+    // chunk, 8 per MFMA step (the K order the weight panels use)
+    auto load_t = [&](uint4 (&T)[4], int64_t chunk) {
+      const uint4* p = reinterpret_cast<const uint4*>(trow + chunk * 64);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) T[s] = p[s];
+    };
+    auto compute = [&](const uint4 (&Wd)[kStageChunks][FN], const uint32_t (&Sd)[FN],
+                       const uint4 (&T)[kStageChunks][4]) {
+#pragma unroll
+      for (int c = 0; c < kStageChunks; ++c) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf8_t Tv = __builtin_bit_cast(bf8_t, T[c][s]);
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const uint32_t wd = (s == 0) ? Wd[c][fn].x : (s == 1) ? Wd[c][fn].y
+                                : (s == 2) ? Wd[c][fn].z : Wd[c][fn].w;
+            const uint32_t sb = (Sd[fn] >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
+            const bf8_t Wv = h8_to_bf8(decode8(wd, e4m3_scale_h2(sb)));
+            acc[fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Wv, Tv, acc[fn], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    uint4 T[kStageChunks][4];
+#pragma unroll
+    for (int d = 0; d < RING - 1; ++d) load_w(W[d], S[d], min(d, nst - 1));
+    for (int st0 = 0; st0 < nst; st0 += RING) {
+#pragma unroll
+      for (int d = 0; d < RING; ++d) {
+        const int st = st0 + d;
+        if (st >= nst) break;
+#pragma unroll
+        for (int c = 0; c < kStageChunks; ++c) load_t(T[c], (int64_t)st * kStageChunks + c);
+        const int nd = (d + RING - 1) % RING;
+        load_w(W[nd], S[nd], min(st + RING - 1, nst - 1));
+        compute(W[d], S[d], T);
+      }
+    }
+    if (wave_on && col < rows_max && my_src >= 0) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        if (EPI == EPI_DOWN)
+          epilogue_group<EPI_DOWN>(a, acc[fn], al, g0 + fn, h, 1.0f, b * a.block_m + col);
+        else
+          epilogue_w16<EPI>(a, acc[fn], al, g0 + fn, h, b * a.block_m + col);
+      }
+    }
+  }
+}
+
+template <int FN, int EPI>
+hipError_t launch_gemv16(const GemmArgs& a, int64_t cap_blocks, const char* name,
+                         hipStream_t s) {
+  const int64_t tasks = cap_blocks * a.n_nt;
+  const int64_t max_wg = 256LL * 4;                  // resident workgroups (4 waves each)
+  const int64_t grid = tasks < max_wg ? tasks : max_wg;
+  if (grid == 0) return hipSuccess;
+  KernelTimer t(name, s);
+  hipLaunchKernelGGL((moe_gemv16_kernel<FN, EPI, 2>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 constexpr int kMaxDevices = 64;
 
 // Raises fn's dynamic LDS limit to at least `lds` bytes on the current device, once per device
@@ -1150,6 +1372,73 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
 size_t moe_gemv_lds_bytes(int block_m, int64_t K) {
   const int64_t rows_max = block_m < 32 ? block_m : 32;
   return 64 * sizeof(int) + (size_t)rows_max * ((K / 2 + K / 16 + 15) & ~(int64_t)15);
+}
+
+hipError_t launch_moe_gemms_w16(const MoeGemmW16& w, hipStream_t s) {
+  const MoeGemmProblem& p = w.p;
+  const bool gated = p.act == BFP4_ACT_SWIGLU || p.act == BFP4_ACT_GEGLU;
+  const int64_t N1 = gated ? 2 * p.I : p.I;
+  const int64_t cap_blocks = p.cap / p.block_m;
+  constexpr int FN = 2;
+  if (p.block_m > 32) return hipErrorInvalidValue;
+
+  GemmArgs g1{};
+  g1.sorted = p.sorted;
+  g1.eids = p.eids;
+  g1.ntpp = p.ntpp;
+  g1.cap = p.cap;
+  g1.sentinel = p.M * p.top_k;
+  g1.top_k = p.top_k;
+  g1.block_m = p.block_m;
+  g1.nloc = p.nloc;
+  g1.gather = 1;
+  const PanelGeom pg1 = panel_geom(N1, p.H);
+  g1.panel = p.panel1;
+  g1.expert_bytes = pg1.expert_bytes;
+  g1.rg_bytes = pg1.rg_bytes;
+  g1.nch = (int)pg1.nch;
+  g1.N = (int)N1;
+  g1.n_nt = (int)((N1 + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g1.alpha_a = p.alpha1_gate;
+  g1.alpha_b = p.alpha1_up;
+  g1.act = p.act;
+  g1.I = p.I;
+  g1.dbg_pre = p.dbg_pre;
+  g1.dbg_inter = p.dbg_inter;
+  g1.w16_x = w.x;
+  g1.w16_stride = w.x_stride;
+  g1.w16_h = w.h;
+
+  GemmArgs g2 = g1;
+  g2.gather = 0;
+  const PanelGeom pg2 = panel_geom(p.H, p.I);
+  g2.panel = p.panel2;
+  g2.expert_bytes = pg2.expert_bytes;
+  g2.rg_bytes = pg2.rg_bytes;
+  g2.nch = (int)pg2.nch;
+  g2.N = (int)p.H;
+  g2.n_nt = (int)((p.H + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g2.alpha_a = p.alpha2;
+  g2.alpha_b = nullptr;
+  g2.y = p.y;
+  g2.Hout = p.H;
+  g2.dbg_pre = nullptr;
+  g2.dbg_inter = nullptr;
+  g2.w16_x = w.h;
+  g2.w16_stride = p.I;
+  g2.w16_h = nullptr;
+
+  static const char* const kName[] = {
+      "gemm1_swiglu_w16_decode", "gemm1_relu2_w16_decode", "gemm1_geglu_w16_decode",
+      "gemm1_gelu_w16_decode", "gemm1_relu_w16_decode", "gemm1_silu_w16_decode",
+      "gemm1_identity_w16_decode"};
+  const char* nm = kName[p.act];
+  hipError_t err = p.act == BFP4_ACT_SWIGLU ? launch_gemv16<FN, EPI_SWIGLU>(g1, cap_blocks, nm, s)
+                 : p.act == BFP4_ACT_RELU2  ? launch_gemv16<FN, EPI_RELU2>(g1, cap_blocks, nm, s)
+                 : p.act == BFP4_ACT_GEGLU  ? launch_gemv16<FN, EPI_GEGLU>(g1, cap_blocks, nm, s)
+                                            : launch_gemv16<FN, EPI_ACT>(g1, cap_blocks, nm, s);
+  if (err != hipSuccess) return err;
+  return launch_gemv16<FN, EPI_DOWN>(g2, cap_blocks, "gemm2_down_w16_decode", s);
 }
 
 int64_t moe_gemm_max_tiles(int64_t cap, int block_m) {

@@ -68,6 +68,17 @@ struct MoeGemmProblem {
   uint16_t* h16;     // block_m > 32: [cap, I] FP16 copy of the requantized intermediate
 };
 hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s);
+
+// NVFP4 weight-only mode on BF16 activations (block_m <= 32): the plan, panels, alphas, act,
+// dbg_* and y fields of MoeGemmProblem as above; a_q, a_sf, a_dec, c2, hq, hsf, tile_ws, a16,
+// h16 unused.
+struct MoeGemmW16 {
+  MoeGemmProblem p;
+  const uint16_t* x;    // [M rows, stride x_stride] BF16 activations
+  int64_t x_stride;
+  uint16_t* h;          // [cap, I] BF16 intermediate
+};
+hipError_t launch_moe_gemms_w16(const MoeGemmW16& w, hipStream_t s);
 int64_t moe_gemm_max_tiles(int64_t cap, int block_m);
 size_t moe_gemm_tile_ws_bytes(int64_t cap, int block_m);
 // LDS bytes of a decode-GEMM workgroup (block_m <= 32) whose token rows have K values

@@ -16,6 +16,7 @@ from . import (
     BFP4_SCALE_PER_GROUP,
     BFP4_SCALE_PER_ROW,
     bfp4_fused_moe_nvfp4,
+    bfp4_fused_moe_w4a16,
     bfp4_moe_plan,
     bfp4_panel_bytes,
     bfp4_plan_capacity,
@@ -24,6 +25,7 @@ from . import (
     bfp4_quantize_nvfp4,
     bfp4_quantize_workspace_size,
     bfp4_workspace_size,
+    bfp4_workspace_size_w4a16,
 )
 
 
@@ -158,4 +160,47 @@ class MoeForward:
                              self.top_k, self.block_m, act, routed_scaling_factor,
                              int(self.do_finalize), out, self.gemm2_out, debug, self.ws,
                              self.ws_bytes, stream)
+        return out if self.do_finalize else (self.gemm2_out, topk_weights, pl.token_to_row)
+
+
+class MoeForwardW4A16:
+    """One forward of the NVFP4 weight-only mode on BF16 activations (decode plans, block_m <=
+    32): routing plan, then bfp4_fused_moe_w4a16 (no activation quantization)."""
+
+    def __init__(self, weights: PreparedWeights, M, top_k, num_experts, block_m,
+                 local_expert_offset=0, do_finalize=True, device="cuda", act=None):
+        if act is None:
+            act = BFP4_ACT_SWIGLU if weights.gated else BFP4_ACT_RELU2
+        if (act in GATED_ACTS) != bool(weights.gated):
+            raise ValueError("activation %d does not match the weights' gating" % act)
+        self.act = act
+        self.w = weights
+        self.M, self.top_k, self.E, self.block_m = M, top_k, num_experts, block_m
+        self.offset = local_expert_offset
+        self.do_finalize = do_finalize
+        self.plan = MoePlanBuffers(M, top_k, weights.num_local_experts, block_m, device)
+        self.ws_bytes = bfp4_workspace_size_w4a16(M, weights.H, weights.I, top_k,
+                                                  weights.num_local_experts, block_m,
+                                                  int(do_finalize))
+        self.ws = _bytes(self.ws_bytes + 256, device)
+        self.gemm2_out = None
+        if not do_finalize:
+            self.gemm2_out = torch.empty((max(self.plan.capacity, 1), weights.H),
+                                         dtype=torch.bfloat16, device=device)
+
+    def __call__(self, x_bf16, topk_ids, topk_weights, out=None, debug=None, weights=None,
+                 stream=None, routed_scaling_factor=1.0):
+        w = self.w if weights is None else weights
+        M, H, I = self.M, w.H, w.I
+        self.plan.build(topk_ids, self.E, self.offset, stream)
+        if out is None and self.do_finalize:
+            out = torch.zeros((M, H), dtype=torch.bfloat16, device=x_bf16.device)
+        pl = self.plan
+        bfp4_fused_moe_w4a16(x_bf16, x_bf16.stride(0), w.panels, w.panels_bytes, w.alpha1_gate,
+                             w.alpha1_up, w.alpha2, pl.sorted_token_ids, pl.expert_ids,
+                             pl.num_tokens_post_padded, pl.token_to_row, pl.capacity,
+                             topk_weights, weights_dtype(topk_weights), M, H, I,
+                             w.num_local_experts, self.top_k, self.block_m, self.act,
+                             routed_scaling_factor, int(self.do_finalize), out, self.gemm2_out,
+                             debug, self.ws, self.ws_bytes, stream)
         return out if self.do_finalize else (self.gemm2_out, topk_weights, pl.token_to_row)

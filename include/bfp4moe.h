@@ -226,6 +226,35 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------------------------
+ * NVFP4 weight-only forward on BF16 activations [Frost, FP4 weight-only paragraph: canonical
+ * E2M1 weights with linear E4M3 K16 scales and one FP32 scale per expert; BF16 input,
+ * pre-activation and intermediate rounding; BF16 expert outputs; the same combine].  Decode-sized
+ * plans only (block_m <= 32, else BFP4_ERR_BLOCK_M).
+ * Per valid plan row r (entry f < M*top_k, token t = f / top_k, local expert e of r's block):
+ *   pre[n] = (sum_h x[t,h] * W1_e[n,h]) * alpha1_{gate|up}[e]     (FP32 accumulate of exact
+ *            products: BF16 x E2M1 x E4M3), then p[n] = bf16(pre[n]);
+ *   h[i]   = bf16(act(p[i]) * p[I+i])  (gated)  or  bf16(act(p[i]))  (one projection);
+ *   y[k]   = bf16((sum_i h[i] * W2_e[k,i]) * alpha2[e]);
+ * then the combine (or the unfinalized triple) exactly as bfp4_fused_moe_nvfp4.
+ * Arguments as bfp4_fused_moe_nvfp4, except: x_bf16 [M rows, row_stride >= H elements,
+ * row_stride % 8 == 0] BF16 activations in place of a_q/a_sf/a_dec, no c2; debug->preact gets
+ * pre (FP32, before the BF16 rounding), debug->inter h (BF16); inter_q/inter_sf are unused.
+ * workspace: >= bfp4_workspace_size_w4a16(...) bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------------------------------- */
+size_t bfp4_workspace_size_w4a16(int64_t M, int64_t H, int64_t I, int top_k,
+                                 int num_local_experts, int block_m, int do_finalize);
+int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void* panels,
+                         size_t panels_bytes, const float* alpha1_gate, const float* alpha1_up,
+                         const float* alpha2, const int32_t* sorted_token_ids,
+                         const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                         const int32_t* token_to_row, size_t capacity, const void* topk_weights,
+                         int weights_dtype, int64_t M, int64_t H, int64_t I,
+                         int num_local_experts, int top_k, int block_m, int act,
+                         float routed_scaling_factor, int do_finalize, uint16_t* out,
+                         uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
  * Finalize an unfinalized triple [cuDNN finalize bullet; Frost combine contract]: the combine of
  * bfp4_fused_moe_nvfp4 applied to gemm2_out [rows, H], topk_weights [M, top_k] (FP32 or BF16 by
  * weights_dtype, as in bfp4_fused_moe_nvfp4) and token_to_row [M, top_k], accumulating into

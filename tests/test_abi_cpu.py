@@ -204,3 +204,43 @@ def test_finalize_and_prepare_validation():
     with pytest.raises(Bfp4Error) as ei:
         bf.bfp4_moe_permute(A, A, A, 4, 48, 2, A, A, 16, A, A, A, 0)
     assert bf.STATUS[ei.value.status] == "BFP4_ERR_SHAPE"
+
+
+def _w16(**kw):
+    args = dict(x_bf16=A, row_stride=256, panels=A + (3 << 16),
+                panels_bytes=bf.bfp4_panel_bytes(8, 256, 128, 1), alpha1_gate=A + (40 << 16),
+                alpha1_up=A + (41 << 16), alpha2=A + (42 << 16), sorted_token_ids=A + (43 << 16),
+                expert_ids=A + (44 << 16), num_tokens_post_padded=A + (45 << 16),
+                token_to_row=A + (46 << 16), capacity=88, topk_weights=A + (47 << 16),
+                weights_dtype=0, M=16, H=256, I=128, num_local_experts=8, top_k=2, block_m=8,
+                act=0, routed_scaling_factor=1.0, do_finalize=1, out=A + (48 << 16),
+                gemm2_out=None, debug=None, workspace=A + (50 << 16),
+                workspace_bytes=bf.bfp4_workspace_size_w4a16(16, 256, 128, 2, 8, 8, 1), stream=0)
+    args.update(kw)
+    with pytest.raises(Bfp4Error) as ei:
+        bf.bfp4_fused_moe_w4a16(**args)
+    return bf.STATUS[ei.value.status]
+
+
+def test_w4a16_validation():
+    # hq [88, 128] BF16 intermediate + y [88, 256] BF16, each rounded up to 256 bytes
+    assert bf.bfp4_workspace_size_w4a16(16, 256, 128, 2, 8, 8, 1) == 88 * 256 + 88 * 512
+    assert _w16(block_m=128, capacity=bf.bfp4_plan_capacity(16, 2, 8, 128)) == "BFP4_ERR_BLOCK_M"
+    assert _w16(row_stride=200) == "BFP4_ERR_SHAPE"
+    assert _w16(row_stride=260) == "BFP4_ERR_SHAPE"
+    assert _w16(H=200) == "BFP4_ERR_SHAPE"
+    assert _w16(act=9) == "BFP4_ERR_MODE"
+    assert _w16(weights_dtype=5) == "BFP4_ERR_MODE"
+    assert _w16(x_bf16=A + 8) == "BFP4_ERR_ALIGN"
+    assert _w16(x_bf16=None) == "BFP4_ERR_NULL"
+    assert _w16(workspace_bytes=64) == "BFP4_ERR_WORKSPACE"
+    assert _w16(out=A + 64) == "BFP4_ERR_OVERLAP"                 # out over x
+    assert _w16(capacity=80) == "BFP4_ERR_CAPACITY"
+
+
+@cpu_only
+def test_w4a16_valid_args_without_device():
+    assert _w16() == "BFP4_ERR_DEVICE"
+    assert _w16(block_m=32, capacity=bf.bfp4_plan_capacity(16, 2, 8, 32),
+                workspace_bytes=bf.bfp4_workspace_size_w4a16(16, 256, 128, 2, 8, 32, 1)) == \
+        "BFP4_ERR_DEVICE"
