@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=2,
                     help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-w4a16", action="store_true",
+                    help="skip the weight-only (BF16 activation) decode measurement")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (for counter-collection runs)")
     ap.add_argument("--no-context", action="store_true",
@@ -194,6 +196,44 @@ def time_graph(s, steps, warmup):
     dt = time.perf_counter() - t0
     del graphs
     return dt
+
+
+def time_w4a16(s, steps, warmup):
+    """The decode step in the NVFP4 weight-only mode on BF16 activations (routing plan + fused
+    weight-only experts + finalize, no activation quantization), on the same inputs and rotating
+    weight replicas: step time of an uninstrumented pass, then the weight-only GEMM1's average
+    launch duration from a pass with HIP events around it."""
+    import torch
+
+    import block_scaled_fp4_plan_amd as bf
+    from block_scaled_fp4_plan_amd import runner
+
+    wl = s.wl
+    f = runner.MoeForwardW4A16(s.weights[0], wl.M, wl.top_k, wl.E, wl.block_m, wl.local_offset)
+
+    def step(i):
+        f(s.x, s.ids_d, s.w_d, out=s.out, weights=s.weights[i % len(s.weights)])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    bf.bfp4_profile_begin(steps * 4 + 16, "gemm1_swiglu_w16")
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    g1_ms, _, name = kernel_ms(bf.bfp4_profile_end()[1], "gemm1")
+    q = NVFP4_BYTES
+    g1_bytes = (s.touched * wl.N1 * wl.H * q + wl.M * wl.H * 2 + s.A * wl.I * 2)
+    ach = g1_bytes / (g1_ms * 1e-3) / 1e9
+    return {"value": wl.M / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "roofline": {"bound": "hbm", "kernel": name, "achieved": ach, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": g1_bytes,
+                         "avg_launch_ms": g1_ms}}
 
 
 def achievable_context(reps=5):
@@ -387,6 +427,8 @@ def main():
             gdt = time_graph(s, args.steps, args.warmup)
             result["config"]["graph_replay_ms_per_step"] = gdt / args.steps * 1e3
             result["config"]["graph_replay_tokens_per_s"] = wl.M / (gdt / args.steps)
+        if not args.no_w4a16:
+            result["w4a16_decode"] = time_w4a16(s, args.steps, args.warmup)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(s)
         del s
