@@ -1079,10 +1079,11 @@ __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
     const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
     const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
                            lane * 16;
-    // lanes past the routed rows read row 0's source (valid memory); their columns are dropped
-    const int my_src = row_src[col < rows_max ? col : 0];
-    const int src = my_src >= 0 ? my_src : 0;
-    const uint16_t* trow = a.w16_x + (int64_t)src * a.w16_stride + 32 * h;
+    // only lanes of routed rows read token data; the others feed zeros (their columns are
+    // dropped), which keeps the L2 traffic to the block's routed rows
+    const int my_src = col < rows_max ? row_src[col] : -1;
+    const bool tok_on = my_src >= 0;
+    const uint16_t* trow = a.w16_x + (int64_t)(tok_on ? my_src : 0) * a.w16_stride + 32 * h;
 
     const float al = lane_alpha<EPI>(a, e, h);
     f32x16_t acc[FN];
@@ -1108,7 +1109,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
     auto load_t = [&](uint4 (&T)[4], int64_t chunk) {
       const uint4* p = reinterpret_cast<const uint4*>(trow + chunk * 64);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) T[s] = p[s];
+      for (int s = 0; s < 4; ++s) T[s] = tok_on ? p[s] : make_uint4(0, 0, 0, 0);
     };
     auto compute = [&](const uint4 (&Wd)[kStageChunks][FN], const uint32_t (&Sd)[FN],
                        const uint4 (&T)[kStageChunks][4]) {
@@ -1144,7 +1145,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
         compute(W[d], S[d], T);
       }
     }
-    if (wave_on && col < rows_max && my_src >= 0) {
+    if (wave_on && tok_on) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         if (EPI == EPI_DOWN)
