@@ -960,15 +960,27 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
 
 typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 
-// 8 exact FP16 weights -> the same 8 values in BF16 (FP16 -> FP32 is exact, and the values need
-// at most 8 significant bits, so the high half of each FP32 is the BF16 value)
-__device__ __forceinline__ bf8_t h8_to_bf8(h8_t v) {
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+
+// 8 E2M1 codes times one E4M3 scale -> 8 exact BF16 values: the codes convert to FP32 times
+// 256 (only the exponent of the conversion's scale operand is used) and the scale enters as the
+// FP32 value s * 2^-8 (read through its FP16 bit pattern, exact for every E4M3 code); every
+// product has at most 6 significant bits, so the FP32 products and their BF16 conversion are
+// exact.
+__device__ __forceinline__ bf8_t decode8_bf16(uint32_t w, uint32_t sf_byte) {
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)((sf_byte & 0x7Fu) << 7));
   u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = __float_as_uint((float)v[2 * i]);
-    const uint32_t hi = __float_as_uint((float)v[2 * i + 1]);
-    r[i] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);   // {hi[31:16], lo[31:16]}
+    float2 p;
+    switch (i) {   // the byte selector must be a compile-time constant
+      case 0: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 0); p = make_float2(v[0], v[1]); break; }
+      case 1: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 1); p = make_float2(v[0], v[1]); break; }
+      case 2: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 2); p = make_float2(v[0], v[1]); break; }
+      default: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 3); p = make_float2(v[0], v[1]); break; }
+    }
+    const bf2_t b2 = {(__bf16)(p.x * s), (__bf16)(p.y * s)};
+    r[i] = __builtin_bit_cast(uint32_t, b2);
   }
   return __builtin_bit_cast(bf8_t, r);
 }
@@ -1123,7 +1135,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
             const uint32_t wd = (s == 0) ? Wd[c][fn].x : (s == 1) ? Wd[c][fn].y
                                 : (s == 2) ? Wd[c][fn].z : Wd[c][fn].w;
             const uint32_t sb = (Sd[fn] >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
-            const bf8_t Wv = h8_to_bf8(decode8(wd, e4m3_scale_h2(sb)));
+            const bf8_t Wv = decode8_bf16(wd, sb);
             acc[fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Wv, Tv, acc[fn], 0, 0, 0);
           }
         }
