@@ -222,6 +222,13 @@ RAGGED_K = Workload("ragged_k", M=384, H=1280, I=640, E=6, top_k=3, block_m=128,
 # down GEMM with 4 n-tiles of 4 stages: each tile's n-tiles run as one stage stream
 CHAIN_N = Workload("chain_n", M=320, H=1024, I=512, E=5, top_k=2, block_m=128, routing="zipf")
 
+# degenerate and limit shapes: one token with one slot; 24 of 40 experts per token; the largest
+# hidden size whose routed rows fit the decode kernels' LDS at block_m 32 (32 rows x 5040 bytes
+# + 256 = 161536 of 163840 bytes)
+ONE_TOKEN = Workload("one_token", M=1, H=256, I=128, E=8, top_k=1, block_m=8)
+WIDE_TOPK = Workload("wide_topk", M=6, H=512, I=256, E=40, top_k=24, block_m=16)
+LDS_LIMIT = Workload("lds_limit", M=40, H=8960, I=128, E=4, top_k=2, block_m=32)
+
 # the other activations, on the decode (block_m 8, 16) and the tiled (block_m 128) kernels
 ACT_WORKLOADS = {
     "tiny_geglu": dataclasses.replace(WORKLOADS["tiny"], name="tiny_geglu", act="geglu"),
@@ -240,12 +247,14 @@ MOE_CASES = [
     ("tiny_geglu", 8), ("tiny_geglu", 128), ("ll_geglu", 8), ("ragged_geglu", 128),
     ("gelu", 8), ("gelu", 128), ("relu", 16), ("relu", 128), ("silu", 8), ("silu", 128),
     ("identity", 8), ("identity", 128), ("skewed_gelu", 16),
+    ("one_token", 8), ("one_token", 128), ("wide_topk", 16), ("wide_topk", 128), ("lds_limit", 32),
 ]
 
 
 def _workload(name):
     return ({"skewed_small": SMALL_SKEWED, "tiny_relu2": TINY_RELU2, "ragged_k": RAGGED_K,
-             "chain_n": CHAIN_N, **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
+             "chain_n": CHAIN_N, "one_token": ONE_TOKEN, "wide_topk": WIDE_TOPK,
+             "lds_limit": LDS_LIMIT, **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
 
 
 def run_gpu_moe(p, block_m, do_finalize=True, debug=True, rsf=1.0):
