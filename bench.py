@@ -377,9 +377,12 @@ def cpu_baseline(s, sample_tokens=1):
                                    ids, s.w[:T], wl.E, wl.local_offset, wl.n_local, oracle.ACT_SWIGLU)
     u = np.stack([u[t] for t in range(T)])
     gap = float(np.linalg.norm(ref - u) / np.linalg.norm(u))
+    flops = 2.0 * T * wl.top_k * (wl.N1 * wl.H + wl.H * wl.I)
     return dict(value=T / dt, unit="tokens/s", cores=1, kind="oracle",
+                host_cores=len(os.sched_getaffinity(0)), gflops=flops / dt / 1e9,
                 sample="%d token(s) of the %s workload (%d experts), per-call path without weight "
-                       "quantization; %.2f s; float64 numpy, single thread; GPU-vs-oracle rel. "
+                       "quantization; %.2f s; float64 numpy (its projections are exact int64 "
+                       "matrix products, one thread); GPU-vs-oracle rel. "
                        "Frobenius error on the sample %.2e" % (T, wl.name, len(experts), dt, err),
                 oracle_nvfp4_vs_fp64_gap=gap)
 
