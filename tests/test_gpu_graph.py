@@ -131,3 +131,46 @@ def test_graph_stable_dispatcher_buffer(bm):
         assert torch.equal(_bits(out[n_routed:]), _bits(out0[n_routed:])), n_routed
         if n_routed:
             assert not torch.equal(_bits(out[:n_routed]), _bits(out0[:n_routed]))
+
+
+def test_graph_in_place_weight_refresh():
+    """In-place weight refresh under a captured graph: new weights are quantized and laid out
+    into the panel buffer and alpha arrays the graph already points to (bfp4_prepare_weights
+    writes caller-owned memory), and the next replay computes with them, bit for bit as an eager
+    call with freshly prepared copies of the same weights."""
+    import block_scaled_fp4_plan_amd as bf
+
+    wl = WORKLOADS["tiny"]
+    say("graph in-place weight refresh")
+    p = Problem(wl)
+    pw = runner.prepare_weights(p.w1, p.w2)
+    fwd_g = runner.MoeForward(pw, p.M, wl.top_k, wl.E, 8)
+    out_g = torch.zeros((p.M, wl.H), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd_g(p.x, p.ids_d, p.w_d, out=out_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd_g(p.x, p.ids_d, p.w_d, out=out_g)
+
+    for step in range(2):
+        g = torch.Generator(device="cuda").manual_seed(11 + step)
+        w1n = (torch.randn(p.w1.shape, device="cuda", generator=g) * 0.03).to(torch.bfloat16)
+        w2n = (torch.randn(p.w2.shape, device="cuda", generator=g) * 0.03).to(torch.bfloat16)
+        E, N1, H = w1n.shape
+        I = w2n.shape[2]
+        q1, s1, a1 = runner.quantize(w1n.reshape(E * N1, H), bf.BFP4_SCALE_PER_GROUP, N1)
+        q2, s2, a2 = runner.quantize(w2n.reshape(E * H, I), bf.BFP4_SCALE_PER_GROUP, H)
+        bf.bfp4_prepare_weights(q1, s1, q2, s2, E, H, I, 1, pw.panels, pw.panels_bytes)
+        pw.alpha1_gate.copy_(a1)
+        pw.alpha1_up.copy_(a1)
+        pw.alpha2.copy_(a2)
+        out_g.zero_()
+        graph.replay()
+        ref = runner.MoeForward(runner.prepare_weights(w1n, w2n), p.M, wl.top_k, wl.E, 8)(
+            p.x, p.ids_d, p.w_d)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out_g), _bits(ref)), step
