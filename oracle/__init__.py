@@ -46,6 +46,7 @@ from .formats import (  # noqa: F401
     round_to_bf16,
     f64_to_bf16_bits,
 )
+from .mx import MX_BLOCK_SIZE, dequantize_mxfp4, e8m0_decode, quantize_mxfp4  # noqa: F401
 from .quant import SCALE_FIXED, SCALE_PER_GROUP, SCALE_PER_ROW, dequantize_nvfp4, quantize_nvfp4  # noqa: F401
 from .moe import (  # noqa: F401
     ACT_GEGLU,

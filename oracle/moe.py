@@ -337,7 +337,19 @@ def dense_loop_moe(a_q, a_sf, a_dec, weights, alpha1_gate, alpha1_up, alpha2, c2
     return (r.view(np.uint32) >> 16).astype(np.uint16)
 
 
-def expert_rows_forward_w16(x_bits, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate, alpha1_up, alpha2, act):
+def _dequantize_weights(q, sf, weight_format):
+    """float64 weights of one matrix: NVFP4 (E4M3 per 16) or MXFP4 (E8M0 per 32)."""
+    if weight_format == "nvfp4":
+        return dequantize_int(q, sf).astype(np.float64) * 2.0 ** -10
+    if weight_format == "mxfp4":
+        from .mx import dequantize_mxfp4
+
+        return dequantize_mxfp4(q, sf)
+    raise ValueError("unknown weight format")
+
+
+def expert_rows_forward_w16(x_bits, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate, alpha1_up, alpha2, act,
+                            weight_format="nvfp4"):
     """One expert in the NVFP4 weight-only mode on BF16 rows (FrostLowLatencyConfig, FP4
     weight-only paragraph: canonical E2M1 payloads with linear E4M3 K16 scales, BF16 input,
     pre-activation and intermediate rounding, BF16 expert outputs).
@@ -350,7 +362,10 @@ def expert_rows_forward_w16(x_bits, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate, alpha
       y     = bf16((sum_i h deq(W2)) * alpha2)       (BF16 expert output)
     Reading taken: the expert's FP32 global weight scale multiplies the sum before the rounding,
     as in the NVFP4 x NVFP4 mode.  Each product of a BF16 value and a dequantized weight is exact
-    in float64 and the sums are float64.  Returns dict(pre, pre_b, h, y) as float64 arrays.
+    in float64 and the sums are float64.  weight_format "mxfp4": E8M0 scales per 32 values
+    (the same paragraph: MXFP4 uses E8M0 K32 scales, dequantized in FP32; oracle.mx), with the
+    alphas as given (1 for MXFP4 weights, which carry no global scale).
+    Returns dict(pre, pre_b, h, y) as float64 arrays.
     """
     x = bf16_bits_to_f32(np.asarray(x_bits, np.uint16)).astype(np.float64)
     N1 = w1_q.shape[0]
@@ -358,8 +373,8 @@ def expert_rows_forward_w16(x_bits, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate, alpha
     gated = is_gated(act)
     if N1 != (2 * I if gated else I):
         raise ValueError("W1 rows do not match the activation")
-    w1 = dequantize_int(w1_q, w1_sf).astype(np.float64) * 2.0 ** -10
-    w2 = dequantize_int(w2_q, w2_sf).astype(np.float64) * 2.0 ** -10
+    w1 = _dequantize_weights(w1_q, w1_sf, weight_format)
+    w2 = _dequantize_weights(w2_q, w2_sf, weight_format)
     alpha_rows = np.full(N1, float(alpha1_up), dtype=np.float64)
     if gated:
         alpha_rows[:I] = float(alpha1_gate)
@@ -372,7 +387,8 @@ def expert_rows_forward_w16(x_bits, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate, alpha
 
 def fused_moe_w4a16(x_bits, weights, alpha1_gate, alpha1_up, alpha2, sorted_token_ids,
                     expert_ids, num_tokens_post_padded, token_to_row, topk_weights, top_k, block_m,
-                    act, routed_scaling_factor=1.0, out0_bits=None, do_finalize=True):
+                    act, routed_scaling_factor=1.0, out0_bits=None, do_finalize=True,
+                    weight_format="nvfp4"):
     """Plan-driven NVFP4 weight-only forward on BF16 activations: every valid plan row r of
     expert e takes token t = entry // top_k through expert_rows_forward_w16, then the same
     ordered combine as the NVFP4 mode (or the unfinalized triple).
@@ -392,7 +408,7 @@ def fused_moe_w4a16(x_bits, weights, alpha1_gate, alpha1_up, alpha2, sorted_toke
         w1q, w1s, w2q, w2s = get(e)
         rs = np.array(rs)
         o = expert_rows_forward_w16(xb[ent[rs] // top_k], w1q, w1s, w2q, w2s, alpha1_gate[e],
-                                    alpha1_up[e], alpha2[e], act)
+                                    alpha1_up[e], alpha2[e], act, weight_format)
         for i, r in enumerate(rs):
             res["y"][int(r)] = o["y"][i]
             res["pre"][int(r)] = o["pre"][i]
