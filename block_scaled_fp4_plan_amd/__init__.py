@@ -35,6 +35,8 @@ BFP4_SCALE_PER_GROUP = 1
 BFP4_SCALE_FIXED = 2
 BFP4_WEIGHTS_F32 = 0
 BFP4_WEIGHTS_BF16 = 1
+BFP4_FORMAT_NVFP4 = 0
+BFP4_FORMAT_MXFP4 = 1
 
 STATUS = {
     0: "BFP4_OK", -1: "BFP4_ERR_NULL", -2: "BFP4_ERR_SHAPE", -3: "BFP4_ERR_ALIGN",
@@ -47,7 +49,7 @@ EXPORTS = [
     "bfp4_moe_plan", "bfp4_quantize_workspace_size", "bfp4_quantize_nvfp4", "bfp4_moe_permute",
     "bfp4_panel_bytes", "bfp4_prepare_weights", "bfp4_workspace_size", "bfp4_fused_moe_nvfp4",
     "bfp4_moe_finalize", "bfp4_profile_begin", "bfp4_profile_end", "bfp4_workspace_size_w4a16",
-    "bfp4_fused_moe_w4a16",
+    "bfp4_fused_moe_w4a16", "bfp4_quantize_mxfp4", "bfp4_prepare_weights_mxfp4",
 ]
 
 
@@ -94,8 +96,10 @@ _sig("bfp4_fused_moe_nvfp4", _I,
 _sig("bfp4_moe_finalize", _I, [_P, _P, _I, _P, _I64, _I64, _I, _F, _P, _P])
 _sig("bfp4_workspace_size_w4a16", _SZ, [_I64, _I64, _I64, _I, _I, _I, _I])
 _sig("bfp4_fused_moe_w4a16", _I,
-     [_P, _I64, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I, _I,
-      _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
+     [_P, _I64, _P, _SZ, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I,
+      _I, _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
+_sig("bfp4_quantize_mxfp4", _I, [_P, _I64, _I64, _I64, _P, _P, _P])
+_sig("bfp4_prepare_weights_mxfp4", _I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _P, _SZ, _P])
 _sig("bfp4_profile_begin", _I, [_I, ctypes.c_char_p])
 _sig("bfp4_profile_end", _I, [ctypes.c_char_p, _SZ])
 
@@ -203,8 +207,20 @@ def bfp4_workspace_size_w4a16(M, H, I, top_k, num_local_experts, block_m, do_fin
     return _lib.bfp4_workspace_size_w4a16(M, H, I, top_k, num_local_experts, block_m, do_finalize)
 
 
-def bfp4_fused_moe_w4a16(x_bf16, row_stride, panels, panels_bytes, alpha1_gate, alpha1_up,
-                         alpha2, sorted_token_ids, expert_ids, num_tokens_post_padded,
+def bfp4_quantize_mxfp4(x_bf16, rows, cols, row_stride, q, sf, stream=None):
+    return _check(_lib.bfp4_quantize_mxfp4(_p(x_bf16), rows, cols, row_stride, _p(q), _p(sf),
+                                           _s(stream)), "bfp4_quantize_mxfp4")
+
+
+def bfp4_prepare_weights_mxfp4(w1_q, w1_sf, w2_q, w2_sf, num_local_experts, H, I, gated, panels,
+                               panels_bytes, stream=None):
+    return _check(_lib.bfp4_prepare_weights_mxfp4(
+        _p(w1_q), _p(w1_sf), _p(w2_q), _p(w2_sf), num_local_experts, H, I, gated, _p(panels),
+        panels_bytes, _s(stream)), "bfp4_prepare_weights_mxfp4")
+
+
+def bfp4_fused_moe_w4a16(x_bf16, row_stride, panels, panels_bytes, weight_format, alpha1_gate,
+                         alpha1_up, alpha2, sorted_token_ids, expert_ids, num_tokens_post_padded,
                          token_to_row, capacity, topk_weights, weights_dtype, M, H, I,
                          num_local_experts, top_k, block_m, act, routed_scaling_factor,
                          do_finalize, out, gemm2_out, debug, workspace, workspace_bytes,
@@ -214,7 +230,8 @@ def bfp4_fused_moe_w4a16(x_bf16, row_stride, panels, panels_bytes, alpha1_gate, 
         dbg = ctypes.byref(bfp4_debug(*(_p(debug.get(k)) for k in
                                         ("preact", "inter", "inter_q", "inter_sf"))))
     return _check(_lib.bfp4_fused_moe_w4a16(
-        _p(x_bf16), row_stride, _p(panels), panels_bytes, _p(alpha1_gate), _p(alpha1_up),
+        _p(x_bf16), row_stride, _p(panels), panels_bytes, weight_format, _p(alpha1_gate),
+        _p(alpha1_up),
         _p(alpha2), _p(sorted_token_ids), _p(expert_ids), _p(num_tokens_post_padded),
         _p(token_to_row), capacity, _p(topk_weights), weights_dtype, M, H, I, num_local_experts,
         top_k, block_m, act, routed_scaling_factor, do_finalize, _p(out), _p(gemm2_out), dbg,

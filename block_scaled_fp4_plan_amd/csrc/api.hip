@@ -374,8 +374,46 @@ size_t bfp4_workspace_size_w4a16(int64_t M, int64_t H, int64_t I, int top_k,
   return ws;
 }
 
+int bfp4_quantize_mxfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row_stride,
+                        uint8_t* q, uint8_t* sf, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 || row_stride < cols || row_stride % 8 ||
+      rows >= (1LL << 31))
+    return BFP4_ERR_SHAPE;
+  if (rows == 0) return BFP4_OK;
+  if (!x_bf16 || !q || !sf) return BFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16)) return BFP4_ERR_ALIGN;
+  size_t xb = (size_t)((rows - 1) * row_stride + cols) * 2;
+  if (overlaps(x_bf16, xb, q, rows * cols / 2) || overlaps(x_bf16, xb, sf, rows * cols / 32))
+    return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_quantize_mxfp4(x_bf16, rows, cols, row_stride, q, sf,
+                                        (hipStream_t)stream));
+}
+
+int bfp4_prepare_weights_mxfp4(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_t* w2_q,
+                               const uint8_t* w2_sf, int num_local_experts, int64_t H, int64_t I,
+                               int gated, void* panels, size_t panels_bytes, void* stream) {
+  if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
+  if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
+  if (!w1_q || !w1_sf || !w2_q || !w2_sf || !panels) return BFP4_ERR_NULL;
+  if (!aligned(w1_q, 16) || !aligned(w2_q, 16) || !aligned(panels, 16)) return BFP4_ERR_ALIGN;
+  if (panels_bytes < bfp4_panel_bytes(num_local_experts, H, I, gated)) return BFP4_ERR_WORKSPACE;
+  int dc = device_check();
+  if (dc) return dc;
+  int64_t N1 = gated ? 2 * I : I;
+  uint8_t* p1 = static_cast<uint8_t*>(panels);
+  uint8_t* p2 = p1 + panel_matrix_bytes(num_local_experts, N1, H);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e =
+      launch_prepare(w1_q, w1_sf, num_local_experts, N1, H, gated ? (int)I : 0, p1, s, true);
+  if (e != hipSuccess) return BFP4_ERR_LAUNCH;
+  return launched(launch_prepare(w2_q, w2_sf, num_local_experts, H, I, 0, p2, s, true));
+}
+
 int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void* panels,
-                         size_t panels_bytes, const float* alpha1_gate, const float* alpha1_up,
+                         size_t panels_bytes, int weight_format, const float* alpha1_gate,
+                         const float* alpha1_up,
                          const float* alpha2, const int32_t* sorted_token_ids,
                          const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                          const int32_t* token_to_row, size_t capacity, const void* topk_weights,
@@ -386,6 +424,7 @@ int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void*
                          size_t workspace_bytes, void* stream) {
   if (act < BFP4_ACT_SWIGLU || act > BFP4_ACT_IDENTITY) return BFP4_ERR_MODE;
   if (weights_dtype != BFP4_WEIGHTS_F32 && weights_dtype != BFP4_WEIGHTS_BF16) return BFP4_ERR_MODE;
+  if (weight_format != BFP4_FORMAT_NVFP4 && weight_format != BFP4_FORMAT_MXFP4) return BFP4_ERR_MODE;
   const size_t wsz = weights_dtype == BFP4_WEIGHTS_BF16 ? 2 : 4;
   const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
   if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
@@ -459,6 +498,7 @@ int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void*
   g.x = x_bf16;
   g.x_stride = row_stride;
   g.h = hbuf;
+  g.mx = weight_format == BFP4_FORMAT_MXFP4;
   hipStream_t s = (hipStream_t)stream;
   if (launch_moe_gemms_w16(g, s) != hipSuccess) return BFP4_ERR_LAUNCH;
   if (!do_finalize) return BFP4_OK;

@@ -83,7 +83,7 @@ __host__ __device__ inline PanelGeom panel_geom(int64_t rows, int64_t K) {
 // One thread per 16-byte piece of the panel of one matrix type.
 __global__ void prepare_kernel(const uint8_t* __restrict__ w_q, const uint8_t* __restrict__ w_sf,
                                int64_t rows, int64_t K, int64_t half_rows, int64_t total_pieces,
-                               uint8_t* __restrict__ panel) {
+                               uint8_t* __restrict__ panel, int mx) {
   int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= total_pieces) return;
   PanelGeom g = panel_geom(rows, K);
@@ -112,9 +112,15 @@ __global__ void prepare_kernel(const uint8_t* __restrict__ w_q, const uint8_t* _
     for (int jj = 0; jj < kSuperChunks; ++jj) {
       int64_t c = sc * kSuperChunks + jj;
       bool ok = c < g.nch;
-      const uint8_t* s = w_sf + row * (K / 16) + 4 * c + 2 * h;
-      b[2 * jj] = ok ? s[0] : 0u;
-      b[2 * jj + 1] = ok ? s[1] : 0u;
+      if (mx) {                 // one E8M0 scale per 32 values fills both 16-value slots
+        const uint8_t* s = w_sf + row * (K / 32) + 2 * c + h;
+        b[2 * jj] = ok ? s[0] : 0u;
+        b[2 * jj + 1] = ok ? s[0] : 0u;
+      } else {
+        const uint8_t* s = w_sf + row * (K / 16) + 4 * c + 2 * h;
+        b[2 * jj] = ok ? s[0] : 0u;
+        b[2 * jj + 1] = ok ? s[1] : 0u;
+      }
     }
     out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
     out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
@@ -985,6 +991,20 @@ __device__ __forceinline__ bf8_t decode8_bf16(uint32_t w, uint32_t sf_byte) {
   return __builtin_bit_cast(bf8_t, r);
 }
 
+// 8 E2M1 codes times one E8M0 scale (MXFP4) -> 8 BF16 values in four conversions: the scale's
+// code is the exponent field of an FP32 with the same bias (127), and the conversion applies only
+// the exponent of its scale operand.  Exact while the products stay in BF16's normal range
+// (scale codes 2..252).
+__device__ __forceinline__ bf8_t decode8_mx(uint32_t w, uint32_t e8m0) {
+  const float sc = __uint_as_float(e8m0 << 23);
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  return __builtin_bit_cast(bf8_t, r);
+}
+
 // GEMM1 epilogue of the weight-only mode: pre = acc * alpha (FP32, reported to dbg_pre), rounded
 // to BF16; the activation of the rounded values, rounded to BF16, is the intermediate h [cap, I]
 // (GEMM2's BF16 token operand).  Gated forms exchange halves between lanes l and l + 32 as the
@@ -1056,7 +1076,8 @@ __device__ __forceinline__ void epilogue_w16(const GemmArgs& a, const f32x16_t& 
   if (a.dbg_inter) *reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + ih) = w;
 }
 
-template <int FN, int EPI, int RING>
+// MX: the weight panels carry MXFP4 (E8M0 scale codes, duplicated into the 16-value slots)
+template <int FN, int EPI, int RING, bool MX>
 __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
   __shared__ int row_src[32];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1135,7 +1156,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
             const uint32_t wd = (s == 0) ? Wd[c][fn].x : (s == 1) ? Wd[c][fn].y
                                 : (s == 2) ? Wd[c][fn].z : Wd[c][fn].w;
             const uint32_t sb = (Sd[fn] >> (8 * (2 * c + (s >> 1)))) & 0xFFu;
-            const bf8_t Wv = decode8_bf16(wd, sb);
+            const bf8_t Wv = MX ? decode8_mx(wd, sb) : decode8_bf16(wd, sb);
             acc[fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Wv, Tv, acc[fn], 0, 0, 0);
           }
         }
@@ -1169,7 +1190,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
   }
 }
 
-template <int FN, int EPI>
+template <int FN, int EPI, bool MX>
 hipError_t launch_gemv16(const GemmArgs& a, int64_t cap_blocks, const char* name,
                          hipStream_t s) {
   const int64_t tasks = cap_blocks * a.n_nt;
@@ -1177,7 +1198,8 @@ hipError_t launch_gemv16(const GemmArgs& a, int64_t cap_blocks, const char* name
   const int64_t grid = tasks < max_wg ? tasks : max_wg;
   if (grid == 0) return hipSuccess;
   KernelTimer t(name, s);
-  hipLaunchKernelGGL((moe_gemv16_kernel<FN, EPI, 2>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((moe_gemv16_kernel<FN, EPI, 2, MX>), dim3((unsigned)grid), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -1244,12 +1266,12 @@ int64_t panel_matrix_bytes(int num_experts, int64_t rows, int64_t K) {
 }
 
 hipError_t launch_prepare(const uint8_t* w_q, const uint8_t* w_sf, int num_experts, int64_t rows,
-                          int64_t K, int gated_rows_half, uint8_t* panel, hipStream_t s) {
+                          int64_t K, int gated_rows_half, uint8_t* panel, hipStream_t s, bool mx) {
   int64_t pieces = panel_matrix_bytes(num_experts, rows, K) / 16;
   if (pieces == 0) return hipSuccess;
   KernelTimer t("prepare_weights", s);
   hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, w_q,
-                     w_sf, rows, K, (int64_t)gated_rows_half, pieces, panel);
+                     w_sf, rows, K, (int64_t)gated_rows_half, pieces, panel, (int)mx);
   return hipGetLastError();
 }
 
@@ -1387,7 +1409,8 @@ size_t moe_gemv_lds_bytes(int block_m, int64_t K) {
   return 64 * sizeof(int) + (size_t)rows_max * ((K / 2 + K / 16 + 15) & ~(int64_t)15);
 }
 
-hipError_t launch_moe_gemms_w16(const MoeGemmW16& w, hipStream_t s) {
+template <bool MX>
+hipError_t launch_moe_gemms_w16_fmt(const MoeGemmW16& w, hipStream_t s) {
   const MoeGemmProblem& p = w.p;
   const bool gated = p.act == BFP4_ACT_SWIGLU || p.act == BFP4_ACT_GEGLU;
   const int64_t N1 = gated ? 2 * p.I : p.I;
@@ -1446,12 +1469,17 @@ hipError_t launch_moe_gemms_w16(const MoeGemmW16& w, hipStream_t s) {
       "gemm1_gelu_w16_decode", "gemm1_relu_w16_decode", "gemm1_silu_w16_decode",
       "gemm1_identity_w16_decode"};
   const char* nm = kName[p.act];
-  hipError_t err = p.act == BFP4_ACT_SWIGLU ? launch_gemv16<FN, EPI_SWIGLU>(g1, cap_blocks, nm, s)
-                 : p.act == BFP4_ACT_RELU2  ? launch_gemv16<FN, EPI_RELU2>(g1, cap_blocks, nm, s)
-                 : p.act == BFP4_ACT_GEGLU  ? launch_gemv16<FN, EPI_GEGLU>(g1, cap_blocks, nm, s)
-                                            : launch_gemv16<FN, EPI_ACT>(g1, cap_blocks, nm, s);
+  hipError_t err =
+      p.act == BFP4_ACT_SWIGLU ? launch_gemv16<FN, EPI_SWIGLU, MX>(g1, cap_blocks, nm, s)
+      : p.act == BFP4_ACT_RELU2 ? launch_gemv16<FN, EPI_RELU2, MX>(g1, cap_blocks, nm, s)
+      : p.act == BFP4_ACT_GEGLU ? launch_gemv16<FN, EPI_GEGLU, MX>(g1, cap_blocks, nm, s)
+                                : launch_gemv16<FN, EPI_ACT, MX>(g1, cap_blocks, nm, s);
   if (err != hipSuccess) return err;
-  return launch_gemv16<FN, EPI_DOWN>(g2, cap_blocks, "gemm2_down_w16_decode", s);
+  return launch_gemv16<FN, EPI_DOWN, MX>(g2, cap_blocks, "gemm2_down_w16_decode", s);
+}
+
+hipError_t launch_moe_gemms_w16(const MoeGemmW16& w, hipStream_t s) {
+  return w.mx ? launch_moe_gemms_w16_fmt<true>(w, s) : launch_moe_gemms_w16_fmt<false>(w, s);
 }
 
 int64_t moe_gemm_max_tiles(int64_t cap, int block_m) {

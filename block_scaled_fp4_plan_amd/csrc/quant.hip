@@ -126,6 +126,37 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(
   }
 }
 
+// MXFP4 (E2M1 with one E8M0 scale per 32 values): one workgroup per row, one thread per block of
+// 32.  Shared exponent X = floor(log2(amax)) - 2 (2: the exponent of the largest E2M1 magnitude),
+// clamped to [-127, 127], scale code X + 127; amax 0 (or below the FP32 normal range, which BF16
+// inputs only reach with X < -127) gives code 0; elements are E2M1 of x * 2^-X (an exact
+// power-of-two product), nearest with ties to even, saturating at 6.
+__global__ __launch_bounds__(kQuantThreads) void quantize_mxfp4_kernel(
+    const uint16_t* __restrict__ x, int64_t cols, int64_t stride, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ sf) {
+  const int64_t r = blockIdx.x;
+  const uint16_t* xr = x + r * stride;
+  const int64_t nblk = cols >> 5;
+  for (int64_t b = threadIdx.x; b < nblk; b += kQuantThreads) {
+    float v[32];
+    load_block16(xr + b * 32, *reinterpret_cast<float(*)[16]>(v));
+    load_block16(xr + b * 32 + 16, *reinterpret_cast<float(*)[16]>(v + 16));
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+    int X = ebits == 0 ? -127 : ebits - 127 - 2;
+    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+    const uint32_t code = (amax == 0.0f || ebits == 0) ? 0u : (uint32_t)(X + 127);
+    const float inv = ldexpf(1.0f, -X);
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = quant8(v + 8 * k, inv);
+    *reinterpret_cast<uint4*>(q + r * (cols >> 1) + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    sf[r * nblk + b] = (uint8_t)code;
+  }
+}
+
 // Permute: one workgroup of 64 threads per capacity row.
 __global__ __launch_bounds__(64) void permute_kernel(const uint8_t* __restrict__ q,
                                                      const uint8_t* __restrict__ sf,
@@ -222,6 +253,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restric
 }
 
 }  // namespace
+
+hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride,
+                                uint8_t* q, uint8_t* sf, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  KernelTimer t("quantize_mxfp4", s);
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3((unsigned)rows), dim3(kQuantThreads), 0, s, x,
+                     cols, stride, q, sf);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, int mode,
                            int64_t group_rows, float fixed, uint8_t* q, uint8_t* sf, float* dec,

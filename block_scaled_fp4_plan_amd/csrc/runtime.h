@@ -26,6 +26,8 @@ hipError_t launch_plan(const int32_t* ids, int64_t A, int top_k, int num_experts
 bool plan_uses_small_kernel(int64_t A);
 int64_t plan_chunks(int64_t A);
 
+hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride,
+                                uint8_t* q, uint8_t* sf, hipStream_t s);
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, int mode,
                            int64_t group_rows, float fixed, uint8_t* q, uint8_t* sf, float* dec,
                            void* ws, hipStream_t s);
@@ -39,8 +41,11 @@ hipError_t launch_finalize(const uint16_t* y, const void* w, bool w_bf16, const 
 
 // Weight panels: see gemm.hip for the layout.
 int64_t panel_matrix_bytes(int num_experts, int64_t rows, int64_t K);
+// mx: w_sf holds one E8M0 scale per 32 values (MXFP4), each written to both 16-value slots of
+// the panel; otherwise one E4M3 scale per 16 values (NVFP4)
 hipError_t launch_prepare(const uint8_t* w_q, const uint8_t* w_sf, int num_experts, int64_t rows,
-                          int64_t K, int gated_rows_half, uint8_t* panel, hipStream_t s);
+                          int64_t K, int gated_rows_half, uint8_t* panel, hipStream_t s,
+                          bool mx = false);
 
 struct MoeGemmProblem {
   const uint8_t* a_q;
@@ -77,6 +82,7 @@ struct MoeGemmW16 {
   const uint16_t* x;    // [M rows, stride x_stride] BF16 activations
   int64_t x_stride;
   uint16_t* h;          // [cap, I] BF16 intermediate
+  bool mx;              // panels hold MXFP4 (E8M0 scales per 32) instead of NVFP4
 };
 hipError_t launch_moe_gemms_w16(const MoeGemmW16& w, hipStream_t s);
 int64_t moe_gemm_max_tiles(int64_t cap, int block_m);

@@ -8,6 +8,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (
+    BFP4_FORMAT_MXFP4,
+    BFP4_FORMAT_NVFP4,
     BFP4_WEIGHTS_BF16,
     BFP4_WEIGHTS_F32,
     BFP4_ACT_RELU2,
@@ -22,6 +24,8 @@ from . import (
     bfp4_plan_capacity,
     bfp4_plan_workspace_size,
     bfp4_prepare_weights,
+    bfp4_prepare_weights_mxfp4,
+    bfp4_quantize_mxfp4,
     bfp4_quantize_nvfp4,
     bfp4_quantize_workspace_size,
     bfp4_workspace_size,
@@ -68,6 +72,34 @@ class PreparedWeights:
     H: int
     I: int
     gated: bool
+    fmt: int = 0              # BFP4_FORMAT_NVFP4 or BFP4_FORMAT_MXFP4
+
+
+def prepare_weights_mxfp4(w1_bf16, w2_bf16, gated=True, keep_linear=False, stream=None):
+    """MXFP4 (E8M0 scales per 32 values) of BF16 stacks W1 [E, N1, H] and W2 [E, H, I], then the
+    panel layout, for the weight-only mode (alphas of 1).  Returns PreparedWeights (and the
+    linear MXFP4 tensors when keep_linear)."""
+    E, N1, H = w1_bf16.shape
+    I = w2_bf16.shape[2]
+    dev = w1_bf16.device
+    q1 = torch.empty((E * N1, H // 2), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((E * N1, H // 32), dtype=torch.uint8, device=dev)
+    q2 = torch.empty((E * H, I // 2), dtype=torch.uint8, device=dev)
+    s2 = torch.empty((E * H, I // 32), dtype=torch.uint8, device=dev)
+    w1 = w1_bf16.reshape(E * N1, H)
+    w2 = w2_bf16.reshape(E * H, I)
+    bfp4_quantize_mxfp4(w1, E * N1, H, w1.stride(0), q1, s1, stream)
+    bfp4_quantize_mxfp4(w2, E * H, I, w2.stride(0), q2, s2, stream)
+    nb = bfp4_panel_bytes(E, H, I, int(gated))
+    panels = _bytes(nb, dev)
+    bfp4_prepare_weights_mxfp4(q1, s1, q2, s2, E, H, I, int(gated), panels, nb, stream)
+    ones = torch.ones(E, dtype=torch.float32, device=dev)
+    pw = PreparedWeights(panels, nb, ones, ones.clone(), ones.clone(), E, H, I, gated,
+                         BFP4_FORMAT_MXFP4)
+    if keep_linear:
+        return pw, (q1.reshape(E, N1, H // 2), s1.reshape(E, N1, H // 32),
+                    q2.reshape(E, H, I // 2), s2.reshape(E, H, I // 32))
+    return pw
 
 
 def prepare_weights(w1_bf16, w2_bf16, gated=True, keep_linear=False, stream=None):
@@ -121,6 +153,8 @@ class MoeForward:
             act = BFP4_ACT_SWIGLU if weights.gated else BFP4_ACT_RELU2
         if (act in GATED_ACTS) != bool(weights.gated):
             raise ValueError("activation %d does not match the weights' gating" % act)
+        if weights.fmt != BFP4_FORMAT_NVFP4:
+            raise ValueError("the NVFP4 x NVFP4 forward needs NVFP4 weights")
         self.act = act
         self.w = weights
         self.M, self.top_k, self.E, self.block_m = M, top_k, num_experts, block_m
@@ -196,7 +230,8 @@ class MoeForwardW4A16:
         if out is None and self.do_finalize:
             out = torch.zeros((M, H), dtype=torch.bfloat16, device=x_bf16.device)
         pl = self.plan
-        bfp4_fused_moe_w4a16(x_bf16, x_bf16.stride(0), w.panels, w.panels_bytes, w.alpha1_gate,
+        bfp4_fused_moe_w4a16(x_bf16, x_bf16.stride(0), w.panels, w.panels_bytes, w.fmt,
+                             w.alpha1_gate,
                              w.alpha1_up, w.alpha2, pl.sorted_token_ids, pl.expert_ids,
                              pl.num_tokens_post_padded, pl.token_to_row, pl.capacity,
                              topk_weights, weights_dtype(topk_weights), M, H, I,

@@ -69,6 +69,10 @@ typedef enum { BFP4_SCALE_PER_ROW = 0, BFP4_SCALE_PER_GROUP = 1, BFP4_SCALE_FIXE
 /* Routing weights [cuDNN, routing weights bullet: unpacked FP32 or BF16]: FP32 values, or BF16
  * bit patterns, which the combine uses as their exact FP32 values. */
 typedef enum { BFP4_WEIGHTS_F32 = 0, BFP4_WEIGHTS_BF16 = 1 } bfp4_weights_dtype;
+/* Expert weight formats of the weight-only mode [Frost, FP4 weight-only paragraph]: NVFP4 (E2M1
+ * with linear E4M3 scales per 16 values and one FP32 scale per expert) or MXFP4 (E2M1 with
+ * UE8M0 power-of-two scales per 32 values, 127 encoding 1.0 [vLLM align_moe_weights_for_fi]). */
+typedef enum { BFP4_FORMAT_NVFP4 = 0, BFP4_FORMAT_MXFP4 = 1 } bfp4_weight_format;
 
 /* Human-readable name of a status code (static storage). */
 const char* bfp4_status_string(int status);
@@ -237,14 +241,41 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
  *   y[k]   = bf16((sum_i h[i] * W2_e[k,i]) * alpha2[e]);
  * then the combine (or the unfinalized triple) exactly as bfp4_fused_moe_nvfp4.
  * Arguments as bfp4_fused_moe_nvfp4, except: x_bf16 [M rows, row_stride >= H elements,
- * row_stride % 8 == 0] BF16 activations in place of a_q/a_sf/a_dec, no c2; debug->preact gets
+ * row_stride % 8 == 0] BF16 activations in place of a_q/a_sf/a_dec, no c2; weight_format
+ * (bfp4_weight_format) names how the panels were prepared (bfp4_prepare_weights or
+ * bfp4_prepare_weights_mxfp4; MXFP4 is exact for scale codes 2..252, where every product stays
+ * in BF16's normal range; another value gives BFP4_ERR_MODE); debug->preact gets
  * pre (FP32, before the BF16 rounding), debug->inter h (BF16); inter_q/inter_sf are unused.
  * workspace: >= bfp4_workspace_size_w4a16(...) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------------------------------- */
+/* ----------------------------------------------------------------------------------------------
+ * MXFP4 quantization of BF16 rows [Frost, FP4 weight-only paragraph: E8M0 K32 scales;
+ * prepare_mxfp4_weight_only_weights: linear E8M0 scales per 32 K values; vLLM
+ * align_moe_weights_for_fi: UE8M0 block scales, 127 = 1.0].  The recipe is not on the pages;
+ * reading taken (the OCP microscaling one): per 32 consecutive values of a row, with amax their
+ * largest magnitude, the shared exponent X = floor(log2(amax)) - 2 (clamped to [-127, 127]; amax
+ * 0 or below the FP32 normal range gives code 0) is stored as the UE8M0 code X + 127, and each
+ * value as the E2M1 code nearest to x * 2^-X (ties to the even code, saturating at 6, sign bit
+ * copied).  Packing as NVFP4: two codes per byte, even value in the low nibble.
+ *   x_bf16 [rows, row_stride >= cols] (16-byte aligned, row_stride % 8 == 0), cols % 32 == 0;
+ *   q [rows, cols/2] (16-byte aligned), sf [rows, cols/32]; q and sf must not overlap x.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_quantize_mxfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row_stride,
+                        uint8_t* q, uint8_t* sf, void* stream);
+
+/* Panels from linear MXFP4 weights (bfp4_quantize_mxfp4 of each expert matrix's rows): W1
+ * [E, N1, H/2] + [E, N1, H/32], W2 [E, H, I/2] + [E, H, I/32]; the same panel layout and size as
+ * bfp4_prepare_weights (each UE8M0 code fills the two 16-value scale slots).  For
+ * bfp4_fused_moe_w4a16 with BFP4_FORMAT_MXFP4 (alphas of 1). */
+int bfp4_prepare_weights_mxfp4(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_t* w2_q,
+                               const uint8_t* w2_sf, int num_local_experts, int64_t H, int64_t I,
+                               int gated, void* panels, size_t panels_bytes, void* stream);
+
 size_t bfp4_workspace_size_w4a16(int64_t M, int64_t H, int64_t I, int top_k,
                                  int num_local_experts, int block_m, int do_finalize);
 int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void* panels,
-                         size_t panels_bytes, const float* alpha1_gate, const float* alpha1_up,
+                         size_t panels_bytes, int weight_format, const float* alpha1_gate,
+                         const float* alpha1_up,
                          const float* alpha2, const int32_t* sorted_token_ids,
                          const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                          const int32_t* token_to_row, size_t capacity, const void* topk_weights,

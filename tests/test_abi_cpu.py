@@ -208,7 +208,8 @@ def test_finalize_and_prepare_validation():
 
 def _w16(**kw):
     args = dict(x_bf16=A, row_stride=256, panels=A + (3 << 16),
-                panels_bytes=bf.bfp4_panel_bytes(8, 256, 128, 1), alpha1_gate=A + (40 << 16),
+                panels_bytes=bf.bfp4_panel_bytes(8, 256, 128, 1), weight_format=0,
+                alpha1_gate=A + (40 << 16),
                 alpha1_up=A + (41 << 16), alpha2=A + (42 << 16), sorted_token_ids=A + (43 << 16),
                 expert_ids=A + (44 << 16), num_tokens_post_padded=A + (45 << 16),
                 token_to_row=A + (46 << 16), capacity=88, topk_weights=A + (47 << 16),
@@ -236,6 +237,31 @@ def test_w4a16_validation():
     assert _w16(workspace_bytes=64) == "BFP4_ERR_WORKSPACE"
     assert _w16(out=A + 64) == "BFP4_ERR_OVERLAP"                 # out over x
     assert _w16(capacity=80) == "BFP4_ERR_CAPACITY"
+    assert _w16(weight_format=2) == "BFP4_ERR_MODE"
+
+
+def test_mxfp4_quantize_and_prepare_validation():
+    def quant(**kw):
+        args = dict(x_bf16=A, rows=4, cols=256, row_stride=256, q=A + (1 << 16), sf=A + (2 << 16),
+                    stream=0)
+        args.update(kw)
+        with pytest.raises(Bfp4Error) as ei:
+            bf.bfp4_quantize_mxfp4(**args)
+        return bf.STATUS[ei.value.status]
+
+    assert quant(cols=48) == "BFP4_ERR_SHAPE"                   # multiple of 32
+    assert quant(row_stride=200) == "BFP4_ERR_SHAPE"
+    assert quant(q=A + 8) == "BFP4_ERR_ALIGN"
+    assert quant(sf=None) == "BFP4_ERR_NULL"
+    assert quant(q=A + 64) == "BFP4_ERR_OVERLAP"
+    if NO_GPU:
+        assert quant() == "BFP4_ERR_DEVICE"
+    with pytest.raises(Bfp4Error) as ei:
+        bf.bfp4_prepare_weights_mxfp4(A, A, A, A, 1, 256, 100, 1, A, 1 << 20, 0)
+    assert bf.STATUS[ei.value.status] == "BFP4_ERR_SHAPE"
+    with pytest.raises(Bfp4Error) as ei:
+        bf.bfp4_prepare_weights_mxfp4(A, A, A, A, 1, 256, 128, 1, A, 100, 0)
+    assert bf.STATUS[ei.value.status] == "BFP4_ERR_WORKSPACE"
 
 
 @cpu_only

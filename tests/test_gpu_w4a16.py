@@ -113,3 +113,88 @@ def test_w4a16_strided_rows_and_nothing_local():
     fwd_off(p.x, p.ids_d, p.w_d, out=out_c)
     torch.cuda.synchronize()
     assert torch.equal(out_c.view(torch.int16), out0.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- MXFP4 weights
+
+def _gpu_mx(bits):
+    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    R, C = x.shape
+    q = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((R, C // 32), dtype=torch.uint8, device="cuda")
+    bf.bfp4_quantize_mxfp4(x, R, C, C, q, sf)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sf.cpu().numpy()
+
+
+def test_mxfp4_quantize_bit_exact():
+    """Every finite BF16 value (rows of 128: one sign and two exponents per row, then shuffled),
+    all-zero and signed-zero blocks, BF16 subnormals next to normal values: GPU codes and UE8M0
+    scales equal the oracle's."""
+    say("mxfp4 quantize")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = bf16_bits_to_f32(bits)
+    bits = np.where(np.isfinite(v), bits, 0).astype(np.uint16)
+    rng = np.random.default_rng(1)
+    edge = np.zeros((4, 128), np.uint16)
+    edge[1, :] = 0x8000                                   # negative zeros
+    edge[2, :32] = 0x0001                                 # BF16 subnormals only
+    edge[2, 32:64] = np.array([0x0001, 0x3F80] * 16)      # subnormals beside 1.0
+    edge[3, :] = 0x7F7F                                   # largest finite BF16
+    for rows in (bits.reshape(512, 128), rng.permutation(bits).reshape(512, 128), edge):
+        q, sf = _gpu_mx(rows)
+        oq, osf = oracle.quantize_mxfp4(bf16_bits_to_f32(rows))
+        assert np.array_equal(sf, osf)
+        assert np.array_equal(q, oq)
+
+
+def _mx_expert(p, e):
+    key = ("mx", e)
+    if key not in p._host_w:
+        b1, b2 = p.host_weight_bits(e)
+        q1, s1 = oracle.quantize_mxfp4(bf16_bits_to_f32(b1))
+        q2, s2 = oracle.quantize_mxfp4(bf16_bits_to_f32(b2))
+        p._host_w[key] = (q1, s1, q2, s2)
+    return p._host_w[key]
+
+
+MX_CASES = [("tiny", 8), ("tiny_geglu", 16), ("decode_ll", 8), ("skewed_relu2", 16),
+            ("decode_m2", 8)]
+
+
+@pytest.mark.parametrize("name,bm", MX_CASES, ids=["%s-bm%d" % c for c in MX_CASES])
+def test_w4a16_mxfp4_matches_oracle(name, bm):
+    wl = WL[name]
+    M = 2 if name == "decode_m2" else None
+    say("w4a16 mxfp4", name, "block_m", bm)
+    p = Problem(wl, M=M)
+    k = wl.top_k
+    pw, lin = runner.prepare_weights_mxfp4(p.w1, p.w2, gated=wl.gated, keep_linear=True)
+    fwd = runner.MoeForwardW4A16(pw, p.M, k, wl.E, bm, wl.local_offset, act=wl.act_code)
+    cap = fwd.plan.capacity
+    dbg = dict(preact=torch.full((cap, wl.N1), float("nan"), device="cuda"),
+               inter=torch.zeros((cap, wl.I), dtype=torch.bfloat16, device="cuda"))
+    out = fwd(p.x, p.ids_d, p.w_d, debug=dbg)
+    torch.cuda.synchronize()
+    out_bits = np_bits(out)
+    srt, eids, P, ttr = p.oracle_plan(bm)
+    experts = sorted(set(int(e) for e in eids[:P // bm]))
+    for e in experts[:3]:                       # the GPU's MXFP4 weights are the oracle's
+        q1, s1, q2, s2 = _mx_expert(p, e)
+        assert np.array_equal(lin[0][e].cpu().numpy(), q1)
+        assert np.array_equal(lin[1][e].cpu().numpy(), s1)
+        assert np.array_equal(lin[2][e].cpu().numpy(), q2)
+        assert np.array_equal(lin[3][e].cpu().numpy(), s2)
+    ones = np.ones(wl.n_local, np.float32)
+    res = oracle.fused_moe_w4a16(p.x_bits, lambda e: _mx_expert(p, e), ones, ones, ones, srt, eids,
+                                 P, ttr, p.w, k, bm, wl.act_code, weight_format="mxfp4")
+    rows = sorted(res["pre"].keys())
+    e_pre = rel_fro(dbg["preact"].cpu().numpy()[rows], np.stack([res["pre"][r] for r in rows]))
+    e_h = rel_fro(bf16_bits_to_f32(np_bits(dbg["inter"])[rows]),
+                  np.stack([res["h"][r] for r in rows]))
+    e_out = rel_fro(bf16_bits_to_f32(out_bits), bf16_bits_to_f32(res["out"]).astype(np.float64))
+    say("pre %.3e  h %.3e  out %.3e" % (e_pre, e_h, e_out))
+    assert e_pre <= 1e-5
+    assert e_h <= 2e-3
+    assert e_out <= 2e-2
+    assert np.any(out_bits != 0)
