@@ -198,10 +198,10 @@ def time_graph(s, steps, warmup):
     return dt
 
 
-def time_w4a16(s, steps, warmup):
-    """The decode step in the NVFP4 weight-only mode on BF16 activations (routing plan + fused
-    weight-only experts + finalize, no activation quantization), on the same inputs and rotating
-    weight replicas: step time of an uninstrumented pass, then the weight-only GEMM1's average
+def time_w4a16(s, steps, warmup, mxfp4=False):
+    """The decode step in the weight-only mode on BF16 activations (routing plan + fused
+    weight-only experts + finalize, no activation quantization) with NVFP4 or MXFP4 weights, on
+    the same inputs and rotating weight replicas: step time of an uninstrumented pass, then the weight-only GEMM1's average
     launch duration from a pass with HIP events around it."""
     import torch
 
@@ -209,10 +209,17 @@ def time_w4a16(s, steps, warmup):
     from block_scaled_fp4_plan_amd import runner
 
     wl = s.wl
-    f = runner.MoeForwardW4A16(s.weights[0], wl.M, wl.top_k, wl.E, wl.block_m, wl.local_offset)
+    weights = s.weights
+    if mxfp4:                # the same BF16 weights as MXFP4 (E8M0 per 32), same replica count
+        pw = runner.prepare_weights_mxfp4(s.w1, s.w2, gated=wl.gated)
+        weights = [pw] + [runner.PreparedWeights(pw.panels.clone(), pw.panels_bytes,
+                                                 pw.alpha1_gate, pw.alpha1_up, pw.alpha2,
+                                                 pw.num_local_experts, pw.H, pw.I, pw.gated,
+                                                 pw.fmt) for _ in range(len(s.weights) - 1)]
+    f = runner.MoeForwardW4A16(weights[0], wl.M, wl.top_k, wl.E, wl.block_m, wl.local_offset)
 
     def step(i):
-        f(s.x, s.ids_d, s.w_d, out=s.out, weights=s.weights[i % len(s.weights)])
+        f(s.x, s.ids_d, s.w_d, out=s.out, weights=weights[i % len(weights)])
 
     for i in range(warmup):
         step(i)
@@ -227,10 +234,15 @@ def time_w4a16(s, steps, warmup):
         step(i)
     torch.cuda.synchronize()
     g1_ms, _, name = kernel_ms(bf.bfp4_profile_end()[1], "gemm1")
-    q = NVFP4_BYTES
+    # algorithmic bytes: the weights in their format (MXFP4: one scale byte per 32 values; the
+    # panels store it in both 16-value slots, so the kernel moves 1/32 B per value more)
+    q = NVFP4_BYTES if not mxfp4 else 0.5 + 1.0 / 32
     g1_bytes = (s.touched * wl.N1 * wl.H * q + wl.M * wl.H * 2 + s.A * wl.I * 2)
     ach = g1_bytes / (g1_ms * 1e-3) / 1e9
+    del weights, f
+    torch.cuda.empty_cache()
     return {"value": wl.M / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "weights": "MXFP4 (E8M0 per 32)" if mxfp4 else "NVFP4 (E4M3 per 16)",
             "roofline": {"bound": "hbm", "kernel": name, "achieved": ach, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": g1_bytes,
                          "avg_launch_ms": g1_ms}}
@@ -432,6 +444,7 @@ def main():
             result["config"]["graph_replay_tokens_per_s"] = wl.M / (gdt / args.steps)
         if not args.no_w4a16:
             result["w4a16_decode"] = time_w4a16(s, args.steps, args.warmup)
+            result["w4a16_mxfp4_decode"] = time_w4a16(s, args.steps, args.warmup, mxfp4=True)
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(s)
         del s
