@@ -117,12 +117,14 @@ def test_w4a16_strided_rows_and_nothing_local():
 
 # ----------------------------------------------------------------------------- MXFP4 weights
 
-def _gpu_mx(bits):
-    x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
-    R, C = x.shape
+def _gpu_mx(bits, pad=0):
+    R, C = bits.shape
+    wide = np.zeros((R, C + pad), np.uint16)
+    wide[:, :C] = bits
+    x = torch.from_numpy(wide.view(np.int16)).view(torch.bfloat16).cuda()[:, :C]
     q = torch.empty((R, C // 2), dtype=torch.uint8, device="cuda")
     sf = torch.empty((R, C // 32), dtype=torch.uint8, device="cuda")
-    bf.bfp4_quantize_mxfp4(x, R, C, C, q, sf)
+    bf.bfp4_quantize_mxfp4(x, R, C, x.stride(0), q, sf)
     torch.cuda.synchronize()
     return q.cpu().numpy(), sf.cpu().numpy()
 
@@ -141,8 +143,9 @@ def test_mxfp4_quantize_bit_exact():
     edge[2, :32] = 0x0001                                 # BF16 subnormals only
     edge[2, 32:64] = np.array([0x0001, 0x3F80] * 16)      # subnormals beside 1.0
     edge[3, :] = 0x7F7F                                   # largest finite BF16
-    for rows in (bits.reshape(512, 128), rng.permutation(bits).reshape(512, 128), edge):
-        q, sf = _gpu_mx(rows)
+    for rows, pad in ((bits.reshape(512, 128), 0), (rng.permutation(bits).reshape(512, 128), 0),
+                      (edge, 0), (rng.permutation(bits).reshape(256, 256), 40)):
+        q, sf = _gpu_mx(rows, pad)                 # pad: rows read through a wider row stride
         oq, osf = oracle.quantize_mxfp4(bf16_bits_to_f32(rows))
         assert np.array_equal(sf, osf)
         assert np.array_equal(q, oq)
