@@ -230,25 +230,6 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------------------------
- * NVFP4 weight-only forward on BF16 activations [Frost, FP4 weight-only paragraph: canonical
- * E2M1 weights with linear E4M3 K16 scales and one FP32 scale per expert; BF16 input,
- * pre-activation and intermediate rounding; BF16 expert outputs; the same combine].  Decode-sized
- * plans only (block_m <= 32, else BFP4_ERR_BLOCK_M).
- * Per valid plan row r (entry f < M*top_k, token t = f / top_k, local expert e of r's block):
- *   pre[n] = (sum_h x[t,h] * W1_e[n,h]) * alpha1_{gate|up}[e]     (FP32 accumulate of exact
- *            products: BF16 x E2M1 x E4M3), then p[n] = bf16(pre[n]);
- *   h[i]   = bf16(act(p[i]) * p[I+i])  (gated)  or  bf16(act(p[i]))  (one projection);
- *   y[k]   = bf16((sum_i h[i] * W2_e[k,i]) * alpha2[e]);
- * then the combine (or the unfinalized triple) exactly as bfp4_fused_moe_nvfp4.
- * Arguments as bfp4_fused_moe_nvfp4, except: x_bf16 [M rows, row_stride >= H elements,
- * row_stride % 8 == 0] BF16 activations in place of a_q/a_sf/a_dec, no c2; weight_format
- * (bfp4_weight_format) names how the panels were prepared (bfp4_prepare_weights or
- * bfp4_prepare_weights_mxfp4; MXFP4 is exact for scale codes 2..252, where every product stays
- * in BF16's normal range; another value gives BFP4_ERR_MODE); debug->preact gets
- * pre (FP32, before the BF16 rounding), debug->inter h (BF16); inter_q/inter_sf are unused.
- * workspace: >= bfp4_workspace_size_w4a16(...) bytes, 256-byte aligned.
- * ---------------------------------------------------------------------------------------------- */
-/* ----------------------------------------------------------------------------------------------
  * MXFP4 quantization of BF16 rows [Frost, FP4 weight-only paragraph: E8M0 K32 scales;
  * prepare_mxfp4_weight_only_weights: linear E8M0 scales per 32 K values; vLLM
  * align_moe_weights_for_fi: UE8M0 block scales, 127 = 1.0].  The recipe is not on the pages;
@@ -271,6 +252,26 @@ int bfp4_prepare_weights_mxfp4(const uint8_t* w1_q, const uint8_t* w1_sf, const 
                                const uint8_t* w2_sf, int num_local_experts, int64_t H, int64_t I,
                                int gated, void* panels, size_t panels_bytes, void* stream);
 
+/* ----------------------------------------------------------------------------------------------
+ * FP4 weight-only forward on BF16 activations, NVFP4 or MXFP4 weights [Frost, FP4 weight-only
+ * paragraph: canonical E2M1 weights with linear E4M3 K16 scales and one FP32 scale per expert
+ * (NVFP4) or E8M0 K32 scales (MXFP4); BF16 input,
+ * pre-activation and intermediate rounding; BF16 expert outputs; the same combine].  Decode-sized
+ * plans only (block_m <= 32, else BFP4_ERR_BLOCK_M).
+ * Per valid plan row r (entry f < M*top_k, token t = f / top_k, local expert e of r's block):
+ *   pre[n] = (sum_h x[t,h] * W1_e[n,h]) * alpha1_{gate|up}[e]     (FP32 accumulate of exact
+ *            products: BF16 x E2M1 x E4M3), then p[n] = bf16(pre[n]);
+ *   h[i]   = bf16(act(p[i]) * p[I+i])  (gated)  or  bf16(act(p[i]))  (one projection);
+ *   y[k]   = bf16((sum_i h[i] * W2_e[k,i]) * alpha2[e]);
+ * then the combine (or the unfinalized triple) exactly as bfp4_fused_moe_nvfp4.
+ * Arguments as bfp4_fused_moe_nvfp4, except: x_bf16 [M rows, row_stride >= H elements,
+ * row_stride % 8 == 0] BF16 activations in place of a_q/a_sf/a_dec, no c2; weight_format
+ * (bfp4_weight_format) names how the panels were prepared (bfp4_prepare_weights or
+ * bfp4_prepare_weights_mxfp4; MXFP4 is exact for scale codes 2..252, where every product stays
+ * in BF16's normal range; another value gives BFP4_ERR_MODE); debug->preact gets
+ * pre (FP32, before the BF16 rounding), debug->inter h (BF16); inter_q/inter_sf are unused.
+ * workspace: >= bfp4_workspace_size_w4a16(...) bytes, 256-byte aligned.
+ * ---------------------------------------------------------------------------------------------- */
 size_t bfp4_workspace_size_w4a16(int64_t M, int64_t H, int64_t I, int top_k,
                                  int num_local_experts, int block_m, int do_finalize);
 int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void* panels,
@@ -301,9 +302,11 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int w
  * Kernel timing with HIP events (measurement support, off by default).
  * bfp4_profile_begin(capacity, name_prefix) creates `capacity` event pairs and starts recording
  * one pair around every kernel the library launches whose name starts with name_prefix (host
- * string; NULL or "" for every kernel): plan_*, quantize_*, permute, prepare_weights, tile_list,
- * decode_tokens, gemm1_<activation>_{decode,prefill} (activation swiglu, relu2, geglu, gelu, relu,
- * silu or identity), gemm2_down_{decode,prefill}, finalize.  The timer is process-wide state:
+ * string; NULL or "" for every kernel): plan_*, quantize_* (quantize_rows, quantize_rows_group,
+ * quantize_rows_fixed, quantize_mxfp4, with fill_u32 and group_amax), permute, prepare_weights,
+ * tile_list, decode_tokens, gemm1_<activation>_{decode,prefill} (activation swiglu, relu2, geglu,
+ * gelu, relu, silu or identity), gemm2_down_{decode,prefill}, the weight-only
+ * gemm1_<activation>_w16_decode and gemm2_down_w16_decode, finalize.  The timer is process-wide state:
  * record from one host thread at a time, and not while a stream is being captured.
  * bfp4_profile_end() stops recording, waits for the
  * recorded events and writes one line per kernel name, "name count total_ms", into buf
