@@ -295,17 +295,20 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
     if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16) || !aligned(debug->inter_q, 8))
       return BFP4_ERR_ALIGN;
   }
-  if (do_finalize) {
-    size_t ob = (size_t)M * H * 2;
+  {
+    // the destination (out [M, H] when finalizing, else gemm2_out [capacity, H]) overlaps no
+    // input and not the workspace
+    const uint16_t* d = do_finalize ? out : gemm2_out;
+    const size_t ob = (do_finalize ? (size_t)M : capacity) * (size_t)H * 2;
     const size_t nl = (size_t)num_local_experts * 4, mk = (size_t)M * top_k * 4;
-    if (overlaps(out, ob, a_q, M * H / 2) || overlaps(out, ob, a_sf, M * H / 16) ||
-        overlaps(out, ob, a_dec, M * 4) || overlaps(out, ob, panels, panels_bytes) ||
-        overlaps(out, ob, alpha1_gate, nl) || overlaps(out, ob, alpha1_up, nl) ||
-        overlaps(out, ob, alpha2, nl) || overlaps(out, ob, sorted_token_ids, capacity * 4) ||
-        overlaps(out, ob, expert_ids, capacity / block_m * 4) ||
-        overlaps(out, ob, num_tokens_post_padded, 4) || overlaps(out, ob, token_to_row, mk) ||
-        overlaps(out, ob, topk_weights, (size_t)M * top_k * wsz) ||
-        overlaps(out, ob, workspace, ws))
+    if (overlaps(d, ob, a_q, M * H / 2) || overlaps(d, ob, a_sf, M * H / 16) ||
+        overlaps(d, ob, a_dec, M * 4) || overlaps(d, ob, panels, panels_bytes) ||
+        overlaps(d, ob, alpha1_gate, nl) || overlaps(d, ob, alpha1_up, nl) ||
+        overlaps(d, ob, alpha2, nl) || overlaps(d, ob, sorted_token_ids, capacity * 4) ||
+        overlaps(d, ob, expert_ids, capacity / block_m * 4) ||
+        overlaps(d, ob, num_tokens_post_padded, 4) || overlaps(d, ob, token_to_row, mk) ||
+        overlaps(d, ob, topk_weights, (size_t)M * top_k * wsz) ||
+        overlaps(d, ob, workspace, ws))
       return BFP4_ERR_OVERLAP;
   }
   int dc = device_check();
@@ -453,17 +456,20 @@ int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void*
   if (debug) {
     if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16)) return BFP4_ERR_ALIGN;
   }
-  if (do_finalize) {
-    size_t ob = (size_t)M * H * 2;
+  {
+    // the destination (out [M, H] when finalizing, else gemm2_out [capacity, H]) overlaps no
+    // input and not the workspace
+    const uint16_t* d = do_finalize ? out : gemm2_out;
+    const size_t ob = (do_finalize ? (size_t)M : capacity) * (size_t)H * 2;
     const size_t nl = (size_t)num_local_experts * 4, mk = (size_t)M * top_k * 4;
     const size_t xb = (size_t)((M - 1) * row_stride + H) * 2;
-    if (overlaps(out, ob, x_bf16, xb) || overlaps(out, ob, panels, panels_bytes) ||
-        overlaps(out, ob, alpha1_gate, nl) || overlaps(out, ob, alpha1_up, nl) ||
-        overlaps(out, ob, alpha2, nl) || overlaps(out, ob, sorted_token_ids, capacity * 4) ||
-        overlaps(out, ob, expert_ids, capacity / block_m * 4) ||
-        overlaps(out, ob, num_tokens_post_padded, 4) || overlaps(out, ob, token_to_row, mk) ||
-        overlaps(out, ob, topk_weights, (size_t)M * top_k * wsz) ||
-        overlaps(out, ob, workspace, ws))
+    if (overlaps(d, ob, x_bf16, xb) || overlaps(d, ob, panels, panels_bytes) ||
+        overlaps(d, ob, alpha1_gate, nl) || overlaps(d, ob, alpha1_up, nl) ||
+        overlaps(d, ob, alpha2, nl) || overlaps(d, ob, sorted_token_ids, capacity * 4) ||
+        overlaps(d, ob, expert_ids, capacity / block_m * 4) ||
+        overlaps(d, ob, num_tokens_post_padded, 4) || overlaps(d, ob, token_to_row, mk) ||
+        overlaps(d, ob, topk_weights, (size_t)M * top_k * wsz) ||
+        overlaps(d, ob, workspace, ws))
       return BFP4_ERR_OVERLAP;
   }
   int dc = device_check();

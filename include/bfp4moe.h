@@ -123,7 +123,8 @@ int bfp4_moe_plan(const int32_t* topk_ids, int64_t M, int top_k, int num_experts
  *   per 16-block: sf = e4m3_rne_sat((bmax * s_enc) / 6); inv = sf ? s_enc / sf : 0;
  *   code = e2m1_rne_sat(x * inv), ties to the even code, sign bit copied from x.
  * Outputs (device, contiguous): q [rows, cols/2], sf [rows, cols/16].
- * Requirements: cols % 32 == 0; row_stride >= cols and % 8 == 0; x 16-byte aligned;
+ * Requirements: cols % 32 == 0; row_stride >= cols and % 8 == 0; x 16-byte aligned, q 8-byte
+ * aligned, dec_scale 4-byte aligned; q and sf must not overlap x;
  * workspace >= bfp4_quantize_workspace_size(rows, mode, group_rows) (PER_GROUP keeps the group
  * maxima there).  Device preconditions: x finite; every row (group) maximum is 0 or >= 2^-106.
  * ---------------------------------------------------------------------------------------------- */
@@ -192,8 +193,10 @@ int bfp4_prepare_weights(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_
  *   topk_weights [M, top_k] FP32 (weights_dtype BFP4_WEIGHTS_F32, 4-byte aligned) or BF16
  *   (BFP4_WEIGHTS_BF16, 2-byte aligned); another weights_dtype gives BFP4_ERR_MODE;
  *   routed_scaling_factor (host) finite;
- *   out [M, H] BF16 (16-byte aligned, must not overlap any input) -- used when do_finalize;
- *   gemm2_out [capacity, H] BF16 -- required when !do_finalize, else may be NULL;
+ *   out [M, H] BF16 (16-byte aligned, must not overlap any input or the workspace) -- used
+ *   when do_finalize;
+ *   gemm2_out [capacity, H] BF16 (16-byte aligned, must not overlap any input or the
+ *   workspace) -- required when !do_finalize, else may be NULL;
  *   debug (may be NULL): optional copies of internal values for verification.
  *   workspace: >= bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize).
  * Requirements: H % 256 == 0 and H >= 256 [Alpha, notes]; I % 128 == 0 [cuDNN, sizes bullet];
@@ -292,7 +295,8 @@ int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void*
  * weights_dtype, as in bfp4_fused_moe_nvfp4) and token_to_row [M, top_k], accumulating into
  * out [M, H].  Bit-identical to the finalized path.
  * Requirements: H % 8 == 0; gemm2_out and out 16-byte aligned, token_to_row 4-byte, the weights
- * aligned to their element size; out must not overlap the inputs.
+ * aligned to their element size; out must not overlap topk_weights or token_to_row (checked)
+ * nor the gemm2_out rows token_to_row names (not checked: their number is not an argument).
  * ---------------------------------------------------------------------------------------------- */
 int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int weights_dtype,
                       const int32_t* token_to_row, int64_t M, int64_t H, int top_k,

@@ -159,6 +159,9 @@ def test_fused_validation():
     assert _fused(do_finalize=0) == "BFP4_ERR_NULL"            # gemm2_out required
     assert _fused(out=A + (1 << 16) + 64) == "BFP4_ERR_OVERLAP"  # out over a_sf
     assert _fused(out=A + (50 << 16) + 512) == "BFP4_ERR_OVERLAP"  # out over workspace
+    # unfinalized: gemm2_out [capacity, H] BF16 (88 x 512 bytes) must not reach an input either
+    assert _fused(do_finalize=0, gemm2_out=A + (46 << 16) - 88 * 512 + 16) == "BFP4_ERR_OVERLAP"
+    assert _fused(do_finalize=0, gemm2_out=A + (50 << 16) + 256) == "BFP4_ERR_OVERLAP"
     assert _fused(num_local_experts=0) == "BFP4_ERR_EXPERTS"
     # decode kernels (block_m <= 32) stage a block's rows whole in LDS: H <= 8960 at block_m 32
     assert _fused(H=9216, block_m=32, capacity=bf.bfp4_plan_capacity(16, 2, 8, 32),
@@ -180,6 +183,8 @@ def test_fused_valid_args_without_device():
                   out=1 << 40) == "BFP4_ERR_DEVICE"
     # BF16 routing weights need 2-byte alignment only
     assert _fused(weights_dtype=1, topk_weights=A + (47 << 16) + 2) == "BFP4_ERR_DEVICE"
+    # unfinalized: gemm2_out ending right where token_to_row starts is accepted
+    assert _fused(do_finalize=0, gemm2_out=A + (46 << 16) - 88 * 512) == "BFP4_ERR_DEVICE"
 
 
 def test_finalize_and_prepare_validation():
@@ -236,6 +241,7 @@ def test_w4a16_validation():
     assert _w16(x_bf16=None) == "BFP4_ERR_NULL"
     assert _w16(workspace_bytes=64) == "BFP4_ERR_WORKSPACE"
     assert _w16(out=A + 64) == "BFP4_ERR_OVERLAP"                 # out over x
+    assert _w16(do_finalize=0, gemm2_out=A + (45 << 16)) == "BFP4_ERR_OVERLAP"  # over the extent
     assert _w16(capacity=80) == "BFP4_ERR_CAPACITY"
     assert _w16(weight_format=2) == "BFP4_ERR_MODE"
 
