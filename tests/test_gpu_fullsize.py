@@ -6,6 +6,10 @@ expert outputs and finalize(unfinalized) are checked over every element; the exp
 computation is checked on a sampled token against the oracle, which quantizes that token's
 experts itself (all W1 rows, sampled W2 rows):  pre-activation within 1e-5, requantization of
 the GPU's BF16 intermediate bit-exact, final output within 2e-2 (relative Frobenius).
+
+The weight-only mode (BF16 activations, NVFP4 or MXFP4 weights) is checked the same way at the
+decode shape: pre-activation within 1e-5, BF16 intermediate within 2e-3, sampled output within
+2e-2, the combine and finalize(unfinalized) over every element.
 """
 
 import numpy as np
@@ -113,3 +117,74 @@ def test_fullsize_skewed_relu2_m16384():
     loc = (ids >= wl.local_offset) & (ids < wl.local_offset + wl.n_local)
     token = int(np.nonzero(loc.sum(axis=1) >= 3)[0][7])
     _check("skewed_relu2", token=token)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_fullsize_w4a16_decode_m8(fmt, n_hidden=512):
+    wl = WORKLOADS["decode"]
+    token = 5
+    say("full-size weight-only decode", fmt, "token", token)
+    p = Problem(wl)
+    M, k, H, I, N1 = wl.M, wl.top_k, wl.H, wl.I, wl.N1
+    if fmt == "mxfp4":
+        pw, lin = runner.prepare_weights_mxfp4(p.w1, p.w2, gated=wl.gated, keep_linear=True)
+    else:
+        pw, lin = runner.prepare_weights(p.w1, p.w2, gated=wl.gated, keep_linear=True)
+    fwd = runner.MoeForwardW4A16(pw, M, k, wl.E, wl.block_m, wl.local_offset, act=wl.act_code)
+    cap = fwd.plan.capacity
+    dbg = dict(preact=torch.full((cap, N1), float("nan"), device="cuda"),
+               inter=torch.zeros((cap, I), dtype=torch.bfloat16, device="cuda"))
+    out = fwd(p.x, p.ids_d, p.w_d, debug=dbg)
+    fwd_u = runner.MoeForwardW4A16(pw, M, k, wl.E, wl.block_m, wl.local_offset,
+                                   do_finalize=False, act=wl.act_code)
+    y, wts, ttr_d = fwd_u(p.x, p.ids_d, p.w_d)
+    out_u = torch.zeros_like(out)
+    bf.bfp4_moe_finalize(y, wts, runner.weights_dtype(wts), ttr_d, M, H, k, 1.0, out_u)
+    torch.cuda.synchronize()
+    out_bits = np_bits(out)
+
+    srt, eids, P, ttr = p.oracle_plan(wl.block_m)
+    assert np.array_equal(fwd.plan.token_to_row.cpu().numpy(), ttr)
+    assert np.array_equal(np_bits(out_u), out_bits)
+    ybits = np_bits(y)
+    ydict = {int(r): bf16_bits_to_f32(ybits[r]).astype(np.float64) for r in ttr.reshape(-1) if r >= 0}
+    assert np.array_equal(oracle.combine(np.zeros((M, H), np.uint16), ydict, p.w, ttr), out_bits)
+
+    rng = np.random.default_rng(token)
+    hs = np.sort(rng.choice(H, n_hidden, replace=False))
+    rows_t = [int(r) for r in ttr[token] if r >= 0]
+    pre_gpu = dbg["preact"][rows_t].cpu().numpy()
+    h_gpu = bf16_bits_to_f32(np_bits(dbg["inter"][rows_t]))
+    pre_ref, h_ref, ys = [], [], {}
+    for j in range(k):
+        r = int(ttr[token, j])
+        if r < 0:
+            continue
+        e = int(eids[r // wl.block_m])
+        b1, b2 = np_bits(p.w1[e]), np_bits(p.w2[e][torch.from_numpy(hs).cuda()])
+        if fmt == "mxfp4":
+            q1, s1 = oracle.quantize_mxfp4(bf16_bits_to_f32(b1))
+            q2, s2 = oracle.quantize_mxfp4(bf16_bits_to_f32(b2))
+            a1 = a2 = 1.0
+        else:
+            q1, s1, a1 = oracle.quantize_expert_rows(np_bits(p.w1[e]), np.arange(N1))
+            q2, s2, a2 = oracle.quantize_expert_rows(np_bits(p.w2[e]), hs)
+        # the GPU's weight quantization is the oracle's, bit for bit, on these rows
+        assert np.array_equal(np_u8(lin[0][e]), q1) and np.array_equal(np_u8(lin[1][e]), s1)
+        hs_d = torch.from_numpy(hs).cuda()
+        assert np.array_equal(np_u8(lin[2][e][hs_d]), q2)
+        assert np.array_equal(np_u8(lin[3][e][hs_d]), s2)
+        o = oracle.expert_rows_forward_w16(p.x_bits[token:token + 1], q1, s1, q2, s2, a1, a1, a2,
+                                           wl.act_code, weight_format=fmt)
+        pre_ref.append(o["pre"][0])
+        h_ref.append(o["h"][0])
+        ys[r] = o["y"][0]
+    e_pre = rel_fro(pre_gpu, np.stack(pre_ref))
+    e_h = rel_fro(h_gpu, np.stack(h_ref))
+    ref = oracle.combine(np.zeros((1, len(hs)), np.uint16), ys, p.w[token:token + 1],
+                         ttr[token:token + 1])
+    e_out = rel_fro(bf16_bits_to_f32(out_bits[token, hs]), bf16_bits_to_f32(ref[0]))
+    say("w4a16 %s: pre %.3e  h %.3e  out(sampled) %.3e" % (fmt, e_pre, e_h, e_out))
+    assert e_pre <= 1e-5
+    assert e_h <= 2e-3
+    assert e_out <= 2e-2
