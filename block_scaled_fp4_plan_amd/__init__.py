@@ -50,6 +50,7 @@ EXPORTS = [
     "bfp4_panel_bytes", "bfp4_prepare_weights", "bfp4_workspace_size", "bfp4_fused_moe_nvfp4",
     "bfp4_moe_finalize", "bfp4_profile_begin", "bfp4_profile_end", "bfp4_workspace_size_w4a16",
     "bfp4_fused_moe_w4a16", "bfp4_quantize_mxfp4", "bfp4_prepare_weights_mxfp4",
+    "bfp4_check_topk_ids", "bfp4_check_plan",
 ]
 
 
@@ -100,6 +101,8 @@ _sig("bfp4_fused_moe_w4a16", _I,
       _I, _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
 _sig("bfp4_quantize_mxfp4", _I, [_P, _I64, _I64, _I64, _P, _P, _P])
 _sig("bfp4_prepare_weights_mxfp4", _I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _P, _SZ, _P])
+_sig("bfp4_check_topk_ids", _I, [_P, _I64, _I, _I, _P, _P])
+_sig("bfp4_check_plan", _I, [_P, _P, _P, _SZ, _I64, _I, _I, _I, _P, _P])
 _sig("bfp4_profile_begin", _I, [_I, ctypes.c_char_p])
 _sig("bfp4_profile_end", _I, [ctypes.c_char_p, _SZ])
 
@@ -243,6 +246,18 @@ def bfp4_moe_finalize(gemm2_out, topk_weights, weights_dtype, token_to_row, M, H
     return _check(_lib.bfp4_moe_finalize(
         _p(gemm2_out), _p(topk_weights), weights_dtype, _p(token_to_row), M, H, top_k,
         routed_scaling_factor, _p(out), _s(stream)), "bfp4_moe_finalize")
+
+
+def bfp4_check_topk_ids(topk_ids, M, top_k, num_experts, report, stream=None):
+    return _check(_lib.bfp4_check_topk_ids(_p(topk_ids), M, top_k, num_experts, _p(report),
+                                           _s(stream)), "bfp4_check_topk_ids")
+
+
+def bfp4_check_plan(sorted_token_ids, expert_ids, num_tokens_post_padded, capacity, M, top_k,
+                    num_local_experts, block_m, report, stream=None):
+    return _check(_lib.bfp4_check_plan(
+        _p(sorted_token_ids), _p(expert_ids), _p(num_tokens_post_padded), capacity, M, top_k,
+        num_local_experts, block_m, _p(report), _s(stream)), "bfp4_check_plan")
 
 
 def bfp4_profile_begin(capacity, name_prefix=None):

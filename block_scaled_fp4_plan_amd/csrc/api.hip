@@ -535,6 +535,42 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int w
                                   (hipStream_t)stream));
 }
 
+int bfp4_check_topk_ids(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
+                        int32_t* report, void* stream) {
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (num_experts <= 0) return BFP4_ERR_EXPERTS;
+  if (!report || (M && !topk_ids)) return BFP4_ERR_NULL;
+  if (!aligned(report, 4) || !aligned(topk_ids, 4)) return BFP4_ERR_ALIGN;
+  if (overlaps(report, 12, topk_ids, (size_t)M * top_k * 4)) return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_check_topk(topk_ids, M, top_k, num_experts, report,
+                                    (hipStream_t)stream));
+}
+
+int bfp4_check_plan(const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                    const int32_t* num_tokens_post_padded, size_t capacity, int64_t M, int top_k,
+                    int num_local_experts, int block_m, int32_t* report, void* stream) {
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
+  if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
+  if (capacity % block_m || capacity >= (1ULL << 31)) return BFP4_ERR_CAPACITY;
+  if (!report || !num_tokens_post_padded || (capacity && (!sorted_token_ids || !expert_ids)))
+    return BFP4_ERR_NULL;
+  if (!aligned(report, 4) || !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_post_padded, 4))
+    return BFP4_ERR_ALIGN;
+  if (overlaps(report, 12, sorted_token_ids, capacity * 4) ||
+      overlaps(report, 12, expert_ids, capacity / block_m * 4) ||
+      overlaps(report, 12, num_tokens_post_padded, 4))
+    return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_check_plan(sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                    (int64_t)capacity, M * top_k, block_m, num_local_experts,
+                                    report, (hipStream_t)stream));
+}
+
 int bfp4_profile_begin(int capacity, const char* name_prefix) {
   if (capacity <= 0 || capacity > (1 << 20)) return BFP4_ERR_SHAPE;
   int dc = device_check();

@@ -36,6 +36,13 @@ hipError_t launch_permute(const uint8_t* q, const uint8_t* sf, const float* dec,
                           int64_t H, int top_k, const int32_t* sorted, const int32_t* ntpp,
                           int64_t cap, uint8_t* qp, uint8_t* sp, float* spd, hipStream_t s);
 
+// Debug validation (validate.hip): counts into report[3], which the launchers initialize.
+hipError_t launch_check_topk(const int32_t* ids, int64_t M, int top_k, int num_experts,
+                             int32_t* report, hipStream_t s);
+hipError_t launch_check_plan(const int32_t* sorted, const int32_t* eids, const int32_t* ntpp,
+                             int64_t cap, int64_t sentinel, int block_m, int nloc,
+                             int32_t* report, hipStream_t s);
+
 hipError_t launch_finalize(const uint16_t* y, const void* w, bool w_bf16, const int32_t* ttr, int64_t M,
                            int64_t H, int top_k, float rsf, uint16_t* out, hipStream_t s);
 

@@ -17,6 +17,8 @@ from . import (
     GATED_ACTS,
     BFP4_SCALE_PER_GROUP,
     BFP4_SCALE_PER_ROW,
+    bfp4_check_plan,
+    bfp4_check_topk_ids,
     bfp4_fused_moe_nvfp4,
     bfp4_fused_moe_w4a16,
     bfp4_moe_plan,
@@ -141,6 +143,27 @@ class MoePlanBuffers:
                       self.num_tokens_post_padded, self.token_to_row, self.capacity, self.ws,
                       self.ws_bytes, stream)
         return self
+
+
+    def check(self, stream=None):
+        """Debug validation of the plan arrays (bfp4_check_plan); waits for the stream and returns
+        (bad entries, bad blocks, bad extent)."""
+        report = torch.empty(3, dtype=torch.int32, device=self.sorted_token_ids.device)
+        bfp4_check_plan(self.sorted_token_ids, self.expert_ids, self.num_tokens_post_padded,
+                        self.capacity, self.M, self.top_k, self.nloc, self.block_m, report, stream)
+        torch.cuda.synchronize(report.device)
+        return tuple(int(v) for v in report.cpu())
+
+
+def check_topk_ids(topk_ids, num_experts, stream=None):
+    """Debug validation of a routing (bfp4_check_topk_ids); waits for the stream and returns
+    (tokens with a repeated expert, ids outside [-1, num_experts), first such token or None)."""
+    M, top_k = topk_ids.shape
+    report = torch.empty(3, dtype=torch.int32, device=topk_ids.device)
+    bfp4_check_topk_ids(topk_ids, M, top_k, num_experts, report, stream)
+    torch.cuda.synchronize(report.device)
+    dup, bad, first = (int(v) for v in report.cpu())
+    return dup, bad, (None if first == 0x7FFFFFFF else first)
 
 
 class MoeForward:

@@ -303,6 +303,34 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int w
                       float routed_scaling_factor, uint16_t* out, void* stream);
 
 /* ----------------------------------------------------------------------------------------------
+ * Debug validation of device-side preconditions (off the hot path; the other calls never read
+ * device memory to validate).  Each call overwrites report[3] (device, int32, 4-byte aligned, not
+ * overlapping the inputs) on `stream`; read it back after the stream has reached it.
+ *
+ * bfp4_check_topk_ids [cuDNN, topk_ids bullet: each token's top_k experts are distinct; -1 marks
+ * an empty slot]: topk_ids [M, top_k] int32.
+ *   report[0] = tokens that hold some id >= 0 more than once;
+ *   report[1] = ids outside [-1, num_experts);
+ *   report[2] = smallest token index counted in either, or 2147483647 when there is none.
+ * Duplicates still give a valid plan (bfp4_moe_plan ranks them stably); out-of-range ids are
+ * unrouted.  Limits as bfp4_moe_plan.
+ *
+ * bfp4_check_plan [Alpha, plan paragraph and parameters]: the preconditions the fused calls place
+ * on a plan they did not build, for this M, top_k, num_local_experts, block_m and capacity.
+ *   report[0] = entries below the extent outside [0, M*top_k] (M*top_k is the padding sentinel);
+ *   report[1] = blocks below the extent whose expert id is outside [0, num_local_experts);
+ *   report[2] = 1 when the extent num_tokens_post_padded[0] is negative, above capacity or not a
+ *               multiple of block_m (entries and blocks are then checked below the extent clamped
+ *               to [0, capacity] and rounded down to a multiple of block_m), else 0.
+ * A plan from bfp4_moe_plan reports {0, 0, 0}.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_check_topk_ids(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
+                        int32_t* report, void* stream);
+int bfp4_check_plan(const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                    const int32_t* num_tokens_post_padded, size_t capacity, int64_t M, int top_k,
+                    int num_local_experts, int block_m, int32_t* report, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
  * Kernel timing with HIP events (measurement support, off by default).
  * bfp4_profile_begin(capacity, name_prefix) creates `capacity` event pairs and starts recording
  * one pair around every kernel the library launches whose name starts with name_prefix (host
@@ -310,7 +338,8 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int w
  * quantize_rows_fixed, quantize_mxfp4, with fill_u32 and group_amax), permute, prepare_weights,
  * tile_list, decode_tokens, gemm1_<activation>_{decode,prefill} (activation swiglu, relu2, geglu,
  * gelu, relu, silu or identity), gemm2_down_{decode,prefill}, the weight-only
- * gemm1_<activation>_w16_decode and gemm2_down_w16_decode, finalize.  The timer is process-wide state:
+ * gemm1_<activation>_w16_decode and gemm2_down_w16_decode, finalize, and the validators'
+ * check_init, check_topk and check_plan.  The timer is process-wide state:
  * record from one host thread at a time, and not while a stream is being captured.
  * bfp4_profile_end() stops recording, waits for the
  * recorded events and writes one line per kernel name, "name count total_ms", into buf

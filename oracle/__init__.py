@@ -67,7 +67,9 @@ from .moe import (  # noqa: F401
     moe_permute,
     moe_plan,
     plan_capacity,
+    plan_violations,
     quantize_expert_rows,
     quantize_expert_weights,
+    routing_violations,
     unquantized_moe_f64,
 )

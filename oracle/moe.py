@@ -86,6 +86,52 @@ def moe_plan(topk_ids, num_experts, local_expert_offset, num_local_experts, bloc
             token_to_row.reshape(M, k).astype(np.int32))
 
 
+def routing_violations(topk_ids, num_experts):
+    """Breaches of the routing's preconditions (CudnnGroupedGemmNvfp4Config, topk_ids bullet:
+    each token's top_k experts are distinct; -1 marks an empty slot).
+
+    Returns (number of tokens holding some id >= 0 more than once,
+             number of ids outside [-1, num_experts),
+             smallest token index counted in either, or None).
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    dup_tokens, bad_ids, first = 0, 0, None
+    for t in range(ids.shape[0]):
+        row = [int(v) for v in ids[t]]
+        bad = sum(1 for v in row if v < -1 or v >= num_experts)
+        ok = [v for v in row if 0 <= v < num_experts]
+        dup = len(set(ok)) < len(ok)
+        dup_tokens += int(dup)
+        bad_ids += bad
+        if (dup or bad) and first is None:
+            first = t
+    return dup_tokens, bad_ids, first
+
+
+def plan_violations(sorted_token_ids, expert_ids, num_tokens_post_padded, capacity, M, top_k,
+                    num_local_experts, block_m):
+    """Breaches of what the fused computation requires of a pre-aligned plan it did not build
+    (alphamoe_nvfp4_aligned_moe page, plan paragraph and parameters): entries name a flat slot
+    f < M * top_k or the padding sentinel M * top_k, every block names a local expert, and the
+    extent num_tokens_post_padded is a multiple of block_m within the capacity.
+
+    Returns (entries below the extent outside [0, M * top_k],
+             blocks below the extent whose expert id is outside [0, num_local_experts),
+             1 if the extent is negative, above capacity or not a multiple of block_m, else 0).
+    With a bad extent, entries and blocks are checked below the extent clamped to
+    [0, capacity] and rounded down to a multiple of block_m.
+    """
+    P = int(num_tokens_post_padded)
+    bad_extent = int(not (0 <= P <= capacity and P % block_m == 0))
+    ext = (min(max(P, 0), capacity) // block_m) * block_m
+    sentinel = M * top_k
+    bad_entries = sum(1 for f in np.asarray(sorted_token_ids[:ext], dtype=np.int64)
+                      if not 0 <= int(f) <= sentinel)
+    bad_blocks = sum(1 for e in np.asarray(expert_ids[:ext // block_m], dtype=np.int64)
+                     if not 0 <= int(e) < num_local_experts)
+    return bad_entries, bad_blocks, bad_extent
+
+
 def moe_permute(q, sf, dec_scale, sorted_token_ids, num_tokens_post_padded, top_k):
     """Gather quantized token rows into plan order (CudnnGroupedGemmNvfp4Config: rows and scale
     rows are permuted into expert order).  Row r < extent takes token f // top_k of its entry f;

@@ -276,3 +276,42 @@ def test_w4a16_valid_args_without_device():
     assert _w16(block_m=32, capacity=bf.bfp4_plan_capacity(16, 2, 8, 32),
                 workspace_bytes=bf.bfp4_workspace_size_w4a16(16, 256, 128, 2, 8, 32, 1)) == \
         "BFP4_ERR_DEVICE"
+
+
+def _status(fn, **args):
+    with pytest.raises(Bfp4Error) as ei:
+        fn(**args)
+    return bf.STATUS[ei.value.status]
+
+
+def test_check_entry_points_validation():
+    def topk(**kw):
+        args = dict(topk_ids=A, M=4, top_k=2, num_experts=8, report=A + (1 << 16), stream=0)
+        args.update(kw)
+        return _status(bf.bfp4_check_topk_ids, **args)
+
+    def plan(**kw):
+        args = dict(sorted_token_ids=A, expert_ids=A + (1 << 16), num_tokens_post_padded=A + (2 << 16),
+                    capacity=88, M=16, top_k=2, num_local_experts=8, block_m=8,
+                    report=A + (3 << 16), stream=0)
+        args.update(kw)
+        return _status(bf.bfp4_check_plan, **args)
+
+    assert topk(M=-1) == "BFP4_ERR_SHAPE"
+    assert topk(top_k=0) == "BFP4_ERR_SHAPE"
+    assert topk(num_experts=0) == "BFP4_ERR_EXPERTS"
+    assert topk(report=None) == "BFP4_ERR_NULL"
+    assert topk(topk_ids=None) == "BFP4_ERR_NULL"
+    assert topk(report=A + (1 << 16) + 2) == "BFP4_ERR_ALIGN"
+    assert topk(report=A + 28) == "BFP4_ERR_OVERLAP"          # inside topk_ids [4, 2] int32
+    assert plan(block_m=12) == "BFP4_ERR_BLOCK_M"
+    assert plan(num_local_experts=0) == "BFP4_ERR_EXPERTS"
+    assert plan(capacity=84) == "BFP4_ERR_CAPACITY"           # not a multiple of block_m
+    assert plan(num_tokens_post_padded=None) == "BFP4_ERR_NULL"
+    assert plan(expert_ids=A + (1 << 16) + 1) == "BFP4_ERR_ALIGN"
+    assert plan(report=A + 344) == "BFP4_ERR_OVERLAP"         # the last entry of sorted [88]
+    if NO_GPU:
+        assert topk() == "BFP4_ERR_DEVICE"
+        assert topk(M=0, topk_ids=None) == "BFP4_ERR_DEVICE"  # an empty routing still reports
+        assert plan() == "BFP4_ERR_DEVICE"
+        assert plan(capacity=0, sorted_token_ids=None, expert_ids=None) == "BFP4_ERR_DEVICE"

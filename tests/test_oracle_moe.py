@@ -102,6 +102,62 @@ def test_generator_topk_distinct():
     assert ids.min() >= 0 and ids.max() < 288
 
 
+def test_routing_violations_pins():
+    """Hand-counted example; the generated routings of every workload are clean; and on random
+    small id matrices the counts equal a second formulation (sorted rows, adjacent equal ids)."""
+    ids = np.array([[0, 1], [2, 2], [-1, -1], [5, -3], [3, 3], [-1, 0]], np.int32)
+    # token 1 and token 4 repeat an id; ids 5 and -3 (token 3) are outside [-1, 4)
+    assert oracle.routing_violations(ids, 4) == (2, 2, 1)
+    assert oracle.routing_violations(np.array([[-1, -1]], np.int32), 4) == (0, 0, None)
+    assert oracle.routing_violations(np.array([[0, 7]], np.int32), 4) == (0, 1, 0)
+    assert oracle.routing_violations(np.zeros((0, 3), np.int32), 4) == (0, 0, None)
+    for name, wl in WORKLOADS.items():
+        r, _ = make_routing(wl, M=min(wl.M, 2048))
+        assert oracle.routing_violations(r, wl.E) == (0, 0, None), name
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        E = int(rng.integers(2, 9))
+        ids = rng.integers(-3, E + 3, size=(50, 4)).astype(np.int32)
+        inr = (ids >= 0) & (ids < E)
+        s_ = np.sort(np.where(inr, ids, -10 - np.arange(4)), axis=1)   # out-of-range ids distinct
+        dup = np.any(s_[:, 1:] == s_[:, :-1], axis=1)
+        bad = (ids < -1) | (ids >= E)
+        bad_tok = bad.any(axis=1)
+        flagged = np.nonzero(dup | bad_tok)[0]
+        first = int(flagged[0]) if flagged.size else None
+        assert oracle.routing_violations(ids, E) == (int(dup.sum()), int(bad.sum()), first)
+
+
+def test_plan_violations_pins():
+    """Every oracle plan is clean; each planted breach is counted once, and entries at or past
+    the extent are not looked at."""
+    rng = np.random.default_rng(4)
+    for bm, off, nloc in ((8, 0, 8), (16, 2, 4), (128, 0, 8)):
+        M, k, E = 37, 3, 8
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
+        srt, eids, P, _ = oracle.moe_plan(ids, E, off, nloc, bm)
+        cap = oracle.plan_capacity(M, k, nloc, bm)
+        assert oracle.plan_violations(srt, eids, P, cap, M, k, nloc, bm) == (0, 0, 0)
+    M, k, nloc, bm = 37, 3, 8, 8
+    ids = np.stack([rng.permutation(8)[:k] for _ in range(M)]).astype(np.int32)
+    srt, eids, P, _ = oracle.moe_plan(ids, 8, 0, nloc, bm)
+    cap = oracle.plan_capacity(M, k, nloc, bm)
+    assert P < cap
+    s2, e2 = srt.copy(), eids.copy()
+    s2[0], s2[P - 1] = -1, M * k + 1                  # two bad entries inside the extent
+    s2[P] = -7                                        # past the extent: not counted
+    e2[1] = nloc                                      # one bad block inside the extent
+    e2[P // bm] = 99                                  # past the extent: not counted
+    assert oracle.plan_violations(s2, e2, P, cap, M, k, nloc, bm) == (2, 1, 0)
+    # bad extents: not a multiple of block_m (checked below P rounded down), above capacity
+    # (checked below capacity), negative (nothing checked)
+    assert oracle.plan_violations(s2, e2, P + 3, cap, M, k, nloc, bm) == (2, 1, 1)
+    # past the real extent the blocks hold -1, so each of them counts
+    assert oracle.plan_violations(s2, e2, cap + bm, cap, M, k, nloc, bm) == \
+        (3, 1 + (cap - P) // bm, 1)
+    assert oracle.plan_violations(s2, e2, -bm, cap, M, k, nloc, bm) == (0, 0, 1)
+
+
 def test_permute_rows():
     rng = np.random.default_rng(2)
     M, k = 6, 2
