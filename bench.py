@@ -8,7 +8,9 @@ preparation happen once, before timing (offline in a serving system).
 Workloads (synthetic, seeded inputs from synth/):
   decode  : M=8,    H=7168, I=2048, E=256, top_k=8, block_m=8   (primary: value = tokens/s)
   prefill : M=4096, H=7168, I=2048, E=256, top_k=8, block_m=128 (reported in "prefill")
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|both]
+  skewed  : M=16384, H=4096, I=1536, E=288 (144 local), top_k=6, squared ReLU, Zipf routing,
+            block_m=128 (reported in "skewed_relu2")
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|both]
 Prints one JSON line.
 """
 
@@ -36,10 +38,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="both", choices=["decode", "prefill", "both"])
+    ap.add_argument("--workload", default="both", choices=["decode", "prefill", "skewed", "both"],
+                    help="both: decode, prefill and the skewed squared-ReLU workload")
     ap.add_argument("--replicas", type=int, default=2,
                     help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-skewed", action="store_true",
+                    help="leave the skewed squared-ReLU workload out of the default run")
     ap.add_argument("--no-w4a16", action="store_true",
                     help="skip the weight-only (BF16 activation) decode measurement")
     ap.add_argument("--no-graph", action="store_true",
@@ -307,9 +312,9 @@ def kernel_rooflines(wl, s, breakdown):
         "quantize_rows": ("hbm", M * H * 2 + M * H * q + M * 4),
         "decode_tokens": ("hbm", M * H * (q + 2)),
         "tile_list": ("latency", 0),
-        "gemm1_swiglu_decode": ("hbm", gemm_bytes(wl, s.touched, A, 1)),
+        "gemm1_%s_decode" % wl.act: ("hbm", gemm_bytes(wl, s.touched, A, 1)),
         "gemm2_down_decode": ("hbm", gemm_bytes(wl, s.touched, A, 2)),
-        "gemm1_swiglu_prefill": ("mfma", 2.0 * A * H * N1),
+        "gemm1_%s_prefill" % wl.act: ("mfma", 2.0 * A * H * N1),
         "gemm2_down_prefill": ("mfma", 2.0 * A * H * I),
         "finalize": ("hbm", A * H * 2 + 2 * M * H * 2 + M * k * 8),
     }
@@ -399,6 +404,37 @@ def cpu_baseline(s, sample_tokens=1):
                 oracle_nvfp4_vs_fp64_gap=gap)
 
 
+def time_tiled(wl, label, args, desc):
+    """One compute-bound workload (tiled prefill kernels): step time and throughput, the dominant
+    GEMM1 launch against the FP16 MFMA peak, every kernel against its own roofline."""
+    import torch
+
+    s, dt, dt_ev, table, breakdown = time_workload(wl, args.steps, args.warmup, 1)
+    ms = dt / args.steps * 1e3
+    gdt = None if args.no_graph else time_graph(s, args.steps, args.warmup)
+    g1_ms, _, g1_name = kernel_ms(table, "gemm1")
+    g1_flops = 2.0 * s.A * wl.H * wl.N1
+    ach = g1_flops / (g1_ms * 1e-3) / 1e12
+    tf = step_flops(wl, s.A) / (ms * 1e-3) / 1e12
+    res = dict(
+        value=wl.M / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, tflops=tf,
+        tflops_frac=tf / F16_MFMA_PEAK_TFLOPS,
+        config={"workload": desc, "assignments": s.A,
+                "padded_rows": int(s.fwd.plan.num_tokens_post_padded.item()),
+                "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
+                "graph_replay_ms_per_step": gdt and gdt / args.steps * 1e3,
+                "graph_replay_tokens_per_s": gdt and wl.M / (gdt / args.steps),
+                "kernels": kernel_rooflines(wl, s, breakdown)},
+        roofline={"bound": "mfma", "kernel": g1_name, "achieved": ach,
+                  "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": ach / F16_MFMA_PEAK_TFLOPS,
+                  "traffic": traffic_for(g1_name, label), "flops_per_launch": g1_flops,
+                  "avg_launch_ms": g1_ms})
+    del s
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -450,29 +486,9 @@ def main():
         del s
         torch.cuda.empty_cache()
     if args.workload in ("prefill", "both"):
-        wl = WORKLOADS["prefill"]
-        s, dt, dt_ev, table, breakdown = time_workload(wl, args.steps, args.warmup, 1)
-        ms = dt / args.steps * 1e3
-        gdt = None if args.no_graph else time_graph(s, args.steps, args.warmup)
-        g1_ms, _, g1_name = kernel_ms(table, "gemm1")
-        g1_flops = 2.0 * s.A * wl.H * wl.N1
-        ach = g1_flops / (g1_ms * 1e-3) / 1e12
-        tf = step_flops(wl, s.A) / (ms * 1e-3) / 1e12
-        pre = dict(
-            value=wl.M / (ms * 1e-3), unit="tokens/s", ms_per_step=ms, tflops=tf,
-            tflops_frac=tf / F16_MFMA_PEAK_TFLOPS,
-            config={"workload": "prefill: M=4096 H=7168 I=2048 E=256 top_k=8 block_m=128 SwiGLU "
-                                "NVFP4", "assignments": s.A,
-                    "padded_rows": int(s.fwd.plan.num_tokens_post_padded.item()),
-                    "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
-                    "graph_replay_ms_per_step": gdt and gdt / args.steps * 1e3,
-                    "graph_replay_tokens_per_s": gdt and wl.M / (gdt / args.steps),
-                    "kernels": kernel_rooflines(wl, s, breakdown)},
-            roofline={"bound": "mfma", "kernel": g1_name, "achieved": ach,
-                      "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": ach / F16_MFMA_PEAK_TFLOPS,
-                      "traffic": traffic_for(g1_name, "prefill"), "flops_per_launch": g1_flops,
-                      "avg_launch_ms": g1_ms})
+        pre = time_tiled(WORKLOADS["prefill"], "prefill", args,
+                         "prefill: M=4096 H=7168 I=2048 E=256 top_k=8 block_m=128 SwiGLU NVFP4")
+        ms = pre["ms_per_step"]
         if "value" in result:
             result["prefill"] = pre
         else:
@@ -480,6 +496,17 @@ def main():
                           steps=args.steps, warmup=args.warmup, ms_per_step=ms,
                           higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
                           data="synthetic", config=pre["config"], roofline=pre["roofline"])
+    if args.workload in ("skewed", "both") and not args.no_skewed:
+        sk = time_tiled(WORKLOADS["skewed_relu2"], "skewed", args,
+                        "skewed: M=16384 H=4096 I=1536 E=288 (experts 0-143 local) top_k=6 "
+                        "block_m=128 squared-ReLU NVFP4, Zipf(1.2) routing")
+        if "value" in result:
+            result["skewed_relu2"] = sk
+        else:
+            result.update(metric=METRIC, value=sk["value"], unit="tokens/s", n_gpus=1,
+                          steps=args.steps, warmup=args.warmup, ms_per_step=sk["ms_per_step"],
+                          higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
+                          data="synthetic", config=sk["config"], roofline=sk["roofline"])
     if not args.no_context:
         result["context"] = achievable_context()
     print(json.dumps(result))
