@@ -7,6 +7,7 @@ computation is checked on a sampled token against the oracle, which quantizes th
 experts itself (all W1 rows, sampled W2 rows):  pre-activation within 1e-5, requantization of
 the GPU's BF16 intermediate bit-exact, final output within 2e-2 (relative Frobenius).
 
+The standalone permutation is checked over every element at the prefill and skewed sizes.
 The weight-only mode (BF16 activations, NVFP4 or MXFP4 weights) is checked the same way at the
 decode shape: pre-activation within 1e-5, BF16 intermediate within 2e-3, sampled output within
 2e-2, the combine and finalize(unfinalized) over every element.
@@ -188,3 +189,34 @@ def test_fullsize_w4a16_decode_m8(fmt, n_hidden=512):
     assert e_pre <= 1e-5
     assert e_h <= 2e-3
     assert e_out <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["prefill", "skewed_relu2"])
+def test_fullsize_permute(name):
+    """The standalone permutation at full size (every element, bit-exact): plan rows below the
+    extent take their token's packed row, scale row and decode scale; sentinel rows and rows past
+    the extent are zero."""
+    from synth import make_activations, make_routing
+
+    wl = WORKLOADS[name]
+    say("full-size permute", name)
+    M, k, H, bm = wl.M, wl.top_k, wl.H, wl.block_m
+    x_bits = make_activations(wl, 0)
+    ids, _ = make_routing(wl, 0)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, sf, dec = runner.quantize(x)
+    pb = runner.MoePlanBuffers(M, k, wl.n_local, bm, "cuda")
+    pb.build(torch.from_numpy(ids).cuda(), wl.E, wl.local_offset)
+    cap = pb.capacity
+    qp = torch.full((cap, H // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    sp = torch.full((cap, H // 16), 0xAB, dtype=torch.uint8, device="cuda")
+    spd = torch.full((cap,), float("nan"), dtype=torch.float32, device="cuda")
+    bf.bfp4_moe_permute(q, sf, dec, M, H, k, pb.sorted_token_ids, pb.num_tokens_post_padded, cap,
+                        qp, sp, spd)
+    torch.cuda.synchronize()
+    srt, _, P, _ = oracle.moe_plan(ids, wl.E, wl.local_offset, wl.n_local, bm)
+    oq, osf, odec = oracle.quantize_nvfp4(bf16_bits_to_f32(x_bits), oracle.SCALE_PER_ROW)
+    wq, wsf, wsd = oracle.moe_permute(oq, osf, odec, srt, P, k)
+    assert np.array_equal(np_u8(qp), wq)
+    assert np.array_equal(np_u8(sp), wsf)
+    assert np.array_equal(spd.cpu().numpy().view(np.uint32), wsd.view(np.uint32))
