@@ -25,8 +25,9 @@ if torch.cuda.is_available():
 SKEWED = Workload("graph_skewed", M=384, H=1280, I=640, E=6, top_k=3, block_m=128,
                   routing="zipf")
 
+# the last two: the decode and prefill workloads at full size, as the bench replays them
 CASES = [("tiny", 8, True), ("tiny", 128, True), ("tiny", 128, False), ("decode_ll", 8, True),
-         ("graph_skewed", 128, True)]
+         ("graph_skewed", 128, True), ("decode", 8, True), ("prefill", 128, True)]
 
 
 def _inputs(wl, seed, M):
