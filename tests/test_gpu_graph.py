@@ -175,3 +175,42 @@ def test_graph_in_place_weight_refresh():
             p.x, p.ids_d, p.w_d)
         torch.cuda.synchronize()
         assert torch.equal(_bits(out_g), _bits(ref)), step
+
+
+W16_CASES = [("tiny", 8, "nvfp4"), ("decode", 8, "nvfp4"), ("decode", 8, "mxfp4")]
+
+
+@pytest.mark.parametrize("name,bm,fmt", W16_CASES, ids=["%s-bm%d-%s" % c for c in W16_CASES])
+def test_graph_replay_w4a16_matches_eager(name, bm, fmt):
+    """The weight-only forward (plan + bfp4_fused_moe_w4a16) captured once and replayed with new
+    inputs equals the eager call bit for bit (the decode case at full size, NVFP4 and MXFP4
+    weights)."""
+    wl = WORKLOADS[name]
+    say("graph replay w4a16", name, "block_m", bm, fmt)
+    p = Problem(wl)
+    prep = runner.prepare_weights_mxfp4 if fmt == "mxfp4" else runner.prepare_weights
+    pw = prep(p.w1, p.w2, gated=wl.gated)
+    fwd_e = runner.MoeForwardW4A16(pw, p.M, wl.top_k, wl.E, bm, wl.local_offset)
+    fwd_g = runner.MoeForwardW4A16(pw, p.M, wl.top_k, wl.E, bm, wl.local_offset)
+    x, ids, w = p.x.clone(), p.ids_d.clone(), p.w_d.clone()
+    out_g = torch.zeros((p.M, wl.H), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd_g(x, ids, w, out=out_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd_g(x, ids, w, out=out_g)
+    for seed in (1, 2, 0, 1):
+        xs, idss, ws = _inputs(wl, seed, p.M)
+        x.copy_(xs)
+        ids.copy_(idss)
+        w.copy_(ws)
+        out_g.zero_()
+        graph.replay()
+        res_e = fwd_e(xs, idss, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out_g), _bits(res_e)), seed
+        assert torch.any(_bits(res_e) != 0)
