@@ -6,12 +6,14 @@ SwiGLU and requantization, GEMM2, ordered FP32 finalize).  Weight quantization a
 preparation happen once, before timing (offline in a serving system).
 
 Workloads (synthetic, seeded inputs from synth/):
-  decode  : M=8,    H=7168, I=2048, E=256, top_k=8, block_m=8   (primary: value = tokens/s)
-  prefill : M=4096, H=7168, I=2048, E=256, top_k=8, block_m=128 (reported in "prefill")
-  skewed  : M=16384, H=4096, I=1536, E=288 (144 local), top_k=6, squared ReLU, Zipf routing,
-            block_m=128 (reported in "skewed_relu2")
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|both]
-Prints one JSON line.
+  decode    : M=8,    H=7168, I=2048, E=256, top_k=8, block_m=8   (primary: value = tokens/s)
+  decode_ll : M=4,    H=2048, I=512,  E=128, top_k=10, block_m=8  (reported in "decode_ll")
+  prefill   : M=4096, H=7168, I=2048, E=256, top_k=8, block_m=128 (reported in "prefill")
+  skewed    : M=16384, H=4096, I=1536, E=288 (144 local), top_k=6, squared ReLU, Zipf routing,
+              block_m=128 (reported in "skewed_relu2")
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|decode_ll|prefill|
+       skewed|all]
+Prints one JSON line on stdout; progress goes to stderr.
 """
 
 import argparse
@@ -38,8 +40,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="both", choices=["decode", "prefill", "skewed", "both"],
-                    help="both: decode, prefill and the skewed squared-ReLU workload")
+    ap.add_argument("--workload", default="all",
+                    choices=["decode", "decode_ll", "prefill", "skewed", "all", "both"],
+                    help="all (or both): decode, decode-LL, prefill and the skewed squared-ReLU "
+                         "workload; the first of them gives the headline value")
     ap.add_argument("--replicas", type=int, default=2,
                     help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -353,55 +357,103 @@ def kernel_ms(table, prefix):
     return None, 0, None
 
 
-def cpu_baseline(s, sample_tokens=1):
-    """The oracle (float64 numpy, as it stands) on a bounded sample: the per-call path for the
-    first token(s): activation quantization, plan, permutation, the token's experts (GEMM1,
-    activation, requantization, GEMM2) and the combine.  Weight quantization is offline on both
-    sides and excluded."""
+def cpu_baseline(s, runs=3, max_experts=None):
+    """The oracle (float64 / exact int64 numpy, as it stands) on the per-call path of this
+    workload: activation quantization, plan, permutation, every routed expert's projections,
+    activation and requantization (oracle.expert_rows_forward, one call per expert, the calls
+    spread over a thread pool of all host cores: numpy's integer matrix products release the
+    interpreter lock), then the ordered combine.  Weight quantization is offline on both sides
+    and excluded.  With max_experts, only that many experts (spread over the range of routed
+    rows per expert) run and the time is extrapolated to all assignments linearly in the number
+    of assignments; the sample is stated.  Returns the median of `runs` timed runs."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     from oracle.formats import bf16_bits_to_f32
     from synth import to_bits
 
     wl = s.wl
-    T = sample_tokens
-    ids = s.ids[:T]
-    experts = sorted(set(int(e) for e in ids.reshape(-1)))
-    wq = {}
-    for e in experts:                                           # offline part (untimed)
-        q1, s1, a1 = oracle.quantize_expert_weights(to_bits(s.w1[e])[None])
-        q2, s2, a2 = oracle.quantize_expert_weights(to_bits(s.w2[e])[None])
-        wq[e] = ((q1[0], s1[0], q2[0], s2[0]), a1[0], a2[0])
-    a1v = np.zeros(wl.n_local, np.float32)
-    a2v = np.zeros(wl.n_local, np.float32)
-    for e in experts:
-        a1v[e], a2v[e] = wq[e][1], wq[e][2]
-    t0 = time.perf_counter()
-    aq, asf, adec = oracle.quantize_nvfp4(bf16_bits_to_f32(s.x_bits[:T]), oracle.SCALE_PER_ROW)
-    srt, eids, P, ttr = oracle.moe_plan(ids, wl.E, wl.local_offset, wl.n_local, wl.block_m)
-    res = oracle.fused_moe_nvfp4(aq, asf, adec, lambda e: wq[e][0], a1v, a1v, a2v, 1.0, srt, eids,
-                                 P, ttr, s.w[:T], wl.top_k, wl.block_m, oracle.ACT_SWIGLU)
-    dt = time.perf_counter() - t0
-    import torch
+    threads = len(os.sched_getaffinity(0))
+    srt, eids, P, ttr = oracle.moe_plan(s.ids, wl.E, wl.local_offset, wl.n_local, wl.block_m)
+    rows_of = {}
+    for r in range(P):
+        if srt[r] < wl.M * wl.top_k:
+            rows_of.setdefault(int(eids[r // wl.block_m]), []).append(r)
+    experts = sorted(rows_of)
+    if max_experts is not None and len(experts) > max_experts:
+        by_size = sorted(experts, key=lambda e: len(rows_of[e]))
+        pick = np.linspace(0, len(by_size) - 1, max_experts).round().astype(int)
+        experts = sorted(set(by_size[i] for i in pick))
+    A_all = sum(len(v) for v in rows_of.values())
+    A_run = sum(len(rows_of[e]) for e in experts)
 
-    out = torch.zeros_like(s.out)                      # one fresh GPU forward for the comparison
-    s.fwd(s.x, s.ids_d, s.w_d, out=out, weights=s.weights[0])
-    torch.cuda.synchronize()
-    got = bf16_bits_to_f32(to_bits(out[:T])).astype(np.float64)
-    ref = bf16_bits_to_f32(res["out"]).astype(np.float64)
-    err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-    # the oracle's own NVFP4-vs-unquantized gap on the same sample (reported, not gated)
-    u = oracle.unquantized_moe_f64(s.x_bits[:T], lambda e: to_bits(s.w1[e]), lambda e: to_bits(s.w2[e]),
-                                   ids, s.w[:T], wl.E, wl.local_offset, wl.n_local, oracle.ACT_SWIGLU)
-    u = np.stack([u[t] for t in range(T)])
-    gap = float(np.linalg.norm(ref - u) / np.linalg.norm(u))
-    flops = 2.0 * T * wl.top_k * (wl.N1 * wl.H + wl.H * wl.I)
-    return dict(value=T / dt, unit="tokens/s", cores=1, kind="oracle",
-                host_cores=len(os.sched_getaffinity(0)), gflops=flops / dt / 1e9,
-                sample="%d token(s) of the %s workload (%d experts), per-call path without weight "
-                       "quantization; %.2f s; float64 numpy (its projections are exact int64 "
-                       "matrix products, one thread); GPU-vs-oracle rel. "
-                       "Frobenius error on the sample %.2e" % (T, wl.name, len(experts), dt, err),
-                oracle_nvfp4_vs_fp64_gap=gap)
+    host_w = {e: (to_bits(s.w1[e]), to_bits(s.w2[e])) for e in experts}
+
+    def quant(e):                                                # offline part (untimed)
+        q1, s1, a1 = oracle.quantize_expert_weights(host_w[e][0][None])
+        q2, s2, a2 = oracle.quantize_expert_weights(host_w[e][1][None])
+        return e, ((q1[0], s1[0], q2[0], s2[0]), a1[0], a2[0])
+
+    with ThreadPoolExecutor(threads) as ex:
+        wq = dict(ex.map(quant, experts))
+    del host_w
+    x = bf16_bits_to_f32(s.x_bits)
+
+    def one_run():
+        t0 = time.perf_counter()
+        aq, asf, adec = oracle.quantize_nvfp4(x, oracle.SCALE_PER_ROW)
+        srt_, eids_, P_, ttr_ = oracle.moe_plan(s.ids, wl.E, wl.local_offset, wl.n_local,
+                                               wl.block_m)
+        qp, sp, spd = oracle.moe_permute(aq, asf, adec, srt_, P_, wl.top_k)
+
+        def expert(e):
+            rs = np.array(rows_of[e])
+            (w1q, w1s, w2q, w2s), a1, a2 = wq[e]
+            return rs, oracle.expert_rows_forward(qp[rs], sp[rs], spd[rs], w1q, w1s, w2q, w2s,
+                                                  a1, a1, a2, 1.0, wl.act_code)["y"]
+
+        y = {}
+        with ThreadPoolExecutor(threads) as ex:
+            for rs, ye in ex.map(expert, experts):
+                for i, r in enumerate(rs):
+                    y[int(r)] = ye[i]
+        if max_experts is None:
+            out = oracle.combine(np.zeros((wl.M, wl.H), np.uint16), y, s.w, ttr_)
+        else:
+            out = None
+        return time.perf_counter() - t0, out
+
+    times, out = [], None
+    for _ in range(runs):
+        dt, out = one_run()
+        times.append(dt)
+    dt = float(np.median(times))
+    flops = 2.0 * A_run * (wl.N1 * wl.H + wl.H * wl.I)
+    full_dt = dt * A_all / A_run
+    res = dict(value=wl.M / full_dt, unit="tokens/s", cores=threads, kind="oracle",
+               runs=runs, run_seconds=times, gflops=flops / dt / 1e9,
+               blas_threads="none: the oracle's projections are exact int64 matrix products")
+    if max_experts is None:
+        res["sample"] = ("the whole per-call path of the %s workload (%d tokens, %d experts, %d "
+                         "assignments), median of %d runs, %d threads; weight quantization "
+                         "excluded" % (wl.name, wl.M, len(experts), A_all, runs, threads))
+        import torch
+
+        o = torch.zeros_like(s.out)                   # one fresh GPU forward for the comparison
+        s.fwd(s.x, s.ids_d, s.w_d, out=o, weights=s.weights[0])
+        torch.cuda.synchronize()
+        got = bf16_bits_to_f32(to_bits(o)).astype(np.float64)
+        ref = bf16_bits_to_f32(out).astype(np.float64)
+        res["gpu_vs_oracle_rel_fro"] = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    else:
+        res["sample"] = ("%d of the %d routed experts of the %s workload (%d of %d assignments, "
+                         "chosen across the range of rows per expert), activation quantization "
+                         "and plan over all %d tokens; %.2f s median of %d runs on %d threads, "
+                         "extrapolated to all assignments linearly in their number (%.1f s); "
+                         "weight quantization excluded"
+                         % (len(experts), len(rows_of), wl.name, A_run, A_all, wl.M, dt, runs,
+                            threads, full_dt))
+    return res
 
 
 def time_tiled(wl, label, args, desc):
@@ -430,6 +482,55 @@ def time_tiled(wl, label, args, desc):
                   "frac": ach / F16_MFMA_PEAK_TFLOPS,
                   "traffic": traffic_for(g1_name, label), "flops_per_launch": g1_flops,
                   "avg_launch_ms": g1_ms})
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline (sample):", wl.name)
+        res["cpu_baseline"] = cpu_baseline(s, runs=1, max_experts=8)
+    del s
+    torch.cuda.empty_cache()
+    return res
+
+
+def log(*a):
+    """Progress of the run on stderr (the JSON result is the only line on stdout)."""
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def time_hbm(wl, args, replicas, desc, label, cpu_runs=3):
+    """One weight-streaming (decode) workload: step time with `replicas` rotated copies of the
+    weight panels, the whole step's algorithmic bytes against the HBM peak, the dominant GEMM1
+    launch against its roofline, every kernel's average duration, HIP-graph replay timing and the
+    oracle's CPU baseline of the same call."""
+    import torch
+
+    s, dt, dt_ev, table, breakdown = time_workload(wl, args.steps, args.warmup, replicas)
+    ms = dt / args.steps * 1e3
+    g1_ms, _, g1_name = kernel_ms(table, "gemm1")
+    g1_bytes = gemm_bytes(wl, s.touched, s.A, 1)
+    ach = g1_bytes / (g1_ms * 1e-3) / 1e9
+    sb = step_bytes(wl, s.touched)
+    res = dict(value=wl.M / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
+               config={"workload": desc, "touched_experts": s.touched, "assignments": s.A,
+                       "step_algorithmic_bytes": sb,
+                       "step_hbm_gbs": sb / (ms * 1e-3) / 1e9,
+                       "step_hbm_frac": sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "weight_replicas": replicas,
+                       "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
+                       "kernels": kernel_rooflines(wl, s, breakdown)},
+               roofline={"bound": "hbm", "kernel": g1_name, "achieved": ach,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                         "traffic": traffic_for(g1_name, label), "bytes_per_launch": g1_bytes,
+                         "avg_launch_ms": g1_ms})
+    if not args.no_graph:
+        gdt = time_graph(s, args.steps, args.warmup)
+        res["config"]["graph_replay_ms_per_step"] = gdt / args.steps * 1e3
+        res["config"]["graph_replay_tokens_per_s"] = wl.M / (gdt / args.steps)
+    if not args.no_w4a16 and label == "decode":
+        log("weight-only decode (NVFP4, MXFP4 weights)")
+        res["w4a16_decode"] = time_w4a16(s, args.steps, args.warmup)
+        res["w4a16_mxfp4_decode"] = time_w4a16(s, args.steps, args.warmup, mxfp4=True)
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline:", wl.name)
+        res["cpu_baseline"] = cpu_baseline(s, runs=cpu_runs)
     del s
     torch.cuda.empty_cache()
     return res
@@ -450,64 +551,47 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    result = {}
-    if args.workload in ("decode", "both"):
-        wl = WORKLOADS["decode"]
-        s, dt, dt_ev, table, breakdown = time_workload(wl, args.steps, args.warmup,
-                                                       args.replicas)
-        ms = dt / args.steps * 1e3
-        g1_ms, g1_n, g1_name = kernel_ms(table, "gemm1")
-        g1_bytes = gemm_bytes(wl, s.touched, s.A, 1)
-        ach = g1_bytes / (g1_ms * 1e-3) / 1e9
-        traffic = traffic_for(g1_name, "decode")
-        result.update(
-            metric=METRIC, value=wl.M / (ms * 1e-3), unit="tokens/s", n_gpus=1,
-            steps=args.steps, warmup=args.warmup, ms_per_step=ms, higher_is_better=True,
-            scaling="weak", vs_baseline=None, dtype="f16", data="synthetic",
-            config={"workload": "decode: M=8 H=7168 I=2048 E=256 top_k=8 block_m=8 SwiGLU NVFP4",
-                    "touched_experts": s.touched, "assignments": s.A,
-                    "step_hbm_gbs": step_bytes(wl, s.touched) / (ms * 1e-3) / 1e9,
-                    "step_hbm_frac": step_bytes(wl, s.touched) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "weight_replicas": args.replicas,
-                    "ms_per_step_with_gemm1_events": dt_ev / args.steps * 1e3,
-                    "kernels": kernel_rooflines(wl, s, breakdown)},
-            roofline={"bound": "hbm", "kernel": g1_name, "achieved": ach, "peak": HBM_PEAK_GBS,
-                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                      "bytes_per_launch": g1_bytes, "avg_launch_ms": g1_ms})
-        if not args.no_graph:
-            gdt = time_graph(s, args.steps, args.warmup)
-            result["config"]["graph_replay_ms_per_step"] = gdt / args.steps * 1e3
-            result["config"]["graph_replay_tokens_per_s"] = wl.M / (gdt / args.steps)
-        if not args.no_w4a16:
-            result["w4a16_decode"] = time_w4a16(s, args.steps, args.warmup)
-            result["w4a16_mxfp4_decode"] = time_w4a16(s, args.steps, args.warmup, mxfp4=True)
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline(s)
-        del s
-        torch.cuda.empty_cache()
-    if args.workload in ("prefill", "both"):
-        pre = time_tiled(WORKLOADS["prefill"], "prefill", args,
-                         "prefill: M=4096 H=7168 I=2048 E=256 top_k=8 block_m=128 SwiGLU NVFP4")
-        ms = pre["ms_per_step"]
-        if "value" in result:
-            result["prefill"] = pre
-        else:
-            result.update(metric=METRIC, value=pre["value"], unit="tokens/s", n_gpus=1,
-                          steps=args.steps, warmup=args.warmup, ms_per_step=ms,
-                          higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
-                          data="synthetic", config=pre["config"], roofline=pre["roofline"])
-    if args.workload in ("skewed", "both") and not args.no_skewed:
-        sk = time_tiled(WORKLOADS["skewed_relu2"], "skewed", args,
-                        "skewed: M=16384 H=4096 I=1536 E=288 (experts 0-143 local) top_k=6 "
-                        "block_m=128 squared-ReLU NVFP4, Zipf(1.2) routing")
-        if "value" in result:
-            result["skewed_relu2"] = sk
-        else:
-            result.update(metric=METRIC, value=sk["value"], unit="tokens/s", n_gpus=1,
-                          steps=args.steps, warmup=args.warmup, ms_per_step=sk["ms_per_step"],
-                          higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
-                          data="synthetic", config=sk["config"], roofline=sk["roofline"])
+    want = {"all": ("decode", "decode_ll", "prefill", "skewed"),
+            "both": ("decode", "decode_ll", "prefill", "skewed")}.get(args.workload,
+                                                                      (args.workload,))
+    if args.no_skewed:
+        want = tuple(w for w in want if w != "skewed")
+    parts = []          # (key of the nested object, result), in order; the first is the headline
+    if "decode" in want:
+        log("decode M=8")
+        parts.append(("decode", time_hbm(
+            WORKLOADS["decode"], args, args.replicas,
+            "decode: M=8 H=7168 I=2048 E=256 top_k=8 block_m=8 SwiGLU NVFP4", "decode")))
+    if "decode_ll" in want:
+        log("decode-LL M=4")
+        # 128 experts x 1.77 MB = 226 MB of weights fit the 256 MB MALL: rotate >= 9 copies so
+        # that every step streams its weights from HBM
+        parts.append(("decode_ll", time_hbm(
+            WORKLOADS["decode_ll"], args, max(args.replicas, 10),
+            "decode-LL: M=4 H=2048 I=512 E=128 top_k=10 block_m=8 SwiGLU NVFP4", "decode_ll")))
+    if "prefill" in want:
+        log("prefill M=4096")
+        parts.append(("prefill", time_tiled(
+            WORKLOADS["prefill"], "prefill", args,
+            "prefill: M=4096 H=7168 I=2048 E=256 top_k=8 block_m=128 SwiGLU NVFP4")))
+    if "skewed" in want:
+        log("skewed M=16384")
+        parts.append(("skewed_relu2", time_tiled(
+            WORKLOADS["skewed_relu2"], "skewed", args,
+            "skewed: M=16384 H=4096 I=1536 E=288 (experts 0-143 local) top_k=6 block_m=128 "
+            "squared-ReLU NVFP4, Zipf(1.2) routing")))
+    head = parts[0][1]
+    result = dict(metric=METRIC, value=head["value"], unit="tokens/s", n_gpus=1,
+                  steps=args.steps, warmup=args.warmup, ms_per_step=head["ms_per_step"],
+                  higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f16",
+                  data="synthetic")
+    for k in ("config", "roofline", "cpu_baseline", "w4a16_decode", "w4a16_mxfp4_decode"):
+        if k in head:
+            result[k] = head[k]
+    for key, r in parts[1:]:
+        result[key] = r
     if not args.no_context:
+        log("achievable-peak context")
         result["context"] = achievable_context()
     print(json.dumps(result))
 

@@ -63,7 +63,8 @@ class Bfp4Error(RuntimeError):
 
 class bfp4_debug(ctypes.Structure):
     _fields_ = [("preact", ctypes.c_void_p), ("inter", ctypes.c_void_p),
-                ("inter_q", ctypes.c_void_p), ("inter_sf", ctypes.c_void_p)]
+                ("inter_q", ctypes.c_void_p), ("inter_sf", ctypes.c_void_p),
+                ("inter_f16", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -196,7 +197,8 @@ def bfp4_fused_moe_nvfp4(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, al
     dbg = None
     if debug is not None:
         dbg = ctypes.byref(bfp4_debug(*(_p(debug.get(k)) for k in
-                                        ("preact", "inter", "inter_q", "inter_sf"))))
+                                        ("preact", "inter", "inter_q", "inter_sf",
+                                         "inter_f16"))))
     return _check(_lib.bfp4_fused_moe_nvfp4(
         _p(a_q), _p(a_sf), _p(a_dec), _p(panels), panels_bytes, _p(alpha1_gate), _p(alpha1_up),
         _p(alpha2), c2, _p(sorted_token_ids), _p(expert_ids), _p(num_tokens_post_padded),
@@ -231,7 +233,8 @@ def bfp4_fused_moe_w4a16(x_bf16, row_stride, panels, panels_bytes, weight_format
     dbg = None
     if debug is not None:
         dbg = ctypes.byref(bfp4_debug(*(_p(debug.get(k)) for k in
-                                        ("preact", "inter", "inter_q", "inter_sf"))))
+                                        ("preact", "inter", "inter_q", "inter_sf",
+                                         "inter_f16"))))
     return _check(_lib.bfp4_fused_moe_w4a16(
         _p(x_bf16), row_stride, _p(panels), panels_bytes, weight_format, _p(alpha1_gate),
         _p(alpha1_up),

@@ -292,7 +292,8 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   if (workspace_bytes < ws || !workspace) return BFP4_ERR_WORKSPACE;
   const int64_t N1 = gated ? 2 * I : I;
   if (debug) {
-    if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16) || !aligned(debug->inter_q, 8))
+    if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16) || !aligned(debug->inter_q, 8) ||
+        !aligned(debug->inter_f16, 16))
       return BFP4_ERR_ALIGN;
   }
   {
@@ -326,7 +327,7 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   if (block_m > 32) {
     a16 = reinterpret_cast<uint16_t*>(w);
     w += align_up((size_t)M * H * 2);
-    h16 = reinterpret_cast<uint16_t*>(w);
+    h16 = (debug && debug->inter_f16) ? debug->inter_f16 : reinterpret_cast<uint16_t*>(w);
     w += align_up(capacity * (size_t)I * 2);
   }
   uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
@@ -354,6 +355,7 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
   p.act = act;
   p.hq = hq;
   p.hsf = hsf;
+  p.keep_hq = debug && (debug->inter_q || debug->inter_sf);
   p.y = y;
   p.dbg_pre = debug ? debug->preact : nullptr;
   p.dbg_inter = debug ? debug->inter : nullptr;

@@ -165,7 +165,7 @@ struct GemmArgs {
   int act;                   // activation code (EPI_ACT picks GELU, ReLU, SiLU or Identity by it)
   float c2;
   int64_t I;
-  uint8_t* hq;
+  uint8_t* hq;               // null: the NVFP4 intermediate is not stored
   uint8_t* hsf;
   uint16_t* h16;             // prefill: FP16 copy of the requantized intermediate [cap, I] or null
   float* dbg_pre;
@@ -421,8 +421,10 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
     }
     uint32_t lo, hi;
     const uint32_t sfb = quant_block16(hv, a.c2, lo, hi);
-    *reinterpret_cast<uint2*>(a.hq + roff(a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
-    a.hsf[roff(a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+    if (a.hq) {                  // the tiled down GEMM reads only h16: hq is debug output there
+      *reinterpret_cast<uint2*>(a.hq + roff(a.I >> 1) + (i0 >> 1)) = make_uint2(lo, hi);
+      a.hsf[roff(a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+    }
     if (a.h16) {                 // the same values, E2M1 x E4M3 exactly in FP16
       h8_t* d = reinterpret_cast<h8_t*>(a.h16 + roff(a.I) + i0);
       d[0] = decode8(lo, e4m3_scale_h2(sfb));
@@ -471,8 +473,10 @@ __device__ __forceinline__ void epilogue_group(const GemmArgs& a, const f32x16_t
   float inv;
   const uint32_t sfb = block_scale(bmax, a.c2, inv);
   const uint32_t codes = quant8(hv, inv);
-  *reinterpret_cast<uint32_t*>(a.hq + roff(a.I >> 1) + (ih >> 1)) = codes;
-  if (h == 0) a.hsf[roff(a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+  if (a.hq) {
+    *reinterpret_cast<uint32_t*>(a.hq + roff(a.I >> 1) + (ih >> 1)) = codes;
+    if (h == 0) a.hsf[roff(a.I >> 4) + (i0 >> 4)] = (uint8_t)sfb;
+  }
   if (a.h16)                     // the same values, E2M1 x E4M3 exactly in FP16
     *reinterpret_cast<h8_t*>(a.h16 + roff(a.I) + ih) = decode8(codes, e4m3_scale_h2(sfb));
 }
@@ -1338,8 +1342,10 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.act = p.act;
   g1.c2 = p.c2;
   g1.I = p.I;
-  g1.hq = p.hq;
-  g1.hsf = p.hsf;
+  // the tiled down GEMM reads the FP16 copy h16, so the tiled gate/up GEMM writes the NVFP4
+  // intermediate only when the caller asks for it
+  g1.hq = (small || p.keep_hq) ? p.hq : nullptr;
+  g1.hsf = (small || p.keep_hq) ? p.hsf : nullptr;
   g1.t16 = small ? nullptr : p.a16;
   g1.t16_rowb = p.H * 2;
   g1.h16 = small ? nullptr : p.h16;

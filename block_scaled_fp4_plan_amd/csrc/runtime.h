@@ -72,6 +72,7 @@ struct MoeGemmProblem {
   int nloc, top_k, block_m, act;
   uint8_t* hq;      // [cap, I/2]
   uint8_t* hsf;     // [cap, I/16]
+  bool keep_hq;     // block_m > 32: also store hq / hsf (GEMM2 reads h16 there)
   uint16_t* y;      // [cap, H]
   float* dbg_pre;
   uint16_t* dbg_inter;

@@ -216,6 +216,11 @@ typedef struct {
   uint16_t* inter;      /* [capacity, I] BF16 activation output or NULL */
   uint8_t* inter_q;     /* [capacity, I/2] requantized intermediate or NULL */
   uint8_t* inter_sf;    /* [capacity, I/16] its E4M3 scales or NULL */
+  uint16_t* inter_f16;  /* block_m > 32 only: [capacity, I] FP16, 16-byte aligned, or NULL: the
+                           exact FP16 decode of (inter_q, inter_sf) that the tiled down GEMM
+                           reads as its token operand (the call uses this buffer in place of its
+                           workspace copy); rows that are not routed are left unwritten; unused
+                           (not written) when block_m <= 32 */
 } bfp4_debug;
 
 size_t bfp4_workspace_size(int64_t M, int64_t H, int64_t I, int top_k, int num_local_experts,
@@ -272,7 +277,8 @@ int bfp4_prepare_weights_mxfp4(const uint8_t* w1_q, const uint8_t* w1_sf, const 
  * (bfp4_weight_format) names how the panels were prepared (bfp4_prepare_weights or
  * bfp4_prepare_weights_mxfp4; MXFP4 is exact for scale codes 2..252, where every product stays
  * in BF16's normal range; another value gives BFP4_ERR_MODE); debug->preact gets
- * pre (FP32, before the BF16 rounding), debug->inter h (BF16); inter_q/inter_sf are unused.
+ * pre (FP32, before the BF16 rounding), debug->inter h (BF16); inter_q, inter_sf and inter_f16
+ * are unused.
  * workspace: >= bfp4_workspace_size_w4a16(...) bytes, 256-byte aligned.
  * ---------------------------------------------------------------------------------------------- */
 size_t bfp4_workspace_size_w4a16(int64_t M, int64_t H, int64_t I, int top_k,

@@ -22,7 +22,8 @@ What it computes follows these web pages (cited by page title and section):
   quantize_nvfp4_per_token_input returns one FP32 *decode* scale per token.
 * FlashInfer, "flashinfer.fused_moe.FrostLowLatencyConfig": BF16 rounding of the activation
   output and of expert outputs; the FP4 weight-only mode (BF16 input, pre-activation and
-  intermediate rounding); combine by ordered, separate FP32 multiply and add; expert
+  intermediate rounding); combine with every FP32 product and sum rounded separately, in slot
+  order; expert
   ids outside the routed range are ignored together with their scores.
 
 Where the pages are silent the reading taken is stated next to the code that takes it.
@@ -60,6 +61,8 @@ from .moe import (  # noqa: F401
     is_gated,
     combine,
     dense_loop_moe,
+    expert_down_projection,
+    expert_gate_up_projection,
     expert_rows_forward,
     expert_rows_forward_w16,
     fused_moe_nvfp4,

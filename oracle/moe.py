@@ -158,7 +158,8 @@ def moe_permute(q, sf, dec_scale, sorted_token_ids, num_tokens_post_padded, top_
 
 def quantize_expert_weights(w_bf16_bits):
     """Per-expert NVFP4 of a BF16 stack [E, rows, cols]: one encode scale per expert matrix
-    (Megatron-Core: "one FP32 global scale per expert"; _global_encode_scale / _quantize_expert).
+    (Megatron-Core flashinfer_nvfp4: a single FP32 global scale for each expert;
+    _global_encode_scale / _quantize_expert).
     Returns (q [E, rows, cols/2], sf [E, rows, cols/16], alpha float32 [E]) where alpha is the
     decode scale of each expert matrix.
     """
@@ -175,9 +176,12 @@ def quantize_expert_rows(w_bf16_bits, rows):
     Returns (q [len(rows), C/2], sf [len(rows), C/16], alpha)."""
     from .quant import _encode_scale, quantize_rows
 
-    w = bf16_bits_to_f32(w_bf16_bits)
-    s_enc = _encode_scale(np.max(np.abs(w)))
-    sel = w[np.asarray(rows)]
+    bits = np.asarray(w_bf16_bits, dtype=np.uint16)
+    # amax of the whole matrix: for finite BF16 values the magnitude order is the integer order
+    # of the 15 low bits, so the largest magnitude is the value of the largest such pattern
+    amax = bf16_bits_to_f32(np.array([np.max(bits & np.uint16(0x7FFF))], np.uint16))[0]
+    s_enc = _encode_scale(amax)
+    sel = bf16_bits_to_f32(bits[np.asarray(rows)])
     q, sf = quantize_rows(sel, np.full(sel.shape[0], s_enc, dtype=np.float32))
     return q, sf, (np.float32(1) / s_enc).astype(np.float32)
 
@@ -204,8 +208,8 @@ def _erf(x):
 def _activation(pre, I, act):
     """Typed activation on float64 pre-activations [rows, N1].
 
-    Gated forms split W1's rows as [gate; up] (alphamoe page: "conventional [gate; up] row
-    order"): SwiGLU with default scalars (CudnnGroupedGemmNvfp4Config activation bullet)
+    Gated forms split W1's rows as [gate; up] (alphamoe page: the usual gate-then-up row
+    order): SwiGLU with default scalars (CudnnGroupedGemmNvfp4Config activation bullet)
     h = silu(gate) * up; GeGLU h = gelu(gate) * up.  One-projection forms: squared ReLU
     (Megatron-Core module) h = max(pre, 0)**2; ReLU max(pre, 0); SiLU silu(pre); GELU gelu(pre);
     Identity h = pre.
@@ -237,8 +241,9 @@ def expert_rows_forward(a_q, a_sf, a_dec, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate,
       pre  = (sum_h deq(a) deq(w1)) * a_dec * alpha1   (gate rows * alpha1_gate, up rows *
              alpha1_up: alphamoe page, output1_scale_gate_scalar / output1_scale_scalar)
       h    = activation(pre), rounded to BF16 (FrostLowLatencyConfig: intermediate rounding)
-      hq   = NVFP4 of h with fixed encode scale c2 (CudnnGroupedGemmNvfp4Config: "global scale
-             of one"; c2 = 1 unless a caller folds another constant in)
+      hq   = NVFP4 of h with fixed encode scale c2 (CudnnGroupedGemmNvfp4Config, permutation
+             bullet: the intermediate's global scale is one; c2 = 1 unless a caller folds
+             another constant in)
       y    = bf16((sum_i deq(hq) deq(w2)) * dec(c2) * alpha2)  (alphamoe page,
              output2_scale_scalar; expert outputs BF16 per FrostLowLatencyConfig)
     Returns dict(pre float64 [R, N1], h float64 (BF16 values) [R, I], hq, hsf, y float64
@@ -250,24 +255,52 @@ def expert_rows_forward(a_q, a_sf, a_dec, w1_q, w1_sf, w2_q, w2_sf, alpha1_gate,
     gated = is_gated(act)
     if N1 != (2 * I if gated else I):
         raise ValueError("W1 rows do not match the activation")
-    s1 = dequantize_int(a_q, a_sf) @ dequantize_int(w1_q, w1_sf).T          # exact int64
     # Non-gated FC1 has a single projection; it takes the up/FC1 scale (output1_scale_scalar).
     alpha_rows = np.full(N1, float(alpha1_up), dtype=np.float64)
     if gated:
         alpha_rows[:I] = float(alpha1_gate)
-    pre = (s1.astype(np.float64) * _TWO_M20) * np.asarray(a_dec, np.float64).reshape(R, 1)
-    pre = pre * alpha_rows.reshape(1, N1)
+    pre = expert_gate_up_projection(a_q, a_sf, a_dec, w1_q, w1_sf, alpha_rows)
     h = round_to_bf16(_activation(pre, I, act))
-    hq, hsf, hdec = quantize_nvfp4(h.astype(np.float32), SCALE_FIXED, fixed_encode_scale=c2)
-    s2 = dequantize_int(hq, hsf) @ dequantize_int(w2_q, w2_sf).T            # exact int64
-    y = round_to_bf16((s2.astype(np.float64) * _TWO_M20) * float(hdec[0]) * float(alpha2))
+    hq, hsf, _ = quantize_nvfp4(h.astype(np.float32), SCALE_FIXED, fixed_encode_scale=c2)
+    y = expert_down_projection(hq, hsf, w2_q, w2_sf, alpha2, c2)
     return dict(pre=pre, h=h, hq=hq, hsf=hsf, y=y)
+
+
+def expert_gate_up_projection(a_q, a_sf, a_dec, w1_q, w1_sf, alpha_rows):
+    """GEMM1 pre-activation of one expert (the first step of expert_rows_forward, on its own so
+    that a caller can take any subset of W1's rows):
+      pre[r, n] = (sum_h deq(a[r, h]) deq(w1[n, h])) * a_dec[r] * alpha_rows[n]
+    a_q [R, H/2], a_sf [R, H/16], a_dec float32 [R]; w1_q [N, H/2], w1_sf [N, H/16];
+    alpha_rows [N]: the FP32 scale of each W1 row (alphamoe page, output1_scale_gate_scalar for
+    gate rows, output1_scale_scalar otherwise).  The sum is exact (int64), then two float64
+    products.  Returns float64 [R, N].
+    """
+    R = a_q.shape[0]
+    N = w1_q.shape[0]
+    s1 = dequantize_int(a_q, a_sf) @ dequantize_int(w1_q, w1_sf).T          # exact int64
+    pre = (s1.astype(np.float64) * _TWO_M20) * np.asarray(a_dec, np.float64).reshape(R, 1)
+    return pre * np.asarray(alpha_rows, np.float64).reshape(1, N)
+
+
+def expert_down_projection(hq, hsf, w2_q, w2_sf, alpha2, c2):
+    """GEMM2 of one expert on rows of the requantized intermediate (the last step of
+    expert_rows_forward, on its own so that a caller can apply it to any NVFP4 intermediate):
+      y = bf16((sum_i deq(hq) deq(w2)) * dec(c2) * alpha2)
+    with dec(c2) = fl32(1 / c2), the decode scale the fixed-scale quantizer returns for encode
+    scale c2 (alphamoe page, output2_scale_scalar; expert outputs rounded to BF16 per
+    FrostLowLatencyConfig numerics).  hq [R, I/2], hsf [R, I/16]; w2 [H, I/2] / [H, I/16].
+    Returns float64 BF16 values [R, H].
+    """
+    s2 = dequantize_int(hq, hsf) @ dequantize_int(w2_q, w2_sf).T            # exact int64
+    hdec = np.float32(1) / np.float32(c2)
+    return round_to_bf16((s2.astype(np.float64) * _TWO_M20) * float(hdec) * float(alpha2))
 
 
 def combine(out0_bits, y_rows, topk_weights, token_to_row, routed_scaling_factor=1.0):
     """Finalize: out[t] = bf16(f32(out0[t]) (+) sum_j fl32(w[t,j] * y[row(t,j)])).
 
-    FrostLowLatencyConfig: "ordered, separate FP32 multiplication and addition"; alphamoe page:
+    FrostLowLatencyConfig numerics: each product and each sum rounded to FP32 on its own, in
+    slot order; alphamoe page:
     contributions are added to the existing out values in FP32, converted to BF16 once.
     Reading taken: j ascending; unrouted slots (token_to_row == -1) are skipped and their weights
     never read (FrostLowLatencyConfig: scores of unrouted slots may be NaN/Inf);

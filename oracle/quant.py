@@ -3,14 +3,14 @@
 Test infrastructure (see the package docstring).
 
 The steps follow the pages' description of the format:
-* blocks of NVFP4_BLOCK_SIZE = 16 consecutive values along a row, each with one E4M3 scale
-  (alphamoe_nvfp4_aligned_moe page: "linear, contiguous, and cover 16 logical values each");
+* blocks of NVFP4_BLOCK_SIZE = 16 consecutive values along a row, each with one E4M3 scale,
+  stored in row order without swizzling (alphamoe_nvfp4_aligned_moe page, layout paragraph);
 * one FP32 scale per token (Megatron-Core flashinfer_nvfp4 module text, and
-  quantize_routed_nvfp4_input), per weight matrix (the same module: "one FP32 global scale per
-  expert"; _global_encode_scale), or a fixed global scale of one for the BF16 intermediate
+  quantize_routed_nvfp4_input), one per weight matrix of each expert (the same module,
+  _global_encode_scale), or a fixed global scale of one for the BF16 intermediate
   (CudnnGroupedGemmNvfp4Config page, permutation bullet);
-* the returned FP32 scale is the *decode* scale (vLLM flashinfer_utils,
-  quantize_nvfp4_per_token_input: "one FP32 decode scale per token");
+* the FP32 scale handed back is the *decode* scale, one per token (vLLM flashinfer_utils,
+  quantize_nvfp4_per_token_input);
 * packing: two E2M1 per byte, even logical value in the low nibble (alphamoe page).
 
 Readings taken where the pages are silent (every FP32 step rounds to nearest even, as numpy

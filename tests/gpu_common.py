@@ -75,3 +75,46 @@ class Problem:
     def oracle_plan(self, block_m):
         wl = self.wl
         return oracle.moe_plan(self.ids, wl.E, wl.local_offset, wl.n_local, block_m)
+
+
+def ulp_bf16(v):
+    """Spacing of the BF16 grid at |v| (the normal spacing below the normal range)."""
+    a = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def _abs_products(q_a, sf_a, q_w, sf_w):
+    """sum_k |deq(a[r, k]) deq(w[n, k])| for every (r, n), exactly (float64 of an int64 sum)."""
+    from oracle.quant import dequantize_int
+
+    return (np.abs(dequantize_int(q_a, sf_a)) @ np.abs(dequantize_int(q_w, sf_w)).T).astype(
+        np.float64) * 2.0 ** -20
+
+
+def check_gate_up(pre_gpu, ref, aq, asf, adec, q1, s1, alpha_rows):
+    """GEMM1 pre-activations of the GPU against the oracle's, element by element: the GPU sums
+    the exact products in FP32 in its own order (each addition rounded, at most K of them), then
+    multiplies by the token and expert scales (two FP32 roundings), so
+    |pre_gpu - ref| <= (K * 2^-23 * sum |products|) * s_tok * alpha + 2^-22 |ref|.
+    Returns the largest error as a fraction of its bound."""
+    K = aq.shape[1] * 2
+    sabs = _abs_products(aq, asf, q1, s1)
+    scale = np.asarray(adec, np.float64).reshape(-1, 1) * np.asarray(alpha_rows, np.float64)
+    bound = K * 2.0 ** -23 * sabs * scale + 2.0 ** -22 * np.abs(ref) + 1e-300
+    d = np.abs(np.asarray(pre_gpu, np.float64) - ref)
+    assert np.all(d <= bound), float((d / bound).max())
+    return float((d / bound).max())
+
+
+def check_down(y_gpu, ref, hq, hsf, q2, s2, alpha2, c2=1.0):
+    """GEMM2 (BF16 expert outputs) of the GPU against oracle.expert_down_projection of the same
+    intermediate: the pre-rounding values differ by at most (I * 2^-23 * sum |products| + 2^-22
+    |ref|) * fl32(1/c2) * alpha2, so after the BF16 rounding by at most that plus one BF16 step.
+    Returns (elements that differ, elements, largest error as a fraction of its bound)."""
+    I = hq.shape[1] * 2
+    sabs = _abs_products(hq, hsf, q2, s2)
+    scale = float(np.float32(1) / np.float32(c2)) * float(alpha2)
+    bound = (I * 2.0 ** -23 * sabs + 2.0 ** -22 * np.abs(ref)) * scale + ulp_bf16(ref)
+    d = np.abs(np.asarray(y_gpu, np.float64) - ref)
+    assert np.all(d <= bound), float((d / bound).max())
+    return int(np.count_nonzero(d)), d.size, float((d / bound).max())

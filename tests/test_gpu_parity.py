@@ -17,7 +17,7 @@ from oracle.formats import bf16_bits_to_f32
 from synth import WORKLOADS
 from synth.workloads import Workload
 
-from gpu_common import Problem, np_bits, np_u8, rel_fro, say
+from gpu_common import Problem, check_down, np_bits, np_u8, rel_fro, say
 
 pytestmark = pytest.mark.gpu
 
@@ -257,6 +257,35 @@ def _workload(name):
              "lds_limit": LDS_LIMIT, **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
 
 
+def check_gemm2(p, eids, bm, rows, dbg, y, c2=1.0, max_flip_frac=0.01):
+    """GEMM2 (down projection) against the oracle on the GPU's own intermediate: for every routed
+    plan row r of expert e, y_gpu[r] against oracle.expert_down_projection of (hq[r], hsf[r]) as
+    the GPU wrote them, with W2_e quantized by the oracle, within the FP32-summation bound of
+    check_down; at most max_flip_frac of the outputs may be one BF16 step off.  With block_m > 32
+    the FP16 copy that the tiled down GEMM reads must be the exact decode of (hq, hsf) on every
+    routed row."""
+    hq = np_u8(dbg["inter_q"])
+    hsf = np_u8(dbg["inter_sf"])
+    if "inter_f16" in dbg:
+        h16 = dbg["inter_f16"].cpu().numpy()[rows].astype(np.float64)
+        assert np.array_equal(h16, oracle.dequantize_nvfp4(hq[rows], hsf[rows]))
+    ybits = np_bits(y)
+    by_e = {}
+    for r in rows:
+        by_e.setdefault(int(eids[r // bm]), []).append(r)
+    flips = total = 0
+    worst = 0.0
+    for e, rs in sorted(by_e.items()):
+        (_, _, q2, s2), _, a2 = p.oracle_expert(e)
+        ref = oracle.expert_down_projection(hq[rs], hsf[rs], q2, s2, a2, c2)
+        got = bf16_bits_to_f32(ybits[rs]).astype(np.float64)
+        f, t, w = check_down(got, ref, hq[rs], hsf[rs], q2, s2, a2, c2)
+        flips, total, worst = flips + f, total + t, max(worst, w)
+    say("gemm2: %d of %d outputs one BF16 step off (worst %.2f of the bound)"
+        % (flips, total, worst))
+    assert flips <= max_flip_frac * total
+
+
 def run_gpu_moe(p, block_m, do_finalize=True, debug=True, rsf=1.0):
     wl = p.wl
     pw, lin = runner.prepare_weights(p.w1, p.w2, gated=wl.gated, keep_linear=True)
@@ -332,7 +361,19 @@ def test_fused_moe_matches_oracle(name, bm):
     # unfinalized triple -> finalize == finalized, bit for bit; run-twice determinism
     fwd2 = runner.MoeForward(pw, p.M, k, wl.E, bm, wl.local_offset, do_finalize=False,
                              act=wl.act_code)
-    y, wts, ttr_d = fwd2(p.x, p.ids_d, p.w_d)
+    cap = fwd2.plan.capacity
+    dbg2 = dict(inter_q=torch.zeros((cap, wl.I // 2), dtype=torch.uint8, device="cuda"),
+                inter_sf=torch.zeros((cap, wl.I // 16), dtype=torch.uint8, device="cuda"))
+    if bm > 32:
+        dbg2["inter_f16"] = torch.full((cap, wl.I), float("nan"), dtype=torch.float16,
+                                       device="cuda")
+    y, wts, ttr_d = fwd2(p.x, p.ids_d, p.w_d, debug=dbg2)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_u8(dbg2["inter_q"])[rows], np_u8(dbg["inter_q"])[rows])
+    # GEMM2 on its own: the expert outputs against the oracle's down projection of the GPU's own
+    # requantized intermediate, every routed row (and the tiled kernels' FP16 operand is the
+    # exact decode of that intermediate)
+    check_gemm2(p, eids, bm, rows, dbg2, y)
     out2 = torch.zeros_like(out)
     bf.bfp4_moe_finalize(y, wts, runner.weights_dtype(wts), ttr_d, M, wl.H, k, 1.0, out2)
     torch.cuda.synchronize()

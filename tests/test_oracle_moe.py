@@ -241,8 +241,8 @@ def test_expert_projection_brute_force(act):
             h = _act_ref(act, float(pre[i]), float(pre[I + i]) if gated else None)
             hb = o["h"][r, i]
             assert abs(hb - h) <= abs(h) * 2.0 ** -8 * 1.0001 + 1e-300
-    # the intermediate is requantized with the fixed encode scale 1 (CudnnGroupedGemmNvfp4Config:
-    # "global scale of one"): block scale = E4M3(fl32(bmax / 6)), elements = E2M1(h / scale)
+    # the intermediate is requantized with the fixed encode scale 1 (CudnnGroupedGemmNvfp4Config,
+    # permutation bullet): block scale = E4M3(fl32(bmax / 6)), elements = E2M1(h / scale)
     hb32 = o["h"].astype(np.float32)
     bmax = np.abs(hb32.reshape(R, -1, 16)).max(axis=2)
     assert np.array_equal(o["hsf"], oracle.e4m3_encode((bmax / np.float32(6)).astype(np.float32)))
@@ -259,6 +259,70 @@ def test_expert_projection_brute_force(act):
             s = sum(HQ[r][i] * W2[hh][i] for i in range(I)) * Fraction(float(a2))
             ref = float(s)
             assert abs(o["y"][r, hh] - ref) <= abs(ref) * 2.0 ** -8 * 1.0001 + 1e-300
+
+
+def _bf16_rne(v):
+    """Exact round-to-nearest-even of a Fraction onto the BF16 grid (8 significant bits)."""
+    if v == 0:
+        return Fraction(0)
+    m = abs(v)
+    e = m.numerator.bit_length() - m.denominator.bit_length()     # 2^e <= m < 2^(e+2)
+    if Fraction(2) ** e > m:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= m:
+        e += 1
+    ulp = Fraction(2) ** (e - 7)
+    r = round(m / ulp) * ulp                                      # Fraction round: half to even
+    return r if v > 0 else -r
+
+
+@pytest.mark.parametrize("c2", [1.0, 0.37, 3.0])
+def test_expert_down_projection_brute_force(c2):
+    """GEMM2 on its own: y[r, k] = bf16(sum_i deq(hq[r, i]) deq(w2[k, i]) * fl32(1 / c2) *
+    alpha2) against exact rational arithmetic, the BF16 rounding done exactly on the rational
+    value; c2 != 1 pins the decode factor of the intermediate's fixed scale, and the [H, I]
+    orientation of W2 (output k reads W2 row k) is fixed by its non-square shape."""
+    rng = np.random.default_rng(23)
+    R, H, I = 3, 48, 32
+    hq, hsf = _rand_nvfp4(rng, R, I)
+    w2q, w2sf = _rand_nvfp4(rng, H, I)
+    a2 = np.float32(0.0071)
+    y = oracle.expert_down_projection(hq, hsf, w2q, w2sf, a2, c2)
+    assert y.shape == (R, H)
+    HQ = _exact_matrix(hq, hsf)
+    W2 = _exact_matrix(w2q, w2sf)
+    dec = Fraction(float(np.float32(1) / np.float32(c2)))
+    for r in range(R):
+        for k in range(H):
+            exact = sum(HQ[r][i] * W2[k][i] for i in range(I)) * dec * Fraction(float(a2))
+            assert Fraction(float(y[r, k])) == _bf16_rne(exact), (r, k)
+    # the same step inside the whole expert forward
+    aq, asf = _rand_nvfp4(rng, R, H)
+    w1q, w1sf = _rand_nvfp4(rng, 2 * I, H)
+    o = oracle.expert_rows_forward(aq, asf, np.full(R, 0.05, np.float32), w1q, w1sf, w2q, w2sf,
+                                   np.float32(0.004), np.float32(0.004), a2, c2, oracle.ACT_SWIGLU)
+    assert np.array_equal(o["y"], oracle.expert_down_projection(o["hq"], o["hsf"], w2q, w2sf, a2,
+                                                                c2))
+
+
+def test_gate_up_projection_on_row_subsets():
+    """GEMM1 on a subset of W1's rows (with their per-row scales) equals the same columns of the
+    whole expert's pre-activation, and the row scales multiply their own columns only."""
+    rng = np.random.default_rng(29)
+    R, H, I = 4, 64, 32
+    aq, asf = _rand_nvfp4(rng, R, H)
+    w1q, w1sf = _rand_nvfp4(rng, 2 * I, H)
+    w2q, w2sf = _rand_nvfp4(rng, H, I)
+    adec = rng.uniform(0.01, 0.1, R).astype(np.float32)
+    ag, au = np.float32(0.003), np.float32(0.005)
+    o = oracle.expert_rows_forward(aq, asf, adec, w1q, w1sf, w2q, w2sf, ag, au, np.float32(1),
+                                   1.0, oracle.ACT_SWIGLU)
+    cols = np.array([0, 7, I - 1, I, I + 5, 2 * I - 1])
+    alpha_rows = np.where(cols < I, ag, au)
+    sub = oracle.expert_gate_up_projection(aq, asf, adec, w1q[cols], w1sf[cols], alpha_rows)
+    assert np.array_equal(sub, o["pre"][:, cols])
+    ones = oracle.expert_gate_up_projection(aq, asf, adec, w1q[cols], w1sf[cols], np.ones(6))
+    assert np.array_equal(ones * alpha_rows.astype(np.float64), sub)
 
 
 def test_activation_closed_forms():

@@ -143,3 +143,10 @@ def test_expert_rows_subset_matches_whole_matrix():
     rows = [3, 17, 40, 63]
     q2, sf2, a2 = oracle.quantize_expert_rows(w, rows)
     assert np.array_equal(q2, q[0, rows]) and np.array_equal(sf2, sf[0, rows]) and a2 == a[0]
+    # the largest magnitude negative, in a row that is not selected, next to BF16 subnormals
+    w[9, 5] = bf16_bits(np.array([-0.75]))[0]
+    w[2, :4] = bf16_bits(np.array([1e-40, -1e-40, 3e-39, 0.0]))
+    q, sf, a = oracle.quantize_expert_weights(w[None])
+    q2, sf2, a2 = oracle.quantize_expert_rows(w, rows + [2])
+    assert a2 == a[0] and a2 == np.float32(1) / (np.float32(2688) / np.float32(0.75))
+    assert np.array_equal(q2, q[0, rows + [2]]) and np.array_equal(sf2, sf[0, rows + [2]])
