@@ -50,8 +50,9 @@ EXPORTS = [
     "bfp4_panel_bytes", "bfp4_prepare_weights", "bfp4_workspace_size", "bfp4_fused_moe_nvfp4",
     "bfp4_moe_finalize", "bfp4_profile_begin", "bfp4_profile_end", "bfp4_workspace_size_w4a16",
     "bfp4_fused_moe_w4a16", "bfp4_quantize_mxfp4", "bfp4_prepare_weights_mxfp4",
-    "bfp4_check_topk_ids", "bfp4_check_plan",
+    "bfp4_check_topk_ids", "bfp4_check_plan", "bfp4_fused_moe_nvfp4_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 64 << 20          # BFP4_NOALLOC_SCRATCH_BYTES
 
 
 class Bfp4Error(RuntimeError):
@@ -95,6 +96,9 @@ _sig("bfp4_workspace_size", _SZ, [_I64, _I64, _I64, _I, _I, _I, _I])
 _sig("bfp4_fused_moe_nvfp4", _I,
      [_P, _P, _P, _P, _SZ, _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I,
       _I, _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
+_sig("bfp4_fused_moe_nvfp4_noalloc", _I,
+     [_P, _P, _P, _P, _SZ, _P, _P, _P, _F, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I,
+      _I, _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P])
 _sig("bfp4_moe_finalize", _I, [_P, _P, _I, _P, _I64, _I64, _I, _F, _P, _P])
 _sig("bfp4_workspace_size_w4a16", _SZ, [_I64, _I64, _I64, _I, _I, _I, _I])
 _sig("bfp4_fused_moe_w4a16", _I,
@@ -206,6 +210,25 @@ def bfp4_fused_moe_nvfp4(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, al
         top_k, block_m,
         act, routed_scaling_factor, do_finalize, _p(out), _p(gemm2_out), dbg, _p(workspace),
         workspace_bytes, _s(stream)), "bfp4_fused_moe_nvfp4")
+
+
+def bfp4_fused_moe_nvfp4_noalloc(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, alpha1_up,
+                                 alpha2, c2, sorted_token_ids, expert_ids,
+                                 num_tokens_post_padded, token_to_row, capacity, topk_weights,
+                                 weights_dtype, M, H, I, num_local_experts, top_k, block_m, act,
+                                 routed_scaling_factor, do_finalize, out, gemm2_out, debug,
+                                 stream=None):
+    dbg = None
+    if debug is not None:
+        dbg = ctypes.byref(bfp4_debug(*(_p(debug.get(k)) for k in
+                                        ("preact", "inter", "inter_q", "inter_sf",
+                                         "inter_f16"))))
+    return _check(_lib.bfp4_fused_moe_nvfp4_noalloc(
+        _p(a_q), _p(a_sf), _p(a_dec), _p(panels), panels_bytes, _p(alpha1_gate), _p(alpha1_up),
+        _p(alpha2), c2, _p(sorted_token_ids), _p(expert_ids), _p(num_tokens_post_padded),
+        _p(token_to_row), capacity, _p(topk_weights), weights_dtype, M, H, I, num_local_experts,
+        top_k, block_m, act, routed_scaling_factor, do_finalize, _p(out), _p(gemm2_out), dbg,
+        _s(stream)), "bfp4_fused_moe_nvfp4_noalloc")
 
 
 def bfp4_workspace_size_w4a16(M, H, I, top_k, num_local_experts, block_m, do_finalize):

@@ -84,6 +84,163 @@ KernelTimer::~KernelTimer() {
 
 using namespace bfp4;
 
+namespace {
+
+// Static scratch for bfp4_fused_moe_nvfp4_noalloc: every GPU the library runs on holds one copy
+// of this array (BFP4_NOALLOC_SCRATCH_BYTES) until the process ends.  Host code never uses its
+// name as an address: scratch_address() asks the runtime for the current device's copy once and
+// keeps it per device.
+__device__ __align__(256) uint8_t scratch[BFP4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// The current device's address of `scratch`: looked up with the device current on the first call
+// on that device (several threads may race here; they store the same address), then cached.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BFP4_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxScratchDevices) return BFP4_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BFP4_ERR_DEVICE;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return BFP4_OK;
+}
+
+int fused_nvfp4_impl(const uint8_t* a_q, const uint8_t* a_sf, const float* a_dec,
+                         const void* panels, size_t panels_bytes, const float* alpha1_gate,
+                         const float* alpha1_up, const float* alpha2, float c2,
+                         const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                         const int32_t* num_tokens_post_padded, const int32_t* token_to_row,
+                         size_t capacity, const void* topk_weights, int weights_dtype,
+                         int64_t M, int64_t H, int64_t I, int num_local_experts, int top_k,
+                         int block_m, int act,
+                         float routed_scaling_factor, int do_finalize, uint16_t* out,
+                         uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (act < BFP4_ACT_SWIGLU || act > BFP4_ACT_IDENTITY) return BFP4_ERR_MODE;
+  if (weights_dtype != BFP4_WEIGHTS_F32 && weights_dtype != BFP4_WEIGHTS_BF16) return BFP4_ERR_MODE;
+  const size_t wsz = weights_dtype == BFP4_WEIGHTS_BF16 ? 2 : 4;
+  const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
+  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
+  if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
+  if (!(isfinite(c2) && c2 > 0.0f) || !isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
+  // the tiled (block_m > 32) GEMMs address their FP16 token operands with 32-bit offsets
+  if (block_m > 32 && (M * H * 2 >= (1LL << 31) || (int64_t)capacity * I * 2 >= (1LL << 31)))
+    return BFP4_ERR_SHAPE;
+  // the decode kernels (block_m <= 32) stage a plan block's token rows whole in LDS
+  if (block_m <= 32 && (moe_gemv_lds_bytes(block_m, H) > kMaxLdsBytes ||
+                        moe_gemv_lds_bytes(block_m, I) > kMaxLdsBytes))
+    return BFP4_ERR_SHAPE;
+  // ... and an expert's weight panels with 32-bit offsets
+  if (block_m > 32 &&
+      (panel_matrix_bytes(1, gated ? 2 * I : I, H) >= (1LL << 31) ||
+       panel_matrix_bytes(1, H, I) >= (1LL << 31)))
+    return BFP4_ERR_SHAPE;
+  size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
+  if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
+    return BFP4_ERR_CAPACITY;
+  if (M == 0) return BFP4_OK;
+  if (!a_q || !a_sf || !a_dec || !panels || !alpha1_gate || !alpha1_up || !alpha2 ||
+      !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !token_to_row ||
+      !topk_weights || (do_finalize && !out) || (!do_finalize && !gemm2_out))
+    return BFP4_ERR_NULL;
+  if (!aligned(a_q, 16) || !aligned(a_sf, 16) || !aligned(panels, 16) || !aligned(out, 16) ||
+      !aligned(gemm2_out, 16) || !aligned(a_dec, 4) || !aligned(alpha1_gate, 4) ||
+      !aligned(alpha1_up, 4) || !aligned(alpha2, 4) || !aligned(topk_weights, wsz) ||
+      !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) || !aligned(token_to_row, 4) ||
+      !aligned(workspace, 256))
+    return BFP4_ERR_ALIGN;
+  if (panels_bytes < bfp4_panel_bytes(num_local_experts, H, I, gated)) return BFP4_ERR_WORKSPACE;
+  size_t ws = bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize);
+  if (workspace_bytes < ws || !workspace) return BFP4_ERR_WORKSPACE;
+  const int64_t N1 = gated ? 2 * I : I;
+  if (debug) {
+    if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16) || !aligned(debug->inter_q, 8) ||
+        !aligned(debug->inter_f16, 16))
+      return BFP4_ERR_ALIGN;
+  }
+  {
+    // the destination (out [M, H] when finalizing, else gemm2_out [capacity, H]) overlaps no
+    // input and not the workspace
+    const uint16_t* d = do_finalize ? out : gemm2_out;
+    const size_t ob = (do_finalize ? (size_t)M : capacity) * (size_t)H * 2;
+    const size_t nl = (size_t)num_local_experts * 4, mk = (size_t)M * top_k * 4;
+    if (overlaps(d, ob, a_q, M * H / 2) || overlaps(d, ob, a_sf, M * H / 16) ||
+        overlaps(d, ob, a_dec, M * 4) || overlaps(d, ob, panels, panels_bytes) ||
+        overlaps(d, ob, alpha1_gate, nl) || overlaps(d, ob, alpha1_up, nl) ||
+        overlaps(d, ob, alpha2, nl) || overlaps(d, ob, sorted_token_ids, capacity * 4) ||
+        overlaps(d, ob, expert_ids, capacity / block_m * 4) ||
+        overlaps(d, ob, num_tokens_post_padded, 4) || overlaps(d, ob, token_to_row, mk) ||
+        overlaps(d, ob, topk_weights, (size_t)M * top_k * wsz) ||
+        overlaps(d, ob, workspace, ws))
+      return BFP4_ERR_OVERLAP;
+  }
+  int dc = device_check();
+  if (dc) return dc;
+
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  uint8_t* hq = (debug && debug->inter_q) ? debug->inter_q : w;
+  w += align_up(capacity * (size_t)(I / 2));
+  uint8_t* hsf = (debug && debug->inter_sf) ? debug->inter_sf : w;
+  w += align_up(capacity * (size_t)(I / 16));
+  uint8_t* tile_ws = w;
+  w += align_up(moe_gemm_tile_ws_bytes((int64_t)capacity, block_m));
+  uint16_t* a16 = nullptr;
+  uint16_t* h16 = nullptr;
+  if (block_m > 32) {
+    a16 = reinterpret_cast<uint16_t*>(w);
+    w += align_up((size_t)M * H * 2);
+    h16 = (debug && debug->inter_f16) ? debug->inter_f16 : reinterpret_cast<uint16_t*>(w);
+    w += align_up(capacity * (size_t)I * 2);
+  }
+  uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
+
+  MoeGemmProblem p{};
+  p.a_q = a_q;
+  p.a_sf = a_sf;
+  p.a_dec = a_dec;
+  p.panel1 = static_cast<const uint8_t*>(panels);
+  p.panel2 = p.panel1 + panel_matrix_bytes(num_local_experts, N1, H);
+  p.alpha1_gate = alpha1_gate;
+  p.alpha1_up = alpha1_up;
+  p.alpha2 = alpha2;
+  p.c2 = c2;
+  p.sorted = sorted_token_ids;
+  p.eids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.cap = (int64_t)capacity;
+  p.M = M;
+  p.H = H;
+  p.I = I;
+  p.nloc = num_local_experts;
+  p.top_k = top_k;
+  p.block_m = block_m;
+  p.act = act;
+  p.hq = hq;
+  p.hsf = hsf;
+  p.keep_hq = debug && (debug->inter_q || debug->inter_sf);
+  p.y = y;
+  p.dbg_pre = debug ? debug->preact : nullptr;
+  p.dbg_inter = debug ? debug->inter : nullptr;
+  p.tile_ws = tile_ws;
+  p.a16 = a16;
+  p.h16 = h16;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_moe_gemms(p, s);
+  if (e != hipSuccess) return BFP4_ERR_LAUNCH;
+  if (!do_finalize) return BFP4_OK;
+  return launched(launch_finalize(y, topk_weights, weights_dtype == BFP4_WEIGHTS_BF16,
+                                  token_to_row, M, H, top_k, routed_scaling_factor, out, s));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* bfp4_status_string(int status) {
@@ -252,122 +409,39 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          float routed_scaling_factor, int do_finalize, uint16_t* out,
                          uint16_t* gemm2_out, const bfp4_debug* debug, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (act < BFP4_ACT_SWIGLU || act > BFP4_ACT_IDENTITY) return BFP4_ERR_MODE;
-  if (weights_dtype != BFP4_WEIGHTS_F32 && weights_dtype != BFP4_WEIGHTS_BF16) return BFP4_ERR_MODE;
-  const size_t wsz = weights_dtype == BFP4_WEIGHTS_BF16 ? 2 : 4;
-  const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
-  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
-  if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
-  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
-  if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
-  if (!(isfinite(c2) && c2 > 0.0f) || !isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
-  // the tiled (block_m > 32) GEMMs address their FP16 token operands with 32-bit offsets
-  if (block_m > 32 && (M * H * 2 >= (1LL << 31) || (int64_t)capacity * I * 2 >= (1LL << 31)))
-    return BFP4_ERR_SHAPE;
-  // the decode kernels (block_m <= 32) stage a plan block's token rows whole in LDS
-  if (block_m <= 32 && (moe_gemv_lds_bytes(block_m, H) > kMaxLdsBytes ||
-                        moe_gemv_lds_bytes(block_m, I) > kMaxLdsBytes))
-    return BFP4_ERR_SHAPE;
-  // ... and an expert's weight panels with 32-bit offsets
-  if (block_m > 32 &&
-      (panel_matrix_bytes(1, gated ? 2 * I : I, H) >= (1LL << 31) ||
-       panel_matrix_bytes(1, H, I) >= (1LL << 31)))
-    return BFP4_ERR_SHAPE;
-  size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
-  if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
-    return BFP4_ERR_CAPACITY;
-  if (M == 0) return BFP4_OK;
-  if (!a_q || !a_sf || !a_dec || !panels || !alpha1_gate || !alpha1_up || !alpha2 ||
-      !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !token_to_row ||
-      !topk_weights || (do_finalize && !out) || (!do_finalize && !gemm2_out))
-    return BFP4_ERR_NULL;
-  if (!aligned(a_q, 16) || !aligned(a_sf, 16) || !aligned(panels, 16) || !aligned(out, 16) ||
-      !aligned(gemm2_out, 16) || !aligned(a_dec, 4) || !aligned(alpha1_gate, 4) ||
-      !aligned(alpha1_up, 4) || !aligned(alpha2, 4) || !aligned(topk_weights, wsz) ||
-      !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) || !aligned(token_to_row, 4) ||
-      !aligned(workspace, 256))
-    return BFP4_ERR_ALIGN;
-  if (panels_bytes < bfp4_panel_bytes(num_local_experts, H, I, gated)) return BFP4_ERR_WORKSPACE;
-  size_t ws = bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize);
-  if (workspace_bytes < ws || !workspace) return BFP4_ERR_WORKSPACE;
-  const int64_t N1 = gated ? 2 * I : I;
-  if (debug) {
-    if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16) || !aligned(debug->inter_q, 8) ||
-        !aligned(debug->inter_f16, 16))
-      return BFP4_ERR_ALIGN;
-  }
-  {
-    // the destination (out [M, H] when finalizing, else gemm2_out [capacity, H]) overlaps no
-    // input and not the workspace
-    const uint16_t* d = do_finalize ? out : gemm2_out;
-    const size_t ob = (do_finalize ? (size_t)M : capacity) * (size_t)H * 2;
-    const size_t nl = (size_t)num_local_experts * 4, mk = (size_t)M * top_k * 4;
-    if (overlaps(d, ob, a_q, M * H / 2) || overlaps(d, ob, a_sf, M * H / 16) ||
-        overlaps(d, ob, a_dec, M * 4) || overlaps(d, ob, panels, panels_bytes) ||
-        overlaps(d, ob, alpha1_gate, nl) || overlaps(d, ob, alpha1_up, nl) ||
-        overlaps(d, ob, alpha2, nl) || overlaps(d, ob, sorted_token_ids, capacity * 4) ||
-        overlaps(d, ob, expert_ids, capacity / block_m * 4) ||
-        overlaps(d, ob, num_tokens_post_padded, 4) || overlaps(d, ob, token_to_row, mk) ||
-        overlaps(d, ob, topk_weights, (size_t)M * top_k * wsz) ||
-        overlaps(d, ob, workspace, ws))
-      return BFP4_ERR_OVERLAP;
-  }
+  return fused_nvfp4_impl(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, alpha1_up, alpha2,
+                          c2, sorted_token_ids, expert_ids, num_tokens_post_padded, token_to_row,
+                          capacity, topk_weights, weights_dtype, M, H, I, num_local_experts,
+                          top_k, block_m, act, routed_scaling_factor, do_finalize, out,
+                          gemm2_out, debug, workspace, workspace_bytes, stream);
+}
+
+int bfp4_fused_moe_nvfp4_noalloc(const uint8_t* a_q, const uint8_t* a_sf, const float* a_dec,
+                                 const void* panels, size_t panels_bytes,
+                                 const float* alpha1_gate, const float* alpha1_up,
+                                 const float* alpha2, float c2, const int32_t* sorted_token_ids,
+                                 const int32_t* expert_ids,
+                                 const int32_t* num_tokens_post_padded,
+                                 const int32_t* token_to_row, size_t capacity,
+                                 const void* topk_weights, int weights_dtype, int64_t M,
+                                 int64_t H, int64_t I, int num_local_experts, int top_k,
+                                 int block_m, int act, float routed_scaling_factor,
+                                 int do_finalize, uint16_t* out, uint16_t* gemm2_out,
+                                 const bfp4_debug* debug, void* stream) {
+  // the workspace this call needs must fit the static scratch array; checked before any device
+  // query, so an oversized call fails without touching the device
+  const size_t need = bfp4_workspace_size(M, H, I, top_k, num_local_experts, block_m, do_finalize);
+  if (need > (size_t)BFP4_NOALLOC_SCRATCH_BYTES) return BFP4_ERR_WORKSPACE;
   int dc = device_check();
   if (dc) return dc;
-
-  uint8_t* w = static_cast<uint8_t*>(workspace);
-  uint8_t* hq = (debug && debug->inter_q) ? debug->inter_q : w;
-  w += align_up(capacity * (size_t)(I / 2));
-  uint8_t* hsf = (debug && debug->inter_sf) ? debug->inter_sf : w;
-  w += align_up(capacity * (size_t)(I / 16));
-  uint8_t* tile_ws = w;
-  w += align_up(moe_gemm_tile_ws_bytes((int64_t)capacity, block_m));
-  uint16_t* a16 = nullptr;
-  uint16_t* h16 = nullptr;
-  if (block_m > 32) {
-    a16 = reinterpret_cast<uint16_t*>(w);
-    w += align_up((size_t)M * H * 2);
-    h16 = (debug && debug->inter_f16) ? debug->inter_f16 : reinterpret_cast<uint16_t*>(w);
-    w += align_up(capacity * (size_t)I * 2);
-  }
-  uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
-
-  MoeGemmProblem p{};
-  p.a_q = a_q;
-  p.a_sf = a_sf;
-  p.a_dec = a_dec;
-  p.panel1 = static_cast<const uint8_t*>(panels);
-  p.panel2 = p.panel1 + panel_matrix_bytes(num_local_experts, N1, H);
-  p.alpha1_gate = alpha1_gate;
-  p.alpha1_up = alpha1_up;
-  p.alpha2 = alpha2;
-  p.c2 = c2;
-  p.sorted = sorted_token_ids;
-  p.eids = expert_ids;
-  p.ntpp = num_tokens_post_padded;
-  p.cap = (int64_t)capacity;
-  p.M = M;
-  p.H = H;
-  p.I = I;
-  p.nloc = num_local_experts;
-  p.top_k = top_k;
-  p.block_m = block_m;
-  p.act = act;
-  p.hq = hq;
-  p.hsf = hsf;
-  p.keep_hq = debug && (debug->inter_q || debug->inter_sf);
-  p.y = y;
-  p.dbg_pre = debug ? debug->preact : nullptr;
-  p.dbg_inter = debug ? debug->inter : nullptr;
-  p.tile_ws = tile_ws;
-  p.a16 = a16;
-  p.h16 = h16;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_moe_gemms(p, s);
-  if (e != hipSuccess) return BFP4_ERR_LAUNCH;
-  if (!do_finalize) return BFP4_OK;
-  return launched(launch_finalize(y, topk_weights, weights_dtype == BFP4_WEIGHTS_BF16,
-                                  token_to_row, M, H, top_k, routed_scaling_factor, out, s));
+  void* ws = nullptr;
+  dc = scratch_address(&ws);
+  if (dc) return dc;
+  return fused_nvfp4_impl(a_q, a_sf, a_dec, panels, panels_bytes, alpha1_gate, alpha1_up, alpha2,
+                          c2, sorted_token_ids, expert_ids, num_tokens_post_padded, token_to_row,
+                          capacity, topk_weights, weights_dtype, M, H, I, num_local_experts,
+                          top_k, block_m, act, routed_scaling_factor, do_finalize, out,
+                          gemm2_out, debug, ws, (size_t)BFP4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t bfp4_workspace_size_w4a16(int64_t M, int64_t H, int64_t I, int top_k,

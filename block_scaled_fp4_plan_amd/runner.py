@@ -20,6 +20,7 @@ from . import (
     bfp4_check_plan,
     bfp4_check_topk_ids,
     bfp4_fused_moe_nvfp4,
+    bfp4_fused_moe_nvfp4_noalloc,
     bfp4_fused_moe_w4a16,
     bfp4_moe_plan,
     bfp4_panel_bytes,
@@ -170,8 +171,11 @@ class MoeForward:
     """One forward: plan, per-token activation quantization, fused experts (+ finalize)."""
 
     def __init__(self, weights: PreparedWeights, M, top_k, num_experts, block_m,
-                 local_expert_offset=0, do_finalize=True, device="cuda", act=None):
-        """act: a BFP4_ACT_* code; by default SwiGLU for gated weights, squared ReLU otherwise."""
+                 local_expert_offset=0, do_finalize=True, device="cuda", act=None,
+                 noalloc=False):
+        """act: a BFP4_ACT_* code; by default SwiGLU for gated weights, squared ReLU otherwise.
+        noalloc: call bfp4_fused_moe_nvfp4_noalloc (the library's static scratch) instead of
+        passing a workspace."""
         if act is None:
             act = BFP4_ACT_SWIGLU if weights.gated else BFP4_ACT_RELU2
         if (act in GATED_ACTS) != bool(weights.gated):
@@ -188,9 +192,10 @@ class MoeForward:
         self.a_q = torch.empty((max(M, 1), H // 2), dtype=torch.uint8, device=device)
         self.a_sf = torch.empty((max(M, 1), H // 16), dtype=torch.uint8, device=device)
         self.a_dec = torch.empty(max(M, 1), dtype=torch.float32, device=device)
+        self.noalloc = noalloc
         self.ws_bytes = bfp4_workspace_size(M, H, I, top_k, weights.num_local_experts, block_m,
                                             int(do_finalize))
-        self.ws = _bytes(self.ws_bytes + 256, device)
+        self.ws = None if noalloc else _bytes(self.ws_bytes + 256, device)
         self.gemm2_out = None
         if not do_finalize:
             self.gemm2_out = torch.empty((max(self.plan.capacity, 1), H), dtype=torch.bfloat16,
@@ -209,14 +214,16 @@ class MoeForward:
         if (act in GATED_ACTS) != bool(w.gated):
             raise ValueError("activation %d does not match the weights' gating" % act)
         pl = self.plan
-        bfp4_fused_moe_nvfp4(self.a_q, self.a_sf, self.a_dec, w.panels, w.panels_bytes,
-                             w.alpha1_gate, w.alpha1_up, w.alpha2, c2, pl.sorted_token_ids,
-                             pl.expert_ids, pl.num_tokens_post_padded, pl.token_to_row,
-                             pl.capacity, topk_weights, weights_dtype(topk_weights), M, H, I,
-                             w.num_local_experts,
-                             self.top_k, self.block_m, act, routed_scaling_factor,
-                             int(self.do_finalize), out, self.gemm2_out, debug, self.ws,
-                             self.ws_bytes, stream)
+        args = (self.a_q, self.a_sf, self.a_dec, w.panels, w.panels_bytes, w.alpha1_gate,
+                w.alpha1_up, w.alpha2, c2, pl.sorted_token_ids, pl.expert_ids,
+                pl.num_tokens_post_padded, pl.token_to_row, pl.capacity, topk_weights,
+                weights_dtype(topk_weights), M, H, I, w.num_local_experts, self.top_k,
+                self.block_m, act, routed_scaling_factor, int(self.do_finalize), out,
+                self.gemm2_out, debug)
+        if self.noalloc:
+            bfp4_fused_moe_nvfp4_noalloc(*args, stream)
+        else:
+            bfp4_fused_moe_nvfp4(*args, self.ws, self.ws_bytes, stream)
         return out if self.do_finalize else (self.gemm2_out, topk_weights, pl.token_to_row)
 
 

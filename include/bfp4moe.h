@@ -238,6 +238,35 @@ int bfp4_fused_moe_nvfp4(const uint8_t* a_q, const uint8_t* a_sf, const float* a
                          size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------------------------
+ * The fused expert computation without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, contract and results as bfp4_fused_moe_nvfp4 (the same kernels
+ * run), minus workspace / workspace_bytes: the workspace lives in a static device array of
+ * BFP4_NOALLOC_SCRATCH_BYTES (64 MiB) that every GPU the library runs on holds until the
+ * process ends.  A call whose bfp4_workspace_size(...) exceeds it returns BFP4_ERR_WORKSPACE
+ * before touching the device (e.g. the decode shapes M=8, H=7168, I=2048, 256 experts fit; a
+ * 4096-token prefill does not: use the workspace entry point).  The call allocates nothing and
+ * calls no allocating routine.  Every call on one GPU uses that GPU's one array, so calls that
+ * overlap in time on one GPU (other streams or threads) race and give undefined results: order
+ * them.  The array keeps the last call's contents; nothing in it needs to start at zero (the
+ * kernels clear their counters themselves).  The first call on each device looks the array's
+ * address up (hipGetSymbolAddress, with that device current); make it outside a stream capture.
+ * ---------------------------------------------------------------------------------------------- */
+#define BFP4_NOALLOC_SCRATCH_BYTES (64u << 20)
+int bfp4_fused_moe_nvfp4_noalloc(const uint8_t* a_q, const uint8_t* a_sf, const float* a_dec,
+                                 const void* panels, size_t panels_bytes,
+                                 const float* alpha1_gate, const float* alpha1_up,
+                                 const float* alpha2, float c2, const int32_t* sorted_token_ids,
+                                 const int32_t* expert_ids,
+                                 const int32_t* num_tokens_post_padded,
+                                 const int32_t* token_to_row, size_t capacity,
+                                 const void* topk_weights, int weights_dtype, int64_t M,
+                                 int64_t H, int64_t I, int num_local_experts, int top_k,
+                                 int block_m, int act, float routed_scaling_factor,
+                                 int do_finalize, uint16_t* out, uint16_t* gemm2_out,
+                                 const bfp4_debug* debug, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
  * MXFP4 quantization of BF16 rows [Frost, FP4 weight-only paragraph: E8M0 K32 scales;
  * prepare_mxfp4_weight_only_weights: linear E8M0 scales per 32 K values; vLLM
  * align_moe_weights_for_fi: UE8M0 block scales, 127 = 1.0].  The recipe is not on the pages;
