@@ -57,6 +57,9 @@ def parse():
                     help="skip the achievable-peak context (read stream, vendor BF16 GEMM)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--graph-vs-eager", action="store_true",
+                    help="only run the workload's step eagerly, pause, then as HIP-graph replays "
+                         "(for a kernel trace comparing the two)")
     return ap.parse_args()
 
 
@@ -73,6 +76,27 @@ def calibrate_copy(copies=4):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": copies}))
+
+
+def graph_vs_eager(wl, steps, warmup):
+    """The step `steps` times eagerly, a 50 ms pause, then `steps` replays of the same step
+    captured in HIP graphs (one per weight copy): under a kernel tracer the two phases show the
+    kernels' durations and the idle time between steps of each."""
+    import torch
+
+    s = Setup(wl, 2)
+    for i in range(warmup):
+        s.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s.step(i)
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / steps * 1e3
+    time.sleep(0.05)
+    graph = time_graph(s, steps, warmup) / steps * 1e3
+    print(json.dumps({"workload": wl.name, "eager_ms_per_step": eager,
+                      "graph_replay_ms_per_step": graph}))
 
 
 def kernel_source_digest():
@@ -550,6 +574,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.graph_vs_eager:
+        graph_vs_eager(WORKLOADS["decode" if args.workload in ("all", "both") else
+                                 args.workload], args.steps, args.warmup)
         return
     want = {"all": ("decode", "decode_ll", "prefill", "skewed"),
             "both": ("decode", "decode_ll", "prefill", "skewed")}.get(args.workload,

@@ -51,6 +51,7 @@ EXPORTS = [
     "bfp4_moe_finalize", "bfp4_profile_begin", "bfp4_profile_end", "bfp4_workspace_size_w4a16",
     "bfp4_fused_moe_w4a16", "bfp4_quantize_mxfp4", "bfp4_prepare_weights_mxfp4",
     "bfp4_check_topk_ids", "bfp4_check_plan", "bfp4_fused_moe_nvfp4_noalloc",
+    "bfp4_moe_plan_quantize",
 ]
 NOALLOC_SCRATCH_BYTES = 64 << 20          # BFP4_NOALLOC_SCRATCH_BYTES
 
@@ -89,6 +90,8 @@ _sig("bfp4_plan_workspace_size", _SZ, [_I64, _I, _I])
 _sig("bfp4_moe_plan", _I, [_P, _I64, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _SZ, _P])
 _sig("bfp4_quantize_workspace_size", _SZ, [_I64, _I, _I64])
 _sig("bfp4_quantize_nvfp4", _I, [_P, _I64, _I64, _I64, _I, _I64, _F, _P, _P, _P, _P, _SZ, _P])
+_sig("bfp4_moe_plan_quantize", _I, [_P, _I64, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _SZ,
+                                    _P, _I64, _I64, _P, _P, _P, _P])
 _sig("bfp4_moe_permute", _I, [_P, _P, _P, _I64, _I64, _I, _P, _P, _SZ, _P, _P, _P, _P])
 _sig("bfp4_panel_bytes", _SZ, [_I, _I64, _I64, _I])
 _sig("bfp4_prepare_weights", _I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _P, _SZ, _P])
@@ -168,6 +171,18 @@ def bfp4_quantize_nvfp4(x_bf16, rows, cols, row_stride, mode, group_rows, fixed_
     return _check(_lib.bfp4_quantize_nvfp4(
         _p(x_bf16), rows, cols, row_stride, mode, group_rows, fixed_encode_scale, _p(q), _p(sf),
         _p(dec_scale), _p(workspace), workspace_bytes, _s(stream)), "bfp4_quantize_nvfp4")
+
+
+def bfp4_moe_plan_quantize(topk_ids, M, top_k, num_experts, local_expert_offset,
+                           num_local_experts, block_m, sorted_token_ids, expert_ids,
+                           num_tokens_post_padded, token_to_row, capacity, plan_workspace,
+                           plan_workspace_bytes, x_bf16, H, row_stride, q, sf, dec_scale,
+                           stream=None):
+    return _check(_lib.bfp4_moe_plan_quantize(
+        _p(topk_ids), M, top_k, num_experts, local_expert_offset, num_local_experts, block_m,
+        _p(sorted_token_ids), _p(expert_ids), _p(num_tokens_post_padded), _p(token_to_row),
+        capacity, _p(plan_workspace), plan_workspace_bytes, _p(x_bf16), H, row_stride, _p(q),
+        _p(sf), _p(dec_scale), _s(stream)), "bfp4_moe_plan_quantize")
 
 
 def bfp4_moe_permute(q, sf, dec_scale, M, H, top_k, sorted_token_ids, num_tokens_post_padded,

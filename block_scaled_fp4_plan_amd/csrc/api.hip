@@ -59,6 +59,55 @@ inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool valid_block_m(int bm) { return bm >= 8 && bm % 8 == 0; }
 
+// Host-side argument checks of the plan (bfp4_moe_plan's contract): BFP4_OK or the status.
+int check_plan_args(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
+                    int local_expert_offset, int num_local_experts, int block_m,
+                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                    const int32_t* num_tokens_post_padded, const int32_t* token_to_row,
+                    size_t capacity, const void* workspace, size_t workspace_bytes) {
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
+  if (num_experts <= 0 || num_local_experts <= 0 || num_local_experts > 1024 ||
+      local_expert_offset < 0 || (int64_t)local_expert_offset + num_local_experts > num_experts)
+    return BFP4_ERR_EXPERTS;
+  size_t need = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
+  if (capacity < need || capacity % block_m || capacity >= (1ULL << 31)) return BFP4_ERR_CAPACITY;
+  if (!num_tokens_post_padded || (capacity && (!sorted_token_ids || !expert_ids)) ||
+      (M && (!topk_ids || !token_to_row)))
+    return BFP4_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_post_padded, 4) || !aligned(token_to_row, 4))
+    return BFP4_ERR_ALIGN;
+  size_t ws = bfp4_plan_workspace_size(M, top_k, num_local_experts);
+  if (workspace_bytes < ws || (ws && !workspace)) return BFP4_ERR_WORKSPACE;
+  return BFP4_OK;
+}
+
+// Host-side argument checks of the quantizer (bfp4_quantize_nvfp4's contract).
+int check_quant_args(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row_stride,
+                     int mode, int64_t group_rows, float fixed_encode_scale, const uint8_t* q,
+                     const uint8_t* sf, const float* dec_scale, const void* workspace,
+                     size_t workspace_bytes) {
+  if (mode < 0 || mode > 2) return BFP4_ERR_MODE;
+  if (rows < 0 || cols <= 0 || cols % 32 || row_stride < cols || row_stride % 8 ||
+      rows >= (1LL << 31))
+    return BFP4_ERR_SHAPE;
+  if (mode == BFP4_SCALE_PER_GROUP && (group_rows <= 0 || rows % group_rows)) return BFP4_ERR_SHAPE;
+  if (mode == BFP4_SCALE_FIXED && !(isfinite(fixed_encode_scale) && fixed_encode_scale > 0.0f))
+    return BFP4_ERR_SCALAR;
+  if (rows == 0) return BFP4_OK;
+  if (!x_bf16 || !q || !sf || (mode != BFP4_SCALE_FIXED && !dec_scale)) return BFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q, 8) || !aligned(dec_scale, 4)) return BFP4_ERR_ALIGN;
+  size_t ws = bfp4_quantize_workspace_size(rows, mode, group_rows);
+  if (workspace_bytes < ws || (ws && !workspace)) return BFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return BFP4_ERR_ALIGN;
+  size_t xb = (size_t)((rows - 1) * row_stride + cols) * 2;
+  if (overlaps(x_bf16, xb, q, rows * cols / 2) || overlaps(x_bf16, xb, sf, rows * cols / 16))
+    return BFP4_ERR_OVERLAP;
+  return BFP4_OK;
+}
+
+
 }  // namespace
 
 KernelTimer::KernelTimer(const char* name, hipStream_t stream) : slot_(-1), stream_(stream) {
@@ -284,21 +333,11 @@ int bfp4_moe_plan(const int32_t* topk_ids, int64_t M, int top_k, int num_experts
                   int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
                   int32_t* token_to_row, size_t capacity, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
-  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
-  if (num_experts <= 0 || num_local_experts <= 0 || num_local_experts > 1024 ||
-      local_expert_offset < 0 || (int64_t)local_expert_offset + num_local_experts > num_experts)
-    return BFP4_ERR_EXPERTS;
-  size_t need = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
-  if (capacity < need || capacity % block_m || capacity >= (1ULL << 31)) return BFP4_ERR_CAPACITY;
-  if (!num_tokens_post_padded || (capacity && (!sorted_token_ids || !expert_ids)) ||
-      (M && (!topk_ids || !token_to_row)))
-    return BFP4_ERR_NULL;
-  if (!aligned(topk_ids, 4) || !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
-      !aligned(num_tokens_post_padded, 4) || !aligned(token_to_row, 4))
-    return BFP4_ERR_ALIGN;
-  size_t ws = bfp4_plan_workspace_size(M, top_k, num_local_experts);
-  if (workspace_bytes < ws || (ws && !workspace)) return BFP4_ERR_WORKSPACE;
+  int st = check_plan_args(topk_ids, M, top_k, num_experts, local_expert_offset,
+                           num_local_experts, block_m, sorted_token_ids, expert_ids,
+                           num_tokens_post_padded, token_to_row, capacity, workspace,
+                           workspace_bytes);
+  if (st) return st;
   int dc = device_check();
   if (dc) return dc;
   return launched(launch_plan(topk_ids, M * top_k, top_k, num_experts, local_expert_offset,
@@ -316,27 +355,49 @@ int bfp4_quantize_nvfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int6
                         int mode, int64_t group_rows, float fixed_encode_scale, uint8_t* q,
                         uint8_t* sf, float* dec_scale, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  if (mode < 0 || mode > 2) return BFP4_ERR_MODE;
-  if (rows < 0 || cols <= 0 || cols % 32 || row_stride < cols || row_stride % 8 ||
-      rows >= (1LL << 31))
-    return BFP4_ERR_SHAPE;
-  if (mode == BFP4_SCALE_PER_GROUP && (group_rows <= 0 || rows % group_rows)) return BFP4_ERR_SHAPE;
-  if (mode == BFP4_SCALE_FIXED && !(isfinite(fixed_encode_scale) && fixed_encode_scale > 0.0f))
-    return BFP4_ERR_SCALAR;
+  int st = check_quant_args(x_bf16, rows, cols, row_stride, mode, group_rows, fixed_encode_scale,
+                            q, sf, dec_scale, workspace, workspace_bytes);
+  if (st) return st;
   if (rows == 0) return BFP4_OK;
-  if (!x_bf16 || !q || !sf || (mode != BFP4_SCALE_FIXED && !dec_scale)) return BFP4_ERR_NULL;
-  if (!aligned(x_bf16, 16) || !aligned(q, 8) || !aligned(dec_scale, 4)) return BFP4_ERR_ALIGN;
-  size_t ws = bfp4_quantize_workspace_size(rows, mode, group_rows);
-  if (workspace_bytes < ws || (ws && !workspace)) return BFP4_ERR_WORKSPACE;
-  if (!aligned(workspace, 4)) return BFP4_ERR_ALIGN;
-  size_t xb = (size_t)((rows - 1) * row_stride + cols) * 2;
-  if (overlaps(x_bf16, xb, q, rows * cols / 2) || overlaps(x_bf16, xb, sf, rows * cols / 16))
-    return BFP4_ERR_OVERLAP;
   int dc = device_check();
   if (dc) return dc;
   return launched(launch_quantize(x_bf16, rows, cols, row_stride, mode, group_rows,
                                   fixed_encode_scale, q, sf, dec_scale, workspace,
                                   (hipStream_t)stream));
+}
+
+int bfp4_moe_plan_quantize(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
+                           int local_expert_offset, int num_local_experts, int block_m,
+                           int32_t* sorted_token_ids, int32_t* expert_ids,
+                           int32_t* num_tokens_post_padded, int32_t* token_to_row,
+                           size_t capacity, void* plan_workspace, size_t plan_workspace_bytes,
+                           const uint16_t* x_bf16, int64_t H, int64_t row_stride, uint8_t* q,
+                           uint8_t* sf, float* dec_scale, void* stream) {
+  int st = check_plan_args(topk_ids, M, top_k, num_experts, local_expert_offset,
+                           num_local_experts, block_m, sorted_token_ids, expert_ids,
+                           num_tokens_post_padded, token_to_row, capacity, plan_workspace,
+                           plan_workspace_bytes);
+  if (st) return st;
+  st = check_quant_args(x_bf16, M, H, row_stride, BFP4_SCALE_PER_ROW, 0, 1.0f, q, sf, dec_scale,
+                        nullptr, 0);
+  if (st) return st;
+  int dc = device_check();
+  if (dc) return dc;
+  const int64_t A = M * top_k;
+  hipStream_t s = (hipStream_t)stream;
+  if (M > 0 && plan_uses_small_kernel(A))
+    return launched(launch_plan_quantize(topk_ids, A, num_experts, local_expert_offset,
+                                         num_local_experts, block_m, sorted_token_ids,
+                                         expert_ids, num_tokens_post_padded, token_to_row,
+                                         (int64_t)capacity, x_bf16, M, H, row_stride, q, sf,
+                                         dec_scale, s));
+  hipError_t e = launch_plan(topk_ids, A, top_k, num_experts, local_expert_offset,
+                             num_local_experts, block_m, sorted_token_ids, expert_ids,
+                             num_tokens_post_padded, token_to_row, (int64_t)capacity,
+                             plan_workspace, s);
+  if (e != hipSuccess || M == 0) return launched(e);
+  return launched(launch_quantize(x_bf16, M, H, row_stride, BFP4_SCALE_PER_ROW, 0, 1.0f, q, sf,
+                                  dec_scale, nullptr, s));
 }
 
 int bfp4_moe_permute(const uint8_t* q, const uint8_t* sf, const float* dec_scale, int64_t M,

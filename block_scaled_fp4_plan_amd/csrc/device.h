@@ -95,6 +95,18 @@ __device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float s_
   return sf;
 }
 
+// Load one 16-value BF16 block as floats (two 16-byte loads).
+__device__ __forceinline__ void load_block16(const uint16_t* p, float (&x)[16]) {
+  uint4 a = *reinterpret_cast<const uint4*>(p);
+  uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+
 // Encode scale from an FP32 amax: 2688 / amax, 1 when amax is 0, infinity clamped.
 __device__ __forceinline__ float encode_scale_from_amax(float amax) {
   if (amax == 0.0f) return 1.0f;

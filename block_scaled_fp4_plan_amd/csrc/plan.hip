@@ -139,10 +139,11 @@ __device__ void write_plan_frame(const int* cnt, const int* start, int nloc, int
   for (int64_t p = P + tid; p < cap; p += blockDim.x) sorted[p] = sentinel;
 }
 
-__global__ __launch_bounds__(1024) void plan_small_kernel(
-    const int32_t* __restrict__ ids, int64_t A, int num_experts, int offset, int nloc,
-    int block_m, int32_t* __restrict__ sorted, int32_t* __restrict__ eids,
-    int32_t* __restrict__ ntpp, int32_t* __restrict__ ttr, int64_t cap) {
+// The whole plan in one 1024-thread workgroup (A <= kSmallMax slots).
+__device__ void plan_small(const int32_t* __restrict__ ids, int64_t A, int num_experts,
+                           int offset, int nloc, int block_m, int32_t* __restrict__ sorted,
+                           int32_t* __restrict__ eids, int32_t* __restrict__ ntpp,
+                           int32_t* __restrict__ ttr, int64_t cap) {
   __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
   __shared__ int32_t sid[kSmallMax];          // the ids, read from memory once
   int tid = threadIdx.x;
@@ -163,6 +164,66 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
   __syncthreads();
   if (tid < 64) scatter_wave(sid, 0, A, num_experts, offset, nloc, start, sorted, ttr);
+}
+
+__global__ __launch_bounds__(1024) void plan_small_kernel(
+    const int32_t* __restrict__ ids, int64_t A, int num_experts, int offset, int nloc,
+    int block_m, int32_t* __restrict__ sorted, int32_t* __restrict__ eids,
+    int32_t* __restrict__ ntpp, int32_t* __restrict__ ttr, int64_t cap) {
+  plan_small(ids, A, num_experts, offset, nloc, block_m, sorted, eids, ntpp, ttr, cap);
+}
+
+// Maximum of v over the workgroup (blockDim a multiple of 64, at most 1024 threads).
+__device__ float block_max_any(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = (int)blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = 0.0f;
+  for (int i = 0; i < nw; ++i) r = __builtin_fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+// The plan (workgroup 0) and the per-token NVFP4 quantization of the activations (workgroup
+// 1 + t quantizes row t) in one launch: the two are independent, and each part computes exactly
+// what its own kernel does (the plan through plan_small; the row through the same amax, encode
+// scale and block quantizer as the per-row quantizer, whose result does not depend on how the
+// row's blocks are spread over threads).
+__global__ __launch_bounds__(1024) void plan_quantize_kernel(
+    const int32_t* __restrict__ ids, int64_t A, int num_experts, int offset, int nloc,
+    int block_m, int32_t* __restrict__ sorted, int32_t* __restrict__ eids,
+    int32_t* __restrict__ ntpp, int32_t* __restrict__ ttr, int64_t cap,
+    const uint16_t* __restrict__ x, int64_t cols, int64_t stride, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ sf, float* __restrict__ dec) {
+  if (blockIdx.x == 0) {
+    plan_small(ids, A, num_experts, offset, nloc, block_m, sorted, eids, ntpp, ttr, cap);
+    return;
+  }
+  __shared__ float red[16];
+  const int64_t r = blockIdx.x - 1;
+  const uint16_t* xr = x + r * stride;
+  const int64_t nblk = cols >> 4;
+  float m = 0.0f;
+  for (int64_t b = threadIdx.x; b < nblk; b += blockDim.x) {
+    float v[16];
+    load_block16(xr + b * 16, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  }
+  m = block_max_any(m, red);
+  const float s_enc = encode_scale_from_amax(m);
+  if (threadIdx.x == 0) dec[r] = 1.0f / s_enc;
+  uint8_t* qr = q + r * (cols >> 1);
+  uint8_t* sr = sf + r * nblk;
+  for (int64_t b = threadIdx.x; b < nblk; b += blockDim.x) {
+    float v[16];
+    load_block16(xr + b * 16, v);
+    uint32_t lo, hi;
+    const uint32_t sc = quant_block16(v, s_enc, lo, hi);
+    *reinterpret_cast<uint2*>(qr + b * 8) = make_uint2(lo, hi);
+    sr[b] = (uint8_t)sc;
+  }
 }
 
 __global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restrict__ ids, int64_t A,
@@ -249,6 +310,18 @@ __global__ __launch_bounds__(64) void plan_scatter_kernel(const int32_t* __restr
 }
 
 }  // namespace
+
+hipError_t launch_plan_quantize(const int32_t* ids, int64_t A, int num_experts, int offset,
+                                int nloc, int block_m, int32_t* sorted, int32_t* eids,
+                                int32_t* ntpp, int32_t* ttr, int64_t cap, const uint16_t* x,
+                                int64_t rows, int64_t cols, int64_t stride, uint8_t* q,
+                                uint8_t* sf, float* dec, hipStream_t s) {
+  KernelTimer t("plan_quantize", s);
+  hipLaunchKernelGGL(plan_quantize_kernel, dim3((unsigned)(1 + rows)), dim3(1024), 0, s, ids, A,
+                     num_experts, offset, nloc, block_m, sorted, eids, ntpp, ttr, cap, x, cols,
+                     stride, q, sf, dec);
+  return hipGetLastError();
+}
 
 bool plan_uses_small_kernel(int64_t A) { return A <= kSmallMax; }
 int64_t plan_chunks(int64_t A) { return (A + kChunk - 1) / kChunk; }

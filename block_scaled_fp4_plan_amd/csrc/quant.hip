@@ -16,18 +16,6 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 
-// Load one 16-value BF16 block as floats (two 16-byte loads).
-__device__ __forceinline__ void load_block16(const uint16_t* p, float (&x)[16]) {
-  uint4 a = *reinterpret_cast<const uint4*>(p);
-  uint4 b = *reinterpret_cast<const uint4*>(p + 8);
-  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-  }
-}
-
 __device__ float block_max_256(float v, float* red) {
   v = wave_max(v);
   int w = threadIdx.x >> 6;

@@ -24,6 +24,12 @@ hipError_t launch_plan(const int32_t* ids, int64_t A, int top_k, int num_experts
                        int nloc, int block_m, int32_t* sorted, int32_t* eids, int32_t* ntpp,
                        int32_t* ttr, int64_t cap, void* ws, hipStream_t s);
 bool plan_uses_small_kernel(int64_t A);
+// plan (A <= the one-workgroup limit) and per-row activation quantization in one launch
+hipError_t launch_plan_quantize(const int32_t* ids, int64_t A, int num_experts, int offset,
+                                int nloc, int block_m, int32_t* sorted, int32_t* eids,
+                                int32_t* ntpp, int32_t* ttr, int64_t cap, const uint16_t* x,
+                                int64_t rows, int64_t cols, int64_t stride, uint8_t* q,
+                                uint8_t* sf, float* dec, hipStream_t s);
 int64_t plan_chunks(int64_t A);
 
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride,

@@ -23,6 +23,7 @@ from . import (
     bfp4_fused_moe_nvfp4_noalloc,
     bfp4_fused_moe_w4a16,
     bfp4_moe_plan,
+    bfp4_moe_plan_quantize,
     bfp4_panel_bytes,
     bfp4_plan_capacity,
     bfp4_plan_workspace_size,
@@ -205,9 +206,13 @@ class MoeForward:
                  stream=None, c2=1.0, routed_scaling_factor=1.0):
         w = self.w if weights is None else weights
         M, H, I = self.M, w.H, w.I
-        self.plan.build(topk_ids, self.E, self.offset, stream)
-        bfp4_quantize_nvfp4(x_bf16, M, H, x_bf16.stride(0), BFP4_SCALE_PER_ROW, 0, 1.0, self.a_q,
-                            self.a_sf, self.a_dec, None, 0, stream)
+        pl = self.plan
+        # routing plan and activation quantization (one launch at decode sizes)
+        bfp4_moe_plan_quantize(topk_ids, M, self.top_k, self.E, self.offset, pl.nloc,
+                               self.block_m, pl.sorted_token_ids, pl.expert_ids,
+                               pl.num_tokens_post_padded, pl.token_to_row, pl.capacity, pl.ws,
+                               pl.ws_bytes, x_bf16, H, x_bf16.stride(0), self.a_q, self.a_sf,
+                               self.a_dec, stream)
         if out is None and self.do_finalize:
             out = torch.zeros((M, H), dtype=torch.bfloat16, device=x_bf16.device)
         act = self.act

@@ -135,6 +135,24 @@ int bfp4_quantize_nvfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int6
                         void* stream);
 
 /* ----------------------------------------------------------------------------------------------
+ * Plan and activation quantization of one batch in one call [Alpha, plan paragraph; MCore,
+ * quantize_routed_nvfp4_input; vLLM quantize_nvfp4_per_token_input].  Writes exactly what
+ * bfp4_moe_plan(topk_ids, M, ...) followed by bfp4_quantize_nvfp4(x_bf16, M, H, row_stride,
+ * BFP4_SCALE_PER_ROW, ...) write, with the same arguments, contracts and errors (plan_workspace
+ * is the plan's workspace; x_bf16 [M rows, row_stride] BF16, q [M, H/2], sf [M, H/16],
+ * dec_scale [M]).  The two are independent, so when the plan fits one workgroup
+ * (M * top_k <= 2048 slots, the decode sizes) they run as one kernel launch, which saves a
+ * launch on the latency-bound decode path; larger batches run the two calls' kernels in order.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_moe_plan_quantize(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
+                           int local_expert_offset, int num_local_experts, int block_m,
+                           int32_t* sorted_token_ids, int32_t* expert_ids,
+                           int32_t* num_tokens_post_padded, int32_t* token_to_row,
+                           size_t capacity, void* plan_workspace, size_t plan_workspace_bytes,
+                           const uint16_t* x_bf16, int64_t H, int64_t row_stride, uint8_t* q,
+                           uint8_t* sf, float* dec_scale, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
  * Permutation of quantized token rows into plan order [cuDNN, permutation bullet]:
  * for plan row r < extent with entry f < M*top_k, row r of the outputs is token f / top_k
  * (q_perm [capacity, H/2], sf_perm [capacity, H/16], s_perm [capacity]); sentinel rows and rows

@@ -47,7 +47,15 @@ from .formats import (  # noqa: F401
     round_to_bf16,
     f64_to_bf16_bits,
 )
-from .mx import MX_BLOCK_SIZE, dequantize_mxfp4, e8m0_decode, quantize_mxfp4  # noqa: F401
+from .mx import (  # noqa: F401
+    MX_BLOCK_SIZE,
+    dequantize_mxfp4,
+    dequantize_mxfp8,
+    e8m0_decode,
+    mx_dot,
+    quantize_mxfp4,
+    quantize_mxfp8,
+)
 from .quant import SCALE_FIXED, SCALE_PER_GROUP, SCALE_PER_ROW, dequantize_nvfp4, quantize_nvfp4  # noqa: F401
 from .moe import (  # noqa: F401
     ACT_GEGLU,
@@ -61,6 +69,9 @@ from .moe import (  # noqa: F401
     is_gated,
     combine,
     dense_loop_moe,
+    dense_loop_moe_mx,
+    fused_moe_mx,
+    expert_rows_forward_mx,
     expert_down_projection,
     expert_gate_up_projection,
     expert_rows_forward,

@@ -502,6 +502,98 @@ def fused_moe_w4a16(x_bits, weights, alpha1_gate, alpha1_up, alpha2, sorted_toke
     return res
 
 
+def expert_rows_forward_mx(x_bits, w1_q, w1_sf, w2_q, w2_sf, act):
+    """One expert with MXFP4 weights on MXFP8 activations (FrostLowLatencyConfig, MX paragraph:
+    MXFP4 weights with MXFP8 inputs, the same typed activations, BF16 expert outputs, ordered FP32
+    combine; an MX intermediate quantization contract of its own).
+
+    x_bits: BF16 bit patterns [R, H] of the rows routed to this expert; w1 [N1, H/2] / [N1, H/32]
+    and w2 [H, I/2] / [H, I/32] MXFP4.  Steps (readings taken, mirroring the NVFP4 recipe with the
+    MX formats; MX weights carry no FP32 global scale):
+      a     = MXFP8 of the rows (oracle.mx.quantize_mxfp8, one E8M0 scale per 32 values of H)
+      pre   = sum_h deq(a) deq(W1)          exact, rounded once to float64 (oracle.mx.mx_dot)
+      h     = bf16(activation(pre))         (BF16 intermediate, as in the NVFP4 mode)
+      hq    = MXFP8 of h                    (the MX intermediate quantization, per 32 values of I)
+      y     = bf16(sum_i deq(hq) deq(W2))   (BF16 expert output)
+    Returns dict(a_q, a_sf, pre, h, hq, hsf, y).
+    """
+    from .mx import mx_dot, mxfp4_int, mxfp8_int, quantize_mxfp8
+
+    x = bf16_bits_to_f32(np.asarray(x_bits, np.uint16))
+    N1 = w1_q.shape[0]
+    I = w2_q.shape[1] * 2
+    if N1 != (2 * I if is_gated(act) else I):
+        raise ValueError("W1 rows do not match the activation")
+    aq, asf = quantize_mxfp8(x)
+    pre = mx_dot(*mxfp8_int(aq, asf), *mxfp4_int(w1_q, w1_sf))
+    h = round_to_bf16(_activation(pre, I, act))
+    hq, hsf = quantize_mxfp8(h.astype(np.float32))
+    y = round_to_bf16(mx_dot(*mxfp8_int(hq, hsf), *mxfp4_int(w2_q, w2_sf)))
+    return dict(a_q=aq, a_sf=asf, pre=pre, h=h, hq=hq, hsf=hsf, y=y)
+
+
+def fused_moe_mx(x_bits, weights, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                 token_to_row, topk_weights, top_k, block_m, act, routed_scaling_factor=1.0,
+                 out0_bits=None, do_finalize=True):
+    """Plan-driven forward with MXFP4 weights and MXFP8 activations: every valid plan row r of
+    expert e takes token t = entry // top_k through expert_rows_forward_mx, then the ordered
+    combine of the NVFP4 mode (or the unfinalized triple).
+    weights: (w1_q, w1_sf, w2_q, w2_sf) stacks indexed by local expert, or a callable.
+    Returns dict(out, y {row}, pre {row}, h {row}, hq {row}, hsf {row}, unfinalized)."""
+    get = _experts_from(weights)
+    xb = np.asarray(x_bits, np.uint16)
+    M, H = xb.shape
+    ent = np.asarray(sorted_token_ids, dtype=np.int64)
+    eids = np.asarray(expert_ids, dtype=np.int64)
+    by_expert = {}
+    for b in range(num_tokens_post_padded // block_m):
+        for r in range(b * block_m, (b + 1) * block_m):
+            if ent[r] < M * top_k:                     # padding rows contribute nothing
+                by_expert.setdefault(int(eids[b]), []).append(r)
+    res = dict(y={}, pre={}, h={}, hq={}, hsf={})
+    for e, rs in sorted(by_expert.items()):
+        w1q, w1s, w2q, w2s = get(e)
+        rs = np.array(rs)
+        o = expert_rows_forward_mx(xb[ent[rs] // top_k], w1q, w1s, w2q, w2s, act)
+        for i, r in enumerate(rs):
+            for key in ("y", "pre", "h", "hq", "hsf"):
+                res[key][int(r)] = o[key][i]
+    res["unfinalized"] = (res["y"], np.asarray(topk_weights, np.float32), np.asarray(token_to_row))
+    res["out"] = None
+    if do_finalize:
+        if out0_bits is None:
+            out0_bits = np.zeros((M, H), dtype=np.uint16)
+        res["out"] = combine(out0_bits, res["y"], topk_weights, token_to_row,
+                             routed_scaling_factor)
+    return res
+
+
+def dense_loop_moe_mx(x_bits, weights, topk_ids, topk_weights, num_experts, local_expert_offset,
+                      num_local_experts, act, routed_scaling_factor=1.0):
+    """Per-token reference of the MX mode with no plan (each token and slot in order, then the
+    ordered combine); must equal fused_moe_mx bit for bit."""
+    get = _experts_from(weights)
+    xb = np.asarray(x_bits, np.uint16)
+    M, k = np.asarray(topk_ids).shape
+    acc = np.zeros((M, xb.shape[1]), np.float32)
+    w = np.asarray(topk_weights, dtype=np.float32)
+    rsf = np.float32(routed_scaling_factor)
+    for t in range(M):
+        for j in range(k):
+            gid = int(topk_ids[t, j])
+            e = gid - local_expert_offset
+            if not (0 <= gid < num_experts and 0 <= e < num_local_experts):
+                continue
+            w1q, w1s, w2q, w2s = get(e)
+            o = expert_rows_forward_mx(xb[t:t + 1], w1q, w1s, w2q, w2s, act)
+            p = np.float32(w[t, j]) * o["y"][0].astype(np.float32)
+            if rsf != np.float32(1.0):
+                p = (p * rsf).astype(np.float32)
+            acc[t] = (acc[t] + p).astype(np.float32)
+    r = round_to_bf16(acc.astype(np.float64)).astype(np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
 def unquantized_moe_f64(x_bits, w1_bits_of, w2_bits_of, topk_ids, topk_weights, num_experts,
                         local_expert_offset, num_local_experts, act, routed_scaling_factor=1.0,
                         tokens=None):

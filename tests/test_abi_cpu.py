@@ -315,3 +315,30 @@ def test_check_entry_points_validation():
         assert topk(M=0, topk_ids=None) == "BFP4_ERR_DEVICE"  # an empty routing still reports
         assert plan() == "BFP4_ERR_DEVICE"
         assert plan(capacity=0, sorted_token_ids=None, expert_ids=None) == "BFP4_ERR_DEVICE"
+
+
+def _pq(**kw):
+    args = dict(topk_ids=A, M=16, top_k=2, num_experts=8, local_expert_offset=0,
+                num_local_experts=8, block_m=8, sorted_token_ids=A + 4096, expert_ids=A + 8192,
+                num_tokens_post_padded=A + 12288, token_to_row=A + 16384, capacity=88,
+                plan_workspace=None, plan_workspace_bytes=0, x_bf16=A + 65536, H=256,
+                row_stride=256, q=A + 2 * 65536, sf=A + 3 * 65536, dec_scale=A + 4 * 65536,
+                stream=0)
+    args.update(kw)
+    with pytest.raises(Bfp4Error) as ei:
+        bf.bfp4_moe_plan_quantize(**args)
+    return bf.STATUS[ei.value.status]
+
+
+def test_plan_quantize_validation():
+    """The combined call rejects what either of the two calls it replaces rejects."""
+    assert _pq(block_m=12) == "BFP4_ERR_BLOCK_M"
+    assert _pq(capacity=80) == "BFP4_ERR_CAPACITY"
+    assert _pq(num_local_experts=9) == "BFP4_ERR_EXPERTS"
+    assert _pq(H=250, row_stride=256) == "BFP4_ERR_SHAPE"          # H % 32
+    assert _pq(row_stride=128) == "BFP4_ERR_SHAPE"                  # stride < H
+    assert _pq(x_bf16=A + 65536 + 2) == "BFP4_ERR_ALIGN"
+    assert _pq(q=None) == "BFP4_ERR_NULL"
+    assert _pq(q=A + 65536) == "BFP4_ERR_OVERLAP"                   # q inside x
+    if NO_GPU:
+        assert _pq() == "BFP4_ERR_DEVICE"

@@ -146,6 +146,58 @@ def test_plan_bit_exact(case):
     assert np.array_equal(got[3], want[3])
 
 
+PQ_CASES = [  # (workload, M): one launch (decode sizes), the two-call fallback, an empty batch
+    ("decode", 8), ("decode_ll", 4), ("tiny", 16), ("decode", 300), ("decode", 0)]
+
+
+@pytest.mark.parametrize("name,M", PQ_CASES, ids=["%s-M%d" % c for c in PQ_CASES])
+def test_plan_quantize_equals_separate_calls(name, M):
+    """bfp4_moe_plan_quantize writes exactly what bfp4_moe_plan and bfp4_quantize_nvfp4 (per row)
+    write: checked bit for bit against the two calls and against the oracle, in one launch
+    (M * top_k <= 2048 slots) and through the two-call path above that."""
+    from synth import make_activations, make_routing
+    wl = WORKLOADS[name]
+    say("plan+quantize", name, "M", M)
+    Mg = max(M, 1)
+    x_bits = make_activations(wl, 0, Mg)[:M]
+    ids, _ = make_routing(wl, 0, Mg)
+    ids = np.ascontiguousarray(ids[:M])
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    x = x.reshape(M, wl.H)
+    idd = torch.from_numpy(ids).cuda().reshape(M, wl.top_k)
+    outs = []
+    for fused in (True, False):
+        pb = runner.MoePlanBuffers(M, wl.top_k, wl.n_local, wl.block_m, "cuda")
+        q = torch.full((Mg, wl.H // 2), 0xAB, dtype=torch.uint8, device="cuda")
+        sf = torch.full((Mg, wl.H // 16), 0xAB, dtype=torch.uint8, device="cuda")
+        dec = torch.full((Mg,), float("nan"), device="cuda")
+        if fused:
+            bf.bfp4_moe_plan_quantize(idd, M, wl.top_k, wl.E, wl.local_offset, wl.n_local,
+                                      wl.block_m, pb.sorted_token_ids, pb.expert_ids,
+                                      pb.num_tokens_post_padded, pb.token_to_row, pb.capacity,
+                                      pb.ws, pb.ws_bytes, x, wl.H, wl.H, q, sf, dec)
+        else:
+            pb.build(idd, wl.E, wl.local_offset)
+            if M:
+                bf.bfp4_quantize_nvfp4(x, M, wl.H, wl.H, bf.BFP4_SCALE_PER_ROW, 0, 1.0, q, sf, dec,
+                                       None, 0)
+        torch.cuda.synchronize()
+        cap = pb.capacity
+        outs.append((pb.sorted_token_ids.cpu().numpy()[:cap],
+                     pb.expert_ids.cpu().numpy()[:cap // wl.block_m],
+                     int(pb.num_tokens_post_padded.item()), pb.token_to_row.cpu().numpy()[:M],
+                     np_u8(q)[:M], np_u8(sf)[:M], dec.cpu().numpy()[:M].view(np.uint32)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    srt, eids, P, ttr = oracle.moe_plan(ids.reshape(M, wl.top_k), wl.E, wl.local_offset,
+                                        wl.n_local, wl.block_m)
+    assert outs[0][2] == P and np.array_equal(outs[0][0], srt) and np.array_equal(outs[0][3], ttr)
+    if M:
+        oq, osf, odec = oracle.quantize_nvfp4(bf16_bits_to_f32(x_bits), oracle.SCALE_PER_ROW)
+        assert np.array_equal(outs[0][4], oq) and np.array_equal(outs[0][5], osf)
+        assert np.array_equal(outs[0][6], odec.view(np.uint32))
+
+
 def test_permute_bit_exact():
     wl = WORKLOADS["decode_ll"]
     say("permute", wl.name)
