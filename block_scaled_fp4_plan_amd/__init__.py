@@ -51,7 +51,7 @@ EXPORTS = [
     "bfp4_moe_finalize", "bfp4_profile_begin", "bfp4_profile_end", "bfp4_workspace_size_w4a16",
     "bfp4_fused_moe_w4a16", "bfp4_quantize_mxfp4", "bfp4_prepare_weights_mxfp4",
     "bfp4_check_topk_ids", "bfp4_check_plan", "bfp4_fused_moe_nvfp4_noalloc",
-    "bfp4_moe_plan_quantize",
+    "bfp4_moe_plan_quantize", "bfp4_quantize_mxfp8", "bfp4_workspace_size_mx", "bfp4_fused_moe_mx",
 ]
 NOALLOC_SCRATCH_BYTES = 64 << 20          # BFP4_NOALLOC_SCRATCH_BYTES
 
@@ -108,6 +108,11 @@ _sig("bfp4_fused_moe_w4a16", _I,
      [_P, _I64, _P, _SZ, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I,
       _I, _I, _F, _I, _P, _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
 _sig("bfp4_quantize_mxfp4", _I, [_P, _I64, _I64, _I64, _P, _P, _P])
+_sig("bfp4_quantize_mxfp8", _I, [_P, _I64, _I64, _I64, _P, _P, _P])
+_sig("bfp4_workspace_size_mx", _SZ, [_I64, _I64, _I64, _I, _I, _I, _I])
+_sig("bfp4_fused_moe_mx", _I,
+     [_P, _P, _P, _SZ, _P, _P, _P, _P, _SZ, _P, _I, _I64, _I64, _I64, _I, _I, _I, _I, _F, _I, _P,
+      _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
 _sig("bfp4_prepare_weights_mxfp4", _I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _P, _SZ, _P])
 _sig("bfp4_check_topk_ids", _I, [_P, _I64, _I, _I, _P, _P])
 _sig("bfp4_check_plan", _I, [_P, _P, _P, _SZ, _I64, _I, _I, _I, _P, _P])
@@ -253,6 +258,33 @@ def bfp4_workspace_size_w4a16(M, H, I, top_k, num_local_experts, block_m, do_fin
 def bfp4_quantize_mxfp4(x_bf16, rows, cols, row_stride, q, sf, stream=None):
     return _check(_lib.bfp4_quantize_mxfp4(_p(x_bf16), rows, cols, row_stride, _p(q), _p(sf),
                                            _s(stream)), "bfp4_quantize_mxfp4")
+
+
+def bfp4_quantize_mxfp8(x_bf16, rows, cols, row_stride, q, sf, stream=None):
+    return _check(_lib.bfp4_quantize_mxfp8(_p(x_bf16), rows, cols, row_stride, _p(q), _p(sf),
+                                           _s(stream)), "bfp4_quantize_mxfp8")
+
+
+def bfp4_workspace_size_mx(M, H, I, top_k, num_local_experts, block_m, do_finalize):
+    return _lib.bfp4_workspace_size_mx(M, H, I, top_k, num_local_experts, block_m, do_finalize)
+
+
+def bfp4_fused_moe_mx(a_q, a_sf, panels, panels_bytes, sorted_token_ids, expert_ids,
+                      num_tokens_post_padded, token_to_row, capacity, topk_weights, weights_dtype,
+                      M, H, I, num_local_experts, top_k, block_m, act, routed_scaling_factor,
+                      do_finalize, out, gemm2_out, debug, workspace, workspace_bytes,
+                      stream=None):
+    dbg = None
+    if debug is not None:
+        dbg = ctypes.byref(bfp4_debug(*(_p(debug.get(k)) for k in
+                                        ("preact", "inter", "inter_q", "inter_sf",
+                                         "inter_f16"))))
+    return _check(_lib.bfp4_fused_moe_mx(
+        _p(a_q), _p(a_sf), _p(panels), panels_bytes, _p(sorted_token_ids), _p(expert_ids),
+        _p(num_tokens_post_padded), _p(token_to_row), capacity, _p(topk_weights), weights_dtype,
+        M, H, I, num_local_experts, top_k, block_m, act, routed_scaling_factor, do_finalize,
+        _p(out), _p(gemm2_out), dbg, _p(workspace), workspace_bytes, _s(stream)),
+        "bfp4_fused_moe_mx")
 
 
 def bfp4_prepare_weights_mxfp4(w1_q, w1_sf, w2_q, w2_sf, num_local_experts, H, I, gated, panels,

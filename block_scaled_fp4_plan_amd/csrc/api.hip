@@ -531,6 +531,120 @@ int bfp4_quantize_mxfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int6
                                         (hipStream_t)stream));
 }
 
+int bfp4_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row_stride,
+                        uint8_t* q, uint8_t* sf, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 || row_stride < cols || row_stride % 8 ||
+      rows >= (1LL << 31))
+    return BFP4_ERR_SHAPE;
+  if (rows == 0) return BFP4_OK;
+  if (!x_bf16 || !q || !sf) return BFP4_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16)) return BFP4_ERR_ALIGN;
+  size_t xb = (size_t)((rows - 1) * row_stride + cols) * 2;
+  if (overlaps(x_bf16, xb, q, rows * cols) || overlaps(x_bf16, xb, sf, rows * cols / 32))
+    return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_quantize_mxfp8(x_bf16, rows, cols, row_stride, q, sf,
+                                        (hipStream_t)stream));
+}
+
+size_t bfp4_workspace_size_mx(int64_t M, int64_t H, int64_t I, int top_k, int num_local_experts,
+                              int block_m, int do_finalize) {
+  size_t cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
+  if (H <= 0 || I <= 0) return 0;
+  size_t ws = align_up(cap * (size_t)I) + align_up(cap * (size_t)(I / 32));
+  if (do_finalize) ws += align_up(cap * (size_t)H * 2);
+  return ws;
+}
+
+int bfp4_fused_moe_mx(const uint8_t* a_q, const uint8_t* a_sf, const void* panels,
+                      size_t panels_bytes, const int32_t* sorted_token_ids,
+                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                      const int32_t* token_to_row, size_t capacity, const void* topk_weights,
+                      int weights_dtype, int64_t M, int64_t H, int64_t I, int num_local_experts,
+                      int top_k, int block_m, int act, float routed_scaling_factor,
+                      int do_finalize, uint16_t* out, uint16_t* gemm2_out,
+                      const bfp4_debug* debug, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (act < BFP4_ACT_SWIGLU || act > BFP4_ACT_IDENTITY) return BFP4_ERR_MODE;
+  if (weights_dtype != BFP4_WEIGHTS_F32 && weights_dtype != BFP4_WEIGHTS_BF16) return BFP4_ERR_MODE;
+  const size_t wsz = weights_dtype == BFP4_WEIGHTS_BF16 ? 2 : 4;
+  const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
+  if (!valid_block_m(block_m) || block_m > 32) return BFP4_ERR_BLOCK_M;
+  if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
+  if (!isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
+  size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
+  if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
+    return BFP4_ERR_CAPACITY;
+  if (M == 0) return BFP4_OK;
+  if (!a_q || !a_sf || !panels || !sorted_token_ids || !expert_ids || !num_tokens_post_padded ||
+      !token_to_row || !topk_weights || (do_finalize && !out) || (!do_finalize && !gemm2_out))
+    return BFP4_ERR_NULL;
+  if (!aligned(a_q, 16) || !aligned(a_sf, 4) || !aligned(panels, 16) || !aligned(out, 16) ||
+      !aligned(gemm2_out, 16) || !aligned(topk_weights, wsz) || !aligned(sorted_token_ids, 4) ||
+      !aligned(expert_ids, 4) || !aligned(token_to_row, 4) || !aligned(workspace, 256))
+    return BFP4_ERR_ALIGN;
+  if (panels_bytes < bfp4_panel_bytes(num_local_experts, H, I, gated)) return BFP4_ERR_WORKSPACE;
+  size_t ws = bfp4_workspace_size_mx(M, H, I, top_k, num_local_experts, block_m, do_finalize);
+  if (workspace_bytes < ws || !workspace) return BFP4_ERR_WORKSPACE;
+  const int64_t N1 = gated ? 2 * I : I;
+  if (debug) {
+    if (!aligned(debug->preact, 4) || !aligned(debug->inter, 16) || !aligned(debug->inter_q, 16))
+      return BFP4_ERR_ALIGN;
+  }
+  {
+    const uint16_t* d = do_finalize ? out : gemm2_out;
+    const size_t ob = (do_finalize ? (size_t)M : capacity) * (size_t)H * 2;
+    const size_t mk = (size_t)M * top_k * 4;
+    if (overlaps(d, ob, a_q, M * H) || overlaps(d, ob, a_sf, M * H / 32) ||
+        overlaps(d, ob, panels, panels_bytes) ||
+        overlaps(d, ob, sorted_token_ids, capacity * 4) ||
+        overlaps(d, ob, expert_ids, capacity / block_m * 4) ||
+        overlaps(d, ob, num_tokens_post_padded, 4) || overlaps(d, ob, token_to_row, mk) ||
+        overlaps(d, ob, topk_weights, (size_t)M * top_k * wsz) ||
+        overlaps(d, ob, workspace, ws))
+      return BFP4_ERR_OVERLAP;
+  }
+  int dc = device_check();
+  if (dc) return dc;
+
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  uint8_t* hq = (debug && debug->inter_q) ? debug->inter_q : w;
+  w += align_up(capacity * (size_t)I);
+  uint8_t* hsf = (debug && debug->inter_sf) ? debug->inter_sf : w;
+  w += align_up(capacity * (size_t)(I / 32));
+  uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
+
+  MoeGemmProblem p{};
+  p.a_q = a_q;
+  p.a_sf = a_sf;
+  p.panel1 = static_cast<const uint8_t*>(panels);
+  p.panel2 = p.panel1 + panel_matrix_bytes(num_local_experts, N1, H);
+  p.sorted = sorted_token_ids;
+  p.eids = expert_ids;
+  p.ntpp = num_tokens_post_padded;
+  p.cap = (int64_t)capacity;
+  p.M = M;
+  p.H = H;
+  p.I = I;
+  p.nloc = num_local_experts;
+  p.top_k = top_k;
+  p.block_m = block_m;
+  p.act = act;
+  p.hq = hq;
+  p.hsf = hsf;
+  p.y = y;
+  p.dbg_pre = debug ? debug->preact : nullptr;
+  p.dbg_inter = debug ? debug->inter : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_moe_gemms_mx(p, s) != hipSuccess) return BFP4_ERR_LAUNCH;
+  if (!do_finalize) return BFP4_OK;
+  return launched(launch_finalize(y, topk_weights, weights_dtype == BFP4_WEIGHTS_BF16,
+                                  token_to_row, M, H, top_k, routed_scaling_factor, out, s));
+}
+
 int bfp4_prepare_weights_mxfp4(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_t* w2_q,
                                const uint8_t* w2_sf, int num_local_experts, int64_t H, int64_t I,
                                int gated, void* panels, size_t panels_bytes, void* stream) {

@@ -95,6 +95,34 @@ __device__ __forceinline__ uint32_t quant_block16(const float (&x)[16], float s_
   return sf;
 }
 
+// MX (E8M0 per 32 values) shared scale of a block with largest magnitude amax, for an element
+// format whose largest magnitude has exponent emax (E2M1: 2, E4M3: 8): X = floor(log2(amax)) -
+// emax clamped to [-127, 127]; code = X + 127, or 0 for amax 0 or below the FP32 normal range
+// (where the clamp gives X = -127 as well).  Returns 2^-X, the exact factor that maps the block
+// onto the element grid; a normal float, since amax < 2^128 keeps X <= 127 - emax.
+constexpr int kE2M1Emax = 2;
+constexpr int kE4M3Emax = 8;
+__device__ __forceinline__ float mx_scale_inverse(float amax, int emax, uint32_t& code) {
+  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  int X = ebits == 0 ? -127 : ebits - 127 - emax;
+  X = X < -127 ? -127 : (X > 127 ? 127 : X);
+  code = (amax == 0.0f || ebits == 0) ? 0u : (uint32_t)(X + 127);
+  return __uint_as_float((uint32_t)(127 - X) << 23);        // 2^-X, a normal float (|X| <= 127)
+}
+
+// Four values -> four signed E4M3FN codes of fl32(x * inv) (value i in byte i): nearest on the
+// E4M3 grid with ties to the even code, saturating at 448, sign bit copied from the product.
+__device__ __forceinline__ uint32_t e4m3_pack4(const float* x, float inv) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float y = x[i] * inv;
+    const uint32_t sgn = (__float_as_uint(y) >> 31) << 7;
+    w |= (sgn | f32_to_e4m3(__builtin_fabsf(y))) << (8 * i);
+  }
+  return w;
+}
+
 // Load one 16-value BF16 block as floats (two 16-byte loads).
 __device__ __forceinline__ void load_block16(const uint16_t* p, float (&x)[16]) {
   uint4 a = *reinterpret_cast<const uint4*>(p);

@@ -1194,6 +1194,260 @@ __global__ __launch_bounds__(256, 4) void moe_gemv16_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// MXFP4 weights on MXFP8 activations, decode-sized plan blocks (block_m <= 32), on gfx950's
+// block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4: A = 32 weight rows x 64 K as FP4, B = 64 K
+// x 32 tokens as FP8, E8M0 scales per row or column and 32-value K block, the scale of K block kb
+// given by lane col + 32 kb).  Operand lane layouts, as measured on gfx950 with an in-bounds
+// probe of the instruction: an FP4 operand lane (col, h) holds K values 32 h .. 32 h + 31 of
+// the 64 (low nibble first); an FP8 operand lane holds K values 16 h .. 16 h + 15 and
+// 32 + 16 h .. 32 + 16 h + 15.  The MXFP4 panels already hold, per 64-value chunk, each lane's
+// 16 bytes (row l % 32, K half l / 32: one MX block) and its E8M0 code, so weights go from the
+// load straight into the MFMA with no decode; each lane reads its token's two 16-byte FP8 pieces
+// of the chunk and the E8M0 code of K block h from memory one stage ahead (the block's few rows
+// stay in L2).  Same tasks and weight stream as moe_gemv16_kernel.  The instruction's internal
+// sum of a chunk's 64 products is not exact to FP32 (measured: within 2^-13.4 of the sum of the
+// products' magnitudes); the running sum over chunks is FP32.
+//   GEMM1  pre = sum_h a w1 (no FP32 scales: MX weights and activations carry only E8M0 block
+//          scales) -> activation -> BF16 -> MXFP8 of each 32-value block of the intermediate
+//   GEMM2  y = bf16(sum_i hq w2)
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// GEMM1 epilogue of the MX mode for the wave's two row groups g0 (even) and g0 + 1, token row r:
+// pre -> activation -> BF16 -> MXFP8 with one E8M0 scale per 32 intermediate values.  Gated: the
+// groups hold the gate and up rows of intermediate values 16 g0 .. 16 g0 + 31, one MX block;
+// after the lane-pair swap lane (col, h) holds 16 g + 8 h + 0..7 of each group.  One projection:
+// group g holds the MX block 32 g .. 32 g + 31, lane h its values 16 h .. 16 h + 15.  The block
+// maximum is taken over the lane pair (l, l ^ 32).
+template <int EPI>
+__device__ __forceinline__ void epilogue_mx(const GemmArgs& a, const f32x16_t (&acc)[2],
+                                            int64_t g0, int h, int64_t r) {
+  uint8_t* hq = a.hq + r * a.I;                     // MXFP8 intermediate: I bytes per row
+  uint8_t* hsf = a.hsf + r * (a.I >> 5);
+  if (one_projection(EPI)) {
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      const int64_t i0 = (g0 + fn) * kGroupRows + 16 * h;
+      float pr[16], hv[16];
+      uint32_t bb[16];
+      float m = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        pr[v] = acc[fn][v];
+        float q;
+        if (EPI == EPI_RELU2) {
+          const float t = pr[v] > 0.0f ? pr[v] : 0.0f;
+          q = t * t;
+        } else {
+          q = act_one(pr[v], a.act);
+        }
+        bb[v] = f32_to_bf16(q);
+        hv[v] = bf16_to_f32(bb[v]);
+        m = __builtin_fmaxf(m, __builtin_fabsf(hv[v]));
+      }
+      if (a.dbg_pre) {
+        float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * a.I + i0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          dp[v] = make_float4(pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]);
+      }
+      if (a.dbg_inter) {
+        uint4* d = reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + i0);
+        d[0] = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
+                          bb[6] | (bb[7] << 16));
+        d[1] = make_uint4(bb[8] | (bb[9] << 16), bb[10] | (bb[11] << 16),
+                          bb[12] | (bb[13] << 16), bb[14] | (bb[15] << 16));
+      }
+      const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                       false, false);
+      m = __builtin_fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
+      uint32_t code;
+      const float inv = mx_scale_inverse(m, kE4M3Emax, code);
+      *reinterpret_cast<uint4*>(hq + i0) =
+          make_uint4(e4m3_pack4(hv, inv), e4m3_pack4(hv + 4, inv), e4m3_pack4(hv + 8, inv),
+                     e4m3_pack4(hv + 12, inv));
+      if (h == 0) hsf[(g0 + fn)] = (uint8_t)code;
+    }
+    return;
+  }
+  // SwiGLU, GeGLU
+  float hv[2][8];
+  uint32_t bb[2][8];
+  float m = 0.0f;
+#pragma unroll
+  for (int fn = 0; fn < 2; ++fn) {
+    const int64_t i0 = (g0 + fn) * 16;
+    if (a.dbg_pre) {
+      float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + h * a.I + i0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dp[v] = make_float4(acc[fn][4 * v], acc[fn][4 * v + 1], acc[fn][4 * v + 2],
+                            acc[fn][4 * v + 3]);
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const auto gu = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[fn][v]),
+                                                       __float_as_uint(acc[fn][8 + v]), false,
+                                                       false);
+      const float gt = __uint_as_float(gu[0]);
+      const float up = __uint_as_float(gu[1]);
+      bb[fn][v] = f32_to_bf16((EPI == EPI_GEGLU ? gelu(gt) : silu(gt)) * up);
+      hv[fn][v] = bf16_to_f32(bb[fn][v]);
+      m = __builtin_fmaxf(m, __builtin_fabsf(hv[fn][v]));
+    }
+    if (a.dbg_inter) {
+      *reinterpret_cast<uint4*>(a.dbg_inter + r * a.I + i0 + 8 * h) =
+          make_uint4(bb[fn][0] | (bb[fn][1] << 16), bb[fn][2] | (bb[fn][3] << 16),
+                     bb[fn][4] | (bb[fn][5] << 16), bb[fn][6] | (bb[fn][7] << 16));
+    }
+  }
+  const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                   false, false);
+  m = __builtin_fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
+  uint32_t code;
+  const float inv = mx_scale_inverse(m, kE4M3Emax, code);
+#pragma unroll
+  for (int fn = 0; fn < 2; ++fn)
+    *reinterpret_cast<uint2*>(hq + (g0 + fn) * 16 + 8 * h) =
+        make_uint2(e4m3_pack4(hv[fn], inv), e4m3_pack4(hv[fn] + 4, inv));
+  if (h == 0) hsf[g0 >> 1] = (uint8_t)code;
+}
+
+template <int EPI, int RING>
+__global__ __launch_bounds__(256, 4) void moe_gemv_mx_kernel(GemmArgs a) {
+  constexpr int FN = 2;                       // the gated MX block spans two row groups
+  __shared__ int row_src[32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  int64_t P = *a.ntpp;
+  if (P > a.cap) P = a.cap;
+  if (P < 0) P = 0;
+  const int64_t nblk = P / a.block_m;
+  const int nst = a.nch / kStageChunks;
+  const int rows_max = min(a.block_m, 32);
+  const int64_t ntask = nblk * a.n_nt;
+  const int64_t K = a.a_rowq;                 // FP8 token row: K bytes, then K / 32 scale codes
+
+  for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const int64_t b = task / a.n_nt;
+    const int nt = (int)(task - b * a.n_nt);
+    const int e = a.eids[b];
+    if (e < 0 || e >= a.nloc) continue;
+    __syncthreads();                                   // previous task done with row_src
+    if (tid < 32) {
+      int src = -1;
+      if (tid < rows_max) {
+        const int64_t ent = a.sorted[b * a.block_m + tid];
+        if (ent >= 0 && ent < a.sentinel) src = a.gather ? (int)(ent / a.top_k)
+                                                         : (int)(b * a.block_m + tid);
+      }
+      row_src[tid] = src;
+    }
+    __syncthreads();
+
+    const int64_t g0 = (int64_t)nt * (4 * FN) + (int64_t)wave * FN;
+    const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
+    const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
+                           lane * 16;
+    // only lanes of routed rows read token data; the others feed zeros (their columns are
+    // dropped)
+    const int my_src = col < rows_max ? row_src[col] : -1;
+    const bool tok_on = my_src >= 0;
+    const uint8_t* trow = a.a_q + (int64_t)(tok_on ? my_src : 0) * K + 16 * h;
+    const uint8_t* tsf = a.a_sf + (int64_t)(tok_on ? my_src : 0) * (K >> 5);
+
+    f32x16_t acc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x16_t{};
+    uint4 W[RING][kStageChunks][FN];
+    uint32_t S[RING][FN];
+
+    auto load_w = [&](uint4 (&Wd)[kStageChunks][FN], uint32_t (&Sd)[FN], int st) {
+      const int64_t sc = st / (kSuperChunks / kStageChunks);
+      const int c0 = (st * kStageChunks) % kSuperChunks;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const uint8_t* base = wbase + fn * a.rg_bytes + sc * kSuperBytes;
+        Sd[fn] = *reinterpret_cast<const uint32_t*>(base + 2 * c0);
+#pragma unroll
+        for (int c = 0; c < kStageChunks; ++c)
+          Wd[c][fn] = *reinterpret_cast<const uint4*>(base + kUnit + (c0 + c) * kUnit);
+      }
+    };
+    // token operand of one stage: per chunk the FP8 bytes 16 h .. 16 h + 15 and 32 + 16 h ..
+    // 32 + 16 h + 15 (the FP8 operand's lane layout), and the stage's four E8M0 codes (chunk c,
+    // K block h: byte 2 c + h)
+    auto load_t = [&](uint4 (&T)[kStageChunks][2], uint32_t& TS, int st) {
+#pragma unroll
+      for (int c = 0; c < kStageChunks; ++c) {
+        const uint4* p = reinterpret_cast<const uint4*>(trow + (int64_t)(st * kStageChunks + c) * 64);
+        T[c][0] = tok_on ? p[0] : make_uint4(0, 0, 0, 0);
+        T[c][1] = tok_on ? p[2] : make_uint4(0, 0, 0, 0);
+      }
+      TS = tok_on ? *reinterpret_cast<const uint32_t*>(tsf + st * 4) : 0u;
+    };
+    auto compute = [&](const uint4 (&Wd)[kStageChunks][FN], const uint32_t (&Sd)[FN],
+                       const uint4 (&T)[kStageChunks][2], uint32_t TS) {
+#pragma unroll
+      for (int c = 0; c < kStageChunks; ++c) {
+        const i32x8_t B = {(int)T[c][0].x, (int)T[c][0].y, (int)T[c][0].z, (int)T[c][0].w,
+                           (int)T[c][1].x, (int)T[c][1].y, (int)T[c][1].z, (int)T[c][1].w};
+        const int sb = (int)((TS >> (8 * (2 * c + h))) & 0xFFu);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const i32x8_t A = {(int)Wd[c][fn].x, (int)Wd[c][fn].y, (int)Wd[c][fn].z,
+                             (int)Wd[c][fn].w, 0, 0, 0, 0};
+          const int sa = (int)((Sd[fn] >> (16 * c)) & 0xFFu);   // chunk c0 + c of the stage
+          acc[fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[fn], 4, 0, 0, sa, 0,
+                                                                    sb);
+        }
+      }
+    };
+
+    uint4 T[RING][kStageChunks][2];
+    uint32_t TS[RING];
+#pragma unroll
+    for (int d = 0; d < RING - 1; ++d) {
+      load_w(W[d], S[d], min(d, nst - 1));
+      load_t(T[d], TS[d], min(d, nst - 1));
+    }
+    for (int st0 = 0; st0 < nst; st0 += RING) {
+#pragma unroll
+      for (int d = 0; d < RING; ++d) {
+        const int st = st0 + d;
+        if (st >= nst) break;
+        const int nd = (d + RING - 1) % RING;
+        load_w(W[nd], S[nd], min(st + RING - 1, nst - 1));
+        load_t(T[nd], TS[nd], min(st + RING - 1, nst - 1));
+        compute(W[d], S[d], T[d], TS[d]);
+      }
+    }
+    if (wave_on && tok_on) {
+      const int64_t r = b * a.block_m + col;
+      if (EPI == EPI_DOWN) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) epilogue_group<EPI_DOWN>(a, acc[fn], 1.0f, g0 + fn, h, 1.0f, r);
+      } else {
+        epilogue_mx<EPI>(a, acc, g0, h, r);
+      }
+    }
+  }
+}
+
+template <int EPI>
+hipError_t launch_gemv_mx(const GemmArgs& a, int64_t cap_blocks, const char* name,
+                          hipStream_t s) {
+  const int64_t tasks = cap_blocks * a.n_nt;
+  const int64_t max_wg = 256LL * 4;                  // resident workgroups (4 waves each)
+  const int64_t grid = tasks < max_wg ? tasks : max_wg;
+  if (grid == 0) return hipSuccess;
+  KernelTimer t(name, s);
+  hipLaunchKernelGGL((moe_gemv_mx_kernel<EPI, 2>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int FN, int EPI, bool MX>
 hipError_t launch_gemv16(const GemmArgs& a, int64_t cap_blocks, const char* name,
                          hipStream_t s) {
@@ -1482,6 +1736,74 @@ hipError_t launch_moe_gemms_w16_fmt(const MoeGemmW16& w, hipStream_t s) {
                                 : launch_gemv16<FN, EPI_ACT, MX>(g1, cap_blocks, nm, s);
   if (err != hipSuccess) return err;
   return launch_gemv16<FN, EPI_DOWN, MX>(g2, cap_blocks, "gemm2_down_w16_decode", s);
+}
+
+hipError_t launch_moe_gemms_mx(const MoeGemmProblem& p, hipStream_t s) {
+  const bool gated = p.act == BFP4_ACT_SWIGLU || p.act == BFP4_ACT_GEGLU;
+  const int64_t N1 = gated ? 2 * p.I : p.I;
+  const int64_t cap_blocks = p.cap / p.block_m;
+  constexpr int FN = 2;
+  if (p.block_m > 32) return hipErrorInvalidValue;
+
+  GemmArgs g1{};
+  g1.a_q = p.a_q;
+  g1.a_sf = p.a_sf;
+  g1.a_rows = p.M;
+  g1.a_rowq = p.H;                 // MXFP8 row: H bytes
+  g1.gather = 1;
+  g1.sorted = p.sorted;
+  g1.eids = p.eids;
+  g1.ntpp = p.ntpp;
+  g1.cap = p.cap;
+  g1.sentinel = p.M * p.top_k;
+  g1.top_k = p.top_k;
+  g1.block_m = p.block_m;
+  g1.nloc = p.nloc;
+  const PanelGeom pg1 = panel_geom(N1, p.H);
+  g1.panel = p.panel1;
+  g1.expert_bytes = pg1.expert_bytes;
+  g1.rg_bytes = pg1.rg_bytes;
+  g1.nch = (int)pg1.nch;
+  g1.N = (int)N1;
+  g1.n_nt = (int)((N1 + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g1.act = p.act;
+  g1.I = p.I;
+  g1.hq = p.hq;
+  g1.hsf = p.hsf;
+  g1.dbg_pre = p.dbg_pre;
+  g1.dbg_inter = p.dbg_inter;
+
+  GemmArgs g2 = g1;
+  g2.a_q = p.hq;
+  g2.a_sf = p.hsf;
+  g2.a_rows = p.cap;
+  g2.a_rowq = p.I;
+  g2.gather = 0;
+  const PanelGeom pg2 = panel_geom(p.H, p.I);
+  g2.panel = p.panel2;
+  g2.expert_bytes = pg2.expert_bytes;
+  g2.rg_bytes = pg2.rg_bytes;
+  g2.nch = (int)pg2.nch;
+  g2.N = (int)p.H;
+  g2.n_nt = (int)((p.H + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g2.y = p.y;
+  g2.Hout = p.H;
+  g2.hq = nullptr;
+  g2.hsf = nullptr;
+  g2.dbg_pre = nullptr;
+  g2.dbg_inter = nullptr;
+
+  static const char* const kName[] = {
+      "gemm1_swiglu_mx_decode", "gemm1_relu2_mx_decode", "gemm1_geglu_mx_decode",
+      "gemm1_gelu_mx_decode", "gemm1_relu_mx_decode", "gemm1_silu_mx_decode",
+      "gemm1_identity_mx_decode"};
+  const char* nm = kName[p.act];
+  hipError_t err = p.act == BFP4_ACT_SWIGLU ? launch_gemv_mx<EPI_SWIGLU>(g1, cap_blocks, nm, s)
+                 : p.act == BFP4_ACT_RELU2  ? launch_gemv_mx<EPI_RELU2>(g1, cap_blocks, nm, s)
+                 : p.act == BFP4_ACT_GEGLU  ? launch_gemv_mx<EPI_GEGLU>(g1, cap_blocks, nm, s)
+                                            : launch_gemv_mx<EPI_ACT>(g1, cap_blocks, nm, s);
+  if (err != hipSuccess) return err;
+  return launch_gemv_mx<EPI_DOWN>(g2, cap_blocks, "gemm2_down_mx_decode", s);
 }
 
 hipError_t launch_moe_gemms_w16(const MoeGemmW16& w, hipStream_t s) {

@@ -145,6 +145,37 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_mxfp4_kernel(
   }
 }
 
+// MXFP8 (E4M3 elements with one E8M0 scale per 32 values): one workgroup per row, one thread per
+// block of 32.  Shared exponent X = floor(log2(amax)) - 8 (8: the exponent of E4M3's largest
+// magnitude, 448 = 1.75 * 2^8), clamped to [-127, 127], scale code X + 127; amax 0 (or below the
+// FP32 normal range, where the clamp gives X = -127 anyway) gives code 0; elements are E4M3 of
+// x * 2^-X (an exact power-of-two product), nearest with ties to even, saturating at 448, with
+// the input's sign bit.
+__global__ __launch_bounds__(kQuantThreads) void quantize_mxfp8_kernel(
+    const uint16_t* __restrict__ x, int64_t cols, int64_t stride, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ sf) {
+  const int64_t r = blockIdx.x;
+  const uint16_t* xr = x + r * stride;
+  const int64_t nblk = cols >> 5;
+  for (int64_t b = threadIdx.x; b < nblk; b += kQuantThreads) {
+    float v[32];
+    load_block16(xr + b * 32, *reinterpret_cast<float(*)[16]>(v));
+    load_block16(xr + b * 32 + 16, *reinterpret_cast<float(*)[16]>(v + 16));
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    uint32_t code;
+    const float inv = mx_scale_inverse(amax, kE4M3Emax, code);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = e4m3_pack4(v + 4 * k, inv);
+    uint4* dst = reinterpret_cast<uint4*>(q + r * cols + b * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    sf[r * nblk + b] = (uint8_t)code;
+  }
+}
+
 // Permute: one workgroup of 64 threads per capacity row.
 __global__ __launch_bounds__(64) void permute_kernel(const uint8_t* __restrict__ q,
                                                      const uint8_t* __restrict__ sf,
@@ -247,6 +278,15 @@ hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, 
   if (rows == 0) return hipSuccess;
   KernelTimer t("quantize_mxfp4", s);
   hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3((unsigned)rows), dim3(kQuantThreads), 0, s, x,
+                     cols, stride, q, sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride,
+                                uint8_t* q, uint8_t* sf, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  KernelTimer t("quantize_mxfp8", s);
+  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)rows), dim3(kQuantThreads), 0, s, x,
                      cols, stride, q, sf);
   return hipGetLastError();
 }

@@ -32,6 +32,8 @@ hipError_t launch_plan_quantize(const int32_t* ids, int64_t A, int num_experts, 
                                 uint8_t* sf, float* dec, hipStream_t s);
 int64_t plan_chunks(int64_t A);
 
+hipError_t launch_quantize_mxfp8(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride,
+                                uint8_t* q, uint8_t* sf, hipStream_t s);
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride,
                                 uint8_t* q, uint8_t* sf, hipStream_t s);
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t stride, int mode,
@@ -87,6 +89,10 @@ struct MoeGemmProblem {
   uint16_t* h16;     // block_m > 32: [cap, I] FP16 copy of the requantized intermediate
 };
 hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s);
+// MXFP4 weights (MXFP4 panels) on MXFP8 activations, block_m <= 32: a_q [M, H] E4M3 bytes, a_sf
+// [M, H/32] E8M0; hq [cap, I] and hsf [cap, I/32] the MXFP8 intermediate; a_dec, alphas, c2,
+// tile_ws, a16, h16 unused.
+hipError_t launch_moe_gemms_mx(const MoeGemmProblem& p, hipStream_t s);
 
 // NVFP4 weight-only mode on BF16 activations (block_m <= 32): the plan, panels, alphas, act,
 // dbg_* and y fields of MoeGemmProblem as above; a_q, a_sf, a_dec, c2, hq, hsf, tile_ws, a16,

@@ -21,6 +21,7 @@ from . import (
     bfp4_check_topk_ids,
     bfp4_fused_moe_nvfp4,
     bfp4_fused_moe_nvfp4_noalloc,
+    bfp4_fused_moe_mx,
     bfp4_fused_moe_w4a16,
     bfp4_moe_plan,
     bfp4_moe_plan_quantize,
@@ -30,9 +31,11 @@ from . import (
     bfp4_prepare_weights,
     bfp4_prepare_weights_mxfp4,
     bfp4_quantize_mxfp4,
+    bfp4_quantize_mxfp8,
     bfp4_quantize_nvfp4,
     bfp4_quantize_workspace_size,
     bfp4_workspace_size,
+    bfp4_workspace_size_mx,
     bfp4_workspace_size_w4a16,
 )
 
@@ -273,4 +276,62 @@ class MoeForwardW4A16:
                              w.num_local_experts, self.top_k, self.block_m, self.act,
                              routed_scaling_factor, int(self.do_finalize), out, self.gemm2_out,
                              debug, self.ws, self.ws_bytes, stream)
+        return out if self.do_finalize else (self.gemm2_out, topk_weights, pl.token_to_row)
+
+
+def quantize_mxfp8(x_bf16, stream=None):
+    """MXFP8 of a 2-D BF16 tensor; returns (q [R, C] u8 E4M3, sf [R, C/32] u8 E8M0)."""
+    rows, cols = x_bf16.shape
+    dev = x_bf16.device
+    q = torch.empty((max(rows, 1), cols), dtype=torch.uint8, device=dev)
+    sf = torch.empty((max(rows, 1), cols // 32), dtype=torch.uint8, device=dev)
+    bfp4_quantize_mxfp8(x_bf16, rows, cols, x_bf16.stride(0), q, sf, stream)
+    return q, sf
+
+
+class MoeForwardMX:
+    """One forward of the MX mode: routing plan, MXFP8 activation quantization, fused experts on
+    MXFP4 weights (+ finalize).  Decode plans (block_m <= 32)."""
+
+    def __init__(self, weights: PreparedWeights, M, top_k, num_experts, block_m,
+                 local_expert_offset=0, do_finalize=True, device="cuda", act=None):
+        if act is None:
+            act = BFP4_ACT_SWIGLU if weights.gated else BFP4_ACT_RELU2
+        if (act in GATED_ACTS) != bool(weights.gated):
+            raise ValueError("activation %d does not match the weights' gating" % act)
+        if weights.fmt != BFP4_FORMAT_MXFP4:
+            raise ValueError("the MX mode needs MXFP4 weights")
+        self.act = act
+        self.w = weights
+        self.M, self.top_k, self.E, self.block_m = M, top_k, num_experts, block_m
+        self.offset = local_expert_offset
+        self.do_finalize = do_finalize
+        self.plan = MoePlanBuffers(M, top_k, weights.num_local_experts, block_m, device)
+        H = weights.H
+        self.a_q = torch.empty((max(M, 1), H), dtype=torch.uint8, device=device)
+        self.a_sf = torch.empty((max(M, 1), H // 32), dtype=torch.uint8, device=device)
+        self.ws_bytes = bfp4_workspace_size_mx(M, H, weights.I, top_k, weights.num_local_experts,
+                                               block_m, int(do_finalize))
+        self.ws = _bytes(self.ws_bytes + 256, device)
+        self.gemm2_out = None
+        if not do_finalize:
+            self.gemm2_out = torch.empty((max(self.plan.capacity, 1), H), dtype=torch.bfloat16,
+                                         device=device)
+
+    def __call__(self, x_bf16, topk_ids, topk_weights, out=None, debug=None, weights=None,
+                 stream=None, routed_scaling_factor=1.0):
+        w = self.w if weights is None else weights
+        M, H, I = self.M, w.H, w.I
+        self.plan.build(topk_ids, self.E, self.offset, stream)
+        if M:
+            bfp4_quantize_mxfp8(x_bf16, M, H, x_bf16.stride(0), self.a_q, self.a_sf, stream)
+        if out is None and self.do_finalize:
+            out = torch.zeros((M, H), dtype=torch.bfloat16, device=x_bf16.device)
+        pl = self.plan
+        bfp4_fused_moe_mx(self.a_q, self.a_sf, w.panels, w.panels_bytes, pl.sorted_token_ids,
+                          pl.expert_ids, pl.num_tokens_post_padded, pl.token_to_row, pl.capacity,
+                          topk_weights, weights_dtype(topk_weights), M, H, I,
+                          w.num_local_experts, self.top_k, self.block_m, self.act,
+                          routed_scaling_factor, int(self.do_finalize), out, self.gemm2_out,
+                          debug, self.ws, self.ws_bytes, stream)
         return out if self.do_finalize else (self.gemm2_out, topk_weights, pl.token_to_row)

@@ -302,10 +302,54 @@ int bfp4_quantize_mxfp4(const uint16_t* x_bf16, int64_t rows, int64_t cols, int6
 /* Panels from linear MXFP4 weights (bfp4_quantize_mxfp4 of each expert matrix's rows): W1
  * [E, N1, H/2] + [E, N1, H/32], W2 [E, H, I/2] + [E, H, I/32]; the same panel layout and size as
  * bfp4_prepare_weights (each UE8M0 code fills the two 16-value scale slots).  For
- * bfp4_fused_moe_w4a16 with BFP4_FORMAT_MXFP4 (alphas of 1). */
+ * bfp4_fused_moe_w4a16 with BFP4_FORMAT_MXFP4 (alphas of 1) and for bfp4_fused_moe_mx. */
 int bfp4_prepare_weights_mxfp4(const uint8_t* w1_q, const uint8_t* w1_sf, const uint8_t* w2_q,
                                const uint8_t* w2_sf, int num_local_experts, int64_t H, int64_t I,
                                int gated, void* panels, size_t panels_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * MXFP8 quantization of BF16 rows (the activation format of the MX mode below) [Frost, MX
+ * paragraph: MXFP4 or MXFP8 weights with MXFP8 inputs].  Reading taken (the OCP microscaling
+ * recipe, as for MXFP4 with E4M3's largest exponent 8 in place of E2M1's 2): per 32 consecutive
+ * values with amax their largest magnitude, the UE8M0 code X + 127 of X = floor(log2(amax)) - 8
+ * (clamped to [-127, 127]; amax 0 or below the FP32 normal range gives code 0), and each value
+ * as the E4M3FN code nearest to x * 2^-X (ties to the even code, saturating at 448, sign bit
+ * copied).
+ *   x_bf16 [rows, row_stride >= cols] (16-byte aligned, row_stride % 8 == 0), cols % 32 == 0;
+ *   q [rows, cols] E4M3 bytes (16-byte aligned), sf [rows, cols/32]; neither may overlap x.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row_stride,
+                        uint8_t* q, uint8_t* sf, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
+ * The fused expert computation with MXFP4 weights on MXFP8 activations [Frost, MX paragraph:
+ * the same typed activations, activation output and expert outputs rounded to BF16, ordered FP32
+ * combine, an intermediate quantization contract of the MX mode's own].  On gfx950's block-scaled
+ * MFMA (FP4 weights x FP8 activations, E8M0 scales per 32 values), no decode of either operand.
+ * Readings taken: MX weights and activations carry no FP32 global scales; the BF16 intermediate
+ * is quantized to MXFP8 (bfp4_quantize_mxfp8's recipe, per 32 values of a row) before GEMM2.
+ * Per valid plan row r (token t, local expert e):
+ *   pre[n] = sum_h a[t,h] * W1_e[n,h]          (FP32 accumulate of exact products)
+ *   h[i]   = bf16(act(pre[i]) * pre[I+i]) (gated) or bf16(act(pre[i]));  hq = MXFP8(h)
+ *   y[k]   = bf16(sum_i hq[i] * W2_e[k,i]);   finalize / unfinalized as bfp4_fused_moe_nvfp4.
+ * Arguments as bfp4_fused_moe_nvfp4, except: a_q [M, H] E4M3 bytes and a_sf [M, H/32] E8M0 from
+ * bfp4_quantize_mxfp8 (no per-token scale); panels from bfp4_prepare_weights_mxfp4; no alphas
+ * or c2; decode-sized plans only (block_m <= 32, else BFP4_ERR_BLOCK_M); workspace >=
+ * bfp4_workspace_size_mx(...) bytes, 256-byte aligned.  debug->preact [capacity, N1] FP32,
+ * debug->inter [capacity, I] BF16, debug->inter_q [capacity, I] (the MXFP8 intermediate, 16-byte
+ * aligned) and debug->inter_sf [capacity, I/32]; inter_f16 unused.
+ * ---------------------------------------------------------------------------------------------- */
+size_t bfp4_workspace_size_mx(int64_t M, int64_t H, int64_t I, int top_k, int num_local_experts,
+                              int block_m, int do_finalize);
+int bfp4_fused_moe_mx(const uint8_t* a_q, const uint8_t* a_sf, const void* panels,
+                      size_t panels_bytes, const int32_t* sorted_token_ids,
+                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                      const int32_t* token_to_row, size_t capacity, const void* topk_weights,
+                      int weights_dtype, int64_t M, int64_t H, int64_t I, int num_local_experts,
+                      int top_k, int block_m, int act, float routed_scaling_factor,
+                      int do_finalize, uint16_t* out, uint16_t* gemm2_out,
+                      const bfp4_debug* debug, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* ----------------------------------------------------------------------------------------------
  * FP4 weight-only forward on BF16 activations, NVFP4 or MXFP4 weights [Frost, FP4 weight-only
