@@ -32,6 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-MoE tokens/s + HBM GB/s (M=8) and TFLOP/s (M=4096), % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA (the issued dtype)
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (the MX mode's FP4 x FP8 products)
+MXFP4_BYTES = 0.5 + 1.0 / 32   # E2M1 data + one E8M0 scale per 32 values
 NVFP4_BYTES = 9.0 / 16.0       # 0.5 B data + 1/16 B E4M3 scale per element
 
 
@@ -41,9 +43,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=["decode", "decode_ll", "prefill", "skewed", "all", "both"],
-                    help="all (or both): decode, decode-LL, prefill and the skewed squared-ReLU "
-                         "workload; the first of them gives the headline value")
+                    choices=["decode", "decode_ll", "prefill", "skewed", "mx", "all", "both"],
+                    help="all (or both): decode, decode-LL, prefill, the skewed squared-ReLU "
+                         "workload and the MX mode (decode and prefill); the first of them gives "
+                         "the headline value")
     ap.add_argument("--replicas", type=int, default=2,
                     help="weight panel copies rotated across steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -514,6 +517,85 @@ def time_tiled(wl, label, args, desc):
     return res
 
 
+def time_mx(wl, args, label, desc):
+    """The MX mode (MXFP4 weights, MXFP8 activations, block-scaled MFMA) on a workload: plan,
+    MXFP8 activation quantization and the fused MX call (+ finalize) per step, with the same
+    inputs; the dominant GEMM1 against the FP8 MFMA peak (tiled, block_m > 32) or the HBM peak
+    (decode), every kernel's average duration."""
+    import torch
+
+    import block_scaled_fp4_plan_amd as bf
+    from block_scaled_fp4_plan_amd import runner
+    from synth import make_activations, make_routing, make_weights
+
+    x_bits = make_activations(wl, 0)
+    ids, w = make_routing(wl, 0)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    ids_d, w_d = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    w1, w2 = make_weights(wl, 0, "cuda")
+    pw = runner.prepare_weights_mxfp4(w1, w2, gated=wl.gated)
+    del w1, w2
+    replicas = [pw]
+    decode = wl.block_m <= 32
+    if decode:                                   # weights from HBM on every step
+        replicas.append(runner.PreparedWeights(pw.panels.clone(), pw.panels_bytes, pw.alpha1_gate,
+                                               pw.alpha1_up, pw.alpha2, pw.num_local_experts, pw.H,
+                                               pw.I, pw.gated, pw.fmt))
+    f = runner.MoeForwardMX(pw, wl.M, wl.top_k, wl.E, wl.block_m, wl.local_offset)
+    out = torch.zeros((wl.M, wl.H), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        f(x, ids_d, w_d, out=out, weights=replicas[i % len(replicas)])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    bf.bfp4_profile_begin(args.steps * 4 + 16, "gemm1")
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    g1_ms, _, g1_name = kernel_ms(bf.bfp4_profile_end()[1], "gemm1")
+    nb = min(args.steps, 20)
+    bf.bfp4_profile_begin(nb * 16 + 64)
+    for i in range(nb):
+        step(i)
+    torch.cuda.synchronize()
+    breakdown = {k: {"ms": tot / c} for k, (c, tot) in bf.bfp4_profile_end()[1].items()}
+    loc = ids.reshape(-1) - wl.local_offset
+    ok = (loc >= 0) & (loc < wl.n_local)
+    A, touched = int(ok.sum()), len(set(loc[ok].tolist()))
+    res = dict(value=wl.M / (ms * 1e-3), unit="tokens/s", ms_per_step=ms,
+               config={"workload": desc, "assignments": A, "touched_experts": touched,
+                       "kernels": breakdown})
+    if decode:
+        g1_bytes = (touched * wl.N1 * wl.H * MXFP4_BYTES + wl.M * wl.H * (1 + 1.0 / 32) +
+                    A * wl.I * (1 + 1.0 / 32))
+        step_b = (touched * (wl.N1 * wl.H + wl.H * wl.I) * MXFP4_BYTES + wl.M * wl.H * 2 +
+                  2 * wl.M * wl.H * 2 + wl.M * wl.top_k * 8)
+        ach = g1_bytes / (g1_ms * 1e-3) / 1e9
+        res["config"]["step_hbm_frac"] = step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+        res["roofline"] = {"bound": "hbm", "kernel": g1_name, "achieved": ach,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                           "traffic": None, "bytes_per_launch": g1_bytes, "avg_launch_ms": g1_ms}
+    else:
+        g1_flops = 2.0 * A * wl.H * wl.N1
+        ach = g1_flops / (g1_ms * 1e-3) / 1e12
+        tf = step_flops(wl, A) / (ms * 1e-3) / 1e12
+        res.update(tflops=tf, tflops_frac=tf / FP8_MFMA_PEAK_TFLOPS)
+        res["roofline"] = {"bound": "mfma", "kernel": g1_name, "achieved": ach,
+                           "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / FP8_MFMA_PEAK_TFLOPS, "traffic": None,
+                           "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms}
+    del f, replicas, pw
+    torch.cuda.empty_cache()
+    return res
+
+
 def log(*a):
     """Progress of the run on stderr (the JSON result is the only line on stdout)."""
     print("[bench]", *a, file=sys.stderr, flush=True)
@@ -579,8 +661,8 @@ def main():
         graph_vs_eager(WORKLOADS["decode" if args.workload in ("all", "both") else
                                  args.workload], args.steps, args.warmup)
         return
-    want = {"all": ("decode", "decode_ll", "prefill", "skewed"),
-            "both": ("decode", "decode_ll", "prefill", "skewed")}.get(args.workload,
+    want = {"all": ("decode", "decode_ll", "prefill", "skewed", "mx"),
+            "both": ("decode", "decode_ll", "prefill", "skewed", "mx")}.get(args.workload,
                                                                       (args.workload,))
     if args.no_skewed:
         want = tuple(w for w in want if w != "skewed")
@@ -602,6 +684,16 @@ def main():
         parts.append(("prefill", time_tiled(
             WORKLOADS["prefill"], "prefill", args,
             "prefill: M=4096 H=7168 I=2048 E=256 top_k=8 block_m=128 SwiGLU NVFP4")))
+    if "mx" in want:
+        log("MX mode: decode M=8 and prefill M=4096")
+        parts.append(("mx_decode", time_mx(
+            WORKLOADS["decode"], args, "decode",
+            "MX decode: M=8 H=7168 I=2048 E=256 top_k=8 block_m=8 SwiGLU, MXFP4 weights x "
+            "MXFP8 activations (block-scaled MFMA)")))
+        parts.append(("mx_prefill", time_mx(
+            WORKLOADS["prefill"], args, "prefill",
+            "MX prefill: M=4096 H=7168 I=2048 E=256 top_k=8 block_m=128 SwiGLU, MXFP4 weights "
+            "x MXFP8 activations (block-scaled MFMA)")))
     if "skewed" in want:
         log("skewed M=16384")
         parts.append(("skewed_relu2", time_tiled(

@@ -552,7 +552,8 @@ size_t bfp4_workspace_size_mx(int64_t M, int64_t H, int64_t I, int top_k, int nu
                               int block_m, int do_finalize) {
   size_t cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
   if (H <= 0 || I <= 0) return 0;
-  size_t ws = align_up(cap * (size_t)I) + align_up(cap * (size_t)(I / 32));
+  size_t ws = align_up(cap * (size_t)I) + align_up(cap * (size_t)(I / 32)) +
+              align_up(moe_gemm_tile_ws_bytes((int64_t)cap, block_m));
   if (do_finalize) ws += align_up(cap * (size_t)H * 2);
   return ws;
 }
@@ -572,12 +573,18 @@ int bfp4_fused_moe_mx(const uint8_t* a_q, const uint8_t* a_sf, const void* panel
   const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
   if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
   if (H < 256 || H % 256 || I < 128 || I % 128) return BFP4_ERR_SHAPE;
-  if (!valid_block_m(block_m) || block_m > 32) return BFP4_ERR_BLOCK_M;
+  if (!valid_block_m(block_m)) return BFP4_ERR_BLOCK_M;
   if (num_local_experts <= 0 || num_local_experts > 1024) return BFP4_ERR_EXPERTS;
   if (!isfinite(routed_scaling_factor)) return BFP4_ERR_SCALAR;
   size_t need_cap = bfp4_plan_capacity(M, top_k, num_local_experts, block_m);
   if (capacity < need_cap || capacity % block_m || capacity >= (1ULL << 31))
     return BFP4_ERR_CAPACITY;
+  // the tiled (block_m > 32) kernels address their FP8 token operands and an expert's panels
+  // with 32-bit offsets
+  if (block_m > 32 && (M * H >= (1LL << 31) || (int64_t)capacity * I >= (1LL << 31) ||
+                       panel_matrix_bytes(1, gated ? 2 * I : I, H) >= (1LL << 31) ||
+                       panel_matrix_bytes(1, H, I) >= (1LL << 31)))
+    return BFP4_ERR_SHAPE;
   if (M == 0) return BFP4_OK;
   if (!a_q || !a_sf || !panels || !sorted_token_ids || !expert_ids || !num_tokens_post_padded ||
       !token_to_row || !topk_weights || (do_finalize && !out) || (!do_finalize && !gemm2_out))
@@ -615,11 +622,14 @@ int bfp4_fused_moe_mx(const uint8_t* a_q, const uint8_t* a_sf, const void* panel
   w += align_up(capacity * (size_t)I);
   uint8_t* hsf = (debug && debug->inter_sf) ? debug->inter_sf : w;
   w += align_up(capacity * (size_t)(I / 32));
+  uint8_t* tile_ws = w;
+  w += align_up(moe_gemm_tile_ws_bytes((int64_t)capacity, block_m));
   uint16_t* y = do_finalize ? reinterpret_cast<uint16_t*>(w) : gemm2_out;
 
   MoeGemmProblem p{};
   p.a_q = a_q;
   p.a_sf = a_sf;
+  p.tile_ws = tile_ws;
   p.panel1 = static_cast<const uint8_t*>(panels);
   p.panel2 = p.panel1 + panel_matrix_bytes(num_local_experts, N1, H);
   p.sorted = sorted_token_ids;

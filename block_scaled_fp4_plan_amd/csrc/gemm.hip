@@ -1221,8 +1221,9 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 // group g holds the MX block 32 g .. 32 g + 31, lane h its values 16 h .. 16 h + 15.  The block
 // maximum is taken over the lane pair (l, l ^ 32).
 template <int EPI>
-__device__ __forceinline__ void epilogue_mx(const GemmArgs& a, const f32x16_t (&acc)[2],
-                                            int64_t g0, int h, int64_t r) {
+__device__ __forceinline__ void epilogue_mx(const GemmArgs& a, const f32x16_t& acc0,
+                                            const f32x16_t& acc1, int64_t g0, int h, int64_t r) {
+  const f32x16_t* acc[2] = {&acc0, &acc1};
   uint8_t* hq = a.hq + r * a.I;                     // MXFP8 intermediate: I bytes per row
   uint8_t* hsf = a.hsf + r * (a.I >> 5);
   if (one_projection(EPI)) {
@@ -1234,7 +1235,7 @@ __device__ __forceinline__ void epilogue_mx(const GemmArgs& a, const f32x16_t (&
       float m = 0.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        pr[v] = acc[fn][v];
+        pr[v] = (*acc[fn])[v];
         float q;
         if (EPI == EPI_RELU2) {
           const float t = pr[v] > 0.0f ? pr[v] : 0.0f;
@@ -1282,13 +1283,13 @@ __device__ __forceinline__ void epilogue_mx(const GemmArgs& a, const f32x16_t (&
       float4* dp = reinterpret_cast<float4*>(a.dbg_pre + r * (2 * a.I) + h * a.I + i0);
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        dp[v] = make_float4(acc[fn][4 * v], acc[fn][4 * v + 1], acc[fn][4 * v + 2],
-                            acc[fn][4 * v + 3]);
+        dp[v] = make_float4((*acc[fn])[4 * v], (*acc[fn])[4 * v + 1], (*acc[fn])[4 * v + 2],
+                            (*acc[fn])[4 * v + 3]);
     }
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      const auto gu = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[fn][v]),
-                                                       __float_as_uint(acc[fn][8 + v]), false,
+      const auto gu = __builtin_amdgcn_permlane32_swap(__float_as_uint((*acc[fn])[v]),
+                                                       __float_as_uint((*acc[fn])[8 + v]), false,
                                                        false);
       const float gt = __uint_as_float(gu[0]);
       const float up = __uint_as_float(gu[1]);
@@ -1430,7 +1431,7 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_mx_kernel(GemmArgs a) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) epilogue_group<EPI_DOWN>(a, acc[fn], 1.0f, g0 + fn, h, 1.0f, r);
       } else {
-        epilogue_mx<EPI>(a, acc, g0, h, r);
+        epilogue_mx<EPI>(a, acc[0], acc[1], g0, h, r);
       }
     }
   }
@@ -1494,6 +1495,300 @@ hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, 
   const int64_t tasks = cap_blocks * a.n_nt;
   const int64_t max_wg = 256LL * 4;                  // resident workgroups (4 waves each)
   const int64_t grid = tasks < max_wg ? tasks : max_wg;
+  if (grid == 0) return hipSuccess;
+  KernelTimer t(name, s);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// MXFP4 weights on MXFP8 activations, prefill-sized plan blocks (block_m > 32), on the block-
+// scaled MFMA.  Persistent grid of one 4-wave workgroup per CU (one wave per SIMD) taking tasks
+// (tile of up to 256 plan rows of one expert, n-tile of 256 weight rows) from the per-XCD ticket
+// queues of the prefill tile list.  Wave w owns the two row groups 8 nt + 2 w and 8 nt + 2 w + 1
+// (so a gated MX block of 32 intermediate values stays inside the wave) against all NFW token
+// fragments of the tile: 2 * NFW accumulators of 16 values (held in AGPRs), and each token
+// fragment read from LDS feeds two MFMAs.  Per 128-K stage the tile's FP8 token rows (128 bytes
+// each) and their four E8M0 codes are copied into a ring of NB LDS buffers by direct buffer-to-LDS
+// loads; inside a row the 16-byte slot u sits at u ^ (row & 7), so the operand reads are free of
+// bank conflicts.  Weights stream from the MXFP4 panels into registers RW - 1 stages ahead and go
+// into the MFMA unchanged.
+constexpr int kMxStageBytes = 128;        // FP8 token bytes per row per stage (128 K values)
+constexpr int kMxTileRows = 256;
+constexpr int kMxRingBytes = 136 * 1024;  // token data + scale buffers
+
+template <int NFW> struct MxDepth {
+  static constexpr int SBUF = NFW * 32 * kMxStageBytes + kMxTileRows * 4;   // data + scales
+  static constexpr int NB0 = kMxRingBytes / SBUF;
+  static constexpr int NB = NB0 > 6 ? 6 : NB0;
+  static constexpr int RW = 3;
+};
+
+template <int NFW, int EPI>
+__device__ __forceinline__ void run_tile_mx(const GemmArgs& a, uint8_t* ring, const int* row_src,
+                                            int e, int nt, int64_t row0) {
+  constexpr int NB = MxDepth<NFW>::NB, RW = MxDepth<NFW>::RW, SBUF = MxDepth<NFW>::SBUF;
+  constexpr int SDATA = NFW * 32 * kMxStageBytes;        // scale dwords follow the data
+  static_assert(NB >= 3, "at least three token stage buffers");
+  // vector memory operations one wave issues per stage: 2 weight groups x (scale dword + 2
+  // chunks), NFW token data pieces and one scale piece
+  constexpr int VM_W = 6, VM_T = NFW + 1, VM_STAGE = VM_W + VM_T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int nst = a.nch / kStageChunks;
+  const int64_t K = a.a_rowq;                            // FP8 bytes per token row
+
+  // weights: this wave's two row groups of n-tile nt through a buffer resource over the expert
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(a.panel + (int64_t)e * a.expert_bytes, (uint32_t)a.expert_bytes);
+  const int g0 = nt * kTileGroups + 2 * wave;
+  const bool wave_on = (g0 + 2) * kGroupRows <= a.N;
+  const int go0 = (wave_on ? g0 : 0) * (int)a.rg_bytes;
+  const int wlane = lane * 16;
+  auto load_s = [&](int g, int st) {
+    const int sc = st / (kSuperChunks / kStageChunks), c0 = (st * kStageChunks) % kSuperChunks;
+    return buffer_load_u32(wrs, wlane, go0 + g * (int)a.rg_bytes + sc * kSuperBytes + 2 * c0);
+  };
+  auto load_w1 = [&](int g, int st, int c) {
+    const int sc = st / (kSuperChunks / kStageChunks), c0 = (st * kStageChunks) % kSuperChunks;
+    return buffer_load_u128(wrs, wlane + (1 + c) * kUnit,
+                            go0 + g * (int)a.rg_bytes + sc * kSuperBytes + c0 * kUnit);
+  };
+
+  // token rows: DMA piece k of this wave (k < NFW) covers tile rows 8 (4 k + wave) .. + 7, lane
+  // L row 8 (4 k + wave) + L / 8, physical slot L % 8 = logical slot (L % 8) ^ (row & 7); the
+  // scale piece covers rows 64 wave .. 64 wave + 63, one dword per lane
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(a.a_q, (uint32_t)(a.a_rows * K));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.a_sf, (uint32_t)(a.a_rows * (K >> 5)));
+  uint32_t t_voff[NFW];
+#pragma unroll
+  for (int k = 0; k < NFW; ++k) {
+    const int row = 8 * (4 * k + wave) + (lane >> 3);
+    const int src = row_src[row] < 0 ? 0 : row_src[row];
+    const uint32_t u = (uint32_t)((lane & 7) ^ (row & 7));
+    t_voff[k] = (uint32_t)src * (uint32_t)K + u * 16;
+  }
+  uint32_t s_voff;
+  {
+    const int row = 64 * wave + lane;
+    const int src = (row < NFW * 32 && row_src[row] >= 0) ? row_src[row] : 0;
+    s_voff = (uint32_t)src * (uint32_t)(K >> 5) * 1u;
+  }
+  auto load_t = [&](int b, int st) {
+    uint8_t* base = ring + b * SBUF;
+#pragma unroll
+    for (int k = 0; k < NFW; ++k)
+      buffer_load_lds16(trs, base + 8 * (4 * k + wave) * kMxStageBytes, t_voff[k],
+                        (uint32_t)st * kMxStageBytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        srs, (__attribute__((address_space(3))) void*)(base + SDATA + 64 * wave * 4), 4, s_voff,
+        (uint32_t)st * 4, 0, 0);
+  };
+
+  f32x16_t acc[2][NFW];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) acc[g][j] = f32x16_t{};
+  uint4 W[RW][2][kStageChunks];
+  uint32_t S[RW][2];
+  auto load_w = [&](int r, int st) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      S[r][g] = load_s(g, st);
+#pragma unroll
+      for (int c = 0; c < kStageChunks; ++c) W[r][g][c] = load_w1(g, st, c);
+    }
+  };
+
+  // ---- prologue: token stages 0 .. NB-2, then weights of stages 0 .. RW-2; every load is
+  // unconditional (stage indices clamped) so the waits below count exactly ----
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b) load_t(b, min(b, nst - 1));
+#pragma unroll
+  for (int r = 0; r < RW - 1; ++r) load_w(r, min(r, nst - 1));
+  // stage 0's rows have landed once at most the later loads are outstanding
+  wait_vmcnt<(NB - 2) * VM_T + (RW - 1) * VM_W>();
+  lds_barrier();
+
+  // one stage: weights of stage st + RW - 1 and token rows of stage st + NB - 1 go out first
+  // (the buffer they refill was released by the barrier that ended stage st - 1), then the two
+  // chunks' MFMAs
+  auto stage = [&](auto RR, int st) {
+    constexpr int R = decltype(RR)::value;
+    const uint8_t* buf = ring + (st % NB) * SBUF;
+    load_w((R + RW - 1) % RW, min(st + RW - 1, nst - 1));
+    load_t((st + NB - 1) % NB, min(st + NB - 1, nst - 1));
+    // token fragment j, chunk c: FP8 operand (lane layout K 16 h .. 16 h + 15 and 32 + 16 h ..
+    // of the chunk, from the swizzled row) and its E8M0 code (K block h of the chunk)
+    const uint32_t sw = (uint32_t)(col & 7);             // row & 7 for every fragment's row
+    auto read_b = [&](int j, int c, i32x8_t& B, int& sb) {
+      const uint8_t* rp = buf + (32 * j + col) * kMxStageBytes;
+      const uint4 b0 = *reinterpret_cast<const uint4*>(rp + (((4 * c + h) ^ sw) << 4));
+      const uint4 b1 = *reinterpret_cast<const uint4*>(rp + (((4 * c + 2 + h) ^ sw) << 4));
+      B = i32x8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                  (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      const uint32_t tsc = *reinterpret_cast<const uint32_t*>(buf + SDATA + (32 * j + col) * 4);
+      sb = (int)((tsc >> (8 * (2 * c + h))) & 0xFFu);
+    };
+    // two-deep pipeline over the fragments: the next fragment's operand is read from LDS while
+    // the current one's two MFMAs (one per row group) issue; the scheduling fences keep the
+    // compiler from hoisting more reads (and their registers) ahead
+#pragma unroll
+    for (int c = 0; c < kStageChunks; ++c) {
+      i32x8_t A[2];
+      int sa[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        A[g] = i32x8_t{(int)W[R][g][c].x, (int)W[R][g][c].y, (int)W[R][g][c].z,
+                       (int)W[R][g][c].w, 0, 0, 0, 0};
+        sa[g] = (int)((S[R][g] >> (16 * c)) & 0xFFu);
+      }
+      i32x8_t Bc, Bn;
+      int sbc, sbn;
+      read_b(0, c, Bc, sbc);
+#pragma unroll
+      for (int j = 0; j < NFW; ++j) {
+        if (j + 1 < NFW) read_b(j + 1, c, Bn, sbn);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          acc[g][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[g], Bc, acc[g][j], 4, 0,
+                                                                      0, sa[g], 0, sbc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < NFW) {
+          Bc = Bn;
+          sbc = sbn;
+        }
+      }
+    }
+    // stage st + 1's rows have landed once at most the loads issued after them are outstanding:
+    // they went out in stage st + 2 - NB (or in the prologue), followed by NB - 2 stages' loads
+    if (st + 1 > NB - 2) wait_vmcnt<(NB - 2) * VM_STAGE>();
+    else wait_vmcnt<(NB - 3) * VM_T + (RW - 1) * VM_W + VM_STAGE>();
+    lds_barrier();
+  };
+  int st0 = 0;
+  for (; st0 + RW - 1 < nst; st0 += RW)
+    unroll_seq([&](auto RR) { stage(RR, st0 + decltype(RR)::value); },
+               std::make_integer_sequence<int, RW>{});
+  unroll_seq([&](auto RR) {
+    if (st0 + decltype(RR)::value < nst) stage(RR, st0 + decltype(RR)::value);
+  }, std::make_integer_sequence<int, RW - 1>{});
+  // every issued weight load is counted by the waits above: keep the ones of the last stages
+  // (never read) alive, then let every DMA land before the LDS ring is reused
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, W[r][0][0])),
+                 "v"(__builtin_bit_cast(u32x4_t, W[r][0][1])),
+                 "v"(__builtin_bit_cast(u32x4_t, W[r][1][0])),
+                 "v"(__builtin_bit_cast(u32x4_t, W[r][1][1])), "v"(S[r][0]), "v"(S[r][1]));
+  wait_vmcnt<0>();
+  if (!wave_on) return;
+  // one fragment's epilogue at a time: the fences keep the compiler from moving every
+  // accumulator out of the AGPRs at once
+#pragma unroll
+  for (int j = 0; j < NFW; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int m = 32 * j + col;
+    if (row_src[m] < 0) continue;
+    if (EPI == EPI_DOWN) {
+      epilogue_group<EPI_DOWN, true>(a, acc[0][j], 1.0f, g0, h, 1.0f, row0 + m);
+      epilogue_group<EPI_DOWN, true>(a, acc[1][j], 1.0f, g0 + 1, h, 1.0f, row0 + m);
+    } else {
+      epilogue_mx<EPI>(a, acc[0][j], acc[1][j], g0, h, row0 + m);
+    }
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void run_nfw_mx(const GemmArgs& a, uint8_t* ring, const int* row_src,
+                                           int e, int nt, int64_t row0, int nfw) {
+  switch (nfw) {
+    case 1: run_tile_mx<1, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 2: run_tile_mx<2, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 3: run_tile_mx<3, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 4: run_tile_mx<4, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 5: run_tile_mx<5, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 6: run_tile_mx<6, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 7: run_tile_mx<7, EPI>(a, ring, row_src, e, nt, row0); break;
+    default: run_tile_mx<8, EPI>(a, ring, row_src, e, nt, row0); break;
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void moe_gemm_mx_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* ring = smem;
+  int* row_src = reinterpret_cast<int*>(smem + kMxRingBytes);
+  int* sh_nvalid = row_src + kMxTileRows;
+  int* sh_task = sh_nvalid + 1;
+  const int tid = threadIdx.x;
+  const int n_tiles = *a.n_tiles;
+  // the ticket queues of moe_gemm_kernel: queue x holds tiles x, x + 8, ...; workgroups of XCD
+  // x take from queue x and move on to the next queues when theirs is empty
+  auto q_tasks = [&](int qq) -> int64_t {
+    return n_tiles > qq ? (int64_t)((n_tiles - qq + kXcds - 1) / kXcds) * a.n_ct : 0;
+  };
+  auto resolve = [&](int& qq, uint32_t ticket) -> int {
+    for (int tries = 0; tries < kXcds; ++tries) {
+      if ((int64_t)ticket < q_tasks(qq)) {
+        const int tile = qq + kXcds * (int)(ticket / a.n_ct);
+        return tile * a.n_ct + (int)(ticket % a.n_ct);
+      }
+      if (tries == kXcds - 1) break;
+      qq = (qq + 1) % kXcds;
+      ticket = atomicAdd(a.task_counter + qq, 1u);
+    }
+    return -1;
+  };
+  int q = (int)(blockIdx.x % kXcds);
+  if (tid == 0) *sh_task = resolve(q, atomicAdd(a.task_counter + q, 1u));
+  __syncthreads();
+  int64_t k = *sh_task;
+  while (k >= 0) {
+    uint32_t ticket = 0;
+    if (tid == 0) ticket = atomicAdd(a.task_counter + q, 1u);   // in flight during this task
+    const int2 t = a.tiles[k / a.n_ct];
+    const int nt = (int)(k % a.n_ct);
+    const int64_t row0 = t.x;
+    const int rows_here = min(kMxTileRows, t.y);
+    const int e = a.eids[row0 / a.block_m];
+    __syncthreads();                         // the previous task is done with LDS
+    if (tid == 0) *sh_nvalid = 0;
+    __syncthreads();
+    {
+      int src = -1;
+      if (tid < rows_here) {
+        const int64_t ent = a.sorted[row0 + tid];
+        if (ent >= 0 && ent < a.sentinel)
+          src = a.gather ? (int)(ent / a.top_k) : (int)(row0 + tid);
+      }
+      row_src[tid] = src;
+      if (src >= 0) atomicMax(sh_nvalid, tid + 1);
+    }
+    __syncthreads();
+    const int nvalid = *sh_nvalid;
+    if (nvalid > 0 && e >= 0 && e < a.nloc)
+      run_nfw_mx<EPI>(a, ring, row_src, e, nt, row0, (nvalid + 31) >> 5);
+    __syncthreads();                         // every thread has read sh_task
+    if (tid == 0) *sh_task = resolve(q, ticket);
+    __syncthreads();
+    k = *sh_task;
+  }
+}
+
+template <int EPI>
+hipError_t launch_gemm_mx(const GemmArgs& a, int64_t max_tiles, const char* name, hipStream_t s) {
+  const size_t lds = (size_t)kMxRingBytes + kMxTileRows * sizeof(int) + 16;
+  auto kern = moe_gemm_mx_kernel<EPI>;
+  static std::atomic<size_t> lds_set[kMaxDevices];
+  hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
+  if (err != hipSuccess) return err;
+  const int64_t total = max_tiles * a.n_ct;
+  const int64_t maxwg = 256;                         // one workgroup per CU
+  int64_t grid = total < maxwg ? total : maxwg;
+  grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   KernelTimer t(name, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
@@ -1743,7 +2038,7 @@ hipError_t launch_moe_gemms_mx(const MoeGemmProblem& p, hipStream_t s) {
   const int64_t N1 = gated ? 2 * p.I : p.I;
   const int64_t cap_blocks = p.cap / p.block_m;
   constexpr int FN = 2;
-  if (p.block_m > 32) return hipErrorInvalidValue;
+  const bool small = p.block_m <= 32;
 
   GemmArgs g1{};
   g1.a_q = p.a_q;
@@ -1793,6 +2088,43 @@ hipError_t launch_moe_gemms_mx(const MoeGemmProblem& p, hipStream_t s) {
   g2.dbg_pre = nullptr;
   g2.dbg_inter = nullptr;
 
+  if (!small) {
+    // tiled kernels: the prefill tile list (tiles of up to 256 plan rows, per-XCD ticket queues)
+    const int64_t max_tiles = moe_gemm_max_tiles(p.cap, p.block_m);
+    int2* tile_tmp = reinterpret_cast<int2*>(p.tile_ws);
+    int2* tiles = tile_tmp + 2 * max_tiles;
+    int32_t* n_tiles = reinterpret_cast<int32_t*>(tiles + max_tiles);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(n_tiles + 1);
+    {
+      KernelTimer t("tile_list", s);
+      hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, p.eids, p.sorted, p.ntpp,
+                         p.cap, p.block_m, (int64_t)(p.M * p.top_k), p.nloc, tile_tmp, tiles,
+                         n_tiles, counters);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    if (p.M * p.H >= (int64_t(1) << 31) || p.cap * p.I >= (int64_t(1) << 31))
+      return hipErrorInvalidValue;         // 32-bit buffer offsets of the token operands
+    for (GemmArgs* g : {&g1, &g2}) {
+      g->tiles = tiles;
+      g->n_tiles = n_tiles;
+      g->n_ct = g->n_nt;
+      g->chain = 1;
+    }
+    g1.task_counter = counters;
+    g2.task_counter = counters + kXcds;
+    static const char* const kNameT[] = {
+        "gemm1_swiglu_mx_prefill", "gemm1_relu2_mx_prefill", "gemm1_geglu_mx_prefill",
+        "gemm1_gelu_mx_prefill", "gemm1_relu_mx_prefill", "gemm1_silu_mx_prefill",
+        "gemm1_identity_mx_prefill"};
+    const char* nm = kNameT[p.act];
+    hipError_t err = p.act == BFP4_ACT_SWIGLU ? launch_gemm_mx<EPI_SWIGLU>(g1, max_tiles, nm, s)
+                   : p.act == BFP4_ACT_RELU2  ? launch_gemm_mx<EPI_RELU2>(g1, max_tiles, nm, s)
+                   : p.act == BFP4_ACT_GEGLU  ? launch_gemm_mx<EPI_GEGLU>(g1, max_tiles, nm, s)
+                                              : launch_gemm_mx<EPI_ACT>(g1, max_tiles, nm, s);
+    if (err != hipSuccess) return err;
+    return launch_gemm_mx<EPI_DOWN>(g2, max_tiles, "gemm2_down_mx_prefill", s);
+  }
   static const char* const kName[] = {
       "gemm1_swiglu_mx_decode", "gemm1_relu2_mx_decode", "gemm1_geglu_mx_decode",
       "gemm1_gelu_mx_decode", "gemm1_relu_mx_decode", "gemm1_silu_mx_decode",

@@ -291,7 +291,7 @@ def quantize_mxfp8(x_bf16, stream=None):
 
 class MoeForwardMX:
     """One forward of the MX mode: routing plan, MXFP8 activation quantization, fused experts on
-    MXFP4 weights (+ finalize).  Decode plans (block_m <= 32)."""
+    MXFP4 weights (+ finalize); decode kernels for block_m <= 32, tiled kernels above."""
 
     def __init__(self, weights: PreparedWeights, M, top_k, num_experts, block_m,
                  local_expert_offset=0, do_finalize=True, device="cuda", act=None):

@@ -334,8 +334,9 @@ int bfp4_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int64_t cols, int6
  *   y[k]   = bf16(sum_i hq[i] * W2_e[k,i]);   finalize / unfinalized as bfp4_fused_moe_nvfp4.
  * Arguments as bfp4_fused_moe_nvfp4, except: a_q [M, H] E4M3 bytes and a_sf [M, H/32] E8M0 from
  * bfp4_quantize_mxfp8 (no per-token scale); panels from bfp4_prepare_weights_mxfp4; no alphas
- * or c2; decode-sized plans only (block_m <= 32, else BFP4_ERR_BLOCK_M); workspace >=
- * bfp4_workspace_size_mx(...) bytes, 256-byte aligned.  debug->preact [capacity, N1] FP32,
+ * or c2; block_m <= 32 runs the decode kernels, block_m > 32 the tiled prefill kernels (which
+ * need M*H and capacity*I below 2^31 bytes and one expert's panel of each matrix below 2^31
+ * bytes, else BFP4_ERR_SHAPE); workspace >= bfp4_workspace_size_mx(...) bytes, 256-byte aligned.  debug->preact [capacity, N1] FP32,
  * debug->inter [capacity, I] BF16, debug->inter_q [capacity, I] (the MXFP8 intermediate, 16-byte
  * aligned) and debug->inter_sf [capacity, I/32]; inter_f16 unused.
  * ---------------------------------------------------------------------------------------------- */

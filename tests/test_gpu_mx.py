@@ -87,8 +87,18 @@ MX_WORKLOADS = {
     "ll_gelu": dataclasses.replace(WORKLOADS["decode_ll"], name="ll_gelu", act="gelu", M=3),
     "wide": Workload("wide", M=6, H=1280, I=384, E=40, top_k=24, block_m=32, act="silu"),
 }
+# the tiled (block_m > 32) kernels: tiles of 1 to 8 token fragments (Zipf loads), K = 1280 and
+# 640 (10 and 5 stages of 128, no multiple of the weight prefetch depth), gated and one-projection
+RAGGED_MX = Workload("ragged_mx", M=384, H=1280, I=640, E=6, top_k=3, block_m=128, routing="zipf")
+MX_WORKLOADS.update({
+    "ragged_mx": RAGGED_MX,
+    "ragged_mx_relu2": dataclasses.replace(RAGGED_MX, name="ragged_mx_relu2", act="relu2"),
+    "skewed_mx_tiled": dataclasses.replace(SKEWED_MX, name="skewed_mx_tiled", M=700, block_m=128),
+})
 MX_CASES = [("tiny", 8), ("decode_ll", 8), ("skewed_mx", 16), ("one_token", 8),
-            ("tiny_geglu", 16), ("ll_gelu", 8), ("wide", 32), ("tiny", 32)]
+            ("tiny_geglu", 16), ("ll_gelu", 8), ("wide", 32), ("tiny", 32),
+            ("tiny", 128), ("ragged_mx", 128), ("ragged_mx_relu2", 128), ("skewed_mx_tiled", 128),
+            ("one_token", 128), ("tiny_geglu", 136)]
 
 
 def _workload(name):
@@ -197,3 +207,82 @@ def test_fused_moe_mx_matches_oracle(name, bm):
              for r in ttr_np.reshape(-1) if r >= 0}
     assert np.array_equal(oracle.combine(np.zeros((M, H), np.uint16), ydict, p.w, ttr_np),
                           out_bits)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_fullsize_mx(name, n_cols=64, extra_rows=4):
+    """The MX mode at the full decode and prefill sizes, in the launch configuration the bench
+    times: activation quantization and the combine of the GPU's expert outputs over every
+    element; on every local expert with routed rows (first and last routed row of each 256-row
+    tile and a few more), at sampled columns: the GPU's MXFP4 weight rows bit-exact with the
+    oracle's, GEMM1 pre-activations and the expert outputs (on the GPU's own MXFP8 intermediate)
+    within the MX bound, the intermediate's requantization bit-exact."""
+    wl = WORKLOADS[name]
+    say("full-size MX", name)
+    p = Problem(wl)
+    M, k, H, I, N1, bm = wl.M, wl.top_k, wl.H, wl.I, wl.N1, wl.block_m
+    pw, lin = runner.prepare_weights_mxfp4(p.w1, p.w2, gated=wl.gated, keep_linear=True)
+    fwd = runner.MoeForwardMX(pw, M, k, wl.E, bm, wl.local_offset, do_finalize=False)
+    cap = fwd.plan.capacity
+    dbg = dict(preact=torch.empty((cap, N1), device="cuda"),
+               inter=torch.empty((cap, I), dtype=torch.bfloat16, device="cuda"),
+               inter_q=torch.empty((cap, I), dtype=torch.uint8, device="cuda"),
+               inter_sf=torch.empty((cap, I // 32), dtype=torch.uint8, device="cuda"))
+    y, wts, ttr_d = fwd(p.x, p.ids_d, p.w_d, debug=dbg)
+    out = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    bf.bfp4_moe_finalize(y, wts, runner.weights_dtype(wts), ttr_d, M, H, k, 1.0, out)
+    torch.cuda.synchronize()
+    aq, asf = oracle.quantize_mxfp8(bf16_bits_to_f32(p.x_bits))
+    assert np.array_equal(np_u8(fwd.a_q), aq) and np.array_equal(np_u8(fwd.a_sf), asf)
+    srt, eids, P, ttr = p.oracle_plan(bm)
+    assert np.array_equal(ttr_d.cpu().numpy(), ttr)
+    ybits = np_bits(y)
+    ydict = {int(r): bf16_bits_to_f32(ybits[r]).astype(np.float64)
+             for r in ttr.reshape(-1) if r >= 0}
+    assert np.array_equal(oracle.combine(np.zeros((M, H), np.uint16), ydict, p.w, ttr),
+                          np_bits(out))
+    rng = np.random.default_rng(19)
+    seg = {}
+    for r in range(P):
+        if srt[r] < M * k:
+            seg.setdefault(int(eids[r // bm]), []).append(r)
+    hq, hsf = np_u8(dbg["inter_q"]), np_u8(dbg["inter_sf"])
+    flips = total = 0
+    for e, rows_e in sorted(seg.items()):
+        pick = {rows_e[0], rows_e[-1]}
+        for t0 in range(rows_e[0], rows_e[-1] + 1, 256):
+            inside = [r for r in rows_e if t0 <= r < t0 + 256]
+            if inside:
+                pick.add(inside[-1])
+        pick.update(int(r) for r in rng.choice(rows_e, min(extra_rows, len(rows_e)), replace=False))
+        rs = sorted(pick)
+        toks = srt[rs] // k
+        if wl.gated:
+            ii = np.sort(rng.choice(I, n_cols // 2, replace=False))
+            cols = np.concatenate([ii, I + ii])
+        else:
+            cols = np.sort(rng.choice(N1, n_cols, replace=False))
+        hs = np.sort(rng.choice(H, n_cols, replace=False))
+        cols_d, hs_d = torch.from_numpy(cols).cuda(), torch.from_numpy(hs).cuda()
+        # MXFP4 is per row and per 32 values: the oracle quantizes just these rows
+        q1, s1 = oracle.quantize_mxfp4(bf16_bits_to_f32(np_bits(p.w1[e][cols_d])))
+        q2, s2 = oracle.quantize_mxfp4(bf16_bits_to_f32(np_bits(p.w2[e][hs_d])))
+        assert np.array_equal(np_u8(lin[0][e][cols_d]), q1)
+        assert np.array_equal(np_u8(lin[1][e][cols_d]), s1)
+        assert np.array_equal(np_u8(lin[2][e][hs_d]), q2)
+        assert np.array_equal(np_u8(lin[3][e][hs_d]), s2)
+        rs_d = torch.tensor(rs, device="cuda")
+        a_int, a_exp = mxfp8_int(aq[toks], asf[toks])
+        w_int, w_exp = mxfp4_int(q1, s1)
+        ref = mx_dot(a_int, a_exp, w_int, w_exp)
+        sabs = mx_dot(np.abs(a_int), a_exp, np.abs(w_int), w_exp)
+        got = dbg["preact"][rs_d][:, cols_d].cpu().numpy().astype(np.float64)
+        bound = _mx_bound(sabs, H) + 1e-300
+        assert np.all(np.abs(got - ref) <= bound), (e, float((np.abs(got - ref) / bound).max()))
+        rq, rsf = oracle.quantize_mxfp8(bf16_bits_to_f32(np_bits(dbg["inter"][rs_d])))
+        assert np.array_equal(hq[rs], rq) and np.array_equal(hsf[rs], rsf)
+        f, t = _check_mx_down(bf16_bits_to_f32(ybits[rs][:, hs]).astype(np.float64), rq, rsf,
+                              q2, s2)
+        flips, total = flips + f, total + t
+    say("full-size MX %s: %d experts; y %d of %d one BF16 step off" % (name, len(seg), flips, total))
+    assert flips <= 0.1 * total
