@@ -1503,200 +1503,232 @@ hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, 
 
 // ---------------------------------------------------------------------------------------------
 // MXFP4 weights on MXFP8 activations, prefill-sized plan blocks (block_m > 32), on the block-
-// scaled MFMA.  Persistent grid of one 4-wave workgroup per CU (one wave per SIMD) taking tasks
+// scaled MFMA.  Persistent grid of one 8-wave workgroup per CU (two waves per SIMD) taking tasks
 // (tile of up to 256 plan rows of one expert, n-tile of 256 weight rows) from the per-XCD ticket
-// queues of the prefill tile list.  Wave w owns the two row groups 8 nt + 2 w and 8 nt + 2 w + 1
-// (so a gated MX block of 32 intermediate values stays inside the wave) against all NFW token
-// fragments of the tile: 2 * NFW accumulators of 16 values (held in AGPRs), and each token
-// fragment read from LDS feeds two MFMAs.  Per 128-K stage the tile's FP8 token rows (128 bytes
-// each) and their four E8M0 codes are copied into a ring of NB LDS buffers by direct buffer-to-LDS
-// loads; inside a row the 16-byte slot u sits at u ^ (row & 7), so the operand reads are free of
-// bank conflicts.  Weights stream from the MXFP4 panels into registers RW - 1 stages ahead and go
-// into the MFMA unchanged.
+// queues of the prefill tile list.  Waves w and w + 4 own the two row groups 8 nt + 2 w and
+// 8 nt + 2 w + 1 (so a gated MX block of 32 intermediate values stays inside one wave); wave w
+// takes the first ceil(NFW / 2) token fragments of the tile, wave w + 4 the others, so a wave
+// holds at most 8 accumulators of 16 values and each token fragment read from LDS feeds two
+// MFMAs.  Per 128-K stage, the tile's FP8 token rows (128 bytes each) with their four E8M0
+// codes, and the n-tile's MXFP4 weight chunks with their scale words, are copied into one
+// stage buffer of an LDS ring by direct buffer-to-LDS loads shared out over the 8 waves; the ring
+// holds NB stages, so both operands are requested NB - 1 stages ahead without holding registers.
+// Inside a token row the 16-byte slot u sits at u ^ (row & 7), so the operand reads are free of
+// bank conflicts; weight chunks keep the panel's lane order (lane l's 16 bytes at 16 l).
 constexpr int kMxStageBytes = 128;        // FP8 token bytes per row per stage (128 K values)
 constexpr int kMxTileRows = 256;
-constexpr int kMxRingBytes = 136 * 1024;  // token data + scale buffers
+constexpr int kMxRingBytes = 158 * 1024;  // stage buffers: tokens, token scales, weights, scales
+constexpr int kMxWBytes = kTileGroups * kStageChunks * kUnit;       // weight chunks per stage
+constexpr int kMxWsBytes = kTileGroups * 256;                       // weight scale words per stage
 
 template <int NFW> struct MxDepth {
-  static constexpr int SBUF = NFW * 32 * kMxStageBytes + kMxTileRows * 4;   // data + scales
+  static constexpr int TDATA = NFW * 32 * kMxStageBytes;             // token rows
+  static constexpr int TSC = TDATA;                                  // token scale dwords
+  static constexpr int WOFF = TSC + kMxTileRows * 4;                 // weight chunks
+  static constexpr int WSC = WOFF + kMxWBytes;                       // weight scale words
+  static constexpr int SBUF = WSC + kMxWsBytes;
   static constexpr int NB0 = kMxRingBytes / SBUF;
   static constexpr int NB = NB0 > 6 ? 6 : NB0;
-  static constexpr int RW = 3;
+  static constexpr int NF0 = (NFW + 1) / 2;          // fragments of waves 0-3; the rest 4-7
 };
 
-template <int NFW, int EPI>
+template <int NFW, int NJ, int EPI>
 __device__ __forceinline__ void run_tile_mx(const GemmArgs& a, uint8_t* ring, const int* row_src,
                                             int e, int nt, int64_t row0) {
-  constexpr int NB = MxDepth<NFW>::NB, RW = MxDepth<NFW>::RW, SBUF = MxDepth<NFW>::SBUF;
-  constexpr int SDATA = NFW * 32 * kMxStageBytes;        // scale dwords follow the data
-  static_assert(NB >= 3, "at least three token stage buffers");
-  // vector memory operations one wave issues per stage: 2 weight groups x (scale dword + 2
-  // chunks), NFW token data pieces and one scale piece
-  constexpr int VM_W = 6, VM_T = NFW + 1, VM_STAGE = VM_W + VM_T;
+  using D = MxDepth<NFW>;
+  constexpr int NB = D::NB, SBUF = D::SBUF;
+  constexpr int NF0 = D::NF0;
+  constexpr int NA = NJ > 0 ? NJ : 1;                    // accumulator fragments declared
+  static_assert(NB >= 3, "at least three stage buffers");
+  // vector memory operations a wave issues per stage: one weight group (scale word and two
+  // chunks), NP token data pieces and one token scale piece
+  constexpr int NP = (4 * NFW + 7) / 8;
+  constexpr int VM_STAGE = 3 + NP + 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = wave & 3, half = wave >> 2;
   const int h = lane >> 5, col = lane & 31;
   const int nst = a.nch / kStageChunks;
   const int64_t K = a.a_rowq;                            // FP8 bytes per token row
 
-  // weights: this wave's two row groups of n-tile nt through a buffer resource over the expert
+  // weights: wave w + 4 h copies row group 8 nt + 2 w + h of the n-tile (local group 2 w + h)
+  // through a buffer resource over the expert; a wave pair past the last row group of the
+  // matrix copies groups 0 and 1 instead and skips the epilogue
   const __amdgpu_buffer_rsrc_t wrs =
       make_rsrc(a.panel + (int64_t)e * a.expert_bytes, (uint32_t)a.expert_bytes);
-  const int g0 = nt * kTileGroups + 2 * wave;
+  const int g0 = nt * kTileGroups + 2 * wg;
   const bool wave_on = (g0 + 2) * kGroupRows <= a.N;
-  const int go0 = (wave_on ? g0 : 0) * (int)a.rg_bytes;
-  const int wlane = lane * 16;
-  auto load_s = [&](int g, int st) {
-    const int sc = st / (kSuperChunks / kStageChunks), c0 = (st * kStageChunks) % kSuperChunks;
-    return buffer_load_u32(wrs, wlane, go0 + g * (int)a.rg_bytes + sc * kSuperBytes + 2 * c0);
-  };
-  auto load_w1 = [&](int g, int st, int c) {
-    const int sc = st / (kSuperChunks / kStageChunks), c0 = (st * kStageChunks) % kSuperChunks;
-    return buffer_load_u128(wrs, wlane + (1 + c) * kUnit,
-                            go0 + g * (int)a.rg_bytes + sc * kSuperBytes + c0 * kUnit);
-  };
+  const int gl = 2 * wg + half;                          // local group this wave copies
+  const int go = (wave_on ? g0 + half : half) * (int)a.rg_bytes;
+  const uint32_t wlane = (uint32_t)lane * 16;
 
-  // token rows: DMA piece k of this wave (k < NFW) covers tile rows 8 (4 k + wave) .. + 7, lane
-  // L row 8 (4 k + wave) + L / 8, physical slot L % 8 = logical slot (L % 8) ^ (row & 7); the
-  // scale piece covers rows 64 wave .. 64 wave + 63, one dword per lane
+  // token rows: the stage's 4 NFW DMA pieces of 8 rows go round the 8 waves, piece
+  // p = wave + 8 k (a wave past the last piece repeats it: the same bytes to the same place);
+  // lane L moves row 8 p + L / 8 into physical slot L % 8 = logical slot (L % 8) ^ (row & 7).
+  // The scale piece covers rows 64 wg .. 64 wg + 63, one dword per lane (waves w and w + 4 move
+  // the same one), so every wave issues the same loads and no branch splits a stage.
   const __amdgpu_buffer_rsrc_t trs = make_rsrc(a.a_q, (uint32_t)(a.a_rows * K));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.a_sf, (uint32_t)(a.a_rows * (K >> 5)));
-  uint32_t t_voff[NFW];
+  uint32_t t_voff[NP];
+  int t_piece[NP];
 #pragma unroll
-  for (int k = 0; k < NFW; ++k) {
-    const int row = 8 * (4 * k + wave) + (lane >> 3);
+  for (int k = 0; k < NP; ++k) {
+    t_piece[k] = min(wave + 8 * k, 4 * NFW - 1);
+    const int row = 8 * t_piece[k] + (lane >> 3);
     const int src = row_src[row] < 0 ? 0 : row_src[row];
     const uint32_t u = (uint32_t)((lane & 7) ^ (row & 7));
     t_voff[k] = (uint32_t)src * (uint32_t)K + u * 16;
   }
   uint32_t s_voff;
   {
-    const int row = 64 * wave + lane;
+    const int row = 64 * wg + lane;
     const int src = (row < NFW * 32 && row_src[row] >= 0) ? row_src[row] : 0;
-    s_voff = (uint32_t)src * (uint32_t)(K >> 5) * 1u;
+    s_voff = (uint32_t)src * (uint32_t)(K >> 5);
   }
-  auto load_t = [&](int b, int st) {
+  auto lds_ptr = [](uint8_t* p) { return (__attribute__((address_space(3))) void*)p; };
+  // stage st into stage buffer b: weight scale word, the two weight chunks, token rows, token
+  // scales (VM_STAGE vector memory operations, always in this order)
+  auto load_stage = [&](int b, int st) {
     uint8_t* base = ring + b * SBUF;
+    const int sc = st / (kSuperChunks / kStageChunks), c0 = (st * kStageChunks) % kSuperChunks;
+    const int wsoff = go + sc * kSuperBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lds_ptr(base + D::WSC + gl * 256), 4, wlane,
+                                             (uint32_t)(wsoff + 2 * c0), 0, 0);
 #pragma unroll
-    for (int k = 0; k < NFW; ++k)
-      buffer_load_lds16(trs, base + 8 * (4 * k + wave) * kMxStageBytes, t_voff[k],
+    for (int c = 0; c < kStageChunks; ++c)
+      buffer_load_lds16(wrs, base + D::WOFF + (gl * kStageChunks + c) * kUnit, wlane,
+                        (uint32_t)(wsoff + (1 + c0 + c) * kUnit));
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+      buffer_load_lds16(trs, base + 8 * t_piece[k] * kMxStageBytes, t_voff[k],
                         (uint32_t)st * kMxStageBytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        srs, (__attribute__((address_space(3))) void*)(base + SDATA + 64 * wave * 4), 4, s_voff,
-        (uint32_t)st * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(base + D::TSC + 64 * wg * 4), 4, s_voff,
+                                             (uint32_t)st * 4, 0, 0);
   };
 
-  f32x16_t acc[2][NFW];
+  f32x16_t acc[2][NA];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int j = 0; j < NFW; ++j) acc[g][j] = f32x16_t{};
-  uint4 W[RW][2][kStageChunks];
-  uint32_t S[RW][2];
-  auto load_w = [&](int r, int st) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      S[r][g] = load_s(g, st);
-#pragma unroll
-      for (int c = 0; c < kStageChunks; ++c) W[r][g][c] = load_w1(g, st, c);
-    }
-  };
+    for (int j = 0; j < NA; ++j) acc[g][j] = f32x16_t{};
 
-  // ---- prologue: token stages 0 .. NB-2, then weights of stages 0 .. RW-2; every load is
-  // unconditional (stage indices clamped) so the waits below count exactly ----
+  // ---- prologue: stages 0 .. NB-2 (stage indices clamped, so every wave issues the same
+  // loads and the waits below count exactly) ----
 #pragma unroll
-  for (int b = 0; b < NB - 1; ++b) load_t(b, min(b, nst - 1));
-#pragma unroll
-  for (int r = 0; r < RW - 1; ++r) load_w(r, min(r, nst - 1));
-  // stage 0's rows have landed once at most the later loads are outstanding
-  wait_vmcnt<(NB - 2) * VM_T + (RW - 1) * VM_W>();
+  for (int b = 0; b < NB - 1; ++b) load_stage(b, min(b, nst - 1));
+  wait_vmcnt<(NB - 2) * VM_STAGE>();                     // stage 0 has landed
   lds_barrier();
 
-  // one stage: weights of stage st + RW - 1 and token rows of stage st + NB - 1 go out first
-  // (the buffer they refill was released by the barrier that ended stage st - 1), then the two
-  // chunks' MFMAs
-  auto stage = [&](auto RR, int st) {
-    constexpr int R = decltype(RR)::value;
-    const uint8_t* buf = ring + (st % NB) * SBUF;
-    load_w((R + RW - 1) % RW, min(st + RW - 1, nst - 1));
-    load_t((st + NB - 1) % NB, min(st + NB - 1, nst - 1));
-    // token fragment j, chunk c: FP8 operand (lane layout K 16 h .. 16 h + 15 and 32 + 16 h ..
-    // of the chunk, from the swizzled row) and its E8M0 code (K block h of the chunk)
-    const uint32_t sw = (uint32_t)(col & 7);             // row & 7 for every fragment's row
-    auto read_b = [&](int j, int c, i32x8_t& B, int& sb) {
-      const uint8_t* rp = buf + (32 * j + col) * kMxStageBytes;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(rp + (((4 * c + h) ^ sw) << 4));
-      const uint4 b1 = *reinterpret_cast<const uint4*>(rp + (((4 * c + 2 + h) ^ sw) << 4));
+  // LDS operand addresses: this lane's row of fragment 0 of this wave's half of the tile, its
+  // four 16-byte slots (chunk c, K halves) and its scale dword; fragment jj adds jj * 4 KiB.
+  // The weight operand of group 2 wg + g, chunk c is this lane's 16 bytes of that chunk.
+  const uint32_t sw = (uint32_t)(col & 7);               // row & 7 for every fragment's row
+  const int j0 = half == 0 ? 0 : NF0;
+  const int hoff = 32 * j0 * kMxStageBytes;              // wave-uniform
+  const int soff = D::TSC + 32 * j0 * 4;
+  uint32_t lb[kStageChunks][2];
+#pragma unroll
+  for (int c = 0; c < kStageChunks; ++c)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      lb[c][k] = (uint32_t)(col * kMxStageBytes) + ((((uint32_t)(4 * c + 2 * k + h)) ^ sw) << 4);
+  const uint32_t ls = (uint32_t)(col * 4);
+  const int woff = D::WOFF + 2 * wg * kStageChunks * kUnit;
+  const int wsc = D::WSC + 2 * wg * 256;
+
+  // The MFMAs of one stage over NF fragments: two-deep pipeline over the fragments (the next
+  // fragment's operand is read from LDS while the current one's two MFMAs issue), the next
+  // chunk's weight operands read during the first fragment of a chunk; the scheduling fences
+  // keep the compiler from hoisting more reads ahead.  Plain vector types for the LDS reads:
+  // read through HIP's uint4 struct, the compiler makes every LDS read wait for the latest
+  // buffer-to-LDS copy to land, which would stall each stage on the copies it has just issued.
+  auto mfmas = [&](auto NJ_, const uint8_t* buf) {
+    constexpr int NF = decltype(NJ_)::value;
+    const uint8_t* hb = buf + hoff;
+    const uint8_t* sbase = buf + soff;
+    auto read_b = [&](int jj, int c, i32x8_t& B, int& sb) {
+      const u32x4_t b0 =
+          *reinterpret_cast<const u32x4_t*>(hb + lb[c][0] + jj * 32 * kMxStageBytes);
+      const u32x4_t b1 =
+          *reinterpret_cast<const u32x4_t*>(hb + lb[c][1] + jj * 32 * kMxStageBytes);
       B = i32x8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
                   (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-      const uint32_t tsc = *reinterpret_cast<const uint32_t*>(buf + SDATA + (32 * j + col) * 4);
+      const uint32_t tsc = *reinterpret_cast<const uint32_t*>(sbase + ls + jj * 32 * 4);
       sb = (int)((tsc >> (8 * (2 * c + h))) & 0xFFu);
     };
-    // two-deep pipeline over the fragments: the next fragment's operand is read from LDS while
-    // the current one's two MFMAs (one per row group) issue; the scheduling fences keep the
-    // compiler from hoisting more reads (and their registers) ahead
+    auto read_a = [&](int c, u32x4_t (&A)[2], uint32_t (&S)[2]) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        A[g] = *reinterpret_cast<const u32x4_t*>(buf + woff + (g * kStageChunks + c) * kUnit +
+                                                 wlane);
+        S[g] = *reinterpret_cast<const uint32_t*>(buf + wsc + g * 256 + 4 * lane);
+      }
+    };
+    u32x4_t Ac[2], An[2];
+    uint32_t Sc[2], Sn[2];
+    read_a(0, Ac, Sc);
 #pragma unroll
     for (int c = 0; c < kStageChunks; ++c) {
+      i32x8_t Bc, Bn;
+      int sbc, sbn;
+      read_b(0, c, Bc, sbc);
+      if (c + 1 < kStageChunks) read_a(c + 1, An, Sn);
       i32x8_t A[2];
       int sa[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        A[g] = i32x8_t{(int)W[R][g][c].x, (int)W[R][g][c].y, (int)W[R][g][c].z,
-                       (int)W[R][g][c].w, 0, 0, 0, 0};
-        sa[g] = (int)((S[R][g] >> (16 * c)) & 0xFFu);
+        A[g] = i32x8_t{(int)Ac[g].x, (int)Ac[g].y, (int)Ac[g].z, (int)Ac[g].w, 0, 0, 0, 0};
+        sa[g] = (int)((Sc[g] >> (16 * c)) & 0xFFu);
       }
-      i32x8_t Bc, Bn;
-      int sbc, sbn;
-      read_b(0, c, Bc, sbc);
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) {
-        if (j + 1 < NFW) read_b(j + 1, c, Bn, sbn);
+      for (int jj = 0; jj < NF; ++jj) {
+        if (jj + 1 < NF) read_b(jj + 1, c, Bn, sbn);
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          acc[g][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[g], Bc, acc[g][j], 4, 0,
-                                                                      0, sa[g], 0, sbc);
+          acc[g][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[g], Bc, acc[g][jj], 4,
+                                                                       0, 0, sa[g], 0, sbc);
         __builtin_amdgcn_sched_barrier(0);
-        if (j + 1 < NFW) {
+        if (jj + 1 < NF) {
           Bc = Bn;
           sbc = sbn;
         }
       }
-    }
-    // stage st + 1's rows have landed once at most the loads issued after them are outstanding:
-    // they went out in stage st + 2 - NB (or in the prologue), followed by NB - 2 stages' loads
-    if (st + 1 > NB - 2) wait_vmcnt<(NB - 2) * VM_STAGE>();
-    else wait_vmcnt<(NB - 3) * VM_T + (RW - 1) * VM_W + VM_STAGE>();
-    lds_barrier();
-  };
-  int st0 = 0;
-  for (; st0 + RW - 1 < nst; st0 += RW)
-    unroll_seq([&](auto RR) { stage(RR, st0 + decltype(RR)::value); },
-               std::make_integer_sequence<int, RW>{});
-  unroll_seq([&](auto RR) {
-    if (st0 + decltype(RR)::value < nst) stage(RR, st0 + decltype(RR)::value);
-  }, std::make_integer_sequence<int, RW - 1>{});
-  // every issued weight load is counted by the waits above: keep the ones of the last stages
-  // (never read) alive, then let every DMA land before the LDS ring is reused
+      if (c + 1 < kStageChunks) {
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
-    asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, W[r][0][0])),
-                 "v"(__builtin_bit_cast(u32x4_t, W[r][0][1])),
-                 "v"(__builtin_bit_cast(u32x4_t, W[r][1][0])),
-                 "v"(__builtin_bit_cast(u32x4_t, W[r][1][1])), "v"(S[r][0]), "v"(S[r][1]));
+        for (int g = 0; g < 2; ++g) {
+          Ac[g] = An[g];
+          Sc[g] = Sn[g];
+        }
+      }
+    }
+  };
+
+  // one stage: stage st + NB - 1 goes out first into the buffer released by the barrier that
+  // ended stage st - 1, then the stage's MFMAs; stage st + 1 has landed once at most the loads
+  // issued after it are outstanding: it went out in stage st + 2 - NB (or in the prologue, which
+  // is followed by fewer loads), followed by NB - 2 stages' loads
+  for (int st = 0; st < nst; ++st) {
+    const uint8_t* buf = ring + (st % NB) * SBUF;
+    load_stage((st + NB - 1) % NB, min(st + NB - 1, nst - 1));
+    if (NJ > 0) mfmas(std::integral_constant<int, NA>{}, buf);
+    wait_vmcnt<(NB - 2) * VM_STAGE>();
+    lds_barrier();
+  }
+  // the clamped loads of the last stages must land before the LDS ring is reused
   wait_vmcnt<0>();
   if (!wave_on) return;
   // one fragment's epilogue at a time: the fences keep the compiler from moving every
-  // accumulator out of the AGPRs at once
+  // accumulator out at once
 #pragma unroll
-  for (int j = 0; j < NFW; ++j) {
+  for (int jj = 0; jj < NJ; ++jj) {
     __builtin_amdgcn_sched_barrier(0);
-    const int m = 32 * j + col;
+    const int m = 32 * (j0 + jj) + col;
     if (row_src[m] < 0) continue;
     if (EPI == EPI_DOWN) {
-      epilogue_group<EPI_DOWN, true>(a, acc[0][j], 1.0f, g0, h, 1.0f, row0 + m);
-      epilogue_group<EPI_DOWN, true>(a, acc[1][j], 1.0f, g0 + 1, h, 1.0f, row0 + m);
+      epilogue_group<EPI_DOWN, true>(a, acc[0][jj], 1.0f, g0, h, 1.0f, row0 + m);
+      epilogue_group<EPI_DOWN, true>(a, acc[1][jj], 1.0f, g0 + 1, h, 1.0f, row0 + m);
     } else {
-      epilogue_mx<EPI>(a, acc[0][j], acc[1][j], g0, h, row0 + m);
+      epilogue_mx<EPI>(a, acc[0][jj], acc[1][jj], g0, h, row0 + m);
     }
   }
 }
@@ -1704,20 +1736,35 @@ __device__ __forceinline__ void run_tile_mx(const GemmArgs& a, uint8_t* ring, co
 template <int EPI>
 __device__ __forceinline__ void run_nfw_mx(const GemmArgs& a, uint8_t* ring, const int* row_src,
                                            int e, int nt, int64_t row0, int nfw) {
+  // waves 0-3 take the first ceil(nfw / 2) token fragments, waves 4-7 the others; each half
+  // runs its own copy of the stage loop, specialised for its fragment count
+  const bool lo = (threadIdx.x >> 6) < 4;
   switch (nfw) {
-    case 1: run_tile_mx<1, EPI>(a, ring, row_src, e, nt, row0); break;
-    case 2: run_tile_mx<2, EPI>(a, ring, row_src, e, nt, row0); break;
-    case 3: run_tile_mx<3, EPI>(a, ring, row_src, e, nt, row0); break;
-    case 4: run_tile_mx<4, EPI>(a, ring, row_src, e, nt, row0); break;
-    case 5: run_tile_mx<5, EPI>(a, ring, row_src, e, nt, row0); break;
-    case 6: run_tile_mx<6, EPI>(a, ring, row_src, e, nt, row0); break;
-    case 7: run_tile_mx<7, EPI>(a, ring, row_src, e, nt, row0); break;
-    default: run_tile_mx<8, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 1:
+      if (lo) run_tile_mx<1, 1, EPI>(a, ring, row_src, e, nt, row0);
+      else run_tile_mx<1, 0, EPI>(a, ring, row_src, e, nt, row0);
+      break;
+    case 2: run_tile_mx<2, 1, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 3:
+      if (lo) run_tile_mx<3, 2, EPI>(a, ring, row_src, e, nt, row0);
+      else run_tile_mx<3, 1, EPI>(a, ring, row_src, e, nt, row0);
+      break;
+    case 4: run_tile_mx<4, 2, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 5:
+      if (lo) run_tile_mx<5, 3, EPI>(a, ring, row_src, e, nt, row0);
+      else run_tile_mx<5, 2, EPI>(a, ring, row_src, e, nt, row0);
+      break;
+    case 6: run_tile_mx<6, 3, EPI>(a, ring, row_src, e, nt, row0); break;
+    case 7:
+      if (lo) run_tile_mx<7, 4, EPI>(a, ring, row_src, e, nt, row0);
+      else run_tile_mx<7, 3, EPI>(a, ring, row_src, e, nt, row0);
+      break;
+    default: run_tile_mx<8, 4, EPI>(a, ring, row_src, e, nt, row0); break;
   }
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void moe_gemm_mx_kernel(GemmArgs a) {
+__global__ __launch_bounds__(512, 1) void moe_gemm_mx_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* ring = smem;
   int* row_src = reinterpret_cast<int*>(smem + kMxRingBytes);
@@ -1757,7 +1804,7 @@ __global__ __launch_bounds__(256, 1) void moe_gemm_mx_kernel(GemmArgs a) {
     __syncthreads();                         // the previous task is done with LDS
     if (tid == 0) *sh_nvalid = 0;
     __syncthreads();
-    {
+    if (tid < kMxTileRows) {
       int src = -1;
       if (tid < rows_here) {
         const int64_t ent = a.sorted[row0 + tid];
@@ -1791,7 +1838,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, int64_t max_tiles, const char* name
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   KernelTimer t(name, s);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, a);
   return hipGetLastError();
 }
 
