@@ -491,38 +491,46 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, Is.
 // stage st + RW - 1 are loaded into registers and the FP16 token rows of stage st + NB - 1 into
 // LDS while stage st computes.  A stage of token rows takes NFW * 8 KiB of the 128 KiB region,
 // so short tiles (short stages) look further ahead.
-template <int NFW, int EPI> struct TileDepth {
+template <int NFW, int G, int EPI> struct TileDepth {
   // 3 stages for short gate/up tiles measured faster than 4; the down GEMM keeps 4, which
-  // divides its 16 stages per n-tile so that n-tiles stream through one pipeline
-  static constexpr int RW = NFW <= 4 ? (EPI == EPI_DOWN ? 4 : 3) : 2;
+  // divides its 16 stages per n-tile so that n-tiles stream through one pipeline.  With two
+  // row groups per wave the weight ring takes twice the registers.
+  static constexpr int RW = G == 2 ? (NFW <= 2 ? (EPI == EPI_DOWN ? 4 : 3) : 2)
+                                   : NFW <= 4 ? (EPI == EPI_DOWN ? 4 : 3) : 2;
   static constexpr int NB0 = kTokRegion / (NFW * 32 * kTokPitch);
   static constexpr int NB = NB0 > 8 ? 8 : NB0;
 };
 
-// One prefill tile of up to kTileRows plan rows of one expert, against kTileGroups weight row
-// groups.  Eight waves, two per SIMD: wave w owns row group g = kTileGroups * nt + w and all NFW
-// token fragments of the tile (32 * NFW plan rows), so each weight fragment is decoded once per
-// tile.  The token operand comes from an exact FP16 copy (the decoded activations for GEMM1,
+// One prefill tile of up to kTileRows plan rows of one expert, against G n-tiles of kTileGroups
+// weight row groups each.  Eight waves, two per SIMD: wave w owns row group g = kTileGroups * nt
+// + w of each of the G n-tiles nt and all NFW token fragments of the tile (32 * NFW plan rows),
+// so each weight fragment is decoded once per tile.  With G = 2 (short down-GEMM tiles) every
+// token operand read from LDS feeds two MFMAs, and the tile's token rows are copied into LDS
+// half as often.  The token operand comes from an exact FP16 copy (the decoded activations for GEMM1,
 // the dequantized intermediate for GEMM2) and is copied into LDS by direct buffer-to-LDS loads:
 // per 128-K stage each wave moves 4 rows of every fragment (one 1 KiB load per fragment), into
 // a ring of NB stage buffers.  Inside a buffer row r's 16-byte slot u (K values 8u .. 8u+7 of the
 // stage) sits at slot u ^ (r & 15), so the MFMA operand reads are free of bank conflicts.
-// Per 16-K step a wave issues its NFW MFMAs, each followed by the LDS read that refills the same
-// token register for the next step, and decodes its weight fragment of the next step.
-template <int NFW, int EPI>
+// Per 16-K step a wave issues its G * NFW MFMAs, each fragment's followed by the LDS read that
+// refills the same token register for the next step, and decodes its weight fragments of the
+// next step.  The task's n-tiles nt0 .. nt0 + nchain - 1 are taken G at a time (units); a unit
+// past the matrix's last n-tile loads group 0 and skips its epilogue.
+template <int NFW, int G, int EPI>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int e, int nt0,
                                          int nchain, int64_t row0) {
   static_assert(NFW >= 1 && NFW <= 8, "at most 8 token fragments per tile");
-  constexpr int RW = TileDepth<NFW, EPI>::RW, NB = TileDepth<NFW, EPI>::NB;
+  static_assert(G == 1 || (G == 2 && NFW <= 4), "two n-tiles at once for short tiles only");
+  constexpr int RW = TileDepth<NFW, G, EPI>::RW, NB = TileDepth<NFW, G, EPI>::NB;
   static_assert(RW >= 2 && RW <= 8, "weight ring of 2 to 8 stages");
   static_assert(NB >= 2, "at least two token stage buffers");
   constexpr int SBUF = NFW * 32 * kTokPitch;      // bytes of one stage buffer
-  // vector memory operations a wave issues per stage: 3 weight loads, then NFW token loads
-  constexpr int VM_STAGE = NFW + 3;
+  // vector memory operations a wave issues per stage: 3 G weight loads, then NFW token loads
+  constexpr int VM_W = 3 * G;
+  constexpr int VM_STAGE = NFW + VM_W;
   // loads issued after the prologue's token load of stage 1: NB - 3 token stages, RW - 1 weight
-  // stages, then stage 0's NFW + 3 (the fewest behind any prologue-loaded stage).  The prologue
-  // issues its token stages before its weight stages.
-  constexpr int kEarlyWait = NB >= 3 ? (NB - 3) * NFW + 3 * (RW - 1) + VM_STAGE : 0;
+  // stages, then stage 0's NFW + VM_W (the fewest behind any prologue-loaded stage).  The
+  // prologue issues its token stages before its weight stages.
+  constexpr int kEarlyWait = NB >= 3 ? (NB - 3) * NFW + VM_W * (RW - 1) + VM_STAGE : 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
@@ -536,6 +544,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   const int wlane = lane * 16;
   auto group_of = [&](int nt) { return nt * kTileGroups + wave; };
   auto group_on = [&](int nt) { return (group_of(nt) + 1) * kGroupRows <= a.N; };
+  const int nunits = (nchain + G - 1) / G;          // units of G n-tiles
 
   // token rows: this lane moves row 32 i + 4 wave + lane / 16 of fragment i, physical slot
   // lane % 16, i.e. logical slot u_l; rows without a routed slot read row 0 (their MFMA columns
@@ -561,14 +570,16 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   };
 
   const float al = lane_alpha<EPI>(a, e, h);
-  f32x16_t acc[NFW];
+  f32x16_t acc[G][NFW];
 #pragma unroll
-  for (int j = 0; j < NFW; ++j) acc[j] = f32x16_t{};
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < NFW; ++j) acc[g][j] = f32x16_t{};
 
-  uint4 W[RW][kStageChunks];
-  uint32_t S[RW];
+  uint4 W[RW][G][kStageChunks];
+  uint32_t S[RW][G];
   h8_t T[NFW];
-  h8_t Wc;
+  h8_t Wc[G];
 
   // weights of local stage st of row-group offset go (bytes): the scale dword (load_s) and
   // 64-value chunk c (load_w1)
@@ -610,21 +621,27 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
   // while the previous n-tile's epilogue runs.  Only the down GEMM streams several n-tiles: the
   // larger gate/up epilogues inside the stage loop would push its registers past the file.
   constexpr bool kStream = EPI == EPI_DOWN;
-  const int cc = (kStream && nst % RW == 0) ? nchain : 1;
-  for (int c0 = 0; c0 < nchain; c0 += cc) {
-    const int ntb = nt0 + c0, cnt = kStream ? min(cc, nchain - c0) : 1;
+  const int cc = (kStream && nst % RW == 0) ? nunits : 1;
+  for (int c0 = 0; c0 < nunits; c0 += cc) {
+    const int ub = c0, cnt = kStream ? min(cc, nunits - c0) : 1;
     const int NS = cnt * nst;                 // stages of this stream
-    // weight row-group byte offset of the n-tile of global stage gs, and its local stage
-    auto wgo = [&](int gs) {
-      const int nt = kStream ? ntb + gs / nst : ntb;
+    // first n-tile of unit u; weight row-group byte offset of n-tile g of the unit of global
+    // stage gs, and its local stage
+    auto unit_nt = [&](int u) { return nt0 + G * u; };
+    auto wgo = [&](int gs, int g) {
+      const int nt = unit_nt(kStream ? ub + gs / nst : ub) + g;
       return (group_on(nt) ? group_of(nt) : 0) * (int)a.rg_bytes;
     };
     auto local = [&](int gs) { return kStream ? gs % nst : gs; };
-    auto load_w = [&](uint4 (&Wd)[kStageChunks], uint32_t& Sd, int gs) {
-      const int go = wgo(gs), ls = local(gs);
-      Sd = load_s(go, ls);
+    auto load_w = [&](uint4 (&Wd)[G][kStageChunks], uint32_t (&Sd)[G], int gs) {
+      const int ls = local(gs);
 #pragma unroll
-      for (int c = 0; c < kStageChunks; ++c) Wd[c] = load_w1(go, ls, c);
+      for (int g = 0; g < G; ++g) {
+        const int go = wgo(gs, g);
+        Sd[g] = load_s(go, ls);
+#pragma unroll
+        for (int c = 0; c < kStageChunks; ++c) Wd[g][c] = load_w1(go, ls, c);
+      }
     };
 
     // ---- prologue: token stages 0 .. NB-2 into buffers 0 .. NB-2, weights of 0 .. RW-2 ----
@@ -641,7 +658,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
     wait_vmcnt<(NB - 2) * NFW + 3 * (RW - 1)>();
     lds_barrier();
     read_all(sm.tok, 0);
-    Wc = dec_w(W[0], S[0], 0);
+#pragma unroll
+    for (int g = 0; g < G; ++g) Wc[g] = dec_w(W[0][g], S[0][g], 0);
 
     // One stage st of the stream; R = st % RW gives the weight slot as a compile-time index;
     // the LDS stage buffer is st % NB.  Stage st refills buffer (st - 1) % NB (read by stage
@@ -653,34 +671,35 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
       const uint8_t* nbuf = sm.tok + ((st + 1) % NB) * SBUF;
       const int tb = (st + NB - 1) % NB, ts = local(min(st + NB - 1, NS - 1));
       const int wslot = (R + RW - 1) % RW, wgs = min(st + RW - 1, NS - 1);
-      const int wgo_s = wgo(wgs), ws = local(wgs);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const h8_t Wn = (q < 7) ? dec_w(W[R], S[R], q + 1)
-                                : dec_w(W[(R + 1) % RW], S[(R + 1) % RW], 0);
+        h8_t Wn[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          Wn[g] = (q < 7) ? dec_w(W[R][g], S[R][g], q + 1)
+                          : dec_w(W[(R + 1) % RW][g], S[(R + 1) % RW][g], 0);
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc, T[j], acc[j], 0, 0, 0);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            acc[g][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc[g], T[j], acc[g][j], 0, 0, 0);
           if (q < 7)
             T[j] = *reinterpret_cast<const h8_t*>(buf + j * 32 * kTokPitch + t_off(q + 1));
-          // The stage's vector memory operations go out in a fixed order: its three weight
-          // loads after the first MFMA, then the token rows one at a time between the MFMAs of
-          // the first half of the stage: a wave stalled issuing a burst of them behind other
-          // waves' requests would have no MFMA in flight.  Only VALU and SALU work crosses these
+          // The stage's vector memory operations go out in a fixed order: its weight loads
+          // after the first MFMAs, then the token rows one at a time between the MFMAs of the
+          // first half of the stage: a wave stalled issuing a burst of them behind other waves'
+          // requests would have no MFMA in flight.  Only VALU and SALU work crosses these
           // points.
           const int m = q * NFW + j;
-          if (m == 0) {
-            S[wslot] = load_s(wgo_s, ws);
-#pragma unroll
-            for (int c = 0; c < kStageChunks; ++c) W[wslot][c] = load_w1(wgo_s, ws, c);
-          }
+          if (m == 0) load_w(W[wslot], S[wslot], wgs);
 #pragma unroll
           for (int i = 0; i < NFW; ++i)
             if (m == 1 + (i * (kSpreadSteps * NFW - 1)) / NFW) load_t1(tb, ts, i);
           if (m == 0) __builtin_amdgcn_sched_barrier(0);
           else __builtin_amdgcn_sched_barrier(0x006);
         }
-        Wc = Wn;
+#pragma unroll
+        for (int g = 0; g < G; ++g) Wc[g] = Wn[g];
       }
       // stage st + 1's rows have landed once at most the loads issued after them are
       // outstanding.  In the steady state they were the last loads of the stage NB - 1 stages
@@ -703,28 +722,35 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
         if (decltype(RR)::value < rem) stage(RR, s0 + ls + decltype(RR)::value);
       }, std::make_integer_sequence<int, RW - 1>{});
       if (c == cnt - 1) {
-        // The explicit waits count three weight loads in every stage, also in the last stages
+        // The explicit waits count the weight loads of every stage, also in the last stages
         // whose weight registers are never read again; this use keeps the compiler from
         // deleting those loads.
 #pragma unroll
         for (int r = 0; r < RW; ++r)
-          asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, W[r][0])),
-                       "v"(__builtin_bit_cast(u32x4_t, W[r][1])), "v"(S[r]));
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, W[r][g][0])),
+                         "v"(__builtin_bit_cast(u32x4_t, W[r][g][1])), "v"(S[r][g]));
         // the clamped token loads of the last stages must land before LDS is reused
         wait_vmcnt<0>();
       }
-      // ---- epilogue of n-tile ntb + c ----
-      const int nt = ntb + c;
-      if (group_on(nt)) {
+      // ---- epilogue of unit ub + c ----
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int nt = unit_nt(ub + c) + g;
+        if (!group_on(nt)) continue;
 #pragma unroll
         for (int j = 0; j < NFW; ++j) {
           const int m = j * 32 + col;
           if (sm.row_src[m] < 0) continue;
-          epilogue_group<EPI, true>(a, acc[j], al, group_of(nt), h, sm.row_scale[m], row0 + m);
+          epilogue_group<EPI, true>(a, acc[g][j], al, group_of(nt), h, sm.row_scale[m],
+                                    row0 + m);
         }
       }
 #pragma unroll
-      for (int j = 0; j < NFW; ++j) acc[j] = f32x16_t{};
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < NFW; ++j) acc[g][j] = f32x16_t{};
     }
   }
 }
@@ -732,15 +758,18 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, const Smem& sm, int 
 template <int EPI>
 __device__ __forceinline__ void run_nfw(const GemmArgs& a, const Smem& sm, int e, int nt,
                                         int nchain, int64_t row0, int nfw) {
+  // down-GEMM tiles of at most 4 fragments run two n-tiles at once (measured faster); the
+  // gate/up GEMM, with its heavier epilogue, keeps one n-tile per pass (measured slower with two)
+  constexpr int GS = EPI == EPI_DOWN ? 2 : 1;
   switch (nfw) {
-    case 1: run_tile<1, EPI>(a, sm, e, nt, nchain, row0); break;
-    case 2: run_tile<2, EPI>(a, sm, e, nt, nchain, row0); break;
-    case 3: run_tile<3, EPI>(a, sm, e, nt, nchain, row0); break;
-    case 4: run_tile<4, EPI>(a, sm, e, nt, nchain, row0); break;
-    case 5: run_tile<5, EPI>(a, sm, e, nt, nchain, row0); break;
-    case 6: run_tile<6, EPI>(a, sm, e, nt, nchain, row0); break;
-    case 7: run_tile<7, EPI>(a, sm, e, nt, nchain, row0); break;
-    default: run_tile<8, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 1: run_tile<1, GS, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 2: run_tile<2, GS, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 3: run_tile<3, GS, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 4: run_tile<4, GS, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 5: run_tile<5, 1, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 6: run_tile<6, 1, EPI>(a, sm, e, nt, nchain, row0); break;
+    case 7: run_tile<7, 1, EPI>(a, sm, e, nt, nchain, row0); break;
+    default: run_tile<8, 1, EPI>(a, sm, e, nt, nchain, row0); break;
   }
 }
 
