@@ -57,7 +57,9 @@ constexpr int kXcds = 8;            // accelerator complex dies (each with its o
 constexpr int kSpreadSteps = 4;     // 16-K steps of a stage over which its token loads go out
 constexpr int kChainGemm1 = 1;      // prefill n-tiles per task, gate/up GEMM
 static_assert(kChainGemm1 == 1, "the gate/up GEMM kernel runs one n-tile per task");
-constexpr int kChainGemm2 = 4;      // prefill n-tiles per task, down GEMM
+constexpr int kChainGemm2 = 4;      // prefill n-tiles per task, down GEMM (2 for short lists)
+constexpr int kMinTasksPerCu = 6;   // down GEMM: fewer tasks per CU at kChainGemm2 halve it
+constexpr int kCus = 256;           // compute units (one persistent workgroup each)
 
 // Logical row (within a 32-row group) held at physical row rho: the MFMA 32x32 accumulator of
 // lane l holds rows 8i + 4*(l/32) + j (i, j in 0..3); they are made logical rows
@@ -789,20 +791,29 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int n_tiles = *a.n_tiles;
+  // the down GEMM halves its n-tile chains when the tile list is short (fewer than
+  // kMinTasksPerCu tasks per CU at the full chain), so that the dynamic schedule still has
+  // tasks to balance; the choice depends on the device-side tile count only, so every
+  // workgroup makes the same one
+  int chain = a.chain;
+  if (EPI == EPI_DOWN && chain > 2 &&
+      (int64_t)n_tiles * a.n_nt < (int64_t)kMinTasksPerCu * kCus * chain)
+    chain = 2;
+  const int n_ct = (a.n_nt + chain - 1) / chain;
   // queue x holds tiles x, x + 8, ... (the tile list alternates long and short tiles, so every
   // queue gets a similar mix); workgroups of XCD x (dispatch places workgroup i on XCD i % 8)
   // take tasks from queue x, so a tile's n-tile tasks share one L2, and move on to the next
   // queues when theirs is empty.  Thread 0 keeps the current queue in q.
   auto q_tasks = [&](int qq) -> int64_t {
-    return n_tiles > qq ? (int64_t)((n_tiles - qq + kXcds - 1) / kXcds) * a.n_ct : 0;
+    return n_tiles > qq ? (int64_t)((n_tiles - qq + kXcds - 1) / kXcds) * n_ct : 0;
   };
   // resolve a ticket of queue q into a task (tile * n_ct + chain), moving on while queues are
   // exhausted; -1 when every queue is
   auto resolve = [&](int& qq, uint32_t ticket) -> int {
     for (int tries = 0; tries < kXcds; ++tries) {
       if ((int64_t)ticket < q_tasks(qq)) {
-        const int tile = qq + kXcds * (int)(ticket / a.n_ct);
-        return tile * a.n_ct + (int)(ticket % a.n_ct);
+        const int tile = qq + kXcds * (int)(ticket / n_ct);
+        return tile * n_ct + (int)(ticket % n_ct);
       }
       if (tries == kXcds - 1) break;
       qq = (qq + 1) % kXcds;
@@ -817,9 +828,9 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   while (k >= 0) {
     uint32_t ticket = 0;
     if (tid == 0) ticket = atomicAdd(a.task_counter + q, 1u);   // in flight during this task
-    const int2 t = a.tiles[k / a.n_ct];
-    const int nt = (int)(k % a.n_ct) * a.chain;
-    const int nchain = EPI == EPI_DOWN ? min(a.chain, a.n_nt - nt) : 1;
+    const int2 t = a.tiles[k / n_ct];
+    const int nt = (int)(k % n_ct) * chain;
+    const int nchain = EPI == EPI_DOWN ? min(chain, a.n_nt - nt) : 1;
     const int64_t row0 = t.x;
     const int rows_here = min(kTileRows, t.y);
     const int e = a.eids[row0 / a.block_m];
@@ -1878,8 +1889,10 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t max_tiles, const char* name, h
   static std::atomic<size_t> lds_set[kMaxDevices];
   hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
   if (err != hipSuccess) return err;
-  const int64_t total = max_tiles * a.n_ct;
-  const int64_t maxwg = 256;                         // one workgroup per CU
+  // the most tasks the kernel can make (the down GEMM may halve its chains to 2)
+  const int64_t n_ct_max = EPI == EPI_DOWN ? (a.n_nt + 1) / 2 : a.n_ct;
+  const int64_t total = max_tiles * n_ct_max;
+  const int64_t maxwg = kCus;                        // one workgroup per CU
   int64_t grid = total < maxwg ? total : maxwg;
   grid = (grid + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
