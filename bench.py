@@ -60,6 +60,11 @@ def parse():
                     help="skip the achievable-peak context (read stream, vendor BF16 GEMM)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--digest-counters", nargs="+", metavar="NAME:FETCH_DIR:WRITE_DIR",
+                    help="only write profiles/traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                         "runs: one NAME:FETCH_DIR:WRITE_DIR per workload run (NAME one of "
+                         "decode, decode_ll, prefill, skewed, mx) and copy:FETCH_DIR:WRITE_DIR "
+                         "for the --calibrate-copy runs; prints the summary table")
     ap.add_argument("--graph-vs-eager", action="store_true",
                     help="only run the workload's step eagerly, pause, then as HIP-graph replays "
                          "(for a kernel trace comparing the two)")
@@ -115,6 +120,104 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
+# rocprofv3 kernel symbols of the GEMMs, per workload run, and the names the bench's event table
+# gives the same launches
+COUNTER_KERNELS = {
+    "decode": {"moe_gemv_kernel<2, 0, 2>": "gemm1_swiglu_decode",
+               "moe_gemv_kernel<2, 2, 2>": "gemm2_down_decode"},
+    "decode_ll": {"moe_gemv_kernel<2, 0, 2>": "gemm1_swiglu_decode",
+                  "moe_gemv_kernel<2, 2, 2>": "gemm2_down_decode"},
+    "prefill": {"moe_gemm_kernel<0>": "gemm1_swiglu_prefill",
+                "moe_gemm_kernel<2>": "gemm2_down_prefill"},
+    "skewed": {"moe_gemm_kernel<1>": "gemm1_relu2_prefill",
+               "moe_gemm_kernel<2>": "gemm2_down_prefill"},
+    "mx": {"moe_gemv_mx_kernel<0, 2>": "gemm1_swiglu_mx_decode",
+           "moe_gemv_mx_kernel<2, 2>": "gemm2_down_mx_decode",
+           "moe_gemm_mx_kernel<0>": "gemm1_swiglu_mx_prefill",
+           "moe_gemm_mx_kernel<2>": "gemm2_down_mx_prefill"},
+}
+
+
+def _counter_rows(d):
+    """(kernel name, counter name, value) of every dispatch in a rocprofv3 csv output dir."""
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def digest_counters(specs):
+    """profiles/traffic.json from rocprofv3 counter runs: per workload and GEMM kernel, the mean
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over every dispatch of the run, scaled by what
+    the same counters read for a plain 1 GiB device copy (bytes moved / counter reading), with the
+    digest of the kernel sources they were taken on.  Prints a markdown table of the result."""
+    runs = {}
+    for spec in specs:
+        name, fdir, wdir = spec.split(":")
+        runs[name] = (_counter_rows(fdir), _counter_rows(wdir))
+    if "copy" not in runs:
+        raise SystemExit("--digest-counters needs the copy:FETCH_DIR:WRITE_DIR calibration runs")
+
+    def mean(rows, counter, key):
+        v = [x for k, c, x in rows if c == counter and key in k]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    n = 1 << 30
+    fk, _ = mean(runs["copy"][0], "FETCH_SIZE", "opy")
+    wk, _ = mean(runs["copy"][1], "WRITE_SIZE", "opy")
+    fscale, wscale = n / (fk * 1024.0), n / (wk * 1024.0)
+    digest = kernel_source_digest()
+    out = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                    "dispatch, one counter per pass, mean over every dispatch of the kernel in the "
+                    "run), scaled by the same counters' readings for a plain 1 GiB device copy "
+                    "(bench.py --calibrate-copy): FETCH_SIZE x %.3f, WRITE_SIZE x %.3f.  "
+                    "source_digest = bench.py kernel_source_digest() of the sources the counters "
+                    "were taken on; bench.py reports traffic only while it matches."
+                    % (fscale, wscale),
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- "
+                        "python3 -u bench.py --workload <w> --steps 3 --warmup 1 "
+                        "--no-cpu-baseline --no-context --no-graph --no-w4a16",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- "
+                        "python3 -u bench.py --workload <w> --steps 3 --warmup 1 "
+                        "--no-cpu-baseline --no-context --no-graph --no-w4a16",
+                        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- "
+                        "python3 -u bench.py --calibrate-copy",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- "
+                        "python3 -u bench.py --calibrate-copy",
+                        "python3 bench.py --digest-counters <w>:<fetch dir>:<write dir> ... "
+                        "copy:<fetch dir>:<write dir>"],
+           "copy_reference": {"bytes_read": n, "bytes_written": n, "fetch_kib": fk,
+                              "write_kib": wk},
+           "fetch_scale": fscale, "write_scale": wscale}
+    lines = ["| workload / kernel | dispatches | FETCH_SIZE raw (KiB) | WRITE_SIZE raw (KiB) | "
+             "HBM bytes per launch (scaled) |", "|---|---|---|---|---|"]
+    for wl_name, (frows, wrows) in runs.items():
+        if wl_name == "copy":
+            continue
+        for sym, kname in COUNTER_KERNELS[wl_name].items():
+            f, nf = mean(frows, "FETCH_SIZE", sym)
+            w, _ = mean(wrows, "WRITE_SIZE", sym)
+            if f is None or w is None:
+                continue
+            fb, wb = f * 1024.0 * fscale, w * 1024.0 * wscale
+            out["%s/%s" % (wl_name, kname)] = {
+                "kernel": sym, "fetch_bytes": int(fb), "write_bytes": int(wb),
+                "bytes_per_launch": int(fb + wb), "fetch_kib_raw": f, "write_kib_raw": w,
+                "dispatches": nf, "source_digest": digest}
+            lines.append("| %s/%s `%s` | %d | %.4g | %.4g | %.4g GB |"
+                         % (wl_name, kname, sym, nf, f, w, (fb + wb) / 1e9))
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print("\n".join(lines))
+    print("\nsource_digest %s; FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (digest, fscale, wscale))
+
+
 def traffic_for(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
     current kernel sources; else None."""
@@ -164,13 +267,33 @@ class Setup:
                  weights=self.weights[i % len(self.weights)])
 
 
+_SPIN_RATE = []
+
+
+def spin_cycles(seconds):
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about `seconds` (its cycle rate
+    measured once)."""
+    import torch
+
+    if not _SPIN_RATE:
+        n = 1 << 22
+        torch.cuda._sleep(n)                    # warm
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_RATE.append(n / max(a.elapsed_time(b) * 1e-3, 1e-6))
+    return int(min(seconds * _SPIN_RATE[0], 2 ** 62))
+
+
 def time_workload(wl, steps, warmup, replicas, timed_prefix="gemm1"):
     """Times `steps` whole steps with nothing but the steps on the stream, then repeats them with
     one HIP event pair around each launch of the dominant GEMM (kernels whose name starts with
     `timed_prefix`) for that kernel's live average duration.  Each event marker costs several
     microseconds of queue time, so the step time comes from the first, uninstrumented pass; the
-    second pass's own step time is returned as well.  A last pass outside both records every
-    kernel for the per-kernel breakdown."""
+    second pass's own GPU time per step is returned as well.  A last pass outside both records
+    every kernel for the per-kernel breakdown."""
     import torch
 
     import block_scaled_fp4_plan_amd as bf
@@ -182,17 +305,24 @@ def time_workload(wl, steps, warmup, replicas, timed_prefix="gemm1"):
     t0 = time.perf_counter()
     for i in range(steps):
         s.step(i)
+    t_enq = time.perf_counter() - t0           # host time to enqueue the steps
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     table, dt_ev = {}, None
     if timed_prefix is not None:
+        # The instrumented steps are queued behind a spin kernel that outlasts their host-side
+        # launches, so the GPU runs them back to back: the event pairs then time the kernel, not
+        # the host's launch rate (which bounds the short decode-LL step).
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         bf.bfp4_profile_begin(steps * 4 + 16, timed_prefix)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        torch.cuda._sleep(spin_cycles(min(2.0 * t_enq + 0.002, 0.05)))
+        ev0.record()
         for i in range(steps):
             s.step(i)
+        ev1.record()
         torch.cuda.synchronize()
-        dt_ev = time.perf_counter() - t0
+        dt_ev = ev0.elapsed_time(ev1) * 1e-3
         table = bf.bfp4_profile_end()[1]
     nb = min(steps, 20)                      # per-kernel breakdown, outside the timed passes
     bf.bfp4_profile_begin(nb * 16 + 64)
@@ -553,9 +683,12 @@ def time_mx(wl, args, label, desc):
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
+    t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / args.steps * 1e3
     bf.bfp4_profile_begin(args.steps * 4 + 16, "gemm1")
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles(min(2.0 * t_enq + 0.002, 0.05)))   # as in time_workload
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
@@ -581,7 +714,8 @@ def time_mx(wl, args, label, desc):
         res["config"]["step_hbm_frac"] = step_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
         res["roofline"] = {"bound": "hbm", "kernel": g1_name, "achieved": ach,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": None, "bytes_per_launch": g1_bytes, "avg_launch_ms": g1_ms}
+                           "traffic": traffic_for(g1_name, "mx"), "bytes_per_launch": g1_bytes,
+                           "avg_launch_ms": g1_ms}
     else:
         g1_flops = 2.0 * A * wl.H * wl.N1
         ach = g1_flops / (g1_ms * 1e-3) / 1e12
@@ -589,7 +723,7 @@ def time_mx(wl, args, label, desc):
         res.update(tflops=tf, tflops_frac=tf / FP8_MFMA_PEAK_TFLOPS)
         res["roofline"] = {"bound": "mfma", "kernel": g1_name, "achieved": ach,
                            "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / FP8_MFMA_PEAK_TFLOPS, "traffic": None,
+                           "frac": ach / FP8_MFMA_PEAK_TFLOPS, "traffic": traffic_for(g1_name, "mx"),
                            "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms}
     del f, replicas, pw
     torch.cuda.empty_cache()
@@ -649,6 +783,9 @@ def main():
               "masking non-local experts); --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.digest_counters:                   # reads counter files only: no GPU needed
+        digest_counters(args.digest_counters)
+        return
     import torch
 
     from synth import WORKLOADS
