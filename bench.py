@@ -647,6 +647,94 @@ def time_tiled(wl, label, args, desc):
     return res
 
 
+def cpu_baseline_mx(wl, ids, w, x_bits, w1, w2, runs=3, max_experts=None, gpu_out=None,
+                    central=False):
+    """The oracle on the MX mode's per-call path (plan, then per routed expert the MXFP8
+    quantization of its rows, the exact MX projections, activation and MXFP8 requantization,
+    oracle.expert_rows_forward_mx, one call per expert over a thread pool of all host cores;
+    then the ordered combine), as cpu_baseline does for the NVFP4 mode; the MXFP4 weight
+    quantization is offline and excluded.  w1 / w2: the BF16 weights (device tensors).  With
+    central, the sampled experts come from the middle half of the range of rows per expert
+    (the oracle's MX path is slow enough that the largest experts alone would take a minute)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from oracle.formats import bf16_bits_to_f32
+    from synth import to_bits
+
+    threads = len(os.sched_getaffinity(0))
+    srt, eids, P, ttr = oracle.moe_plan(ids, wl.E, wl.local_offset, wl.n_local, wl.block_m)
+    rows_of = {}
+    for r in range(P):
+        if srt[r] < wl.M * wl.top_k:
+            rows_of.setdefault(int(eids[r // wl.block_m]), []).append(r)
+    experts = sorted(rows_of)
+    if max_experts is not None and len(experts) > max_experts:
+        by_size = sorted(experts, key=lambda e: len(rows_of[e]))
+        lo, hi = (len(by_size) // 4, (3 * len(by_size)) // 4) if central else (0, len(by_size) - 1)
+        pick = np.linspace(lo, hi, max_experts).round().astype(int)
+        experts = sorted(set(by_size[i] for i in pick))
+    A_all = sum(len(v) for v in rows_of.values())
+    A_run = sum(len(rows_of[e]) for e in experts)
+
+    def quant(e):                                                # offline part (untimed)
+        q1, s1 = oracle.quantize_mxfp4(bf16_bits_to_f32(to_bits(w1[e])))
+        q2, s2 = oracle.quantize_mxfp4(bf16_bits_to_f32(to_bits(w2[e])))
+        return e, (q1, s1, q2, s2)
+
+    with ThreadPoolExecutor(threads) as ex:
+        wq = dict(ex.map(quant, experts))
+
+    def one_run():
+        t0 = time.perf_counter()
+        srt_, eids_, P_, ttr_ = oracle.moe_plan(ids, wl.E, wl.local_offset, wl.n_local,
+                                               wl.block_m)
+
+        def expert(e):
+            rs = np.array(rows_of[e])
+            return rs, oracle.expert_rows_forward_mx(x_bits[srt_[rs] // wl.top_k], *wq[e],
+                                                     wl.act_code)["y"]
+
+        y = {}
+        with ThreadPoolExecutor(threads) as ex:
+            for rs, ye in ex.map(expert, experts):
+                for i, r in enumerate(rs):
+                    y[int(r)] = ye[i]
+        out = (oracle.combine(np.zeros((wl.M, wl.H), np.uint16), y, w, ttr_)
+               if max_experts is None else None)
+        return time.perf_counter() - t0, out
+
+    times, out = [], None
+    for _ in range(runs):
+        dt, out = one_run()
+        times.append(dt)
+    dt = float(np.median(times))
+    flops = 2.0 * A_run * (wl.N1 * wl.H + wl.H * wl.I)
+    full_dt = dt * A_all / A_run
+    res = dict(value=wl.M / full_dt, unit="tokens/s", cores=threads, kind="oracle",
+               runs=runs, run_seconds=times, gflops=flops / dt / 1e9,
+               blas_threads="none: the oracle's MX projections are exact int64 matrix products")
+    if max_experts is None:
+        res["sample"] = ("the whole per-call path of the %s workload in the MX mode (%d tokens, "
+                         "%d experts, %d assignments), median of %d runs, %d threads; MXFP4 weight "
+                         "quantization excluded" % (wl.name, wl.M, len(experts), A_all, runs,
+                                                    threads))
+        if gpu_out is not None:
+            got = bf16_bits_to_f32(to_bits(gpu_out)).astype(np.float64)
+            ref = bf16_bits_to_f32(out).astype(np.float64)
+            res["gpu_vs_oracle_rel_fro"] = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    else:
+        res["sample"] = ("%d of the %d routed experts of the %s workload in the MX mode (%d of %d "
+                         "assignments, chosen across the %s of rows per expert), plan over all "
+                         "%d tokens; %.2f s median of %d runs on %d threads, extrapolated to all "
+                         "assignments linearly in their number (%.1f s); MXFP4 weight "
+                         "quantization excluded"
+                         % (len(experts), len(rows_of), wl.name, A_run, A_all,
+                            "middle half of the range" if central else "range", wl.M, dt, runs,
+                            threads, full_dt))
+    return res
+
+
 def time_mx(wl, args, label, desc):
     """The MX mode (MXFP4 weights, MXFP8 activations, block-scaled MFMA) on a workload: plan,
     MXFP8 activation quantization and the fused MX call (+ finalize) per step, with the same
@@ -664,7 +752,9 @@ def time_mx(wl, args, label, desc):
     ids_d, w_d = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
     w1, w2 = make_weights(wl, 0, "cuda")
     pw = runner.prepare_weights_mxfp4(w1, w2, gated=wl.gated)
-    del w1, w2
+    if args.no_cpu_baseline:                     # else kept for the oracle's weight quantization
+        del w1, w2
+        w1 = w2 = None
     replicas = [pw]
     decode = wl.block_m <= 32
     if decode:                                   # weights from HBM on every step
@@ -725,7 +815,19 @@ def time_mx(wl, args, label, desc):
                            "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": ach / FP8_MFMA_PEAK_TFLOPS, "traffic": traffic_for(g1_name, "mx"),
                            "flops_per_launch": g1_flops, "avg_launch_ms": g1_ms}
-    del f, replicas, pw
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline (MX mode):", wl.name)
+        if decode:
+            o = torch.zeros_like(out)                 # one fresh GPU forward for the comparison
+            f(x, ids_d, w_d, out=o, weights=replicas[0])
+            torch.cuda.synchronize()
+            # one run: the oracle's MX dot products are several times slower than its NVFP4
+            # ones, and one run of this path already takes seconds
+            res["cpu_baseline"] = cpu_baseline_mx(wl, ids, w, x_bits, w1, w2, runs=1, gpu_out=o)
+        else:
+            res["cpu_baseline"] = cpu_baseline_mx(wl, ids, w, x_bits, w1, w2, runs=1,
+                                                  max_experts=4, central=True)
+    del f, replicas, pw, w1, w2
     torch.cuda.empty_cache()
     return res
 
