@@ -310,13 +310,15 @@ def time_workload(wl, steps, warmup, replicas, timed_prefix="gemm1"):
     dt = time.perf_counter() - t0
     table, dt_ev = {}, None
     if timed_prefix is not None:
-        # The instrumented steps are queued behind a spin kernel that outlasts their host-side
-        # launches, so the GPU runs them back to back: the event pairs then time the kernel, not
-        # the host's launch rate (which bounds the short decode-LL step).
+        # When the host's launches pace the GPU (the short decode-LL step: enqueueing took most of
+        # the pass), the instrumented steps are queued behind a spin kernel that outlasts their
+        # host-side launches, so the GPU runs them back to back and the event pairs time the
+        # kernel, not the launch rate.  GPU-bound workloads run as they are.
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         bf.bfp4_profile_begin(steps * 4 + 16, timed_prefix)
         torch.cuda.synchronize()
-        torch.cuda._sleep(spin_cycles(min(2.0 * t_enq + 0.002, 0.05)))
+        if t_enq > 0.5 * dt:
+            torch.cuda._sleep(spin_cycles(min(2.0 * t_enq + 0.002, 0.05)))
         ev0.record()
         for i in range(steps):
             s.step(i)
@@ -778,7 +780,8 @@ def time_mx(wl, args, label, desc):
     ms = (time.perf_counter() - t0) / args.steps * 1e3
     bf.bfp4_profile_begin(args.steps * 4 + 16, "gemm1")
     torch.cuda.synchronize()
-    torch.cuda._sleep(spin_cycles(min(2.0 * t_enq + 0.002, 0.05)))   # as in time_workload
+    if t_enq > 0.5 * ms * 1e-3 * args.steps:                          # as in time_workload
+        torch.cuda._sleep(spin_cycles(min(2.0 * t_enq + 0.002, 0.05)))
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
