@@ -1924,7 +1924,14 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   // Decode: one plan block of <= 32 rows per task; prefill: tiles of up to kTileRows plan rows
   // (several blocks of one expert, or slices of larger blocks) from the device-built tile list.
   const bool small = p.block_m <= 32;
-  const int FN = 2;
+  // row groups per task: tiled n-tiles are 4 * 2 groups (256 rows); a decode task takes 4 FN
+  // groups, FN = 1 (half-size tasks) when a GEMM would otherwise have fewer tasks than CUs
+  // (the few-token, small-matrix shapes), counting at most one plan block per assignment
+  const int64_t est_blocks = std::min<int64_t>(cap_blocks, p.M * p.top_k);
+  auto fn_for = [&](int64_t n) {
+    return small && est_blocks * ((n + 255) / 256) < kCus ? 1 : 2;
+  };
+  const int FN1 = fn_for(N1), FN2 = fn_for(p.H);
 
   GemmArgs g1{};
   g1.a_q = p.a_q;
@@ -1972,7 +1979,7 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.rg_bytes = pg1.rg_bytes;
   g1.nch = (int)pg1.nch;
   g1.N = (int)N1;
-  g1.n_nt = (int)((N1 + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g1.n_nt = (int)((N1 + 4 * FN1 * 32 - 1) / (4 * FN1 * 32));
   g1.chain = kChainGemm1;
   g1.n_ct = (g1.n_nt + g1.chain - 1) / g1.chain;
   g1.alpha_a = p.alpha1_gate;
@@ -2008,7 +2015,7 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g2.rg_bytes = pg2.rg_bytes;
   g2.nch = (int)pg2.nch;
   g2.N = (int)p.H;
-  g2.n_nt = (int)((p.H + 4 * FN * 32 - 1) / (4 * FN * 32));
+  g2.n_nt = (int)((p.H + 4 * FN2 * 32 - 1) / (4 * FN2 * 32));
   g2.chain = kChainGemm2;
   g2.n_ct = (g2.n_nt + g2.chain - 1) / g2.chain;
   g2.alpha_a = p.alpha2;
@@ -2024,12 +2031,19 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
         "gemm1_swiglu_decode", "gemm1_relu2_decode", "gemm1_geglu_decode", "gemm1_gelu_decode",
         "gemm1_relu_decode", "gemm1_silu_decode", "gemm1_identity_decode"};
     const char* nm = kName[p.act];
-    err = p.act == BFP4_ACT_SWIGLU ? launch_gemv<2, EPI_SWIGLU>(g1, cap_blocks, nm, s)
-        : p.act == BFP4_ACT_RELU2  ? launch_gemv<2, EPI_RELU2>(g1, cap_blocks, nm, s)
-        : p.act == BFP4_ACT_GEGLU  ? launch_gemv<2, EPI_GEGLU>(g1, cap_blocks, nm, s)
-                              : launch_gemv<2, EPI_ACT>(g1, cap_blocks, nm, s);
+    if (FN1 == 1)
+      err = p.act == BFP4_ACT_SWIGLU ? launch_gemv<1, EPI_SWIGLU>(g1, cap_blocks, nm, s)
+          : p.act == BFP4_ACT_RELU2  ? launch_gemv<1, EPI_RELU2>(g1, cap_blocks, nm, s)
+          : p.act == BFP4_ACT_GEGLU  ? launch_gemv<1, EPI_GEGLU>(g1, cap_blocks, nm, s)
+                                : launch_gemv<1, EPI_ACT>(g1, cap_blocks, nm, s);
+    else
+      err = p.act == BFP4_ACT_SWIGLU ? launch_gemv<2, EPI_SWIGLU>(g1, cap_blocks, nm, s)
+          : p.act == BFP4_ACT_RELU2  ? launch_gemv<2, EPI_RELU2>(g1, cap_blocks, nm, s)
+          : p.act == BFP4_ACT_GEGLU  ? launch_gemv<2, EPI_GEGLU>(g1, cap_blocks, nm, s)
+                                : launch_gemv<2, EPI_ACT>(g1, cap_blocks, nm, s);
     if (err != hipSuccess) return err;
-    return launch_gemv<2, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s);
+    return FN2 == 1 ? launch_gemv<1, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s)
+                    : launch_gemv<2, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s);
   }
   // the prefill kernels address their FP16 token operands with 32-bit buffer offsets
   if (p.M * p.H * 2 >= (int64_t(1) << 31) || p.cap * p.I * 2 >= (int64_t(1) << 31))
