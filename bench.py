@@ -125,7 +125,7 @@ def kernel_source_digest():
 COUNTER_KERNELS = {
     "decode": {"moe_gemv_kernel<2, 0, 2>": "gemm1_swiglu_decode",
                "moe_gemv_kernel<2, 2, 2>": "gemm2_down_decode"},
-    "decode_ll": {"moe_gemv_kernel<2, 0, 2>": "gemm1_swiglu_decode",
+    "decode_ll": {"moe_gemv_kernel<1, 0, 2>": "gemm1_swiglu_decode",     # half-size tasks
                   "moe_gemv_kernel<2, 2, 2>": "gemm2_down_decode"},
     "prefill": {"moe_gemm_kernel<0>": "gemm1_swiglu_prefill",
                 "moe_gemm_kernel<2>": "gemm2_down_prefill"},
