@@ -151,7 +151,7 @@ def _counter_rows(d):
     return rows
 
 
-def digest_counters(specs):
+def digest_counters(specs, out_path=None):
     """profiles/traffic.json from rocprofv3 counter runs: per workload and GEMM kernel, the mean
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over every dispatch of the run, scaled by what
     the same counters read for a plain 1 GiB device copy (bytes moved / counter reading), with the
@@ -211,17 +211,18 @@ def digest_counters(specs):
                 "dispatches": nf, "source_digest": digest}
             lines.append("| %s/%s `%s` | %d | %.4g | %.4g | %.4g GB |"
                          % (wl_name, kname, sym, nf, f, w, (fb + wb) / 1e9))
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+    with open(out_path or os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print("\n".join(lines))
     print("\nsource_digest %s; FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (digest, fscale, wscale))
+    return out
 
 
-def traffic_for(kernel, workload):
+def traffic_for(kernel, workload, path=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
     current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
