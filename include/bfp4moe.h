@@ -329,15 +329,17 @@ int bfp4_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int64_t cols, int6
  * Readings taken: MX weights and activations carry no FP32 global scales; the BF16 intermediate
  * is quantized to MXFP8 (bfp4_quantize_mxfp8's recipe, per 32 values of a row) before GEMM2.
  * Per valid plan row r (token t, local expert e):
- *   pre[n] = sum_h a[t,h] * W1_e[n,h]          (FP32 accumulate of exact products)
+ *   pre[n] = sum_h a[t,h] * W1_e[n,h]          (exact products, FP32 accumulation; the
+ *            instruction sums each 64-product chunk with an error of up to about 2^-13 of the
+ *            chunk's sum of magnitudes, measured)
  *   h[i]   = bf16(act(pre[i]) * pre[I+i]) (gated) or bf16(act(pre[i]));  hq = MXFP8(h)
  *   y[k]   = bf16(sum_i hq[i] * W2_e[k,i]);   finalize / unfinalized as bfp4_fused_moe_nvfp4.
  * Arguments as bfp4_fused_moe_nvfp4, except: a_q [M, H] E4M3 bytes and a_sf [M, H/32] E8M0 from
  * bfp4_quantize_mxfp8 (no per-token scale); panels from bfp4_prepare_weights_mxfp4; no alphas
  * or c2; block_m <= 32 runs the decode kernels, block_m > 32 the tiled prefill kernels (which
  * need M*H and capacity*I below 2^31 bytes and one expert's panel of each matrix below 2^31
- * bytes, else BFP4_ERR_SHAPE); workspace >= bfp4_workspace_size_mx(...) bytes, 256-byte aligned.  debug->preact [capacity, N1] FP32,
- * debug->inter [capacity, I] BF16, debug->inter_q [capacity, I] (the MXFP8 intermediate, 16-byte
+ * bytes, else BFP4_ERR_SHAPE); workspace >= bfp4_workspace_size_mx(...) bytes, 256-byte
+ * aligned.  debug->preact [capacity, N1] FP32, debug->inter [capacity, I] BF16, debug->inter_q [capacity, I] (the MXFP8 intermediate, 16-byte
  * aligned) and debug->inter_sf [capacity, I/32]; inter_f16 unused.
  * ---------------------------------------------------------------------------------------------- */
 size_t bfp4_workspace_size_mx(int64_t M, int64_t H, int64_t I, int top_k, int num_local_experts,
