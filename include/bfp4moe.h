@@ -65,7 +65,11 @@ typedef enum {
   BFP4_ACT_SILU = 5,      /* silu(x) */
   BFP4_ACT_IDENTITY = 6   /* x */
 } bfp4_act;
-typedef enum { BFP4_SCALE_PER_ROW = 0, BFP4_SCALE_PER_GROUP = 1, BFP4_SCALE_FIXED = 2 } bfp4_scale_mode;
+typedef enum {
+  BFP4_SCALE_PER_ROW = 0,
+  BFP4_SCALE_PER_GROUP = 1,
+  BFP4_SCALE_FIXED = 2
+} bfp4_scale_mode;
 /* Routing weights [cuDNN, routing weights bullet: unpacked FP32 or BF16]: FP32 values, or BF16
  * bit patterns, which the combine uses as their exact FP32 values. */
 typedef enum { BFP4_WEIGHTS_F32 = 0, BFP4_WEIGHTS_BF16 = 1 } bfp4_weights_dtype;
@@ -339,8 +343,9 @@ int bfp4_quantize_mxfp8(const uint16_t* x_bf16, int64_t rows, int64_t cols, int6
  * or c2; block_m <= 32 runs the decode kernels, block_m > 32 the tiled prefill kernels (which
  * need M*H and capacity*I below 2^31 bytes and one expert's panel of each matrix below 2^31
  * bytes, else BFP4_ERR_SHAPE); workspace >= bfp4_workspace_size_mx(...) bytes, 256-byte
- * aligned.  debug->preact [capacity, N1] FP32, debug->inter [capacity, I] BF16, debug->inter_q [capacity, I] (the MXFP8 intermediate, 16-byte
- * aligned) and debug->inter_sf [capacity, I/32]; inter_f16 unused.
+ * aligned.  debug->preact [capacity, N1] FP32, debug->inter [capacity, I] BF16,
+ * debug->inter_q [capacity, I] (the MXFP8 intermediate, 16-byte aligned) and debug->inter_sf
+ * [capacity, I/32]; inter_f16 unused.
  * ---------------------------------------------------------------------------------------------- */
 size_t bfp4_workspace_size_mx(int64_t M, int64_t H, int64_t I, int top_k, int num_local_experts,
                               int block_m, int do_finalize);
