@@ -123,10 +123,12 @@ def kernel_source_digest():
 # rocprofv3 kernel symbols of the GEMMs, per workload run, and the names the bench's event table
 # gives the same launches
 COUNTER_KERNELS = {
-    "decode": {"moe_gemv_kernel<2, 0, 2>": "gemm1_swiglu_decode",
-               "moe_gemv_kernel<2, 2, 2>": "gemm2_down_decode"},
-    "decode_ll": {"moe_gemv_kernel<1, 0, 2>": "gemm1_swiglu_decode",     # half-size tasks
-                  "moe_gemv_kernel<2, 2, 2>": "gemm2_down_decode"},
+    # moe_gemv_kernel<FN, KS, EPI, RING, OCC>: decode-LL splits K over 4 (gate/up) and 2 (down)
+    # waves
+    "decode": {"moe_gemv_kernel<2, 1, 0, 2, 4>": "gemm1_swiglu_decode",
+               "moe_gemv_kernel<2, 1, 2, 2, 4>": "gemm2_down_decode"},
+    "decode_ll": {"moe_gemv_kernel<1, 4, 0, 3, 4>": "gemm1_swiglu_decode",
+                  "moe_gemv_kernel<1, 2, 2, 3, 4>": "gemm2_down_decode"},
     "prefill": {"moe_gemm_kernel<0>": "gemm1_swiglu_prefill",
                 "moe_gemm_kernel<2>": "gemm2_down_prefill"},
     "skewed": {"moe_gemm_kernel<1>": "gemm1_relu2_prefill",

@@ -868,82 +868,64 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
   }
 }
 
-// Decode-sized plan blocks (block_m <= 32).  A workgroup task is (plan block, 4*FN weight row
-// groups).  The block's routed token rows (at most 32) are copied once, still packed (NVFP4
-// bytes and scale bytes for the whole K), into LDS; after one barrier every wave streams its own
-// FN weight row groups from HBM RING-1 stages ahead in registers and reads its token operand
-// from LDS, with no further barrier, so the four weight streams never wait for each other.
-template <int FN, int EPI, int RING>
-__global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
+// Decode-sized plan blocks (block_m <= 32).  A workgroup task is (plan block, 4 * FN / KS weight
+// row groups): the four waves form 4 / KS sets of KS waves, each set owns FN row groups, and the
+// KS waves of a set take consecutive parts of the K stages of the same row groups.  The block's
+// routed token rows (at most 32) are copied once, still packed (NVFP4 bytes and scale bytes for
+// the whole K), into LDS; every wave streams its weights from HBM RING - 1 stages ahead in
+// registers and reads its token operand from LDS with no barrier inside the K loop.  The first
+// weight stages are requested before the token rows are staged (they depend only on the
+// block's expert), so the weight stream's latency overlaps the token gather.  With KS > 1 the
+// waves of a set hand their partial FP32 sums to the set's first wave through LDS, which adds
+// them in wave order before the epilogue: a few-token GEMM with few row groups then keeps more
+// waves streaming, each with a shorter dependent chain of loads.
+template <int FN, int KS, int EPI, int RING, int OCC>
+__global__ __launch_bounds__(256, OCC) void moe_gemv_kernel(GemmArgs a) {
+  static_assert(KS == 1 || KS == 2 || KS == 4, "the four waves split K in 1, 2 or 4 parts");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* row_src = reinterpret_cast<int*>(smem);
   float* row_scale = reinterpret_cast<float*>(smem + 32 * sizeof(int));
   uint8_t* tok = smem + 64 * sizeof(int);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
+  const int kp = wave % KS, set = wave / KS;           // K part and wave set
   // per staged row: K/2 packed bytes then K/16 scale bytes, rounded up to 16 bytes
   const int64_t pitch = (a.a_rowq + (a.a_rowq >> 3) + 15) & ~(int64_t)15;
+  const int rows_max = min(a.block_m, 32);
+  // partial sums of waves kp > 0: [set][kp - 1][fn][4 float4][64 lanes], after the token rows
+  float4* red = reinterpret_cast<float4*>(tok + rows_max * pitch);
+  // The first task's expert and plan entries are read together with the plan extent: block
+  // blockIdx.x / n_nt is below capacity / block_m for every workgroup of the grid (at most
+  // capacity / block_m * n_nt workgroups), so the reads stay inside expert_ids and
+  // sorted_token_ids whatever the extent turns out to be.
+  const int64_t b_first = blockIdx.x / a.n_nt;
+  const int e_first = a.eids[b_first];
+  const int ent_first = tid < rows_max ? a.sorted[b_first * a.block_m + tid] : -1;
   int64_t P = *a.ntpp;
+  // all three values are taken here, so the compiler issues the three reads together instead
+  // of sinking the first two to their uses behind the extent test
+  asm volatile("" ::"s"(e_first), "v"(ent_first), "s"((int)P));
   if (P > a.cap) P = a.cap;
   if (P < 0) P = 0;
   const int64_t nblk = P / a.block_m;
   const int64_t ntask = nblk * a.n_nt;
   const int nst = a.nch / kStageChunks;
-  const int rows_max = min(a.block_m, 32);
+  // this wave's K stages [s_lo, s_lo + n); s_lo < nst, n may be 0 when nst < KS
+  const int s_lo = kp * nst / KS, n = (kp + 1) * nst / KS - s_lo;
 
   for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+    const bool first = task == blockIdx.x;
     const int64_t b = task / a.n_nt;
     const int nt = (int)(task - b * a.n_nt);
-    const int e = a.eids[b];
+    const int e = first ? e_first : a.eids[b];
     if (e < 0 || e >= a.nloc) continue;
-    __syncthreads();                                   // previous task done with LDS
-    if (tid < 32) {
-      int src = -1;
-      float sc = 0.0f;
-      if (tid < rows_max) {
-        const int64_t ent = a.sorted[b * a.block_m + tid];
-        if (ent >= 0 && ent < a.sentinel) {
-          if (a.gather) {
-            src = (int)(ent / a.top_k);
-            sc = a.a_dec[src];
-          } else {
-            src = (int)(b * a.block_m + tid);
-            sc = a.a_const_scale;
-          }
-        }
-      }
-      row_src[tid] = src;
-      row_scale[tid] = sc;
-    }
-    __syncthreads();
-    // stage the routed rows: packed bytes in 16-byte units (K/2 is a multiple of 64), scale
-    // bytes in 8-byte units (K/16 is a multiple of 8)
-    const int64_t q16 = a.a_rowq >> 4, s8 = (a.a_rowq >> 3) >> 3;
-    for (int r = 0; r < rows_max; ++r) {
-      const int src = row_src[r];
-      if (src < 0) continue;
-      const uint4* sq = reinterpret_cast<const uint4*>(a.a_q + (int64_t)src * a.a_rowq);
-      const uint2* ss = reinterpret_cast<const uint2*>(a.a_sf + (int64_t)src * (a.a_rowq >> 3));
-      uint8_t* d = tok + r * pitch;
-      for (int64_t i = tid; i < q16; i += 256) reinterpret_cast<uint4*>(d)[i] = sq[i];
-      for (int64_t i = tid; i < s8; i += 256) reinterpret_cast<uint2*>(d + a.a_rowq)[i] = ss[i];
-    }
-    __syncthreads();
 
-    const int64_t g0 = (int64_t)nt * (4 * FN) + (int64_t)wave * FN;
+    const int64_t g0 = (int64_t)nt * (4 / KS * FN) + (int64_t)set * FN;
     const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
     const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
                            lane * 16;
-    // lanes past the staged rows read row 0; their MFMA columns are discarded
-    const uint8_t* trow = tok + (col < rows_max ? col : 0) * pitch;
-
-    const float al = lane_alpha<EPI>(a, e, h);
-    f32x16_t acc[FN];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x16_t{};
     uint4 W[RING][kStageChunks][FN];
     uint32_t S[RING][FN];
-
     auto load_w = [&](uint4 (&Wd)[kStageChunks][FN], uint32_t (&Sd)[FN], int st) {
       const int64_t sc = st / (kSuperChunks / kStageChunks);
       const int c0 = (st * kStageChunks) % kSuperChunks;
@@ -956,6 +938,72 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
           Wd[c][fn] = *reinterpret_cast<const uint4*>(base + kUnit + (c0 + c) * kUnit);
       }
     };
+    // the first RING - 1 stages (clamped to the wave's range; a wave with no stages re-reads
+    // stage s_lo, which stays in range, and never uses it)
+#pragma unroll
+    for (int d = 0; d < RING - 1; ++d) load_w(W[d], S[d], s_lo + min(d, max(n - 1, 0)));
+
+    // These barriers order LDS only (row table, token rows, partial sums), so they do not wait
+    // for the weight loads in flight.
+    lds_barrier();                                     // previous task done with LDS
+    // row table: the source row of each of the block's plan rows (-1: padding or masked),
+    // then its scale, read while the rows are staged
+    int src = -1;
+    if (tid < 32) {
+      if (tid < rows_max) {
+        const int ent = first ? ent_first : a.sorted[b * a.block_m + tid];
+        if (ent >= 0 && ent < a.sentinel) src = a.gather ? (int)(ent / a.top_k) : (int)(b * a.block_m + tid);
+      }
+      row_src[tid] = src;
+    }
+    lds_barrier();
+    const float sc_v = (tid < 32 && src >= 0) ? (a.gather ? a.a_dec[src] : a.a_const_scale) : 0.0f;
+    // stage the routed rows: per row, its packed bytes in 16-byte units (K/2 is a multiple of
+    // 64), then its scale bytes in 8-byte units (K/16 is a multiple of 8); the units of all rows
+    // are spread over the threads, two loads in flight per thread before their LDS stores
+    const int q16 = (int)(a.a_rowq >> 4), per_row = q16 + (int)(a.a_rowq >> 6);
+    const int total = rows_max * per_row;
+    for (int u0 = tid; u0 < total; u0 += 2 * 256) {
+      uint4 v[2];
+      int dst[2];                        // LDS byte offset of the unit, -1: nothing to stage
+      bool wide[2];                      // a 16-byte unit (packed values), else 8 scale bytes
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int u = u0 + j * 256;
+        dst[j] = -1;
+        wide[j] = false;
+        if (u < total) {
+          const int r = u / per_row, i = u - r * per_row;
+          const int sr = row_src[r];
+          if (sr >= 0 && i < q16) {
+            v[j] = *reinterpret_cast<const uint4*>(a.a_q + (int64_t)sr * a.a_rowq + 16 * i);
+            dst[j] = r * (int)pitch + 16 * i;
+            wide[j] = true;
+          } else if (sr >= 0) {
+            const uint2 t = *reinterpret_cast<const uint2*>(
+                a.a_sf + (int64_t)sr * (a.a_rowq >> 3) + 8 * (i - q16));
+            v[j] = make_uint4(t.x, t.y, 0u, 0u);
+            dst[j] = r * (int)pitch + (int)a.a_rowq + 8 * (i - q16);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (dst[j] < 0) continue;
+        if (wide[j]) *reinterpret_cast<uint4*>(tok + dst[j]) = v[j];
+        else *reinterpret_cast<uint2*>(tok + dst[j]) = make_uint2(v[j].x, v[j].y);
+      }
+    }
+    if (tid < 32) row_scale[tid] = sc_v;
+    lds_barrier();
+
+    // lanes past the staged rows read row 0; their MFMA columns are discarded
+    const uint8_t* trow = tok + (col < rows_max ? col : 0) * pitch;
+    const float al = lane_alpha<EPI>(a, e, h);
+    f32x16_t acc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x16_t{};
+
     auto compute = [&](const uint4 (&Wd)[kStageChunks][FN], const uint32_t (&Sd)[FN], int st) {
       const uint2 tsc = *reinterpret_cast<const uint2*>(trow + a.a_rowq + st * 8);
 #pragma unroll
@@ -979,21 +1027,49 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_kernel(GemmArgs a) {
       }
     };
 
-    // weight loads are unconditional (stage index clamped) so the compiler's waits count them
-    // exactly; the tail of the last ring pass leaves through the break
-#pragma unroll
-    for (int d = 0; d < RING - 1; ++d) load_w(W[d], S[d], min(d, nst - 1));
-    for (int st0 = 0; st0 < nst; st0 += RING) {
+    // weight loads are unconditional (stage index clamped to the wave's last stage) so the
+    // compiler's waits count them exactly; the tail of the last ring pass leaves through the
+    // break
+    for (int st0 = 0; st0 < n; st0 += RING) {
 #pragma unroll
       for (int d = 0; d < RING; ++d) {
         const int st = st0 + d;
-        if (st >= nst) break;
+        if (st >= n) break;
         const int nd = (d + RING - 1) % RING;
-        load_w(W[nd], S[nd], min(st + RING - 1, nst - 1));
-        compute(W[d], S[d], st);
+        load_w(W[nd], S[nd], s_lo + min(st + RING - 1, n - 1));
+        compute(W[d], S[d], s_lo + st);
       }
     }
-    if (wave_on && col < rows_max && row_src[col] >= 0) {
+    if (KS > 1) {
+      // waves kp > 0 hand their partial sums to wave kp = 0 of their set
+      float4* mine = red + ((set * (KS - 1) + (kp > 0 ? kp - 1 : 0)) * FN) * 4 * 64 + lane;
+      if (kp > 0) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            mine[(fn * 4 + i) * 64] = make_float4(acc[fn][4 * i], acc[fn][4 * i + 1],
+                                                  acc[fn][4 * i + 2], acc[fn][4 * i + 3]);
+      }
+      lds_barrier();
+      if (kp == 0) {
+#pragma unroll
+        for (int q = 1; q < KS; ++q) {
+          const float4* part = red + ((set * (KS - 1) + q - 1) * FN) * 4 * 64 + lane;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float4 v = part[(fn * 4 + i) * 64];
+              acc[fn][4 * i] += v.x;
+              acc[fn][4 * i + 1] += v.y;
+              acc[fn][4 * i + 2] += v.z;
+              acc[fn][4 * i + 3] += v.w;
+            }
+        }
+      }
+    }
+    if (kp == 0 && wave_on && col < rows_max && row_src[col] >= 0) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
         epilogue_group<EPI>(a, acc[fn], al, g0 + fn, h, row_scale[col], b * a.block_m + col);
@@ -1523,22 +1599,60 @@ hipError_t ensure_dynamic_lds(const void* fn, size_t lds, std::atomic<size_t>* d
   return hipSuccess;
 }
 
-template <int FN, int EPI>
+// LDS of a decode task: the row table and staged token rows, then the partial sums that the
+// waves with K part > 0 hand over (FN accumulators of 64 lanes x 16 floats each).
+size_t gemv_lds_bytes(int block_m, int64_t K, int fn, int ks) {
+  return moe_gemv_lds_bytes(block_m, K) + (size_t)(4 - 4 / ks) * fn * 64 * 16 * sizeof(float);
+}
+
+template <int FN, int KS, int RING, int OCC, int EPI>
 hipError_t launch_gemv(const GemmArgs& a, int64_t cap_blocks, const char* name, hipStream_t s) {
-  constexpr int RING = 2;
-  auto kern = moe_gemv_kernel<FN, EPI, RING>;
-  const size_t lds = moe_gemv_lds_bytes(a.block_m, 2 * a.a_rowq);
+  auto kern = moe_gemv_kernel<FN, KS, EPI, RING, OCC>;
+  const size_t lds = gemv_lds_bytes(a.block_m, 2 * a.a_rowq, FN, KS);
   if (lds > kMaxLdsBytes) return hipErrorInvalidValue;
   static std::atomic<size_t> lds_set[kMaxDevices];
   hipError_t err = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, lds_set);
   if (err != hipSuccess) return err;
   const int64_t tasks = cap_blocks * a.n_nt;
-  const int64_t max_wg = 256LL * 4;                  // resident workgroups (4 waves each)
+  const int64_t max_wg = 256LL * OCC;                // resident workgroups (4 waves each)
   const int64_t grid = tasks < max_wg ? tasks : max_wg;
   if (grid == 0) return hipSuccess;
   KernelTimer t(name, s);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+// Task shape of a decode GEMM with N weight rows and K values per row, for at most `blocks`
+// plan blocks: FN row groups per wave and K split over KS waves.  With at least two tasks of 8
+// row groups per CU (the 7168- and 4096-row matrices of an 8-token step) the weight stream is
+// HBM-bound: two row groups per wave and the whole K, which amortizes the task set-up over the
+// longest chains.  Below that (few tokens on small matrices) the GEMM is latency-bound: one
+// row group per wave, and K split over the most waves (4 or 2) that keep the row-group streams
+// times KS within twice the 4096 resident waves and give each wave at least two 128-K stages
+// (measured on the 4-token, 2048 x 512 shape: 20 against 23 us for the gate/up GEMM, 13 against
+// 14 us for the down GEMM).
+struct GemvShape {
+  int fn, ks;
+};
+GemvShape gemv_shape(int64_t blocks, int64_t N, int64_t K, int block_m) {
+  const int64_t groups = (N + kGroupRows - 1) / kGroupRows;
+  if (blocks * ((N + 255) / 256) >= 2 * kCus) return {2, 1};
+  const int64_t streams = blocks * groups, nst = K / (kChunkK * kStageChunks);
+  const size_t lds_cap = kMaxLdsBytes / 4;          // four workgroups per CU
+  for (int ks = 4; ks > 1; ks /= 2)
+    if (streams * ks <= 2 * 4LL * kCus * 4 && nst >= 2 * ks &&
+        gemv_lds_bytes(block_m, K, 1, ks) <= lds_cap)
+      return {1, ks};
+  return {1, 1};
+}
+
+template <int EPI>
+hipError_t launch_gemv_shape(const GemvShape& sh, const GemmArgs& a, int64_t cap_blocks,
+                             const char* name, hipStream_t s) {
+  if (sh.fn == 2) return launch_gemv<2, 1, 2, 4, EPI>(a, cap_blocks, name, s);
+  if (sh.ks == 4) return launch_gemv<1, 4, 3, 4, EPI>(a, cap_blocks, name, s);
+  if (sh.ks == 2) return launch_gemv<1, 2, 3, 4, EPI>(a, cap_blocks, name, s);
+  return launch_gemv<1, 1, 2, 4, EPI>(a, cap_blocks, name, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1924,14 +2038,12 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   // Decode: one plan block of <= 32 rows per task; prefill: tiles of up to kTileRows plan rows
   // (several blocks of one expert, or slices of larger blocks) from the device-built tile list.
   const bool small = p.block_m <= 32;
-  // row groups per task: tiled n-tiles are 4 * 2 groups (256 rows); a decode task takes 4 FN
-  // groups, FN = 1 (half-size tasks) when a GEMM would otherwise have fewer tasks than CUs
-  // (the few-token, small-matrix shapes), counting at most one plan block per assignment
+  // row groups per task: tiled n-tiles are 4 * 2 groups (256 rows); a decode task takes
+  // 4 FN / KS groups (gemv_shape), counting at most one plan block per assignment
   const int64_t est_blocks = std::min<int64_t>(cap_blocks, p.M * p.top_k);
-  auto fn_for = [&](int64_t n) {
-    return small && est_blocks * ((n + 255) / 256) < kCus ? 1 : 2;
-  };
-  const int FN1 = fn_for(N1), FN2 = fn_for(p.H);
+  const GemvShape sh1 = small ? gemv_shape(est_blocks, N1, p.H, (int)p.block_m) : GemvShape{2, 1};
+  const GemvShape sh2 = small ? gemv_shape(est_blocks, p.H, p.I, (int)p.block_m) : GemvShape{2, 1};
+  const int64_t rows1 = 4 * sh1.fn / sh1.ks * kGroupRows, rows2 = 4 * sh2.fn / sh2.ks * kGroupRows;
 
   GemmArgs g1{};
   g1.a_q = p.a_q;
@@ -1979,7 +2091,7 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g1.rg_bytes = pg1.rg_bytes;
   g1.nch = (int)pg1.nch;
   g1.N = (int)N1;
-  g1.n_nt = (int)((N1 + 4 * FN1 * 32 - 1) / (4 * FN1 * 32));
+  g1.n_nt = (int)((N1 + rows1 - 1) / rows1);
   g1.chain = kChainGemm1;
   g1.n_ct = (g1.n_nt + g1.chain - 1) / g1.chain;
   g1.alpha_a = p.alpha1_gate;
@@ -2015,7 +2127,7 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
   g2.rg_bytes = pg2.rg_bytes;
   g2.nch = (int)pg2.nch;
   g2.N = (int)p.H;
-  g2.n_nt = (int)((p.H + 4 * FN2 * 32 - 1) / (4 * FN2 * 32));
+  g2.n_nt = (int)((p.H + rows2 - 1) / rows2);
   g2.chain = kChainGemm2;
   g2.n_ct = (g2.n_nt + g2.chain - 1) / g2.chain;
   g2.alpha_a = p.alpha2;
@@ -2031,19 +2143,12 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
         "gemm1_swiglu_decode", "gemm1_relu2_decode", "gemm1_geglu_decode", "gemm1_gelu_decode",
         "gemm1_relu_decode", "gemm1_silu_decode", "gemm1_identity_decode"};
     const char* nm = kName[p.act];
-    if (FN1 == 1)
-      err = p.act == BFP4_ACT_SWIGLU ? launch_gemv<1, EPI_SWIGLU>(g1, cap_blocks, nm, s)
-          : p.act == BFP4_ACT_RELU2  ? launch_gemv<1, EPI_RELU2>(g1, cap_blocks, nm, s)
-          : p.act == BFP4_ACT_GEGLU  ? launch_gemv<1, EPI_GEGLU>(g1, cap_blocks, nm, s)
-                                : launch_gemv<1, EPI_ACT>(g1, cap_blocks, nm, s);
-    else
-      err = p.act == BFP4_ACT_SWIGLU ? launch_gemv<2, EPI_SWIGLU>(g1, cap_blocks, nm, s)
-          : p.act == BFP4_ACT_RELU2  ? launch_gemv<2, EPI_RELU2>(g1, cap_blocks, nm, s)
-          : p.act == BFP4_ACT_GEGLU  ? launch_gemv<2, EPI_GEGLU>(g1, cap_blocks, nm, s)
-                                : launch_gemv<2, EPI_ACT>(g1, cap_blocks, nm, s);
+    err = p.act == BFP4_ACT_SWIGLU ? launch_gemv_shape<EPI_SWIGLU>(sh1, g1, cap_blocks, nm, s)
+        : p.act == BFP4_ACT_RELU2  ? launch_gemv_shape<EPI_RELU2>(sh1, g1, cap_blocks, nm, s)
+        : p.act == BFP4_ACT_GEGLU  ? launch_gemv_shape<EPI_GEGLU>(sh1, g1, cap_blocks, nm, s)
+                              : launch_gemv_shape<EPI_ACT>(sh1, g1, cap_blocks, nm, s);
     if (err != hipSuccess) return err;
-    return FN2 == 1 ? launch_gemv<1, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s)
-                    : launch_gemv<2, EPI_DOWN>(g2, cap_blocks, "gemm2_down_decode", s);
+    return launch_gemv_shape<EPI_DOWN>(sh2, g2, cap_blocks, "gemm2_down_decode", s);
   }
   // the prefill kernels address their FP16 token operands with 32-bit buffer offsets
   if (p.M * p.H * 2 >= (int64_t(1) << 31) || p.cap * p.I * 2 >= (int64_t(1) << 31))

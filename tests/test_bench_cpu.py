@@ -47,8 +47,8 @@ def _write_counters(d, rows):
 
 
 def test_digest_counters_scales_by_the_copy_calibration(tmp_path):
-    g1 = "void bfp4::(anonymous namespace)::moe_gemv_kernel<2, 0, 2>(bfp4::GemmArgs)"
-    g2 = "void bfp4::(anonymous namespace)::moe_gemv_kernel<2, 2, 2>(bfp4::GemmArgs)"
+    g1 = "void bfp4::(anonymous namespace)::moe_gemv_kernel<2, 1, 0, 2, 4>(bfp4::GemmArgs)"
+    g2 = "void bfp4::(anonymous namespace)::moe_gemv_kernel<2, 1, 2, 2, 4>(bfp4::GemmArgs)"
     other = "void bfp4::(anonymous namespace)::moe_gemv16_kernel<2, 0, 2, true>(bfp4::GemmArgs)"
     # decode run: two dispatches of each GEMM (means 1500 and 300 KiB fetched), one unrelated
     _write_counters(tmp_path / "df", [(g1, "FETCH_SIZE", 1000), (g1, "FETCH_SIZE", 2000),

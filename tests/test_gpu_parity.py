@@ -280,6 +280,9 @@ CHAIN_N = Workload("chain_n", M=320, H=1024, I=512, E=5, top_k=2, block_m=128, r
 ONE_TOKEN = Workload("one_token", M=1, H=256, I=128, E=8, top_k=1, block_m=8)
 WIDE_TOPK = Workload("wide_topk", M=6, H=512, I=256, E=40, top_k=24, block_m=16)
 LDS_LIMIT = Workload("lds_limit", M=40, H=8960, I=128, E=4, top_k=2, block_m=32)
+# few tokens on few row groups: the decode kernels split K over the waves of a workgroup, here
+# in parts of unequal length (GEMM1: 10 stages of 128 over 4 waves; GEMM2: 5 over 2)
+KS_RAGGED = Workload("ks_ragged", M=3, H=1280, I=640, E=12, top_k=3, block_m=8)
 
 # the other activations, on the decode (block_m 8, 16) and the tiled (block_m 128) kernels
 ACT_WORKLOADS = {
@@ -300,13 +303,14 @@ MOE_CASES = [
     ("gelu", 8), ("gelu", 128), ("relu", 16), ("relu", 128), ("silu", 8), ("silu", 128),
     ("identity", 8), ("identity", 128), ("skewed_gelu", 16),
     ("one_token", 8), ("one_token", 128), ("wide_topk", 16), ("wide_topk", 128), ("lds_limit", 32),
+    ("ks_ragged", 8),
 ]
 
 
 def _workload(name):
     return ({"skewed_small": SMALL_SKEWED, "tiny_relu2": TINY_RELU2, "ragged_k": RAGGED_K,
              "chain_n": CHAIN_N, "one_token": ONE_TOKEN, "wide_topk": WIDE_TOPK,
-             "lds_limit": LDS_LIMIT, **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
+             "lds_limit": LDS_LIMIT, "ks_ragged": KS_RAGGED, **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
 
 
 def check_gemm2(p, eids, bm, rows, dbg, y, c2=1.0, max_flip_frac=0.01):
