@@ -688,7 +688,8 @@ int bfp4_fused_moe_w4a16(const uint16_t* x_bf16, int64_t row_stride, const void*
                          size_t workspace_bytes, void* stream) {
   if (act < BFP4_ACT_SWIGLU || act > BFP4_ACT_IDENTITY) return BFP4_ERR_MODE;
   if (weights_dtype != BFP4_WEIGHTS_F32 && weights_dtype != BFP4_WEIGHTS_BF16) return BFP4_ERR_MODE;
-  if (weight_format != BFP4_FORMAT_NVFP4 && weight_format != BFP4_FORMAT_MXFP4) return BFP4_ERR_MODE;
+  if (weight_format != BFP4_FORMAT_NVFP4 && weight_format != BFP4_FORMAT_MXFP4)
+    return BFP4_ERR_MODE;
   const size_t wsz = weights_dtype == BFP4_WEIGHTS_BF16 ? 2 : 4;
   const int gated = act == BFP4_ACT_SWIGLU || act == BFP4_ACT_GEGLU;
   if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;

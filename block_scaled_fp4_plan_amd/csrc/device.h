@@ -20,7 +20,9 @@ constexpr float kE4M3Max = 448.0f;
 constexpr float kE2M1Max = 6.0f;
 constexpr float kEncodeNumerator = 2688.0f;   // kE4M3Max * kE2M1Max, exact
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
 
 // float -> BF16 bits, round to nearest even (finite inputs; overflow rounds to infinity).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {

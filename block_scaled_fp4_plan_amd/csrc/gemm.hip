@@ -49,7 +49,7 @@ constexpr int kSuperChunks = 8;     // chunks sharing one 1 KiB scale unit
 constexpr int kUnit = 1024;
 constexpr int kSuperBytes = (kSuperChunks + 1) * kUnit;
 constexpr int kStageChunks = 2;     // chunks per pipeline stage (128 K values)
-constexpr int kTokPitch = 256;      // LDS bytes per token row per stage: 128 FP16, 16-byte slots swizzled
+constexpr int kTokPitch = 256;      // LDS bytes per token row per stage: 128 FP16, swizzled slots
 constexpr int kTokRegion = 128 * 1024;   // LDS bytes of prefill token stage buffers
 constexpr int kTileRows = 256;      // plan rows per prefill tile (8 token fragments)
 constexpr int kTileGroups = 8;      // weight row groups per prefill task (one per wave)
@@ -508,11 +508,11 @@ template <int NFW, int G, int EPI> struct TileDepth {
 // + w of each of the G n-tiles nt and all NFW token fragments of the tile (32 * NFW plan rows),
 // so each weight fragment is decoded once per tile.  With G = 2 (short down-GEMM tiles) every
 // token operand read from LDS feeds two MFMAs, and the tile's token rows are copied into LDS
-// half as often.  The token operand comes from an exact FP16 copy (the decoded activations for GEMM1,
-// the dequantized intermediate for GEMM2) and is copied into LDS by direct buffer-to-LDS loads:
-// per 128-K stage each wave moves 4 rows of every fragment (one 1 KiB load per fragment), into
-// a ring of NB stage buffers.  Inside a buffer row r's 16-byte slot u (K values 8u .. 8u+7 of the
-// stage) sits at slot u ^ (r & 15), so the MFMA operand reads are free of bank conflicts.
+// half as often.  The token operand comes from an exact FP16 copy (the decoded activations for
+// GEMM1, the dequantized intermediate for GEMM2) and is copied into LDS by direct buffer-to-LDS
+// loads: per 128-K stage each wave moves 4 rows of every fragment (one 1 KiB load per fragment),
+// into a ring of NB stage buffers.  Inside a buffer row r's 16-byte slot u (K values 8u .. 8u+7
+// of the stage) sits at slot u ^ (r & 15), so the MFMA operand reads are free of bank conflicts.
 // Per 16-K step a wave issues its G * NFW MFMAs, each fragment's followed by the LDS read that
 // refills the same token register for the next step, and decodes its weight fragments of the
 // next step.  The task's n-tiles nt0 .. nt0 + nchain - 1 are taken G at a time (units); a unit
@@ -860,7 +860,8 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
     __syncthreads();
     const int nvalid = *sm.sh_nvalid;
     // the tile list holds local experts and tiles with a routed row only
-    if (nvalid > 0 && e >= 0 && e < a.nloc) run_nfw<EPI>(a, sm, e, nt, nchain, row0, (nvalid + 31) >> 5);
+    if (nvalid > 0 && e >= 0 && e < a.nloc)
+      run_nfw<EPI>(a, sm, e, nt, nchain, row0, (nvalid + 31) >> 5);
     __syncthreads();                         // every thread has read sh_task
     if (tid == 0) *sm.sh_task = resolve(q, ticket);
     __syncthreads();
@@ -922,8 +923,8 @@ __global__ __launch_bounds__(256, OCC) void moe_gemv_kernel(GemmArgs a) {
 
     const int64_t g0 = (int64_t)nt * (4 / KS * FN) + (int64_t)set * FN;
     const bool wave_on = (g0 + FN) * kGroupRows <= a.N;
-    const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes + (wave_on ? g0 : 0) * a.rg_bytes +
-                           lane * 16;
+    const uint8_t* wbase = a.panel + (int64_t)e * a.expert_bytes +
+                           (wave_on ? g0 : 0) * a.rg_bytes + lane * 16;
     uint4 W[RING][kStageChunks][FN];
     uint32_t S[RING][FN];
     auto load_w = [&](uint4 (&Wd)[kStageChunks][FN], uint32_t (&Sd)[FN], int st) {
@@ -952,12 +953,14 @@ __global__ __launch_bounds__(256, OCC) void moe_gemv_kernel(GemmArgs a) {
     if (tid < 32) {
       if (tid < rows_max) {
         const int ent = first ? ent_first : a.sorted[b * a.block_m + tid];
-        if (ent >= 0 && ent < a.sentinel) src = a.gather ? (int)(ent / a.top_k) : (int)(b * a.block_m + tid);
+        if (ent >= 0 && ent < a.sentinel)
+          src = a.gather ? (int)(ent / a.top_k) : (int)(b * a.block_m + tid);
       }
       row_src[tid] = src;
     }
     lds_barrier();
-    const float sc_v = (tid < 32 && src >= 0) ? (a.gather ? a.a_dec[src] : a.a_const_scale) : 0.0f;
+    const float sc_v =
+        (tid < 32 && src >= 0) ? (a.gather ? a.a_dec[src] : a.a_const_scale) : 0.0f;
     // stage the routed rows: per row, its packed bytes in 16-byte units (K/2 is a multiple of
     // 64), then its scale bytes in 8-byte units (K/16 is a multiple of 8); the units of all rows
     // are spread over the threads, two loads in flight per thread before their LDS stores
@@ -1100,10 +1103,26 @@ __device__ __forceinline__ bf8_t decode8_bf16(uint32_t w, uint32_t sf_byte) {
   for (int i = 0; i < 4; ++i) {
     float2 p;
     switch (i) {   // the byte selector must be a compile-time constant
-      case 0: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 0); p = make_float2(v[0], v[1]); break; }
-      case 1: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 1); p = make_float2(v[0], v[1]); break; }
-      case 2: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 2); p = make_float2(v[0], v[1]); break; }
-      default: { const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 3); p = make_float2(v[0], v[1]); break; }
+      case 0: {
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 0);
+        p = make_float2(v[0], v[1]);
+        break;
+      }
+      case 1: {
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 1);
+        p = make_float2(v[0], v[1]);
+        break;
+      }
+      case 2: {
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 2);
+        p = make_float2(v[0], v[1]);
+        break;
+      }
+      default: {
+        const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 3);
+        p = make_float2(v[0], v[1]);
+        break;
+      }
     }
     const bf2_t b2 = {(__bf16)(p.x * s), (__bf16)(p.y * s)};
     r[i] = __builtin_bit_cast(uint32_t, b2);
@@ -1499,7 +1518,8 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_mx_kernel(GemmArgs a) {
     auto load_t = [&](uint4 (&T)[kStageChunks][2], uint32_t& TS, int st) {
 #pragma unroll
       for (int c = 0; c < kStageChunks; ++c) {
-        const uint4* p = reinterpret_cast<const uint4*>(trow + (int64_t)(st * kStageChunks + c) * 64);
+        const uint4* p =
+            reinterpret_cast<const uint4*>(trow + (int64_t)(st * kStageChunks + c) * 64);
         T[c][0] = tok_on ? p[0] : make_uint4(0, 0, 0, 0);
         T[c][1] = tok_on ? p[2] : make_uint4(0, 0, 0, 0);
       }
@@ -1545,7 +1565,8 @@ __global__ __launch_bounds__(256, 4) void moe_gemv_mx_kernel(GemmArgs a) {
       const int64_t r = b * a.block_m + col;
       if (EPI == EPI_DOWN) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) epilogue_group<EPI_DOWN>(a, acc[fn], 1.0f, g0 + fn, h, 1.0f, r);
+        for (int fn = 0; fn < FN; ++fn)
+          epilogue_group<EPI_DOWN>(a, acc[fn], 1.0f, g0 + fn, h, 1.0f, r);
       } else {
         epilogue_mx<EPI>(a, acc[0], acc[1], g0, h, r);
       }

@@ -244,8 +244,9 @@ __global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restri
 
 // Turns the per-chunk histograms into per-chunk starting positions (in place) and writes the
 // plan frame.
-__global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ hist, int64_t nchunks,
-                                                         int64_t A, int nloc, int block_m,
+__global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ hist,
+                                                         int64_t nchunks, int64_t A, int nloc,
+                                                         int block_m,
                                                          int32_t* __restrict__ sorted,
                                                          int32_t* __restrict__ eids,
                                                          int32_t* __restrict__ ntpp, int64_t cap) {
@@ -285,8 +286,9 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ h
   write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
 }
 
-__global__ __launch_bounds__(64) void plan_scatter_kernel(const int32_t* __restrict__ ids, int64_t A,
-                                                          int num_experts, int offset, int nloc,
+__global__ __launch_bounds__(64) void plan_scatter_kernel(const int32_t* __restrict__ ids,
+                                                          int64_t A, int num_experts, int offset,
+                                                          int nloc,
                                                           const int32_t* __restrict__ pos0,
                                                           int32_t* __restrict__ sorted,
                                                           int32_t* __restrict__ ttr) {
