@@ -25,6 +25,7 @@ namespace {
 constexpr int kMaxLocal = 1024;
 constexpr int64_t kSmallMax = 2048;   // slots handled by the single-workgroup kernel
 constexpr int kChunk = 1024;          // slots per chunk in the multi-workgroup path
+constexpr int kScanCache = 24576;     // chunk counts the scan keeps in LDS (16 bits each)
 
 __device__ __forceinline__ int local_id(int32_t id, int num_experts, int offset, int nloc) {
   int e = id - offset;
@@ -251,7 +252,43 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ h
                                                          int32_t* __restrict__ eids,
                                                          int32_t* __restrict__ ntpp, int64_t cap) {
   __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
+  // the chunk counts (each at most kChunk, so 16 bits) when they fit: read once by all threads
+  // with their loads in flight together, instead of twice by one thread per expert
+  __shared__ uint16_t counts[kScanCache];
   int tid = threadIdx.x;
+  const int64_t n = nchunks * nloc;
+  if (n <= kScanCache) {
+    constexpr int kLoads = 8;
+    for (int64_t i0 = tid; i0 < n; i0 += kLoads * 1024) {
+      int v[kLoads];
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) v[j] = i0 + j * 1024 < n ? hist[i0 + j * 1024] : 0;
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j)
+        if (i0 + j * 1024 < n) counts[i0 + j * 1024] = (uint16_t)v[j];
+    }
+    __syncthreads();
+    int c = 0;
+    if (tid < nloc) {
+      for (int64_t g = 0; g < nchunks; ++g) c += counts[g * nloc + tid];
+      cnt[tid] = c;
+    }
+    int seg = (tid < nloc) ? (c + block_m - 1) / block_m * block_m : 0;
+    int P;
+    int excl = block_excl_scan_1024(seg, tmp, P);
+    if (tid < nloc) {
+      start[tid] = excl;
+      int pos = excl;
+      for (int64_t g = 0; g < nchunks; ++g) {
+        const int v = counts[g * nloc + tid];
+        hist[g * nloc + tid] = pos;
+        pos += v;
+      }
+    }
+    __syncthreads();
+    write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
+    return;
+  }
   // the chunk histograms are read kBatch at a time (independent loads in flight together)
   constexpr int kBatch = 16;
   int c = 0;

@@ -121,6 +121,8 @@ PLAN_CASES = [  # (M, top_k, E, offset, nloc, block_m, kind)
     (8192, 8, 256, 0, 256, 128, "distinct"), (8193, 8, 256, 0, 256, 128, "distinct"),
     (700, 8, 600, 40, 512, 8, "noisy"), (700, 8, 600, 40, 513, 8, "noisy"),
     (257, 8, 64, 0, 64, 16, "distinct"),
+    # 32 chunks of slots x 1024 local experts: more chunk counts than the scan keeps in LDS
+    (4096, 8, 1024, 0, 1024, 16, "distinct"),
 ]
 
 
