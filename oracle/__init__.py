@@ -24,7 +24,8 @@ What it computes follows these web pages (cited by page title and section):
   output and of expert outputs; the FP4 weight-only mode (BF16 input, pre-activation and
   intermediate rounding); combine with every FP32 product and sum rounded separately, in slot
   order; expert
-  ids outside the routed range are ignored together with their scores.
+  ids outside the routed range are ignored together with their scores; packed routing scores
+  keep their BF16 rounding (the packed word's layout is a reading stated in ``moe.unpack_routing``).
 
 Where the pages are silent the reading taken is stated next to the code that takes it.
 
@@ -78,6 +79,7 @@ from .moe import (  # noqa: F401
     expert_rows_forward_w16,
     fused_moe_nvfp4,
     fused_moe_w4a16,
+    unpack_routing,
     moe_permute,
     moe_plan,
     plan_capacity,

@@ -86,6 +86,24 @@ def moe_plan(topk_ids, num_experts, local_expert_offset, num_local_experts, bloc
             token_to_row.reshape(M, k).astype(np.int32))
 
 
+def unpack_routing(packed):
+    """Packed routing slots -> (topk_ids int32, topk_weights as BF16 bit patterns uint16).
+
+    CudnnGroupedGemmNvfp4Config, routing weights bullet, accepts routing weights packed as well as
+    unpacked; FrostLowLatencyConfig, numerics paragraph, says packed routing scores keep their BF16
+    rounding.  Neither page gives the bit layout.  Reading used here: one 32-bit word per
+    (token, slot), the score's BF16 bits in the high 16 bits and the expert id as a two's-complement
+    16-bit integer in the low 16 bits (so an empty slot, id -1, has low half 0xFFFF).  The id is
+    sign-extended; the score bits are returned unchanged (their value is the exact FP32 of a BF16,
+    which the combine then uses as it does for unpacked BF16 weights).
+    """
+    w = np.asarray(packed).astype(np.int64) & 0xFFFFFFFF
+    low = w & 0xFFFF
+    ids = np.where(low >= 0x8000, low - 0x10000, low).astype(np.int32)
+    scores = (w >> 16).astype(np.uint16)
+    return ids, scores
+
+
 def routing_violations(topk_ids, num_experts):
     """Breaches of the routing's preconditions (CudnnGroupedGemmNvfp4Config, topk_ids bullet:
     each token's top_k experts are distinct; -1 marks an empty slot).

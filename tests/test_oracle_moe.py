@@ -24,6 +24,7 @@ from synth import WORKLOADS, make_activations, make_routing, make_weights, to_bi
 from synth.workloads import Workload
 
 GOLDEN_COMBINE = os.path.join(os.path.dirname(__file__), "golden", "combine_order.txt")
+GOLDEN_PACKED = os.path.join(os.path.dirname(__file__), "golden", "packed_routing.txt")
 
 
 # ----------------------------------------------------------------------------- plan
@@ -608,3 +609,23 @@ def test_w16_plan_path_equals_per_token_loop(wl):
     dense = oracle.f64_to_bf16_bits(acc.astype(np.float64))
     assert np.array_equal(outs[0], dense)
     assert np.any(outs[0] != 0)
+
+
+def test_golden_packed_routing():
+    """oracle.unpack_routing against hand-derived words (tests/golden/packed_routing.txt): ids
+    sign-extended from the low 16 bits, BF16 score bits from the high 16, values as written."""
+    rows = []
+    with open(GOLDEN_PACKED) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                w, e, sb, v = line.split()
+                rows.append((int(w, 16), int(e), int(sb, 16), float(v)))
+    words = np.array([r[0] for r in rows], dtype=np.uint32).view(np.int32).reshape(1, -1)
+    ids, scores = oracle.unpack_routing(words)
+    assert ids.dtype == np.int32 and scores.dtype == np.uint16
+    assert ids.tolist() == [[r[1] for r in rows]]
+    assert scores.tolist() == [[r[2] for r in rows]]
+    vals = bf16_bits_to_f32(scores[0])
+    for got, (_, _, _, want) in zip(vals, rows):
+        assert (np.isnan(got) and np.isnan(want)) or got == want
+
