@@ -797,6 +797,23 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int w
                                   (hipStream_t)stream));
 }
 
+int bfp4_unpack_routing(const int32_t* packed, int64_t M, int top_k, int32_t* topk_ids,
+                        uint16_t* topk_weights, void* stream) {
+  if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;
+  if (M == 0) return BFP4_OK;
+  if (!packed || !topk_ids || !topk_weights) return BFP4_ERR_NULL;
+  if (!aligned(packed, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 2))
+    return BFP4_ERR_ALIGN;
+  const size_t n = (size_t)M * top_k;
+  if (overlaps(packed, n * 4, topk_ids, n * 4) || overlaps(packed, n * 4, topk_weights, n * 2) ||
+      overlaps(topk_ids, n * 4, topk_weights, n * 2))
+    return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_unpack_routing(packed, (int64_t)n, topk_ids, topk_weights,
+                                        (hipStream_t)stream));
+}
+
 int bfp4_check_topk_ids(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,
                         int32_t* report, void* stream) {
   if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;

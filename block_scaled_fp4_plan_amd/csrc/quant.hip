@@ -207,6 +207,19 @@ __global__ __launch_bounds__(64) void permute_kernel(const uint8_t* __restrict__
   if (threadIdx.x == 0) spd[r] = valid ? dec[t] : 0.0f;
 }
 
+// Packed routing slots -> expert ids and BF16 scores, one thread per slot.  A packed slot is one
+// 32-bit word: the score's BF16 bits in the high half, the expert id as a signed 16-bit integer
+// in the low half (sign-extended here; -1, an empty slot, is 0xFFFF).
+__global__ __launch_bounds__(256) void unpack_routing_kernel(const int32_t* __restrict__ packed,
+                                                             int64_t n, int32_t* __restrict__ ids,
+                                                             uint16_t* __restrict__ weights) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = (uint32_t)packed[i];
+  ids[i] = (int32_t)(int16_t)(uint16_t)(w & 0xFFFFu);
+  weights[i] = (uint16_t)(w >> 16);
+}
+
 // Finalize: one thread per (token, 8 consecutive hidden values).
 // WBF16: the routing weights are BF16 bit patterns, used as their exact FP32 values
 template <bool WBF16>
@@ -320,6 +333,15 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_
     hipLaunchKernelGGL(quantize_rows_kernel<2>, grid, block, 0, s, x, cols, stride, group_rows,
                        fixed, nullptr, q, sf, dec);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_routing(const int32_t* packed, int64_t n, int32_t* ids,
+                                uint16_t* weights, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  KernelTimer t("unpack_routing", s);
+  hipLaunchKernelGGL(unpack_routing_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     packed, n, ids, weights);
   return hipGetLastError();
 }
 

@@ -51,6 +51,9 @@ hipError_t launch_check_plan(const int32_t* sorted, const int32_t* eids, const i
                              int64_t cap, int64_t sentinel, int block_m, int nloc,
                              int32_t* report, hipStream_t s);
 
+hipError_t launch_unpack_routing(const int32_t* packed, int64_t n, int32_t* ids,
+                                uint16_t* weights, hipStream_t s);
+
 hipError_t launch_finalize(const uint16_t* y, const void* w, bool w_bf16, const int32_t* ttr,
                            int64_t M, int64_t H, int top_k, float rsf, uint16_t* out,
                            hipStream_t s);

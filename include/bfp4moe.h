@@ -408,6 +408,25 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int w
                       float routed_scaling_factor, uint16_t* out, void* stream);
 
 /* ----------------------------------------------------------------------------------------------
+ * Unpack packed routing [cuDNN, routing weights bullet: packed, or unpacked FP32 / BF16; Frost,
+ * numerics paragraph: packed routing scores keep their BF16 rounding].  The pages give no bit
+ * layout; a packed slot here is one 32-bit word holding the score's BF16 bits in its high 16 bits
+ * and the expert id as a two's-complement 16-bit integer in its low 16 bits (an empty slot, id
+ * -1, has low half 0xFFFF).
+ *   packed       [M, top_k] int32 (device, 4-byte aligned);
+ *   topk_ids     [M, top_k] int32 out: the ids, sign-extended (device, 4-byte aligned);
+ *   topk_weights [M, top_k] BF16 bit patterns out: the score bits unchanged (device, 2-byte
+ *                aligned).
+ * The outputs are the routing inputs of bfp4_moe_plan / bfp4_moe_plan_quantize and, with
+ * BFP4_WEIGHTS_BF16, of the fused calls and bfp4_moe_finalize; ids outside the routed range are
+ * unrouted slots there whatever their score (NaN included).  The three arrays must not overlap
+ * (checked).  Errors: BFP4_ERR_SHAPE (M < 0, top_k <= 0, M * top_k >= 2^31), BFP4_ERR_NULL,
+ * BFP4_ERR_ALIGN, BFP4_ERR_OVERLAP, BFP4_ERR_DEVICE.  M == 0 returns BFP4_OK and launches nothing.
+ * ---------------------------------------------------------------------------------------------- */
+int bfp4_unpack_routing(const int32_t* packed, int64_t M, int top_k, int32_t* topk_ids,
+                        uint16_t* topk_weights, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
  * Debug validation of device-side preconditions (off the hot path; the other calls never read
  * device memory to validate).  Each call overwrites report[3] (device, int32, 4-byte aligned, not
  * overlapping the inputs) on `stream`; read it back after the stream has reached it.

@@ -317,6 +317,29 @@ def test_check_entry_points_validation():
         assert plan(capacity=0, sorted_token_ids=None, expert_ids=None) == "BFP4_ERR_DEVICE"
 
 
+def test_unpack_routing_validation():
+    def unpack(**kw):
+        args = dict(packed=A, M=4, top_k=2, topk_ids=A + (1 << 16), topk_weights=A + (2 << 16),
+                    stream=0)
+        args.update(kw)
+        with pytest.raises(Bfp4Error) as ei:
+            bf.bfp4_unpack_routing(**args)
+        return bf.STATUS[ei.value.status]
+
+    assert unpack(M=-1) == "BFP4_ERR_SHAPE"
+    assert unpack(top_k=0) == "BFP4_ERR_SHAPE"
+    assert unpack(M=1 << 28, top_k=8) == "BFP4_ERR_SHAPE"        # M * top_k = 2^31
+    assert unpack(packed=None) == "BFP4_ERR_NULL"
+    assert unpack(topk_weights=None) == "BFP4_ERR_NULL"
+    assert unpack(topk_ids=A + (1 << 16) + 2) == "BFP4_ERR_ALIGN"
+    assert unpack(topk_weights=A + (2 << 16) + 1) == "BFP4_ERR_ALIGN"
+    assert unpack(topk_ids=A + 28) == "BFP4_ERR_OVERLAP"          # inside packed [4, 2] int32
+    assert unpack(topk_weights=A + (1 << 16) + 30) == "BFP4_ERR_OVERLAP"   # inside topk_ids
+    assert bf.bfp4_unpack_routing(None, 0, 2, None, None) == 0     # empty: nothing to do
+    if NO_GPU:
+        assert unpack() == "BFP4_ERR_DEVICE"
+
+
 def _pq(**kw):
     args = dict(topk_ids=A, M=16, top_k=2, num_experts=8, local_expert_offset=0,
                 num_local_experts=8, block_m=8, sorted_token_ids=A + 4096, expert_ids=A + 8192,

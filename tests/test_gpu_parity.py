@@ -502,6 +502,49 @@ def test_bf16_routing_weights(bm):
     assert np.any(comb != 0)
 
 
+def test_unpack_routing_bit_exact():
+    """bfp4_unpack_routing ([cuDNN] routing weights bullet; [Frost] numerics paragraph: packed
+    scores keep their BF16 rounding) equals oracle.unpack_routing bit for bit on every word of a
+    random sample and on the edge words (ids -1, -32768, 32767 and past the experts; NaN, infinite,
+    subnormal and negative scores); the unpacked routing of the tiny workload then gives the same
+    output as the BF16-weight call on the oracle's unpacking of the same words."""
+    rng = np.random.default_rng(11)
+    M, k = 1000, 7
+    words = rng.integers(-(1 << 31), 1 << 31, (M, k), dtype=np.int64)
+    edge = np.array([0x3F80FFFF, 0x7FC08000, 0x7F807FFF, 0xFF800010, 0x00010000, 0x80000005,
+                     0xBF800100], dtype=np.uint32).view(np.int32)
+    words[0] = edge
+    words = words.astype(np.int32)
+    ids_d = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((M, k), dtype=torch.int16, device="cuda")
+    bf.bfp4_unpack_routing(torch.from_numpy(words).cuda(), M, k, ids_d, w_d)
+    torch.cuda.synchronize()
+    want_ids, want_w = oracle.unpack_routing(words)
+    assert np.array_equal(ids_d.cpu().numpy(), want_ids)
+    assert np.array_equal(w_d.cpu().numpy().view(np.uint16), want_w)
+
+    wl = WORKLOADS["tiny"]
+    p = Problem(wl)
+    w_bf16 = np_bits(p.w_d.to(torch.bfloat16)).astype(np.int64)
+    packed = ((w_bf16 << 16) | (p.ids.astype(np.int64) & 0xFFFF)).astype(np.uint32).view(np.int32)
+    packed[0, 1] = np.uint32(0x7FC0FFFF).view(np.int32)          # an empty slot with a NaN score
+    ids_g = torch.empty_like(p.ids_d)
+    w_g = torch.empty((p.M, wl.top_k), dtype=torch.bfloat16, device="cuda")
+    bf.bfp4_unpack_routing(torch.from_numpy(packed).cuda(), p.M, wl.top_k, ids_g, w_g)
+    oid, ow = oracle.unpack_routing(packed)
+    pw = runner.prepare_weights(p.w1, p.w2)
+    for bm in (8, 128):
+        fwd = runner.MoeForward(pw, p.M, wl.top_k, wl.E, bm)
+        got = fwd(p.x, ids_g, w_g)
+        torch.cuda.synchronize()
+        got = got.clone()
+        want = fwd(p.x, torch.from_numpy(oid).cuda(),
+                   torch.from_numpy(ow.view(np.int16)).cuda().view(torch.bfloat16))
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+        assert torch.any(got != 0)
+
+
 def test_masked_slots_nan_weights_and_all_masked_token():
     wl = SMALL_SKEWED
     say("masking with NaN weights")
