@@ -420,10 +420,13 @@ def time_w4a16(s, steps, warmup, mxfp4=False):
 
 
 def achievable_context(reps=5):
-    """Achievable-peak context on this GPU: a plain read stream (torch's sum over 4 GiB of FP32),
-    a device copy, and a BF16 GEMM of the prefill's GEMM1 shape through torch.matmul (the vendor
-    BLAS)."""
+    """Achievable-peak context on this GPU: plain read streams over 4 GiB (torch's sum of FP32,
+    and the library's XOR-checksum diagnostic, which reads with the decode GEMMs' 16-byte lane
+    loads), a device copy, and a BF16 GEMM of the prefill's GEMM1 shape through torch.matmul
+    (the vendor BLAS)."""
     import torch
+
+    import block_scaled_fp4_plan_amd as bf
 
     x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
     x.sum()
@@ -433,6 +436,19 @@ def achievable_context(reps=5):
         x.sum()
     torch.cuda.synchronize()
     read_gbs = x.numel() * 4 * reps / (time.perf_counter() - t0) / 1e9
+    partial = torch.zeros(bf.XOR_PARTIALS, dtype=torch.int32, device="cuda")
+    nbytes = x.numel() * 4
+    bf.bfp4_xor_checksum(x, nbytes, partial)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps * 4):
+        bf.bfp4_xor_checksum(x, nbytes, partial)
+    e1.record()
+    torch.cuda.synchronize()
+    xor_gbs = nbytes * reps * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # 2^30 copies of one word: their XOR is zero
+    xor_ok = int(np.bitwise_xor.reduce(partial.cpu().numpy().view(np.uint32))) == 0
     y = torch.empty_like(x)
     y.copy_(x)
     torch.cuda.synchronize()
@@ -455,6 +471,9 @@ def achievable_context(reps=5):
     del a, b
     torch.cuda.empty_cache()
     return {"read_stream_gbs": read_gbs, "read_stream": "torch sum over 4 GiB FP32",
+            "read_stream_lane16_gbs": xor_gbs if xor_ok else None,
+            "read_stream_lane16": "bfp4_xor_checksum over 4 GiB (16-byte loads per lane, four in "
+                                  "flight per wave, 16384 waves)",
             "copy_gbs": copy_gbs, "copy": "torch copy of 4 GiB, bytes read + written",
             "bf16_gemm_tflops": gemm_tf,
             "bf16_gemm": "torch.matmul BF16 %dx%dx%d (vendor BLAS)" % (m, n, k)}

@@ -52,8 +52,9 @@ EXPORTS = [
     "bfp4_fused_moe_w4a16", "bfp4_quantize_mxfp4", "bfp4_prepare_weights_mxfp4",
     "bfp4_check_topk_ids", "bfp4_check_plan", "bfp4_fused_moe_nvfp4_noalloc",
     "bfp4_moe_plan_quantize", "bfp4_quantize_mxfp8", "bfp4_workspace_size_mx", "bfp4_fused_moe_mx",
-    "bfp4_unpack_routing",
+    "bfp4_unpack_routing", "bfp4_xor_checksum",
 ]
+XOR_PARTIALS = 16384                      # BFP4_XOR_PARTIALS
 NOALLOC_SCRATCH_BYTES = 64 << 20          # BFP4_NOALLOC_SCRATCH_BYTES
 
 
@@ -116,6 +117,7 @@ _sig("bfp4_fused_moe_mx", _I,
       _P, ctypes.POINTER(bfp4_debug), _P, _SZ, _P])
 _sig("bfp4_prepare_weights_mxfp4", _I, [_P, _P, _P, _P, _I, _I64, _I64, _I, _P, _SZ, _P])
 _sig("bfp4_unpack_routing", _I, [_P, _I64, _I, _P, _P, _P])
+_sig("bfp4_xor_checksum", _I, [_P, _SZ, _P, _P])
 _sig("bfp4_check_topk_ids", _I, [_P, _I64, _I, _I, _P, _P])
 _sig("bfp4_check_plan", _I, [_P, _P, _P, _SZ, _I64, _I, _I, _I, _P, _P])
 _sig("bfp4_profile_begin", _I, [_I, ctypes.c_char_p])
@@ -326,6 +328,11 @@ def bfp4_moe_finalize(gemm2_out, topk_weights, weights_dtype, token_to_row, M, H
 def bfp4_unpack_routing(packed, M, top_k, topk_ids, topk_weights, stream=None):
     return _check(_lib.bfp4_unpack_routing(_p(packed), M, top_k, _p(topk_ids), _p(topk_weights),
                                            _s(stream)), "bfp4_unpack_routing")
+
+
+def bfp4_xor_checksum(buf, nbytes, partial, stream=None):
+    return _check(_lib.bfp4_xor_checksum(_p(buf), nbytes, _p(partial), _s(stream)),
+                  "bfp4_xor_checksum")
 
 
 def bfp4_check_topk_ids(topk_ids, M, top_k, num_experts, report, stream=None):

@@ -797,6 +797,16 @@ int bfp4_moe_finalize(const uint16_t* gemm2_out, const void* topk_weights, int w
                                   (hipStream_t)stream));
 }
 
+int bfp4_xor_checksum(const void* buf, size_t bytes, uint32_t* partial, void* stream) {
+  if (bytes % 16 || bytes >= (1ULL << 62)) return BFP4_ERR_SHAPE;
+  if (!partial || (bytes && !buf)) return BFP4_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(partial, 4)) return BFP4_ERR_ALIGN;
+  if (overlaps(buf, bytes, partial, (size_t)BFP4_XOR_PARTIALS * 4)) return BFP4_ERR_OVERLAP;
+  int dc = device_check();
+  if (dc) return dc;
+  return launched(launch_xor_checksum(buf, (int64_t)bytes, partial, (hipStream_t)stream));
+}
+
 int bfp4_unpack_routing(const int32_t* packed, int64_t M, int top_k, int32_t* topk_ids,
                         uint16_t* topk_weights, void* stream) {
   if (M < 0 || top_k <= 0 || M * (int64_t)top_k >= (1LL << 31)) return BFP4_ERR_SHAPE;

@@ -51,6 +51,9 @@ hipError_t launch_check_plan(const int32_t* sorted, const int32_t* eids, const i
                              int64_t cap, int64_t sentinel, int block_m, int nloc,
                              int32_t* report, hipStream_t s);
 
+hipError_t launch_xor_checksum(const void* buf, int64_t bytes, uint32_t* partial,
+                               hipStream_t s);
+
 hipError_t launch_unpack_routing(const int32_t* packed, int64_t n, int32_t* ids,
                                 uint16_t* weights, hipStream_t s);
 

@@ -5,6 +5,7 @@
 // (FlashInfer "flashinfer.fused_moe.alphamoe_nvfp4_aligned_moe", plan parameters).  The fused
 // calls do not check these on the device; these kernels count violations into a three-int
 // report that the caller reads back.
+#include "bfp4moe.h"
 #include "runtime.h"
 
 namespace bfp4 {
@@ -67,6 +68,38 @@ __global__ __launch_bounds__(kCheckThreads) void check_plan_kernel(
   }
 }
 
+// XOR checksum of a device buffer, a diagnostic outside the MoE path (the benchmark times it as
+// the HBM read rate a plain stream reaches on the same GPU): kXorWaves waves each read one
+// contiguous slice, 16 bytes per lane per load with kXorDepth loads in flight, and write the XOR
+// of the slice's 32-bit words to partial[wave].
+constexpr int kXorGroups = 4096, kXorWaves = kXorGroups * 4, kXorDepth = 4;
+static_assert(kXorWaves == BFP4_XOR_PARTIALS, "one partial word per wave");
+
+typedef uint32_t xu32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void xor_checksum_kernel(const xu32x4_t* __restrict__ src,
+                                                           int64_t n16, int64_t per_wave,
+                                                           uint32_t* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t base = wave * per_wave;
+  const int64_t end = base + per_wave < n16 ? base + per_wave : n16;
+  uint32_t acc = 0;
+  for (int64_t i = base + lane; i < end; i += 64 * kXorDepth) {
+    xu32x4_t v[kXorDepth];
+#pragma unroll
+    for (int d = 0; d < kXorDepth; ++d) {
+      const int64_t j = i + 64 * d;
+      v[d] = j < end ? src[j] : xu32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int d = 0; d < kXorDepth; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  if (lane == 0) partial[wave] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_check_topk(const int32_t* ids, int64_t M, int top_k, int num_experts,
@@ -98,6 +131,16 @@ hipError_t launch_check_plan(const int32_t* sorted, const int32_t* eids, const i
   const dim3 grid((unsigned)((n + kCheckThreads - 1) / kCheckThreads));
   hipLaunchKernelGGL(check_plan_kernel, grid, dim3(kCheckThreads), 0, s, sorted, eids, ntpp, cap,
                      sentinel, block_m, nloc, report);
+  return hipGetLastError();
+}
+
+hipError_t launch_xor_checksum(const void* buf, int64_t bytes, uint32_t* partial,
+                               hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  const int64_t per_wave = (n16 + kXorWaves - 1) / kXorWaves;
+  KernelTimer t("xor_checksum", s);
+  hipLaunchKernelGGL(xor_checksum_kernel, dim3(kXorGroups), dim3(256), 0, s,
+                     static_cast<const xu32x4_t*>(buf), n16, per_wave, partial);
   return hipGetLastError();
 }
 

@@ -427,6 +427,17 @@ int bfp4_unpack_routing(const int32_t* packed, int64_t M, int top_k, int32_t* to
                         uint16_t* topk_weights, void* stream);
 
 /* ----------------------------------------------------------------------------------------------
+ * Diagnostic outside the MoE path (no page defines it): the XOR of all 32-bit words of a device
+ * buffer, read as a plain stream, which the benchmark times as the HBM read rate the GPU reaches
+ * without any MoE work.  buf [bytes] (device, 16-byte aligned, bytes a multiple of 16);
+ * partial [BFP4_XOR_PARTIALS] uint32 out (device, 4-byte aligned, not overlapping buf): one
+ * word per reading wave, whose XOR is the buffer's.  Errors: BFP4_ERR_SHAPE, BFP4_ERR_NULL,
+ * BFP4_ERR_ALIGN, BFP4_ERR_OVERLAP, BFP4_ERR_DEVICE.
+ * ---------------------------------------------------------------------------------------------- */
+#define BFP4_XOR_PARTIALS 16384
+int bfp4_xor_checksum(const void* buf, size_t bytes, uint32_t* partial, void* stream);
+
+/* ----------------------------------------------------------------------------------------------
  * Debug validation of device-side preconditions (off the hot path; the other calls never read
  * device memory to validate).  Each call overwrites report[3] (device, int32, 4-byte aligned, not
  * overlapping the inputs) on `stream`; read it back after the stream has reached it.

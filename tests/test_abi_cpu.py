@@ -340,6 +340,24 @@ def test_unpack_routing_validation():
         assert unpack() == "BFP4_ERR_DEVICE"
 
 
+def test_xor_checksum_validation():
+    def xs(**kw):
+        args = dict(buf=A, nbytes=4096, partial=A + (1 << 20), stream=0)
+        args.update(kw)
+        with pytest.raises(Bfp4Error) as ei:
+            bf.bfp4_xor_checksum(**args)
+        return bf.STATUS[ei.value.status]
+
+    assert xs(nbytes=4100) == "BFP4_ERR_SHAPE"                  # not a multiple of 16
+    assert xs(partial=None) == "BFP4_ERR_NULL"
+    assert xs(buf=None) == "BFP4_ERR_NULL"
+    assert xs(buf=A + 8) == "BFP4_ERR_ALIGN"
+    assert xs(partial=A + (1 << 20) + 2) == "BFP4_ERR_ALIGN"
+    assert xs(partial=A + 4092) == "BFP4_ERR_OVERLAP"
+    if NO_GPU:
+        assert xs() == "BFP4_ERR_DEVICE"
+
+
 def _pq(**kw):
     args = dict(topk_ids=A, M=16, top_k=2, num_experts=8, local_expert_offset=0,
                 num_local_experts=8, block_m=8, sorted_token_ids=A + 4096, expert_ids=A + 8192,

@@ -15,6 +15,7 @@ from gpu_common import say
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
+    import block_scaled_fp4_plan_amd as bf
     from block_scaled_fp4_plan_amd import runner
 
 
@@ -85,3 +86,20 @@ def test_check_plan_matches_oracle(name, bm):
         say("extent", ext, "expected", exp, "got", got)
         assert got == exp, ext
     assert oracle.plan_violations(srt, eids, P, cap, M, k, nloc, bm)[:2] == (2, 1)
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000003, 64 << 20])
+def test_xor_checksum_matches_numpy(nbytes):
+    """bfp4_xor_checksum (the benchmark's read-stream diagnostic): the XOR of its partial words
+    equals numpy's XOR of every 32-bit word of the buffer, for sizes that do and do not divide
+    evenly over its reading waves."""
+    say("xor checksum", nbytes)
+    rng = np.random.default_rng(nbytes % 1000)
+    host = rng.integers(0, 1 << 32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    partial = torch.zeros(bf.XOR_PARTIALS, dtype=torch.int32, device="cuda")
+    bf.bfp4_xor_checksum(buf, nbytes, partial)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(partial.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
+
