@@ -495,7 +495,7 @@ def kernel_rooflines(wl, s, breakdown):
     work = {
         "plan": ("latency", M * k * 12),                  # id read, plan entry, token_to_row
         "quantize_rows": ("hbm", M * H * 2 + M * H * q + M * 4),
-        "decode_tokens": ("hbm", M * H * (q + 2)),
+        "tile_list_decode_tokens": ("hbm", M * H * (q + 2)),   # the FP16 token copy's bytes
         "tile_list": ("latency", 0),
         "gemm1_%s_decode" % wl.act: ("hbm", gemm_bytes(wl, s.touched, A, 1)),
         "gemm2_down_decode": ("hbm", gemm_bytes(wl, s.touched, A, 2)),

@@ -198,7 +198,7 @@ constexpr bool one_projection(int epi) { return epi == EPI_RELU2 || epi == EPI_A
 //     (counting sort) and interleaved longest / shortest for the dynamic schedule of the GEMMs;
 //  3. the GEMMs' per-XCD ticket counters are cleared.
 // tmp holds max_tiles int2 + max_tiles int; tiles max_tiles int2.
-__global__ __launch_bounds__(1024) void tile_list_kernel(
+__device__ void tile_list_body(
     const int32_t* __restrict__ eids, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ ntpp, int64_t cap, int block_m, int64_t sentinel, int nloc,
     int2* __restrict__ tmp, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles,
@@ -305,17 +305,41 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(
   }
 }
 
-// Exact FP16 copy of NVFP4 rows (E2M1 x E4M3, without the row's FP32 decode scale): one thread
-// per 8 values.
-__global__ void decode_rows_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sf,
-                                   int64_t n8, int64_t cols, uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const int64_t v0 = i * 8;                   // first value; 8 values never straddle a row
+__global__ __launch_bounds__(1024) void tile_list_kernel(
+    const int32_t* __restrict__ eids, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ ntpp, int64_t cap, int block_m, int64_t sentinel, int nloc,
+    int2* __restrict__ tmp, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    uint32_t* __restrict__ counters) {
+  tile_list_body(eids, sorted, ntpp, cap, block_m, sentinel, nloc, tmp, tiles, n_tiles, counters);
+}
+
+// Exact FP16 copy of NVFP4 rows (E2M1 x E4M3, without the row's FP32 decode scale) for the
+// values v0 = 8 i .. 8 i + 7 (8 values never straddle a row).
+__device__ __forceinline__ void decode_rows_unit(const uint8_t* __restrict__ q,
+                                                 const uint8_t* __restrict__ sf, int64_t i,
+                                                 uint16_t* __restrict__ out) {
+  const int64_t v0 = i * 8;
   const uint32_t w = *reinterpret_cast<const uint32_t*>(q + (v0 >> 1));
   const uint32_t sb = sf[v0 >> 4];
-  (void)cols;
   *reinterpret_cast<h8_t*>(out + v0) = decode8(w, e4m3_scale_h2(sb));
+}
+
+// The NVFP4 prefill's two preparations of GEMM1 in one launch, as they are independent:
+// workgroup 0 builds the tile list (tile_list_body), workgroup 1 + j decodes the activation
+// values 8192 j .. 8192 j + 8191 into their exact FP16 copy (one thread per 8 values).
+__global__ __launch_bounds__(1024) void tile_list_decode_kernel(
+    const int32_t* __restrict__ eids, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ ntpp, int64_t cap, int block_m, int64_t sentinel, int nloc,
+    int2* __restrict__ tmp, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    uint32_t* __restrict__ counters, const uint8_t* __restrict__ q,
+    const uint8_t* __restrict__ sf, int64_t n8, uint16_t* __restrict__ out) {
+  if (blockIdx.x == 0) {
+    tile_list_body(eids, sorted, ntpp, cap, block_m, sentinel, nloc, tmp, tiles, n_tiles,
+                   counters);
+    return;
+  }
+  const int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x;
+  if (i < n8) decode_rows_unit(q, sf, i, out);
 }
 
 struct Smem {
@@ -2092,17 +2116,11 @@ hipError_t launch_moe_gemms(const MoeGemmProblem& p, hipStream_t s) {
     g1.n_tiles = n_tiles;
     g1.task_counter = counters;
     const int64_t n8 = p.M * (p.H / 8);
-    if (n8 > 0) {
-      KernelTimer t("decode_tokens", s);
-      hipLaunchKernelGGL(decode_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
-                         p.a_q, p.a_sf, n8, p.H, p.a16);
-      hipError_t err = hipGetLastError();
-      if (err != hipSuccess) return err;
-    }
-    KernelTimer t("tile_list", s);
-    hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(1024), 0, s, p.eids, p.sorted, p.ntpp, p.cap,
-                       p.block_m, (int64_t)(p.M * p.top_k), p.nloc, tile_tmp, tiles, n_tiles,
-                       counters);
+    KernelTimer t("tile_list_decode_tokens", s);
+    hipLaunchKernelGGL(tile_list_decode_kernel, dim3((unsigned)(1 + (n8 + 1023) / 1024)),
+                       dim3(1024), 0, s, p.eids, p.sorted, p.ntpp, p.cap, p.block_m,
+                       (int64_t)(p.M * p.top_k), p.nloc, tile_tmp, tiles, n_tiles, counters,
+                       p.a_q, p.a_sf, n8, p.a16);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
