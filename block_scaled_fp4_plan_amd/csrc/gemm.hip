@@ -153,7 +153,7 @@ struct GemmArgs {
   int64_t cap;
   int64_t sentinel;
   int top_k, block_m, nloc;
-  const int2* tiles;         // prefill tiles {first row, rows}, longest and shortest alternating
+  const int2* tiles;         // prefill tiles {first row, rows}, ordered by length
   const int32_t* n_tiles;
   uint32_t* task_counter;    // prefill: one ticket counter per XCD queue (cleared by the tile list)
   // weights
@@ -195,14 +195,16 @@ constexpr bool one_projection(int epi) { return epi == EPI_RELU2 || epi == EPI_A
 //     blocks of one local expert segment (aligned to the segment's first block); otherwise
 //     kTileRows-row slices of each block of a local expert;
 //  2. each tile's token-fragment count (up to its last routed row), tiles ranked by it
-//     (counting sort) and interleaved longest / shortest for the dynamic schedule of the GEMMs;
+//     (counting sort) and handed to the dynamic schedule of the GEMMs either longest first
+//     (the FP16-MFMA kernels) or interleaved longest / shortest (the MX kernels), whichever
+//     measured faster for each;
 //  3. the GEMMs' per-XCD ticket counters are cleared.
 // tmp holds max_tiles int2 + max_tiles int; tiles max_tiles int2.
 __device__ void tile_list_body(
     const int32_t* __restrict__ eids, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ ntpp, int64_t cap, int block_m, int64_t sentinel, int nloc,
     int2* __restrict__ tmp, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-    uint32_t* __restrict__ counters) {
+    uint32_t* __restrict__ counters, bool longest_first) {
   __shared__ int scan[1024];
   __shared__ int carry_start, carry_count;
   __shared__ int hist[9], offs[9];
@@ -294,13 +296,14 @@ __device__ void tile_list_body(
     for (int c = 0; c < 2 * kXcds; ++c) counters[c] = 0u;
   }
   __syncthreads();
-  // rank r in decreasing fragment count -> position: the longest and the shortest tiles
-  // alternate (r0, r(n-1), r1, r(n-2), ...), so that the tasks in flight at any time mix
+  // rank r in decreasing fragment count -> position: r itself (the long tiles first, so the
+  // short ones fill the end of the schedule), or the longest and the shortest tiles
+  // alternating (r0, r(n-1), r1, r(n-2), ...), so that the tasks in flight at any time mix
   // MFMA-bound and weight-streaming-bound tiles
   const int n = offs[0];
   for (int t = tid; t < nt_all; t += 1024) {
     const int r = atomicAdd(&offs[nfw_of[t]], 1);
-    const int pos = (r < (n + 1) / 2) ? 2 * r : 2 * (n - 1 - r) + 1;
+    const int pos = longest_first ? r : (r < (n + 1) / 2) ? 2 * r : 2 * (n - 1 - r) + 1;
     tiles[pos] = tmp[t];
   }
 }
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(
     const int32_t* __restrict__ ntpp, int64_t cap, int block_m, int64_t sentinel, int nloc,
     int2* __restrict__ tmp, int2* __restrict__ tiles, int32_t* __restrict__ n_tiles,
     uint32_t* __restrict__ counters) {
-  tile_list_body(eids, sorted, ntpp, cap, block_m, sentinel, nloc, tmp, tiles, n_tiles, counters);
+  tile_list_body(eids, sorted, ntpp, cap, block_m, sentinel, nloc, tmp, tiles, n_tiles, counters,
+                 false);
 }
 
 // Exact FP16 copy of NVFP4 rows (E2M1 x E4M3, without the row's FP32 decode scale) for the
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(1024) void tile_list_decode_kernel(
     const uint8_t* __restrict__ sf, int64_t n8, uint16_t* __restrict__ out) {
   if (blockIdx.x == 0) {
     tile_list_body(eids, sorted, ntpp, cap, block_m, sentinel, nloc, tmp, tiles, n_tiles,
-                   counters);
+                   counters, true);
     return;
   }
   const int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x;
@@ -824,8 +828,8 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_kernel(GemmArgs a) {
       (int64_t)n_tiles * a.n_nt < (int64_t)kMinTasksPerCu * kCus * chain)
     chain = 2;
   const int n_ct = (a.n_nt + chain - 1) / chain;
-  // queue x holds tiles x, x + 8, ... (the tile list alternates long and short tiles, so every
-  // queue gets a similar mix); workgroups of XCD x (dispatch places workgroup i on XCD i % 8)
+  // queue x holds tiles x, x + 8, ... (the tile list is ordered by length, so every queue gets
+  // a similar mix); workgroups of XCD x (dispatch places workgroup i on XCD i % 8)
   // take tasks from queue x, so a tile's n-tile tasks share one L2, and move on to the next
   // queues when theirs is empty.  Thread 0 keeps the current queue in q.
   auto q_tasks = [&](int qq) -> int64_t {

@@ -123,6 +123,9 @@ PLAN_CASES = [  # (M, top_k, E, offset, nloc, block_m, kind)
     (257, 8, 64, 0, 64, 16, "distinct"),
     # 32 chunks of slots x 1024 local experts: more chunk counts than the scan keeps in LDS
     (4096, 8, 1024, 0, 1024, 16, "distinct"),
+    # chunk counts kept in LDS, split over 3 threads per expert (71 chunks) and over all 1024
+    # threads for a single local expert (69 chunks, most threads with none)
+    (9000, 8, 300, 0, 300, 64, "zipf"), (70000, 1, 4, 0, 1, 8, "noisy"),
 ]
 
 
