@@ -94,11 +94,14 @@ MX_WORKLOADS.update({
     "ragged_mx": RAGGED_MX,
     "ragged_mx_relu2": dataclasses.replace(RAGGED_MX, name="ragged_mx_relu2", act="relu2"),
     "skewed_mx_tiled": dataclasses.replace(SKEWED_MX, name="skewed_mx_tiled", M=700, block_m=128),
+    # one expert with about 98 % of the tokens: a segment of five tiles
+    "hot_expert_mx": Workload("hot_expert_mx", M=1100, H=256, I=128, E=4, top_k=1, block_m=128,
+                              routing="zipf", zipf_s=6.0),
 })
 MX_CASES = [("tiny", 8), ("decode_ll", 8), ("skewed_mx", 16), ("one_token", 8),
             ("tiny_geglu", 16), ("ll_gelu", 8), ("wide", 32), ("tiny", 32),
             ("tiny", 128), ("ragged_mx", 128), ("ragged_mx_relu2", 128), ("skewed_mx_tiled", 128),
-            ("one_token", 128), ("tiny_geglu", 136)]
+            ("one_token", 128), ("tiny_geglu", 136), ("hot_expert_mx", 128)]
 
 
 def _workload(name):

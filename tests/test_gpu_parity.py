@@ -289,6 +289,12 @@ LDS_LIMIT = Workload("lds_limit", M=40, H=8960, I=128, E=4, top_k=2, block_m=32)
 # in parts of unequal length (GEMM1: 10 stages of 128 over 4 waves; GEMM2: 5 over 2)
 KS_RAGGED = Workload("ks_ragged", M=3, H=1280, I=640, E=12, top_k=3, block_m=8)
 
+# one expert takes about 98 % of the tokens (Zipf exponent 6 over 4 experts): its segment spans
+# five tiles of up to 256 rows, handed out one after another from the tile list beside the
+# other experts' short tiles
+HOT_EXPERT = Workload("hot_expert", M=1100, H=256, I=128, E=4, top_k=1, block_m=128,
+                      routing="zipf", zipf_s=6.0)
+
 # the other activations, on the decode (block_m 8, 16) and the tiled (block_m 128) kernels
 ACT_WORKLOADS = {
     "tiny_geglu": dataclasses.replace(WORKLOADS["tiny"], name="tiny_geglu", act="geglu"),
@@ -308,14 +314,15 @@ MOE_CASES = [
     ("gelu", 8), ("gelu", 128), ("relu", 16), ("relu", 128), ("silu", 8), ("silu", 128),
     ("identity", 8), ("identity", 128), ("skewed_gelu", 16),
     ("one_token", 8), ("one_token", 128), ("wide_topk", 16), ("wide_topk", 128), ("lds_limit", 32),
-    ("ks_ragged", 8),
+    ("ks_ragged", 8), ("hot_expert", 128), ("hot_expert", 8),
 ]
 
 
 def _workload(name):
     return ({"skewed_small": SMALL_SKEWED, "tiny_relu2": TINY_RELU2, "ragged_k": RAGGED_K,
              "chain_n": CHAIN_N, "one_token": ONE_TOKEN, "wide_topk": WIDE_TOPK,
-             "lds_limit": LDS_LIMIT, "ks_ragged": KS_RAGGED, **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
+             "lds_limit": LDS_LIMIT, "ks_ragged": KS_RAGGED, "hot_expert": HOT_EXPERT,
+             **ACT_WORKLOADS}.get(name) or WORKLOADS[name])
 
 
 def check_gemm2(p, eids, bm, rows, dbg, y, c2=1.0, max_flip_frac=0.01):
