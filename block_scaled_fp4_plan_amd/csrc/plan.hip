@@ -25,6 +25,7 @@ namespace {
 constexpr int kMaxLocal = 1024;
 constexpr int64_t kSmallMax = 2048;   // slots handled by the single-workgroup kernel
 constexpr int kChunk = 1024;          // slots per chunk in the multi-workgroup path
+constexpr int kScatterWaves = 4;      // waves ranking one chunk's slots in the scatter
 constexpr int kScanCache = 24576;     // chunk counts the scan keeps in LDS (16 bits each)
 
 __device__ __forceinline__ int local_id(int32_t id, int num_experts, int offset, int nloc) {
@@ -323,29 +324,47 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ h
   write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
 }
 
-__global__ __launch_bounds__(64) void plan_scatter_kernel(const int32_t* __restrict__ ids,
-                                                          int64_t A, int num_experts, int offset,
-                                                          int nloc,
-                                                          const int32_t* __restrict__ pos0,
-                                                          int32_t* __restrict__ sorted,
-                                                          int32_t* __restrict__ ttr) {
-  __shared__ int run[kMaxLocal];
-  // the chunk's starting positions, 4 loads in flight per lane
-  for (int e0 = threadIdx.x; e0 < nloc; e0 += 4 * 64) {
-    int v[4];
+// Ranks and scatters the slots of chunk blockIdx.x: wave w takes the slots of quarter w of the
+// chunk, starting each local expert at the chunk's position plus the counts of the earlier
+// quarters, so that the slots still land in ascending order within each expert.
+__global__ __launch_bounds__(64 * kScatterWaves) void plan_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t A, int num_experts, int offset, int nloc,
+    const int32_t* __restrict__ pos0, int32_t* __restrict__ sorted, int32_t* __restrict__ ttr) {
+  __shared__ int run[kScatterWaves * kMaxLocal];
+  constexpr int kThreads = 64 * kScatterWaves, kSub = kChunk / kScatterWaves;
+  static_assert(kSub == kThreads, "one slot of each quarter per thread in the count");
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int64_t f0 = (int64_t)blockIdx.x * kChunk;
+  const int64_t f1 = f0 + kChunk < A ? f0 + kChunk : A;
+  for (int i = tid; i < kScatterWaves * nloc; i += kThreads) run[i] = 0;
+  // the local ids of slot f0 + tid of every quarter, loads in flight together
+  int ev[kScatterWaves];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 64 * i;
-      v[i] = e < nloc ? pos0[(int64_t)blockIdx.x * nloc + e] : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (e0 + 64 * i < nloc) run[e0 + 64 * i] = v[i];
+  for (int q = 0; q < kScatterWaves; ++q) {
+    const int64_t f = f0 + (int64_t)q * kSub + tid;
+    ev[q] = f < f1 ? ids[f] : -1;
   }
   __syncthreads();
-  int64_t f0 = (int64_t)blockIdx.x * kChunk;
-  int64_t f1 = f0 + kChunk < A ? f0 + kChunk : A;
-  scatter_wave(ids, f0, f1, num_experts, offset, nloc, run, sorted, ttr);
+#pragma unroll
+  for (int q = 0; q < kScatterWaves; ++q) {
+    const int e = local_id(ev[q], num_experts, offset, nloc);
+    if (e >= 0) atomicAdd(&run[q * nloc + e], 1);
+  }
+  __syncthreads();
+  // counts -> starting positions of each quarter, per expert
+  for (int e = tid; e < nloc; e += kThreads) {
+    int p = pos0[(int64_t)blockIdx.x * nloc + e];
+#pragma unroll
+    for (int q = 0; q < kScatterWaves; ++q) {
+      const int c = run[q * nloc + e];
+      run[q * nloc + e] = p;
+      p += c;
+    }
+  }
+  __syncthreads();
+  const int64_t s0 = f0 + (int64_t)w * kSub;
+  const int64_t s1 = s0 + kSub < f1 ? s0 + kSub : f1;
+  if (s0 < s1) scatter_wave(ids, s0, s1, num_experts, offset, nloc, run + w * nloc, sorted, ttr);
 }
 
 }  // namespace
@@ -388,8 +407,8 @@ hipError_t launch_plan(const int32_t* ids, int64_t A, int top_k, int num_experts
                        sorted, eids, ntpp, cap);
   }
   KernelTimer t("plan_scatter", s);
-  hipLaunchKernelGGL(plan_scatter_kernel, dim3((unsigned)nch), dim3(64), 0, s, ids, A, num_experts,
-                     offset, nloc, hist, sorted, ttr);
+  hipLaunchKernelGGL(plan_scatter_kernel, dim3((unsigned)nch), dim3(64 * kScatterWaves), 0, s, ids,
+                     A, num_experts, offset, nloc, hist, sorted, ttr);
   return hipGetLastError();
 }
 
