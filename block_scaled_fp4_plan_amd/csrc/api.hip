@@ -325,7 +325,8 @@ size_t bfp4_plan_workspace_size(int64_t M, int top_k, int num_local_experts) {
   if (M < 0 || top_k <= 0 || num_local_experts <= 0) return 0;
   int64_t A = M * top_k;
   if (plan_uses_small_kernel(A)) return 0;
-  return (size_t)(plan_chunks(A) * num_local_experts * sizeof(int32_t));
+  // one count per chunk and local expert, then each local expert's count and segment start
+  return (size_t)((plan_chunks(A) + 2) * num_local_experts * sizeof(int32_t));
 }
 
 int bfp4_moe_plan(const int32_t* topk_ids, int64_t M, int top_k, int num_experts,

@@ -244,14 +244,13 @@ __global__ __launch_bounds__(256) void plan_count_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e < nloc; e += 256) hist[(int64_t)blockIdx.x * nloc + e] = h[e];
 }
 
-// Turns the per-chunk histograms into per-chunk starting positions (in place) and writes the
-// plan frame.
+// Turns the per-chunk histograms into per-chunk starting positions (in place), writes the
+// extent and publishes each local expert's count and segment start (fr[e], fr[nloc + e]) for
+// the scatter's workgroups, which write the rest of the plan frame.
 __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ hist,
-                                                         int64_t nchunks, int64_t A, int nloc,
-                                                         int block_m,
-                                                         int32_t* __restrict__ sorted,
-                                                         int32_t* __restrict__ eids,
-                                                         int32_t* __restrict__ ntpp, int64_t cap) {
+                                                         int64_t nchunks, int nloc, int block_m,
+                                                         int32_t* __restrict__ fr,
+                                                         int32_t* __restrict__ ntpp) {
   __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
   // the chunk counts (each at most kChunk, so 16 bits) when they fit: read once by all threads
   // with their loads in flight together, instead of twice by one thread per expert
@@ -285,9 +284,10 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ h
         hist[g * nloc + tid] = pos;
         pos += v;
       }
+      fr[tid] = c;
+      fr[nloc + tid] = excl;
     }
-    __syncthreads();
-    write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
+    if (tid == 0) *ntpp = P;
     return;
   }
   // the chunk histograms are read kBatch at a time (independent loads in flight together)
@@ -319,17 +319,22 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int32_t* __restrict__ h
         pos += v[i];
       }
     }
+    fr[tid] = c;
+    fr[nloc + tid] = excl;
   }
-  __syncthreads();
-  write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
+  if (tid == 0) *ntpp = P;
 }
 
 // Ranks and scatters the slots of chunk blockIdx.x: wave w takes the slots of quarter w of the
 // chunk, starting each local expert at the chunk's position plus the counts of the earlier
-// quarters, so that the slots still land in ascending order within each expert.
+// quarters, so that the slots still land in ascending order within each expert.  The
+// workgroups also share out the plan frame (expert_ids, the padding entries of every segment,
+// the sentinel tail up to the capacity) from the counts and starts the scan published in fr.
 __global__ __launch_bounds__(64 * kScatterWaves) void plan_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t A, int num_experts, int offset, int nloc,
-    const int32_t* __restrict__ pos0, int32_t* __restrict__ sorted, int32_t* __restrict__ ttr) {
+    const int32_t* __restrict__ pos0, const int32_t* __restrict__ fr,
+    const int32_t* __restrict__ ntpp, int block_m, int64_t cap, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ eids, int32_t* __restrict__ ttr) {
   __shared__ int run[kScatterWaves * kMaxLocal];
   constexpr int kThreads = 64 * kScatterWaves, kSub = kChunk / kScatterWaves;
   static_assert(kSub == kThreads, "one slot of each quarter per thread in the count");
@@ -365,6 +370,38 @@ __global__ __launch_bounds__(64 * kScatterWaves) void plan_scatter_kernel(
   const int64_t s0 = f0 + (int64_t)w * kSub;
   const int64_t s1 = s0 + kSub < f1 ? s0 + kSub : f1;
   if (s0 < s1) scatter_wave(ids, s0, s1, num_experts, offset, nloc, run + w * nloc, sorted, ttr);
+
+  // plan frame.  Expert e = blockIdx.x + gridDim.x * (w + kScatterWaves * k) goes to wave w of
+  // this workgroup: its lanes read the counts and starts of 64 such experts at a time, then the
+  // wave writes each segment's block ids and padding entries with consecutive lanes on
+  // consecutive words.
+  const int lane = tid & 63;
+  const int sentinel = (int)A;
+  const int64_t stride_e = (int64_t)gridDim.x * kScatterWaves;
+  for (int64_t k0 = 0; blockIdx.x + (int64_t)gridDim.x * w + stride_e * k0 < nloc; k0 += 64) {
+    const int64_t el = blockIdx.x + (int64_t)gridDim.x * w + stride_e * (k0 + lane);
+    const int c_l = el < nloc ? fr[el] : 0;
+    const int s_l = el < nloc ? fr[nloc + el] : 0;
+    for (int j = 0; j < 64; ++j) {
+      const int64_t e = blockIdx.x + (int64_t)gridDim.x * w + stride_e * (k0 + j);
+      if (e >= nloc) break;
+      const int c = __builtin_amdgcn_readlane(c_l, j);
+      if (c == 0) continue;
+      const int st = __builtin_amdgcn_readlane(s_l, j);
+      const int seg = (c + block_m - 1) / block_m * block_m;
+      for (int b = st / block_m + lane; b < (st + seg) / block_m; b += 64) eids[b] = (int)e;
+      for (int q = st + c + lane; q < st + seg; q += 64) sorted[q] = sentinel;
+    }
+  }
+  // the tail past the extent P, in one slice per workgroup
+  const int64_t P = *ntpp;
+  const int64_t nb0 = P / block_m, nb1 = cap / block_m;
+  const int64_t bl = (nb1 - nb0 + gridDim.x - 1) / gridDim.x;
+  const int64_t b_lo = nb0 + bl * blockIdx.x, b_hi = b_lo + bl < nb1 ? b_lo + bl : nb1;
+  for (int64_t b = b_lo + tid; b < b_hi; b += kThreads) eids[b] = -1;
+  const int64_t pl = (cap - P + gridDim.x - 1) / gridDim.x;
+  const int64_t p_lo = P + pl * blockIdx.x, p_hi = p_lo + pl < cap ? p_lo + pl : cap;
+  for (int64_t p = p_lo + tid; p < p_hi; p += kThreads) sorted[p] = sentinel;
 }
 
 }  // namespace
@@ -403,12 +440,13 @@ hipError_t launch_plan(const int32_t* ids, int64_t A, int top_k, int num_experts
   }
   {
     KernelTimer t("plan_scan", s);
-    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nch, A, nloc, block_m,
-                       sorted, eids, ntpp, cap);
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nch, nloc, block_m,
+                       hist + nch * nloc, ntpp);
   }
   KernelTimer t("plan_scatter", s);
   hipLaunchKernelGGL(plan_scatter_kernel, dim3((unsigned)nch), dim3(64 * kScatterWaves), 0, s, ids,
-                     A, num_experts, offset, nloc, hist, sorted, ttr);
+                     A, num_experts, offset, nloc, hist, hist + nch * nloc, ntpp, block_m, cap,
+                     sorted, eids, ttr);
   return hipGetLastError();
 }
 
