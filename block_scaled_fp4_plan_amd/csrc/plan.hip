@@ -148,6 +148,7 @@ __device__ void plan_small(const int32_t* __restrict__ ids, int64_t A, int num_e
                            int32_t* __restrict__ ttr, int64_t cap) {
   __shared__ int cnt[kMaxLocal], start[kMaxLocal], tmp[1024];
   __shared__ int32_t sid[kSmallMax];          // the ids, read from memory once
+  __shared__ int run[kMaxLocal];               // the scatter's running positions
   int tid = threadIdx.x;
   if (tid < nloc) cnt[tid] = 0;
   __syncthreads();
@@ -161,11 +162,16 @@ __device__ void plan_small(const int32_t* __restrict__ ids, int64_t A, int num_e
   int seg = (tid < nloc) ? (cnt[tid] + block_m - 1) / block_m * block_m : 0;
   int P;
   int excl = block_excl_scan_1024(seg, tmp, P);
-  if (tid < nloc) start[tid] = excl;
+  if (tid < nloc) {
+    start[tid] = excl;
+    run[tid] = excl;
+  }
   __syncthreads();
+  // wave 0 scatters (advancing its own copy of the starts) while the other waves write the
+  // frame, whose padding entries and tail the scatter never touches; wave 0 writes its share of
+  // the frame afterwards
+  if (tid < 64) scatter_wave(sid, 0, A, num_experts, offset, nloc, run, sorted, ttr);
   write_plan_frame(cnt, start, nloc, block_m, P, cap, (int32_t)A, sorted, eids, ntpp);
-  __syncthreads();
-  if (tid < 64) scatter_wave(sid, 0, A, num_experts, offset, nloc, start, sorted, ttr);
 }
 
 __global__ __launch_bounds__(1024) void plan_small_kernel(
